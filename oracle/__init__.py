@@ -1,0 +1,15 @@
+"""CPU reference (oracle) for SwiAttn routed dual-branch attention.
+
+TEST INFRASTRUCTURE: only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  It shares no code with the HIP
+library and imports nothing from it.
+"""
+from .swiattn_ref import (  # noqa: F401
+    attend_rows,
+    compact,
+    decode,
+    full_key_range,
+    prefill,
+    route,
+    swa_key_range,
+)

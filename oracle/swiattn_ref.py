@@ -1,0 +1,268 @@
+"""SwiAttn routed dual-branch attention: plain CPU reference in float64.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke
+check of the package entry file and the CPU-baseline leg of the benchmark
+may import or call this module.  The HIP library never routes through it,
+and this module imports nothing from the HIP package (it shares no code,
+tables or helpers with it).
+
+Sources (cited by page title and section):
+  [SwiAttn]  paper-daily report on SwiAttn (Peking University),
+             section 2 "方法详解" (router, hard gate with STE, the two branches
+             and their gated combination, shared KV cache in decode, adaptive
+             regulariser).
+  [Glossary] weimeta glossary "滑窗注意力 Sliding Window Attention 是什么？",
+             section "详细解释" (the SWA key set), the W=4 visualisation table,
+             and the FAQ entry on W equal to the context length.
+
+Every floating-point step runs in float64 on the values the caller passes
+(bf16 or fp32 values decoded exactly).  Readings taken where the pages leave
+a step open are marked "Reading:" in the docstrings.
+
+Pins: every function below is checked by the CPU tests against something
+other than itself (the printed W=4 table, W>=N equals causal attention,
+W=1 returns V, all-ones / all-zeros gates against torch's CPU
+scaled_dot_product_attention in float64, a pure-Python brute force on tiny
+inputs, closed forms for the router, decode equal to the last prefill row).
+No function here is parity-unpinned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "route",
+    "compact",
+    "swa_key_range",
+    "full_key_range",
+    "attend_rows",
+    "prefill",
+    "decode",
+]
+
+NEAR_THRESHOLD = 1e-5
+
+
+# ---------------------------------------------------------------------------
+# Router  ([SwiAttn] section 2, router paragraph)
+# ---------------------------------------------------------------------------
+def route(H, r, bias):
+    """Per-token router: a linear map of the hidden state, a sigmoid, then a
+    hard threshold at 0.5.
+
+    [SwiAttn] section 2: the soft gate is sigmoid(R(H)) with R linear; the
+    forward value of the straight-through estimator is the 0/1 indicator of
+    soft gate > 0.5 (the sigmoid term and its stop-gradient copy cancel in
+    value, so the forward value is the indicator itself).
+
+    Reading: R(H) = H.r + bias with r of shape [hidden, G] (one logit per
+    gate group).  The threshold is strict, so a logit of exactly 0 routes to
+    the window branch.
+
+    H [B,N,hidden], r [hidden,G], bias [G]  ->  dict with
+      z    float64 [B,N,G]  router logits
+      soft float64 [B,N,G]  sigmoid(z)
+      gate uint8   [B,N,G]  1 = full branch, 0 = window branch
+      near bool    [B,N,G]  |z| < 1e-5 (either decision is acceptable there)
+    """
+    Hd = np.asarray(H, dtype=np.float64)
+    rd = np.asarray(r, dtype=np.float64)
+    bd = np.asarray(bias, dtype=np.float64)
+    z = Hd @ rd + bd  # [B,N,G]
+    with np.errstate(over="ignore"):
+        soft = 1.0 / (1.0 + np.exp(-z))
+    gate = (soft > 0.5).astype(np.uint8)
+    near = np.abs(z) < NEAR_THRESHOLD
+    return {"z": z, "soft": soft, "gate": gate, "near": near}
+
+
+def compact(gate):
+    """Ascending positions of the tokens routed to the full branch.
+
+    gate uint8 [B,N,G]  ->  idx int32 [B,G,N] (first cnt entries valid, the
+    rest -1), cnt int32 [B,G].
+
+    Reading: the pages fix no order; ascending position is the one order that
+    is unique given the gate.
+    """
+    g = np.asarray(gate)
+    B, N, G = g.shape
+    idx = np.full((B, G, N), -1, dtype=np.int32)
+    cnt = np.zeros((B, G), dtype=np.int32)
+    for b in range(B):
+        for k in range(G):
+            pos = np.flatnonzero(g[b, :, k] != 0)
+            idx[b, k, : pos.size] = pos
+            cnt[b, k] = pos.size
+    return idx, cnt
+
+
+# ---------------------------------------------------------------------------
+# Key sets of the two branches
+# ---------------------------------------------------------------------------
+def swa_key_range(i, W):
+    """Window branch key set of query position i: the W most recent keys,
+    self included, clipped at position 0 -> inclusive [max(0, i-W+1), i].
+
+    [Glossary] section "详细解释" and the W=4 table (row t4 drops t0)."""
+    return max(0, i - W + 1), i
+
+
+def full_key_range(i):
+    """Full branch key set of query position i: every key up to and including
+    i -> inclusive [0, i].
+
+    Reading: causal.  [Glossary] FAQ on W equal to the context length states
+    that the window mask then becomes the whole lower triangle, identical to
+    full attention, so full attention here is the causal one."""
+    return 0, i
+
+
+# ---------------------------------------------------------------------------
+# Softmax attention over an explicit key interval per row
+# ---------------------------------------------------------------------------
+def attend_rows(q, K, V, lo, hi, scale):
+    """Softmax attention of each query row over its own inclusive key interval.
+
+    q [R,d], K [L,d], V [L,dv], lo/hi int [R] (lo <= hi)  ->
+      O   float64 [R,dv]  sum_j p_j v_j / sum_j p_j,  p_j = exp(s_j - max s)
+      lse float64 [R]     log sum_j exp(s_j)
+    with s_j = scale * <q, k_j> for lo <= j <= hi.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    lo = np.asarray(lo, dtype=np.int64)
+    hi = np.asarray(hi, dtype=np.int64)
+    R = q.shape[0]
+    O = np.empty((R, V.shape[1]), dtype=np.float64)
+    lse = np.empty(R, dtype=np.float64)
+    if R == 0:
+        return O, lse
+    # rows are independent: evaluate them in batches that bound memory
+    order = np.argsort(hi, kind="stable")
+    n = max(1, (1 << 24) // (int(hi.max()) + 1))  # score elements per batch
+    start = 0
+    while start < R:
+        sel = order[start : start + n]
+        kmax = int(hi[sel].max()) + 1
+        kmin = int(lo[sel].min())
+        j = np.arange(kmin, kmax)
+        s = scale * (q[sel] @ K[kmin:kmax].T)
+        mask = (j[None, :] >= lo[sel, None]) & (j[None, :] <= hi[sel, None])
+        s = np.where(mask, s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        l = p.sum(axis=1, keepdims=True)
+        O[sel] = (p @ V[kmin:kmax]) / l
+        lse[sel] = m[:, 0] + np.log(l[:, 0])
+        start += sel.size
+    return O, lse
+
+
+def _head_maps(Hq, Hkv, G):
+    if Hq % Hkv or Hq % G:
+        raise ValueError("Hq must be a multiple of Hkv and of G")
+    # Reading: consecutive grouping of query heads onto KV heads and gate groups
+    return Hq // Hkv, Hq // G
+
+
+# ---------------------------------------------------------------------------
+# Prefill: both branches on shared Q/K/V, gated combination
+# ---------------------------------------------------------------------------
+def prefill(Q, K, V, gate, W, scale=None, both_branch=False, rows=None):
+    """Dual-branch attention forward over a prefix.
+
+    [SwiAttn] section 2, dual-branch paragraph: both branches use the same Q,
+    K, V; the output is O = sigma * O_FULL + (1 - sigma) * O_SWA.  With the
+    hard gate sigma in {0,1} this is a per-token selection.
+    [SwiAttn] section 2, regulariser paragraph: the per-token branch
+    discrepancy is the squared L2 norm of O_FULL - O_SWA.
+
+    Reading: the discrepancy of token i sums the squares over every query head
+    and every channel of the attention output (no output projection is named).
+
+    Q [B,N,Hq,d], K/V [B,N,Hkv,d], gate [B,N,G] (0/1)
+    rows: optional sorted token positions to evaluate (default all N)
+    ->  dict
+      O     float64 [B,R,Hq,d]
+      lse   float64 [B,R,Hq]      natural-log normaliser of the chosen branch
+      diff  float64 [B,R]         only when both_branch
+      O_full, O_swa float64 [B,R,Hq,d]  only when both_branch
+    """
+    Q = np.asarray(Q)
+    K = np.asarray(K)
+    V = np.asarray(V)
+    gate = np.asarray(gate)
+    B, N, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    G = gate.shape[2]
+    hk, hg = _head_maps(Hq, Hkv, G)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)  # Reading: the pages fix no softmax scale
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.size
+    dv = V.shape[3]
+    O = np.empty((B, R, Hq, dv))
+    lse = np.empty((B, R, Hq))
+    if both_branch:
+        Of = np.empty((B, R, Hq, dv))
+        Os = np.empty((B, R, Hq, dv))
+    sw = np.array([swa_key_range(int(i), W) for i in rows], dtype=np.int64).reshape(R, 2)
+    fu = np.array([full_key_range(int(i)) for i in rows], dtype=np.int64).reshape(R, 2)
+    for b in range(B):
+        for h in range(Hq):
+            kv, g = h // hk, h // hg
+            qh = Q[b, rows, h, :]
+            sig = gate[b, rows, g] != 0
+            if both_branch:
+                o_f, l_f = attend_rows(qh, K[b, :, kv], V[b, :, kv], fu[:, 0], fu[:, 1], scale)
+                o_s, l_s = attend_rows(qh, K[b, :, kv], V[b, :, kv], sw[:, 0], sw[:, 1], scale)
+                Of[b, :, h], Os[b, :, h] = o_f, o_s
+                O[b, :, h] = np.where(sig[:, None], o_f, o_s)
+                lse[b, :, h] = np.where(sig, l_f, l_s)
+            else:
+                lo = np.where(sig, fu[:, 0], sw[:, 0])
+                hi = np.where(sig, fu[:, 1], sw[:, 1])
+                O[b, :, h], lse[b, :, h] = attend_rows(qh, K[b, :, kv], V[b, :, kv], lo, hi, scale)
+    out = {"O": O, "lse": lse}
+    if both_branch:
+        out["O_full"], out["O_swa"] = Of, Os
+        out["diff"] = ((Of - Os) ** 2).sum(axis=(2, 3))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Decode: one new query per sequence against the shared KV cache
+# ---------------------------------------------------------------------------
+def decode(q, Kc, Vc, cache_len, gate, W, scale=None):
+    """One decode step per sequence, both branches reading one KV cache.
+
+    [SwiAttn] section 2: in decode the two branches share the KV cache.
+    Reading: the cache of sequence b already holds the new token, so the
+    query sits at position L-1 with L = cache_len[b]; the full branch reads
+    keys [0, L-1] and the window branch the last min(W, L) of them.  The cache
+    is linear (no ring buffer), since any later token may route full.
+
+    q [B,Hq,d], Kc/Vc [B,Lmax,Hkv,d], cache_len int [B] (1 <= L <= Lmax),
+    gate [B,G]  ->  dict  o float64 [B,Hq,d], lse float64 [B,Hq]
+    """
+    q = np.asarray(q)
+    gate = np.asarray(gate)
+    B, Hq, d = q.shape
+    Hkv = Kc.shape[2]
+    G = gate.shape[1]
+    hk, hg = _head_maps(Hq, Hkv, G)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.empty((B, Hq, Vc.shape[3]))
+    lse = np.empty((B, Hq))
+    for b in range(B):
+        i = int(cache_len[b]) - 1
+        for h in range(Hq):
+            kv, g = h // hk, h // hg
+            lo, hi = full_key_range(i) if gate[b, g] else swa_key_range(i, W)
+            ob, lb = attend_rows(q[b, h][None, :], np.asarray(Kc[b, : i + 1, kv]),
+                                 np.asarray(Vc[b, : i + 1, kv]), [lo], [hi], scale)
+            o[b, h], lse[b, h] = ob[0], lb[0]
+    return {"o": o, "lse": lse}

@@ -1,0 +1,260 @@
+"""Checks that pin the CPU reference to facts fixed by the pages and by
+mathematics.  Each check raises AssertionError on a mismatch; the oracle pin
+tests call them on the reference as written, and the mutation tests call them
+on copies with a planted mistake to show that the mistake is caught.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle.swiattn_ref as ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_w4_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "swa_mask_w4.txt"), encoding="utf-8") as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([int(c) for c in line])
+    return np.array(rows, dtype=bool)
+
+
+def check_w4_key_ranges():
+    """The window key set of each of the 7 rows equals the printed table."""
+    table = load_w4_table()
+    for i in range(7):
+        lo, hi = ref.swa_key_range(i, 4)
+        got = np.array([lo <= j <= hi for j in range(7)])
+        assert np.array_equal(got, table[i]), (i, got, table[i])
+
+
+def check_w4_attention_weights():
+    """With q = 0 every attended key gets the same weight, and V = identity
+    makes the output row equal to the weight vector: the attended set and the
+    normalisation both show up in the output of the full prefill path."""
+    table = load_w4_table()
+    N = 7
+    Q = np.zeros((1, N, 1, N))
+    K = np.random.default_rng(0).standard_normal((1, N, 1, N))
+    V = np.eye(N)[None, :, None, :]
+    out = ref.prefill(Q, K, V, np.zeros((1, N, 1), np.uint8), W=4)["O"][0, :, 0, :]
+    expect = table / table.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(out, expect, rtol=0, atol=1e-15)
+
+
+def check_full_branch_causal():
+    """Gate all ones with q = 0, V = identity gives the uniform lower triangle
+    (the full branch sees every key up to and including itself)."""
+    N = 9
+    Q = np.zeros((1, N, 1, N))
+    K = np.random.default_rng(1).standard_normal((1, N, 1, N))
+    V = np.eye(N)[None, :, None, :]
+    out = ref.prefill(Q, K, V, np.ones((1, N, 1), np.uint8), W=3)["O"][0, :, 0, :]
+    tri = np.tril(np.ones((N, N)))
+    np.testing.assert_allclose(out, tri / tri.sum(axis=1, keepdims=True), rtol=0, atol=1e-15)
+
+
+def _rand_qkv(seed, B, N, Hq, Hkv, d):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, N, Hq, d)), rng.standard_normal((B, N, Hkv, d)),
+            rng.standard_normal((B, N, Hkv, d)))
+
+
+def check_window_covering_all_equals_full():
+    """W >= N: the window mask is the whole lower triangle, so both branches
+    coincide and the output does not depend on the gate."""
+    Q, K, V = _rand_qkv(2, 1, 40, 4, 2, 8)
+    gate = (np.random.default_rng(3).random((1, 40, 2)) < 0.5).astype(np.uint8)
+    for W in (40, 57):
+        a = ref.prefill(Q, K, V, np.zeros_like(gate), W=W)["O"]
+        b = ref.prefill(Q, K, V, np.ones_like(gate), W=W)["O"]
+        c = ref.prefill(Q, K, V, gate, W=W, both_branch=True)
+        assert np.array_equal(a, b)
+        assert np.array_equal(a, c["O"])
+        assert np.all(c["diff"] == 0.0)
+
+
+def check_window_one_returns_v():
+    """W = 1: each row attends only to itself, so the output is its own value
+    row of the KV head the query head maps to."""
+    Q, K, V = _rand_qkv(4, 2, 33, 4, 2, 8)
+    out = ref.prefill(Q, K, V, np.zeros((2, 33, 1), np.uint8), W=1)["O"]
+    for h in range(4):
+        assert np.array_equal(out[:, :, h], V[:, :, h // 2])
+
+
+def _torch_sdpa(Q, K, V, mask):
+    """torch CPU scaled_dot_product_attention in float64 with a boolean mask
+    [N,N] (True = attend); K/V heads are repeated for grouped queries."""
+    Hq, Hkv = Q.shape[2], K.shape[2]
+    q = torch.from_numpy(Q).permute(0, 2, 1, 3)
+    k = torch.from_numpy(K).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    v = torch.from_numpy(V).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=torch.from_numpy(mask))
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def check_gate_extremes_against_sdpa():
+    """Gate all ones = causal attention, all zeros = band attention, each
+    against torch's own scaled_dot_product_attention in float64."""
+    B, N, Hq, Hkv, d, W = 2, 96, 4, 2, 16, 20
+    Q, K, V = _rand_qkv(5, B, N, Hq, Hkv, d)
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    causal = j <= i
+    band = causal & (j > i - W)
+    ones = ref.prefill(Q, K, V, np.ones((B, N, 1), np.uint8), W=W)["O"]
+    zeros = ref.prefill(Q, K, V, np.zeros((B, N, 1), np.uint8), W=W)["O"]
+    np.testing.assert_allclose(ones, _torch_sdpa(Q, K, V, causal), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(zeros, _torch_sdpa(Q, K, V, band), rtol=0, atol=1e-12)
+    # a mixed gate selects per token and per head group
+    gate = (np.random.default_rng(6).random((B, N, 2)) < 0.4).astype(np.uint8)
+    mixed = ref.prefill(Q, K, V, gate, W=W)["O"]
+    full_ref, band_ref = _torch_sdpa(Q, K, V, causal), _torch_sdpa(Q, K, V, band)
+    for h in range(Hq):
+        sel = gate[:, :, h // 2].astype(bool)[..., None]
+        np.testing.assert_allclose(mixed[:, :, h], np.where(sel, full_ref[:, :, h], band_ref[:, :, h]),
+                                   rtol=0, atol=1e-12)
+
+
+def check_rows_before_window_have_no_discrepancy():
+    """Rows i < W see the same keys in both branches: discrepancy exactly 0;
+    later rows differ."""
+    Q, K, V = _rand_qkv(7, 1, 64, 2, 2, 8)
+    out = ref.prefill(Q, K, V, np.zeros((1, 64, 1), np.uint8), W=16, both_branch=True)
+    assert np.all(out["diff"][:, :16] == 0.0)
+    assert np.all(out["diff"][:, 16:] > 0.0)
+
+
+def check_decode_equals_last_prefill_row():
+    """Decoding at cache length L reproduces prefill row L-1 of the same
+    sequence (shared cache, same key sets); entries beyond L are ignored."""
+    B, Lmax, Hq, Hkv, d, W = 3, 50, 4, 2, 8, 12
+    Q, K, V = _rand_qkv(8, B, Lmax, Hq, Hkv, d)
+    lens = np.array([50, 31, 5])
+    gate = np.array([[1], [0], [0]], np.uint8)
+    Kj, Vj = K.copy(), V.copy()
+    for b in range(B):
+        Kj[b, lens[b]:] = 1e3  # junk beyond the cache length
+        Vj[b, lens[b]:] = -1e3
+    q = np.stack([Q[b, lens[b] - 1] for b in range(B)])
+    dec = ref.decode(q, Kj, Vj, lens, gate, W)["o"]
+    for b in range(B):
+        L = lens[b]
+        g = np.broadcast_to(gate[b], (1, L, 1)).astype(np.uint8)
+        pre = ref.prefill(Q[b:b + 1, :L], K[b:b + 1, :L], V[b:b + 1, :L], g, W)["O"][0, L - 1]
+        np.testing.assert_allclose(dec[b], pre, rtol=0, atol=1e-13)
+
+
+def brute_force(Q, K, V, gate, W, scale):
+    """Independent pure-Python evaluation: explicit loops, math.exp."""
+    B, N, Hq, d = Q.shape
+    Hkv, G = K.shape[2], gate.shape[2]
+    Of = np.zeros(Q.shape)
+    Os = np.zeros(Q.shape)
+    for b in range(B):
+        for h in range(Hq):
+            kv = h * Hkv // Hq
+            for i in range(N):
+                for which, out in (("full", Of), ("swa", Os)):
+                    keys = [j for j in range(N) if j <= i and (which == "full" or i - j < W)]
+                    s = [scale * sum(Q[b, i, h, c] * K[b, j, kv, c] for c in range(d)) for j in keys]
+                    mx = max(s)
+                    w = [math.exp(x - mx) for x in s]
+                    tot = sum(w)
+                    for c in range(d):
+                        out[b, i, h, c] = sum(wj * V[b, j, kv, c] for wj, j in zip(w, keys)) / tot
+    sel = np.stack([gate[:, :, h * G // Hq] for h in range(Hq)], axis=2).astype(bool)[..., None]
+    O = np.where(sel, Of, Os)
+    diff = ((Of - Os) ** 2).sum(axis=(2, 3))
+    return O, diff
+
+
+def check_brute_force_tiny():
+    B, N, Hq, Hkv, d, W = 1, 11, 4, 2, 3, 4
+    Q, K, V = _rand_qkv(9, B, N, Hq, Hkv, d)
+    gate = (np.random.default_rng(10).random((B, N, 2)) < 0.5).astype(np.uint8)
+    scale = 0.7
+    O_bf, diff_bf = brute_force(Q, K, V, gate, W, scale)
+    out = ref.prefill(Q, K, V, gate, W, scale=scale, both_branch=True)
+    np.testing.assert_allclose(out["O"], O_bf, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out["diff"], diff_bf, rtol=1e-12, atol=1e-14)
+    # the default scale is 1/sqrt(d)
+    dflt = ref.prefill(Q, K, V, gate, W)["O"]
+    O_bf2, _ = brute_force(Q, K, V, gate, W, 1.0 / math.sqrt(d))
+    np.testing.assert_allclose(dflt, O_bf2, rtol=0, atol=1e-12)
+
+
+def check_convex_hull():
+    """Softmax weights are non-negative and sum to one: every output channel
+    lies between the smallest and largest attended value."""
+    Q, K, V = _rand_qkv(11, 1, 80, 2, 1, 8)
+    gate = (np.random.default_rng(12).random((1, 80, 1)) < 0.3).astype(np.uint8)
+    W = 10
+    O = ref.prefill(Q * 3, K, V, gate, W)["O"]
+    for i in range(80):
+        lo = 0 if gate[0, i, 0] else max(0, i - W + 1)
+        vs = V[0, lo:i + 1, 0]
+        for h in range(2):
+            assert np.all(O[0, i, h] >= vs.min(axis=0) - 1e-12)
+            assert np.all(O[0, i, h] <= vs.max(axis=0) + 1e-12)
+
+
+def check_router_closed_form():
+    """One-hot hidden states make each logit c * r[k, g] + bias exactly; the
+    gate is 1 exactly when the logit is positive (sigmoid above one half),
+    a logit of exactly 0 routes to the window branch."""
+    hidden, G = 8, 2
+    r = np.arange(hidden * G, dtype=np.float64).reshape(hidden, G) / 4.0 - 1.5
+    bias = np.array([0.25, -0.5])
+    ks = [0, 3, 5, 7, 2, 6]
+    cs = [1.0, -2.0, 0.5, 3.0, -1.0, 2.0]
+    H = np.zeros((1, len(ks), hidden))
+    for t, (k, c) in enumerate(zip(ks, cs)):
+        H[0, t, k] = c
+    out = ref.route(H, r, bias)
+    expect = np.array([[c * r[k, g] + bias[g] for g in range(G)] for k, c in zip(ks, cs)])
+    np.testing.assert_array_equal(out["z"][0], expect)
+    np.testing.assert_array_equal(out["gate"][0], (expect > 0).astype(np.uint8))
+    # a logit of exactly zero: strict threshold -> 0; just above -> 1
+    Hz = np.array([[[1.0], [1.0]]])
+    z0 = ref.route(Hz, np.array([[0.5]]), np.array([-0.5]))
+    z1 = ref.route(Hz, np.array([[0.5]]), np.array([-0.4999]))
+    assert z0["gate"][0, 0, 0] == 0 and z0["near"][0, 0, 0]
+    assert z1["gate"][0, 0, 0] == 1 and not z1["near"][0, 0, 0]
+
+
+def check_compact():
+    gate = (np.random.default_rng(13).random((2, 300, 3)) < 0.2).astype(np.uint8)
+    gate[1, :, 2] = 0
+    gate[0, :, 1] = 1
+    idx, cnt = ref.compact(gate)
+    for b in range(2):
+        for g in range(3):
+            pos = [i for i in range(300) if gate[b, i, g]]
+            assert cnt[b, g] == len(pos)
+            assert list(idx[b, g, : len(pos)]) == pos
+            assert np.all(idx[b, g, len(pos):] == -1)
+
+
+ALL_PINS = [
+    check_w4_key_ranges,
+    check_w4_attention_weights,
+    check_full_branch_causal,
+    check_window_covering_all_equals_full,
+    check_window_one_returns_v,
+    check_gate_extremes_against_sdpa,
+    check_rows_before_window_have_no_discrepancy,
+    check_decode_equals_last_prefill_row,
+    check_brute_force_tiny,
+    check_convex_hull,
+    check_router_closed_form,
+    check_compact,
+]

@@ -1,0 +1,79 @@
+"""Plant plausible mistakes in a copy of the CPU reference and show that the
+pins catch each one.  Mistakes are planted on the CPU only."""
+import numpy as np
+import pytest
+
+import oracle.swiattn_ref as ref
+from tests import pins
+
+_attend = ref.attend_rows
+
+
+def _attend_no_scale(q, K, V, lo, hi, scale):
+    return _attend(q, K, V, lo, hi, 1.0)
+
+
+def _attend_transposed_kv(q, K, V, lo, hi, scale):
+    return _attend(q, V, K, lo, hi, scale)
+
+
+def _attend_unnormalised(q, K, V, lo, hi, scale):
+    O, lse = _attend(q, K, V, lo, hi, scale)
+    n = (np.asarray(hi) - np.asarray(lo) + 1)[:, None]
+    return O * n, lse
+
+
+def _attend_drop_last_key(q, K, V, lo, hi, scale):
+    hi = np.asarray(hi)
+    lo = np.asarray(lo)
+    return _attend(q, K, V, lo, np.maximum(lo, hi - 1), scale)
+
+
+MUTANTS = {
+    # the explanatory example on the SWA introduction page counts one key too many
+    "window_one_key_too_many": ("swa_key_range", lambda i, W: (max(0, i - W), i)),
+    "window_excludes_self": ("swa_key_range", lambda i, W: (max(0, i - W), max(0, i - 1))),
+    # reading the glossary's "all N keys" literally (non-causal full branch)
+    "full_branch_not_causal": ("full_key_range", lambda i: (0, i + 1)),
+    "full_branch_is_window": ("full_key_range", lambda i: (max(0, i - 3), i)),
+    "missing_softmax_scale": ("attend_rows", _attend_no_scale),
+    "k_and_v_swapped": ("attend_rows", _attend_transposed_kv),
+    "unnormalised_weights": ("attend_rows", _attend_unnormalised),
+    "drops_newest_key": ("attend_rows", _attend_drop_last_key),
+}
+
+
+def _run_all_pins():
+    failures = 0
+    for check in pins.ALL_PINS:
+        try:
+            check()
+        except (AssertionError, IndexError, ValueError):
+            failures += 1
+    return failures
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(monkeypatch, name):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(ref, attr, fn)
+    assert _run_all_pins() > 0, f"no pin caught the planted mistake {name}"
+
+
+def test_router_mutants_caught(monkeypatch):
+    real = ref.route
+
+    def sign_flip(H, r, bias):
+        out = real(H, r, bias)
+        out["gate"] = (out["soft"] < 0.5).astype(np.uint8)
+        return out
+
+    def non_strict(H, r, bias):
+        out = real(H, r, bias)
+        out["gate"] = (out["soft"] >= 0.5).astype(np.uint8)
+        return out
+
+    for m in (sign_flip, non_strict):
+        monkeypatch.setattr(ref, "route", m)
+        with pytest.raises(AssertionError):
+            pins.check_router_closed_form()
