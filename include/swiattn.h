@@ -1,0 +1,169 @@
+/*
+ * swiattn.h - C ABI of the SwiAttn routed dual-branch attention library
+ * (libswiattn.so, HIP for AMD MI355X / gfx950).
+ *
+ * The method (paper-daily report on SwiAttn, section 2 "方法详解"):
+ *   - a per-token router: a linear map of the layer's hidden state gives a
+ *     logit z, the soft gate is sigmoid(z), and the forward value of the
+ *     straight-through estimator is the hard gate 1[sigmoid(z) > 0.5];
+ *   - two attention branches on the same Q, K, V: full causal attention and
+ *     sliding-window attention (SWA); the output is
+ *     O = gate * O_FULL + (1 - gate) * O_SWA;
+ *   - during decode both branches read one shared KV cache;
+ *   - the adaptive regulariser uses the per-token squared L2 distance
+ *     between the two branch outputs.
+ * The SWA key set of query i is the W most recent keys including i itself,
+ * [i-W+1, i] clipped at 0 (weimeta glossary "滑窗注意力 Sliding Window
+ * Attention 是什么？", section "详细解释" and its W=4 table); the full
+ * branch is causal, [0, i] (same glossary, FAQ on W equal to the context
+ * length, where the window mask becomes the whole lower triangle).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *     aligned, dense row-major in the layouts given below.  The library
+ *     allocates nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (0 = the default stream) and returns
+ *     without synchronising the host.  Faults inside kernels surface at the
+ *     caller's next synchronisation.
+ *   - The dtype argument selects the storage type of Q/K/V/O (and of H, r
+ *     for the router): SWIATTN_BF16 (bfloat16) or SWIATTN_F32 (float32).
+ *     Scores, softmax statistics and accumulators are float32 in both cases;
+ *     bf16 outputs are rounded to nearest even.
+ *   - Head mapping: query head h reads KV head h / (Hq/Hkv) and gate group
+ *     h / (Hq/G).  The two group sizes Hq/Hkv and Hq/G must nest (one divides
+ *     the other) and Hq/Hkv must be at most 32.
+ *   - Supported head dims: d = 64 or 128.
+ *   - Return value: SWIATTN_OK (0) or a negative error code.  Argument
+ *     errors are detected on the host before anything is enqueued; then no
+ *     output is touched.
+ */
+#ifndef SWIATTN_H
+#define SWIATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* swiattn_stream_t; /* same object as hipStream_t */
+
+typedef enum { SWIATTN_BF16 = 0, SWIATTN_F32 = 1 } swiattn_dtype_t;
+
+enum {
+  SWIATTN_OK = 0,
+  SWIATTN_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad scale      */
+  SWIATTN_ERR_UNSUPPORTED = -2, /* d not 64/128, group sizes not nested   */
+  SWIATTN_ERR_WORKSPACE = -3,   /* workspace null or smaller than needed  */
+  SWIATTN_ERR_HIP = -4          /* a HIP launch or runtime call failed    */
+};
+
+/* Both-branch mode for swiattn_prefill: compute both branches for every
+ * token and also write the per-token branch discrepancy `diff`. */
+#define SWIATTN_FLAG_BOTH_BRANCH 1u
+
+/*
+ * swiattn_route - router logits, hard gate, and compaction of the tokens
+ * routed to the full branch.
+ * (SwiAttn report, section 2, router paragraph.)
+ *
+ *   H     [B,N,hidden] dtype   hidden states; may be NULL (see below)
+ *   r     [hidden,G]   dtype   router weight (one column per gate group)
+ *   bias  [G]          float   router bias
+ *   gate  [B,N,G]      uint8   out: 1 = full branch, 0 = window branch.
+ *                              When H == NULL it is an INPUT instead and
+ *                              only the compaction runs (r, bias unused).
+ *   z_out [B,N,G]      float   out, optional (NULL = not written): logits
+ *   idx   [B,G,N]      int32   out: ascending token positions with gate=1;
+ *                              entries at or beyond cnt are unspecified
+ *   cnt   [B,G]        int32   out: number of gate=1 tokens
+ *
+ * z = sum_k H[b,i,k] r[k,g] + bias[g], accumulated in float32 in a fixed
+ * order (bitwise reproducible); gate = (z > 0), which equals
+ * sigmoid(z) > 0.5 without rounding a sigmoid.
+ * Errors: INVALID_ARG for B,N,hidden,G < 1 or a required NULL pointer.
+ */
+int swiattn_route(const void* H, const void* r, const float* bias, uint8_t* gate,
+                  float* z_out, int32_t* idx, int32_t* cnt, int B, int N, int hidden,
+                  int G, swiattn_dtype_t dtype, swiattn_stream_t stream);
+
+/*
+ * swiattn_prefill_workspace_size - bytes of device workspace that
+ * swiattn_prefill needs for these sizes (an upper bound over every gate).
+ * Returns 0 if the arguments are invalid.
+ */
+size_t swiattn_prefill_workspace_size(int B, int N, int Hq, int Hkv, int G, int d, int W,
+                                      swiattn_dtype_t dtype, unsigned flags);
+
+/*
+ * swiattn_prefill - dual-branch attention forward over whole sequences.
+ * (SwiAttn report, section 2, dual-branch and regulariser paragraphs.)
+ *
+ *   Q     [B,N,Hq,d]   dtype   queries (positions already encoded)
+ *   K, V  [B,N,Hkv,d]  dtype   keys and values shared by both branches
+ *   gate  [B,N,G]      uint8   hard gate (nonzero = full branch)
+ *   idx   [B,G,N]      int32   compacted gate=1 positions, ascending, as
+ *   cnt   [B,G]        int32   written by swiattn_route; ignored in
+ *                              both-branch mode (may be NULL there)
+ *   O     [B,N,Hq,d]   dtype   out: gate ? O_FULL : O_SWA, every row written
+ *   diff  [B,N]        float   out, both-branch mode only (else may be
+ *                              NULL): sum over heads and channels of
+ *                              (O_FULL - O_SWA)^2 in float32
+ *   W >= 1 (W >= N makes the two branches identical); scale > 0 is the
+ *   softmax scale (1/sqrt(d) for standard attention).
+ *   ws, ws_bytes: device workspace of at least
+ *   swiattn_prefill_workspace_size(...) bytes, clobbered.
+ *
+ * Hard-gate mode runs the window branch for every row, the far part
+ * [0, i-W] of the full branch only for gathered gate=1 rows, and merges the
+ * two key sets by their log-sum-exp.  Both-branch mode runs one causal pass
+ * per query tile that snapshots the window result on the way.
+ * Errors: INVALID_ARG (sizes < 1, NULL pointers, Hq % Hkv, Hq % G, scale),
+ * UNSUPPORTED (d, group nesting, Hq/Hkv > 32), WORKSPACE.
+ */
+int swiattn_prefill(const void* Q, const void* K, const void* V, const uint8_t* gate,
+                    const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B,
+                    int N, int Hq, int Hkv, int G, int d, int W, float scale,
+                    swiattn_dtype_t dtype, unsigned flags, void* ws, size_t ws_bytes,
+                    swiattn_stream_t stream);
+
+/*
+ * swiattn_decode_workspace_size - bytes of device workspace for
+ * swiattn_decode (upper bound over every gate and cache length).
+ * Returns 0 if the arguments are invalid.
+ */
+size_t swiattn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int G, int d, int W,
+                                     swiattn_dtype_t dtype);
+
+/*
+ * swiattn_decode - one routed decode step per sequence on a shared KV cache.
+ * (SwiAttn report, section 2: both branches share the KV cache in decode.)
+ *
+ *   q      [B,Hq,d]        dtype  the new token's queries
+ *   Kc, Vc [B,Lmax,Hkv,d]  dtype  linear cache; positions 0..L-1 are valid
+ *                                 and position L-1 holds the new token
+ *   cache_len [B]          int32  L per sequence, 1 <= L <= Lmax (device
+ *                                 memory: values outside are clamped)
+ *   gate   [B,G]           uint8  hard gate of the new token
+ *   o      [B,Hq,d]        dtype  out
+ *   The full branch reads keys [0, L-1], the window branch the last
+ *   min(W, L) keys.  Work is split over key chunks on the device from the
+ *   gate and L (no host synchronisation) and merged by log-sum-exp.
+ * Errors: as swiattn_prefill.
+ */
+int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t* cache_len,
+                   const uint8_t* gate, void* o, int B, int Lmax, int Hq, int Hkv, int G,
+                   int d, int W, float scale, swiattn_dtype_t dtype, void* ws,
+                   size_t ws_bytes, swiattn_stream_t stream);
+
+/* Static text for an error code. */
+const char* swiattn_strerror(int code);
+
+/* Library version, e.g. "0.1.0". */
+const char* swiattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SWIATTN_H */

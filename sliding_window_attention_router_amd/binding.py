@@ -1,0 +1,240 @@
+"""ctypes binding of libswiattn.so.
+
+Argument marshalling only: shapes and dtypes are checked, torch tensors are
+turned into device pointers and the current HIP stream, and every step of
+the computation runs in the library's kernels.  Torch provides device memory
+and streams, nothing else.  There is no fallback: if the library is missing
+or a call fails, a SwiAttnError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "SwiAttnError",
+    "lib",
+    "route",
+    "prefill",
+    "decode",
+    "prefill_workspace_size",
+    "decode_workspace_size",
+    "strerror",
+    "SYMBOLS",
+    "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswiattn.so")
+FLAG_BOTH_BRANCH = 1
+_DTYPES = {torch.bfloat16: 0, torch.float32: 1}
+
+_vp, _i32, _u32, _f32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_float, ctypes.c_size_t
+# exported symbol -> (restype, argtypes); mirrors include/swiattn.h
+SYMBOLS = {
+    "swiattn_route": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "swiattn_prefill_workspace_size": (_sz, [_i32] * 8 + [_u32]),
+    "swiattn_prefill": (_i32, [_vp] * 8 + [_i32] * 7 + [_f32, _i32, _u32, _vp, _sz, _vp]),
+    "swiattn_decode_workspace_size": (_sz, [_i32] * 8),
+    "swiattn_decode": (_i32, [_vp] * 6 + [_i32] * 7 + [_f32, _i32, _vp, _sz, _vp]),
+    "swiattn_strerror": (ctypes.c_char_p, [_i32]),
+    "swiattn_version": (ctypes.c_char_p, []),
+}
+
+
+class SwiAttnError(RuntimeError):
+    pass
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """Load libswiattn.so (once).  Raises SwiAttnError if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise SwiAttnError(
+                    f"{LIB_PATH} is not built; run `python -m sliding_window_attention_router_amd.build`")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SYMBOLS.items():
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = handle
+    return _lib
+
+
+def strerror(code):
+    return lib().swiattn_strerror(int(code)).decode()
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise SwiAttnError(f"{what} failed: {strerror(rc)} (code {rc})")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+    return _DTYPES[t.dtype]
+
+
+def _need(t, name, shape=None, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def route(H=None, r=None, bias=None, *, gate=None, want_z=False):
+    """Router logits, hard gate and compaction.
+
+    H [B,N,hidden], r [hidden,G] (bf16 or fp32), bias [G] fp32 -> gate.
+    Pass H=None and gate=[B,N,G] uint8 to only compact a given gate.
+    Returns (gate uint8 [B,N,G], idx int32 [B,G,N], cnt int32 [B,G], z or None).
+    """
+    L = lib()
+    if H is None:
+        _need(gate, "gate", dtype=torch.uint8)
+        B, N, G = gate.shape
+        dev, hidden, code = gate.device, 0, 0
+        z = None
+    else:
+        _need(H, "H")
+        code = _dtype_code(H)
+        B, N, hidden = H.shape
+        dev = H.device
+        _need(r, "r", dtype=H.dtype, device=dev)
+        if r.dim() != 2 or r.shape[0] != hidden:
+            raise ValueError("r must be [hidden, G]")
+        G = r.shape[1]
+        _need(bias, "bias", shape=(G,), dtype=torch.float32, device=dev)
+        gate = torch.empty((B, N, G), dtype=torch.uint8, device=dev)
+        z = torch.empty((B, N, G), dtype=torch.float32, device=dev) if want_z else None
+    idx = torch.empty((B, G, N), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, G), dtype=torch.int32, device=dev)
+    rc = L.swiattn_route(_p(H), _p(r), _p(bias), _p(gate), _p(z), _p(idx), _p(cnt),
+                         B, N, hidden, G, code, _stream(dev))
+    _check(rc, "swiattn_route")
+    return gate, idx, cnt, z
+
+
+def prefill_workspace_size(B, N, Hq, Hkv, G, d, W, dtype=torch.bfloat16, both_branch=False):
+    return int(lib().swiattn_prefill_workspace_size(B, N, Hq, Hkv, G, d, W, _DTYPES[dtype],
+                                                    FLAG_BOTH_BRANCH if both_branch else 0))
+
+
+def decode_workspace_size(B, Lmax, Hq, Hkv, G, d, W, dtype=torch.bfloat16):
+    return int(lib().swiattn_decode_workspace_size(B, Lmax, Hq, Hkv, G, d, W, _DTYPES[dtype]))
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        raise SwiAttnError("invalid sizes (workspace size query returned 0)")
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _need(workspace, "workspace", dtype=torch.uint8, device=device)
+    return workspace
+
+
+def prefill(Q, K, V, gate, W, *, idx=None, cnt=None, scale=None, both_branch=False,
+            out=None, diff=None, workspace=None):
+    """Dual-branch prefill.  Q [B,N,Hq,d], K/V [B,N,Hkv,d], gate [B,N,G] uint8.
+
+    In hard-gate mode the compacted positions (idx, cnt) from route() are
+    used, or computed here by the library's compaction if not given.
+    Returns (O [B,N,Hq,d], diff [B,N] fp32 or None).
+    """
+    L = lib()
+    _need(Q, "Q")
+    code = _dtype_code(Q)
+    B, N, Hq, d = Q.shape
+    dev = Q.device
+    _need(K, "K", dtype=Q.dtype, device=dev)
+    if K.dim() != 4 or K.shape[0] != B or K.shape[1] != N or K.shape[3] != d:
+        raise ValueError("K must be [B,N,Hkv,d]")
+    Hkv = K.shape[2]
+    _need(V, "V", shape=K.shape, dtype=Q.dtype, device=dev)
+    _need(gate, "gate", dtype=torch.uint8, device=dev)
+    if gate.dim() != 3 or gate.shape[:2] != (B, N):
+        raise ValueError("gate must be [B,N,G]")
+    G = gate.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if not both_branch and (idx is None or cnt is None):
+        _, idx, cnt, _ = route(None, gate=gate)
+    if not both_branch:
+        _need(idx, "idx", shape=(B, G, N), dtype=torch.int32, device=dev)
+        _need(cnt, "cnt", shape=(B, G), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty_like(Q)
+    _need(out, "out", shape=Q.shape, dtype=Q.dtype, device=dev)
+    if both_branch:
+        if diff is None:
+            diff = torch.empty((B, N), dtype=torch.float32, device=dev)
+        _need(diff, "diff", shape=(B, N), dtype=torch.float32, device=dev)
+    else:
+        diff = None
+    flags = FLAG_BOTH_BRANCH if both_branch else 0
+    nbytes = int(L.swiattn_prefill_workspace_size(B, N, Hq, Hkv, G, d, W, code, flags))
+    ws = _workspace(nbytes, dev, workspace)
+    rc = L.swiattn_prefill(_p(Q), _p(K), _p(V), _p(gate), _p(idx if not both_branch else None),
+                           _p(cnt if not both_branch else None), _p(out), _p(diff),
+                           B, N, Hq, Hkv, G, d, W, float(scale), code, flags,
+                           _p(ws), ws.numel(), _stream(dev))
+    _check(rc, "swiattn_prefill")
+    return out, diff
+
+
+def decode(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None, workspace=None):
+    """Routed decode.  q [B,Hq,d], Kc/Vc [B,Lmax,Hkv,d], cache_len int32 [B],
+    gate uint8 [B,G].  Returns o [B,Hq,d]."""
+    L = lib()
+    _need(q, "q")
+    code = _dtype_code(q)
+    B, Hq, d = q.shape
+    dev = q.device
+    _need(Kc, "Kc", dtype=q.dtype, device=dev)
+    if Kc.dim() != 4 or Kc.shape[0] != B or Kc.shape[3] != d:
+        raise ValueError("Kc must be [B,Lmax,Hkv,d]")
+    Lmax, Hkv = Kc.shape[1], Kc.shape[2]
+    _need(Vc, "Vc", shape=Kc.shape, dtype=q.dtype, device=dev)
+    _need(cache_len, "cache_len", shape=(B,), dtype=torch.int32, device=dev)
+    _need(gate, "gate", dtype=torch.uint8, device=dev)
+    if gate.dim() != 2 or gate.shape[0] != B:
+        raise ValueError("gate must be [B,G]")
+    G = gate.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", shape=q.shape, dtype=q.dtype, device=dev)
+    nbytes = int(L.swiattn_decode_workspace_size(B, Lmax, Hq, Hkv, G, d, W, code))
+    ws = _workspace(nbytes, dev, workspace)
+    rc = L.swiattn_decode(_p(q), _p(Kc), _p(Vc), _p(cache_len), _p(gate), _p(out),
+                          B, Lmax, Hq, Hkv, G, d, W, float(scale), code, _p(ws), ws.numel(),
+                          _stream(dev))
+    _check(rc, "swiattn_decode")
+    return out

@@ -1,0 +1,83 @@
+"""Build libswiattn.so in-tree with hipcc for gfx950.
+
+    python -m sliding_window_attention_router_amd.build
+
+Every HIP source is compiled with packed-FP32 instruction selection turned
+off (the host pass warns that it does not know the feature; that is
+harmless).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libswiattn.so")
+SOURCES = ["api.cpp", "route.hip", "prefill.hip", "decode.hip"]
+ARCH = "gfx950"
+
+
+def hipcc():
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build libswiattn.so)")
+
+
+def flags():
+    return [
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-Wall",
+        "-Wno-unused-function",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        f"-I{os.path.join(os.path.dirname(PKG), 'include')}",
+    ]
+
+
+def build(verbose=False):
+    """Compile every source to an object in a temporary folder (in parallel),
+    link them into libswiattn.so next to this file (atomically replaced).
+    The sources compile concurrently, one hipcc process each."""
+    cc = hipcc()
+    tmp = tempfile.mkdtemp(prefix="swiattn_build_")
+    try:
+        procs, objs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            objs.append(obj)
+            lang = ["-x", "hip"] if src.endswith(".hip") else []
+            cmd = [cc, *flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        errors = []
+        for src, p in procs:
+            out, _ = p.communicate()
+            text = out.decode(errors="replace")
+            text = "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l)
+            if p.returncode != 0:
+                errors.append(f"{src}:\n{text}")
+            elif verbose and text.strip():
+                print(text)
+        if errors:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+        tmp_lib = LIB + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+        os.replace(tmp_lib, LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,364 @@
+// Flash-attention building blocks for the SwiAttn kernels on gfx950.
+//
+// Orientation.  Every wave owns 32 query rows.  Scores are formed
+// transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (A = a 32-key slice
+// of K from LDS, B = the wave's queries kept in registers), so the 32x32
+// accumulator puts one query per lane column: lane l holds query l%32 and 16
+// keys.  The softmax state (running max, running sum) of a query therefore
+// lives in its two lanes l and l^32, and the only cross-lane step is one xor
+// shuffle by 32.  The output is accumulated transposed as well,
+// O^T = V^T P^T, which lets P^T come straight from the score accumulators
+// (same lane <-> query mapping) and makes the per-query rescale a per-lane
+// multiply.  V is staged transposed in LDS so that an A operand (one
+// channel, 8 keys) is two 8-byte LDS reads.
+//
+// The contraction index of an MFMA may be permuted freely as long as A and B
+// use the same permutation; the P^T / V^T operands use the permutation that
+// the 32x32 accumulator layout hands out (lane group g holds keys
+// 8*(i/4) + 4*g + i%4 of each 32-key slice).
+//
+// float32 inputs use the same structure with v_mfma_f32_32x32x2f32.
+#pragma once
+#include "common.hpp"
+
+namespace swi {
+
+constexpr int kBN = 64;  // keys per LDS block
+constexpr int kQR = 32;  // query rows per wave
+
+template <typename T, int D>
+struct Lds;
+template <int D>
+struct Lds<bf16_t, D> {
+  // K block [kBN][D]: row stride D*2+16 bytes puts consecutive keys 4 banks
+  // apart, so 16-byte operand reads of 16 lanes cover all 64 banks once.
+  static constexpr int kKStride = D * 2 + 16;
+  // V block transposed [D][kBN]: row stride kBN*2+8 bytes (34 dwords) maps
+  // 32 consecutive channels onto distinct even banks for 8-byte reads.
+  static constexpr int kVStride = kBN * 2 + 8;
+  static constexpr int kKBytes = kBN * kKStride;
+  static constexpr int kBytes = kKBytes + D * kVStride;
+};
+template <int D>
+struct Lds<float, D> {
+  static constexpr int kKStride = (D + 2) * 4;  // [kBN][D+2] floats
+  static constexpr int kVStride = (D + 8) * 4;  // [kBN][D+8] floats, not transposed
+  static constexpr int kKBytes = kBN * kKStride;
+  static constexpr int kBytes = kKBytes + kBN * kVStride;
+};
+
+// ---------------------------------------------------------------------------
+// Global -> register -> LDS staging of one block of kBN keys of one KV head.
+// Rows at or beyond `kend` are zero-filled (never read from memory).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NT>
+struct KVLoader;
+
+template <int D, int NT>
+struct KVLoader<bf16_t, D, NT> {
+  using L = Lds<bf16_t, D>;
+  static constexpr int CPR = D / 8;  // 16-byte pieces per row
+  static constexpr int KU = kBN * CPR;
+  static constexpr int KPER = (KU + NT - 1) / NT;
+  static constexpr int VU = (kBN / 4) * CPR;  // pieces of (4 keys x 8 channels)
+  static constexpr int VPER = (VU + NT - 1) / NT;
+  u32x4 kr[KPER];
+  u32x4 vr[VPER][4];
+
+  SWI_DEV void load(const bf16_t* __restrict__ Kb, const bf16_t* __restrict__ Vb, int64_t rs,
+                    int kb, int kend, int tid) {
+#pragma unroll
+    for (int j = 0; j < KPER; ++j) {
+      const int u = tid + NT * j;
+      const int key = u / CPR, c = u - key * CPR;
+      const int kk = kb + key;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if ((KU % NT == 0 || u < KU) && kk < kend)
+        v = *reinterpret_cast<const u32x4*>(Kb + kk * rs + c * 8);
+      kr[j] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < VPER; ++j) {
+      const int u = tid + NT * j;
+      const int kg = u / CPR, c = u - kg * CPR;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = kb + 4 * kg + r;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if ((VU % NT == 0 || u < VU) && kk < kend)
+          v = *reinterpret_cast<const u32x4*>(Vb + kk * rs + c * 8);
+        vr[j][r] = v;
+      }
+    }
+  }
+
+  SWI_DEV void store(char* lds, int tid) const {
+#pragma unroll
+    for (int j = 0; j < KPER; ++j) {
+      const int u = tid + NT * j;
+      if (KU % NT != 0 && u >= KU) continue;
+      const int key = u / CPR, c = u - key * CPR;
+      *reinterpret_cast<u32x4*>(lds + key * L::kKStride + c * 16) = kr[j];
+    }
+    char* vt = lds + L::kKBytes;
+#pragma unroll
+    for (int j = 0; j < VPER; ++j) {
+      const int u = tid + NT * j;
+      if (VU % NT != 0 && u >= VU) continue;
+      const int kg = u / CPR, c = u - kg * CPR;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t a0 = vr[j][0][e], a1 = vr[j][1][e], a2 = vr[j][2][e], a3 = vr[j][3][e];
+        // channel 2e: low halves of the four keys; channel 2e+1: high halves
+        u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
+        u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
+        const int ch = c * 8 + 2 * e;
+        *reinterpret_cast<u32x2*>(vt + ch * L::kVStride + kg * 8) = lo;
+        *reinterpret_cast<u32x2*>(vt + (ch + 1) * L::kVStride + kg * 8) = hi;
+      }
+    }
+  }
+};
+
+template <int D, int NT>
+struct KVLoader<float, D, NT> {
+  using L = Lds<float, D>;
+  static constexpr int CPR = D / 4;
+  static constexpr int KU = kBN * CPR;
+  static constexpr int KPER = (KU + NT - 1) / NT;
+  u32x4 kr[KPER];
+  u32x4 vr[KPER];
+
+  SWI_DEV void load(const float* __restrict__ Kb, const float* __restrict__ Vb, int64_t rs,
+                    int kb, int kend, int tid) {
+#pragma unroll
+    for (int j = 0; j < KPER; ++j) {
+      const int u = tid + NT * j;
+      const int key = u / CPR, c = u - key * CPR;
+      const int kk = kb + key;
+      u32x4 k = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
+      if ((KU % NT == 0 || u < KU) && kk < kend) {
+        k = *reinterpret_cast<const u32x4*>(Kb + kk * rs + c * 4);
+        v = *reinterpret_cast<const u32x4*>(Vb + kk * rs + c * 4);
+      }
+      kr[j] = k;
+      vr[j] = v;
+    }
+  }
+  SWI_DEV void store(char* lds, int tid) const {
+#pragma unroll
+    for (int j = 0; j < KPER; ++j) {
+      const int u = tid + NT * j;
+      if (KU % NT != 0 && u >= KU) continue;
+      const int key = u / CPR, c = u - key * CPR;
+      uint32_t* kp = reinterpret_cast<uint32_t*>(lds + key * L::kKStride) + c * 4;
+      uint32_t* vp = reinterpret_cast<uint32_t*>(lds + L::kKBytes + key * L::kVStride) + c * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kp[e] = kr[j][e];
+        vp[e] = vr[j][e];
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Online softmax update shared by both cores.  s[mt][i] holds the raw score
+// of key kb + 32*mt + 8*(i/4) + 4*g + i%4 for this lane's query.  On return
+// s holds the unnormalised probabilities, m/l are updated and the
+// accumulators rescaled.  Keys outside [lo, hi] are dropped when `masked`.
+// ---------------------------------------------------------------------------
+template <int MD>
+SWI_DEV void online_softmax(f32x16 (&s)[2], f32x16 (&acc)[MD], float& m, float& l, int kb,
+                            bool masked, int lo, int hi, float sl2, int g) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float x = s[mt][i] * sl2;
+      if (masked) {
+        const int j = kb + mt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+        if (j < lo || j > hi) x = kNegInf;
+      }
+      s[mt][i] = x;
+      mx = fmaxf(mx, x);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  const float mn = fmaxf(m, mx);
+  const float mu = (mn == kNegInf) ? 0.f : mn;
+  const float alpha = fast_exp2(m - mu);
+  float ls = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(s[mt][i] - mu);
+      s[mt][i] = p;
+      ls += p;
+    }
+  }
+  l = l * alpha + ls;
+  m = mn;
+#pragma unroll
+  for (int md = 0; md < MD; ++md) acc[md] *= alpha;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 core
+// ---------------------------------------------------------------------------
+template <int D>
+struct CoreBF16 {
+  using L = Lds<bf16_t, D>;
+  static constexpr int KS = D / 16;  // k-steps of the score product
+  static constexpr int MD = D / 32;  // 32-channel tiles of the output
+  bf16x8 qreg[KS];
+  f32x16 acc[MD];
+  float m, l;
+
+  SWI_DEV void init() {
+    m = kNegInf;
+    l = 0.f;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) acc[md] = f32x16{};
+  }
+  // qrow: this lane's query row (nullptr = padding row, zeros)
+  SWI_DEV void load_q(const bf16_t* qrow, int g) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qreg[ks] = qrow ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + g * 8) : bf16x8{};
+  }
+  SWI_DEV void block(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
+                     int g) {
+    f32x16 s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      s[mt] = f32x16{};
+      const char* kp = lds + (mt * 32 + q) * L::kKStride + g * 16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + ks * 32);
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[mt], 0, 0, 0);
+      }
+    }
+    online_softmax<MD>(s, acc, m, l, kb, masked, lo, hi, sl2, g);
+    bf16x8 pb[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[st][e] = bf16_t(s[st >> 1][(st & 1) * 8 + e]);
+    const char* vt = lds + L::kKBytes;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const char* vp = vt + (md * 32 + q) * L::kVStride + g * 8;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(vp + st * 32);
+        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(vp + st * 32 + 16);
+        const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], acc[md], 0, 0, 0);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// float32 core (same structure, v_mfma_f32_32x32x2f32)
+// ---------------------------------------------------------------------------
+template <int D>
+struct CoreF32 {
+  using L = Lds<float, D>;
+  static constexpr int KS = D / 2;
+  static constexpr int MD = D / 32;
+  float qreg[KS];
+  f32x16 acc[MD];
+  float m, l;
+
+  SWI_DEV void init() {
+    m = kNegInf;
+    l = 0.f;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) acc[md] = f32x16{};
+  }
+  SWI_DEV void load_q(const float* qrow, int g) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qreg[ks] = qrow ? qrow[ks * 2 + g] : 0.f;
+  }
+  SWI_DEV void block(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
+                     int g) {
+    f32x16 s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      s[mt] = f32x16{};
+      const float* kp = reinterpret_cast<const float*>(lds + (mt * 32 + q) * L::kKStride) + g;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kp[ks * 2], qreg[ks], s[mt], 0, 0, 0);
+    }
+    online_softmax<MD>(s, acc, m, l, kb, masked, lo, hi, sl2, g);
+    const char* vs = lds + L::kKBytes;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int st = 0; st < 32; ++st) {
+        const int i = st & 15, mt = st >> 4;
+        const int key = mt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+        const float a = *reinterpret_cast<const float*>(vs + key * L::kVStride + (md * 32 + q) * 4);
+        acc[md] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[mt][i], acc[md], 0, 0, 0);
+      }
+    }
+  }
+};
+
+template <typename T, int D>
+struct CoreSel;
+template <int D>
+struct CoreSel<bf16_t, D> {
+  using type = CoreBF16<D>;
+};
+template <int D>
+struct CoreSel<float, D> {
+  using type = CoreF32<D>;
+};
+
+// Total row sum over the lane pair, the log2-domain normaliser, and 1/sum
+// (0 for a row that saw no key).
+SWI_DEV float finish_row(float m, float l, float& lse2) {
+  const float lt = l + __shfl_xor(l, 32, kWave);
+  lse2 = lt > 0.f ? m + fast_log2(lt) : kNegInf;
+  return lt > 0.f ? 1.f / lt : 0.f;
+}
+
+// Channel held by accumulator element i of output tile md in lane group g.
+SWI_DEV constexpr int acc_channel(int md, int i, int g) {
+  return md * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+}
+
+// Store this lane's half of an output row (channels acc_channel(...)).
+template <int MD>
+SWI_DEV void store_row(bf16_t* orow, const f32x16 (&acc)[MD], float inv, int g) {
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = bf16_t(acc[md][i4 * 4 + e] * inv);
+      *reinterpret_cast<bf16x4*>(orow + md * 32 + i4 * 8 + g * 4) = v;
+    }
+}
+template <int MD>
+SWI_DEV void store_row(float* orow, const f32x16 (&acc)[MD], float inv, int g) {
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[md][i4 * 4 + e] * inv;
+      *reinterpret_cast<f32x4*>(orow + md * 32 + i4 * 8 + g * 4) = v;
+    }
+}
+
+}  // namespace swi

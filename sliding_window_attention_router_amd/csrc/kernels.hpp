@@ -1,0 +1,61 @@
+// Host-side launchers of the SwiAttn kernels (internal to libswiattn.so).
+// Arguments have been validated by the C ABI layer before these are called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swi {
+
+// ---- router -------------------------------------------------------------
+hipError_t launch_route(const void* H, const void* r, const float* bias, uint8_t* gate,
+                        float* z_out, int B, int N, int hidden, int G, bool f32, hipStream_t s);
+hipError_t launch_compact(const uint8_t* gate, int32_t* idx, int32_t* cnt, int B, int N, int G,
+                          hipStream_t s);
+
+// ---- prefill ------------------------------------------------------------
+struct PrefillShape {
+  int B, N, Hq, Hkv, G, d, W;
+  float scale;
+  bool f32;
+  bool both_branch;
+};
+
+// Workspace plan: byte offsets of each buffer inside the caller's workspace.
+struct PrefillPlan {
+  int HK;         // query heads per KV head
+  int HG;         // query heads per gate group
+  int hpu;        // heads per far unit: min(HK, HG)
+  int units;      // far units per sequence: Hq / hpu
+  int tpt_band;   // tokens per band / fused tile: 128 / HK
+  int tpt_far;    // gathered tokens per far tile: 128 / hpu
+  int band_tiles; // ceil(N / tpt_band)
+  int far_tiles;  // per (b, unit): ceil(N / tpt_far)
+  int max_items;  // upper bound on far work items
+  size_t off_lse, off_sched, off_part_o, off_part_lse, off_diffp, bytes;
+};
+
+bool plan_prefill(const PrefillShape& sh, PrefillPlan* p);
+hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const void* Q,
+                          const void* K, const void* V, const uint8_t* gate, const int32_t* idx,
+                          const int32_t* cnt, void* O, float* diff, void* ws, hipStream_t s);
+
+// ---- decode -------------------------------------------------------------
+struct DecodeShape {
+  int B, Lmax, Hq, Hkv, G, d, W;
+  float scale;
+  bool f32;
+};
+struct DecodePlan {
+  int HK, HG;
+  int chunk;      // keys per work item
+  int max_items;  // B * Hkv * ceil(Lmax / chunk)
+  int grid;       // persistent workgroups
+  size_t off_sched, off_part_o, off_part_lse, bytes;
+};
+bool plan_decode(const DecodeShape& sh, DecodePlan* p);
+hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void* q,
+                         const void* Kc, const void* Vc, const int32_t* cache_len,
+                         const uint8_t* gate, void* o, void* ws, hipStream_t s);
+
+}  // namespace swi

@@ -1,0 +1,567 @@
+// SwiAttn dual-branch prefill on gfx950.
+//
+// SwiAttn report, section 2 (dual-branch paragraph): the full branch and
+// the sliding-window branch share Q, K, V and the output is
+// gate * O_FULL + (1 - gate) * O_SWA with a hard 0/1 gate.  The window of
+// query i is [i-W+1, i] (weimeta SWA glossary, section "详细解释"), the full
+// branch is causal [0, i].
+//
+// Hard-gate mode (three kernels after an on-device schedule):
+//   band_kernel   window branch for every row; writes O and the window
+//                 log-sum-exp (log2 units)
+//   far_kernel    for the gathered gate=1 rows only: the far keys [0, i-W]
+//                 (the full set minus the window), split into key chunks
+//   merge_kernel  log-sum-exp merge of window + far partials = O_FULL for
+//                 the gathered rows, written over their window output
+// The window and far key sets are disjoint and cover [0, i], so the merge is
+// the exact full softmax up to rounding.
+//
+// Both-branch mode (fused_kernel): one causal pass per query tile that
+// walks the window keys first, snapshots O_SWA in registers, continues over
+// the far keys to O_FULL, and writes gate ? O_FULL : O_SWA and the
+// per-(head, token) squared distance; diff_kernel sums it over heads
+// (the regulariser paragraph of the same section uses this distance).
+#include <climits>
+
+#include "attn_core.hpp"
+#include "kernels.hpp"
+
+namespace swi {
+
+constexpr int kThreads = 256;      // 4 waves, 128 query rows per workgroup
+constexpr int kRows = 128;
+constexpr int kTargetItems = 2048;  // far work items aimed for per launch
+constexpr int kMinChunkBlocks = 8;  // far chunk is at least 8 x 64 keys
+constexpr int kSchedThreads = 1024;
+
+struct PrefillArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  const uint8_t* gate;
+  const int32_t* idx;
+  const int32_t* cnt;
+  float* lse_s;     // [B,Hq,N] window-branch normaliser, log2 units
+  int32_t* sched;   // far schedule (layout in far_schedule_kernel)
+  float* part_o;    // [max_items][kRows][D]
+  float* part_lse;  // [max_items][kRows]
+  float* diffp;     // [B,Hq,N]
+  float* diff;      // [B,N]
+  int B, N, Hq, Hkv, G, W;
+  int HK, HG, hpu, units, tpt_band, tpt_far, band_tiles, far_tiles, max_items;
+  float sl2;  // softmax scale * log2(e)
+};
+
+// schedule layout inside a.sched (int32):
+//   [0] total items  [1] blocks per chunk
+//   item_start[nT] | n_items[nT] | pair_start[nbu+1] | item_tile[max] | item_chunk[max]
+struct SchedView {
+  int32_t *item_start, *n_items, *pair_start, *item_tile, *item_chunk;
+  SWI_DEV SchedView(const PrefillArgs& a) {
+    const int nT = a.B * a.units * a.far_tiles;
+    const int nbu = a.B * a.units;
+    item_start = a.sched + 2;
+    n_items = item_start + nT;
+    pair_start = n_items + nT;
+    item_tile = pair_start + nbu + 1;
+    item_chunk = item_tile + a.max_items;
+  }
+};
+
+// Per-wave bounds used to skip blocks no row of the wave needs and to drop
+// the mask inside blocks every row of the wave fully covers.
+struct WaveBounds {
+  int min_lo, max_hi, max_lo, min_hi;
+  // A valid row with an empty range (lo > hi) needs no block but forces the
+  // mask everywhere, so it never accumulates keys it does not own.
+  SWI_DEV void init(bool valid, int lo, int hi) {
+    const bool live = valid && lo <= hi;
+    min_lo = wave_min_i(live ? lo : INT_MAX);
+    max_hi = wave_max_i(live ? hi : -1);
+    max_lo = wave_max_i(valid ? lo : -1);
+    min_hi = wave_min_i(valid ? hi : INT_MAX);
+  }
+  SWI_DEV bool needed(int kb) const { return kb <= max_hi && kb + kBN - 1 >= min_lo; }
+  SWI_DEV bool masked(int kb) const { return kb < max_lo || kb + kBN - 1 > min_hi; }
+};
+
+// ---------------------------------------------------------------------------
+// Window branch over every row.  Grid (band_tiles, B*Hkv).  Rows of a tile
+// are tpt_band consecutive tokens x the HK query heads of one KV head.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, 2) void band_kernel(PrefillArgs a) {
+  using Core = typename CoreSel<T, D>::type;
+  __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
+  const int tile = blockIdx.x;
+  const int b = blockIdx.y / a.Hkv, kvh = blockIdx.y - b * a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane & 31, g = lane >> 5;
+  const int q0 = tile * a.tpt_band;
+  const int qlast = min(a.N - 1, q0 + a.tpt_band - 1);
+  const int r = wave * kQR + q;
+  const int slot = r / a.HK, hh = r - slot * a.HK;
+  const int tok = q0 + slot;
+  const bool valid = slot < a.tpt_band && tok < a.N;
+  const int h = kvh * a.HK + hh;
+  const int lo = valid ? max(0, tok - a.W + 1) : 0;
+  const int hi = valid ? tok : -1;
+  WaveBounds wb;
+  wb.init(valid, lo, hi);
+
+  Core c;
+  c.init();
+  const T* Qp = static_cast<const T*>(a.Q);
+  c.load_q(valid ? Qp + ((int64_t(b) * a.N + tok) * a.Hq + h) * D : nullptr, g);
+
+  const T* Kb = static_cast<const T*>(a.K) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
+  const T* Vb = static_cast<const T*>(a.V) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
+  const int64_t rs = int64_t(a.Hkv) * D;
+  const int kb0 = (max(0, q0 - a.W + 1) / kBN) * kBN;
+  KVLoader<T, D, kThreads> ld;
+  ld.load(Kb, Vb, rs, kb0, a.N, tid);
+  for (int kb = kb0; kb <= qlast; kb += kBN) {
+    __syncthreads();
+    ld.store(lds, tid);
+    __syncthreads();
+    if (kb + kBN <= qlast) ld.load(Kb, Vb, rs, kb + kBN, a.N, tid);
+    if (wb.needed(kb)) c.block(lds, kb, wb.masked(kb), lo, hi, a.sl2, q, g);
+  }
+  float lse2;
+  const float inv = finish_row(c.m, c.l, lse2);
+  if (valid) {
+    T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D;
+    store_row<Core::MD>(orow, c.acc, inv, g);
+    if (g == 0 && a.lse_s) a.lse_s[(int64_t(b) * a.Hq + h) * a.N + tok] = lse2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// On-device schedule of the far part (one 1024-thread workgroup).
+// A far tile is tpt_far consecutive gathered tokens x hpu heads of one unit
+// (heads that share both the KV head and the gate group).  Its far keys are
+// [0, t_last - W] where t_last is its largest token; the tile is cut into
+// chunks of `cb` 64-key blocks, cb chosen so that the launch has about
+// kTargetItems chunks in total.
+// ---------------------------------------------------------------------------
+SWI_DEV int block_excl_scan(int v, int* sh, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const int nw = blockDim.x / 64;
+    const int x = lane < nw ? sh[lane] : 0;
+    int w = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(w, o, 64);
+      if (lane >= o) w += t;
+    }
+    if (lane < nw) sh[lane] = w - x;
+    if (lane == nw - 1) sh[32] = w;
+  }
+  __syncthreads();
+  const int res = sh[wave] + incl - v;
+  total = sh[32];
+  __syncthreads();
+  return res;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs a) {
+  __shared__ int sh[33];
+  __shared__ long long red[kSchedThreads / 64];
+  SchedView sv(a);
+  const int tid = threadIdx.x;
+  const int nT = a.B * a.units * a.far_tiles;
+  const int per_b = a.units * a.far_tiles;
+  // pass 1: 64-key blocks of far work per tile
+  long long mine = 0;
+  for (int T_ = tid; T_ < nT; T_ += kSchedThreads) {
+    const int b = T_ / per_b, rem = T_ - b * per_b;
+    const int u = rem / a.far_tiles, t = rem - u * a.far_tiles;
+    const int g = (u * a.hpu) / a.HG;
+    const int c = a.cnt[b * a.G + g];
+    const int ntok = min(a.tpt_far, c - t * a.tpt_far);
+    int blocks = 0;
+    if (ntok > 0) {
+      const int tlast = a.idx[(int64_t(b) * a.G + g) * a.N + t * a.tpt_far + ntok - 1];
+      const int fh = tlast - a.W;
+      if (fh >= 0) blocks = fh / kBN + 1;
+    }
+    sv.n_items[T_] = blocks;
+    mine += blocks;
+  }
+  for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = mine;
+  __syncthreads();
+  long long total_blocks = 0;
+  for (int w = 0; w < kSchedThreads / 64; ++w) total_blocks += red[w];
+  const int cb = int(max<long long>(kMinChunkBlocks, (total_blocks + kTargetItems - 1) / kTargetItems));
+  // pass 2: chunks per tile and their exclusive prefix
+  int carry = 0;
+  for (int base = 0; base < nT; base += kSchedThreads) {
+    const int T_ = base + tid;
+    const int v = T_ < nT ? (sv.n_items[T_] + cb - 1) / cb : 0;
+    int tot;
+    const int ex = block_excl_scan(v, sh, tot);
+    if (T_ < nT) {
+      sv.item_start[T_] = carry + ex;
+      sv.n_items[T_] = v;
+    }
+    carry += tot;
+  }
+  // pass 3: item list
+  for (int T_ = tid; T_ < nT; T_ += kSchedThreads) {
+    const int s = sv.item_start[T_], n = sv.n_items[T_];
+    for (int k = 0; k < n; ++k) {
+      sv.item_tile[s + k] = T_;
+      sv.item_chunk[s + k] = k;
+    }
+  }
+  // gathered (row, head) pairs per (batch, unit), for the merge
+  if (tid == 0) {
+    int s = 0;
+    for (int bu = 0; bu < a.B * a.units; ++bu) {
+      const int b = bu / a.units, u = bu - b * a.units;
+      const int g = (u * a.hpu) / a.HG;
+      sv.pair_start[bu] = s;
+      s += a.cnt[b * a.G + g] * a.hpu;
+    }
+    sv.pair_start[a.B * a.units] = s;
+    a.sched[0] = carry;
+    a.sched[1] = cb;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Far part of the full branch for gathered rows.  One workgroup per work
+// item (tile, chunk); grid = upper bound, idle workgroups exit at once.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, 2) void far_kernel(PrefillArgs a) {
+  using Core = typename CoreSel<T, D>::type;
+  __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
+  const int item = blockIdx.x;
+  if (item >= a.sched[0]) return;
+  SchedView sv(a);
+  const int cb = a.sched[1];
+  const int T_ = sv.item_tile[item], ch = sv.item_chunk[item];
+  const int per_b = a.units * a.far_tiles;
+  const int b = T_ / per_b, rem = T_ - b * per_b;
+  const int u = rem / a.far_tiles, t = rem - u * a.far_tiles;
+  const int g_gate = (u * a.hpu) / a.HG;
+  const int kvh = (u * a.hpu) / a.HK;
+  const int c = a.cnt[b * a.G + g_gate];
+  const int32_t* ix = a.idx + (int64_t(b) * a.G + g_gate) * a.N;
+  const int ntok = min(a.tpt_far, c - t * a.tpt_far);
+  const int far_hi = ix[t * a.tpt_far + ntok - 1] - a.W;
+  const int c0 = ch * cb * kBN;
+  const int c1 = min(far_hi + 1, (ch + 1) * cb * kBN);  // keys [c0, c1)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane & 31, g = lane >> 5;
+  const int r = wave * kQR + q;
+  const int slot = r / a.hpu, hh = r - slot * a.hpu;
+  const bool valid = slot < ntok;
+  const int tok = valid ? ix[t * a.tpt_far + slot] : 0;
+  const int h = u * a.hpu + hh;
+  const int lo = c0;
+  const int hi = valid ? min(tok - a.W, c1 - 1) : -1;
+  WaveBounds wb;
+  wb.init(valid, lo, hi);
+
+  Core c_;
+  c_.init();
+  const T* Qp = static_cast<const T*>(a.Q);
+  c_.load_q(valid ? Qp + ((int64_t(b) * a.N + tok) * a.Hq + h) * D : nullptr, g);
+  const T* Kb = static_cast<const T*>(a.K) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
+  const T* Vb = static_cast<const T*>(a.V) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
+  const int64_t rs = int64_t(a.Hkv) * D;
+  KVLoader<T, D, kThreads> ld;
+  ld.load(Kb, Vb, rs, c0, c1, tid);
+  for (int kb = c0; kb < c1; kb += kBN) {
+    __syncthreads();
+    ld.store(lds, tid);
+    __syncthreads();
+    if (kb + kBN < c1) ld.load(Kb, Vb, rs, kb + kBN, c1, tid);
+    if (wb.needed(kb)) c_.block(lds, kb, wb.masked(kb), lo, hi, a.sl2, q, g);
+  }
+  float lse2;
+  const float inv = finish_row(c_.m, c_.l, lse2);
+  if (valid) {
+    float* prow = a.part_o + (int64_t(item) * kRows + r) * D;
+    store_row<Core::MD>(prow, c_.acc, inv, g);
+    if (g == 0) a.part_lse[int64_t(item) * kRows + r] = lse2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge for gathered rows: O_FULL = LSE-weighted window output + far
+// partials.  Persistent grid; one wave per gathered (row, head) pair.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(PrefillArgs a) {
+  SchedView sv(a);
+  const int nbu = a.B * a.units;
+  const int total = sv.pair_start[nbu];
+  const int lane = threadIdx.x & 63;
+  const int nwaves = gridDim.x * (blockDim.x / 64);
+  constexpr int PL = D / 64;  // channels per lane
+  for (int p = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); p < total; p += nwaves) {
+    int lo = 0, hi = nbu - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sv.pair_start[mid] <= p) lo = mid;
+      else hi = mid - 1;
+    }
+    const int bu = lo;
+    const int b = bu / a.units, u = bu - b * a.units;
+    const int pp = p - sv.pair_start[bu];
+    const int gi = pp / a.hpu, hh = pp - gi * a.hpu;
+    const int g_gate = (u * a.hpu) / a.HG;
+    const int tok = a.idx[(int64_t(b) * a.G + g_gate) * a.N + gi];
+    if (tok < a.W) continue;  // far set empty: the window result is the full result
+    const int h = u * a.hpu + hh;
+    const int t = gi / a.tpt_far, slot = gi - t * a.tpt_far;
+    const int r = slot * a.hpu + hh;
+    const int T_ = (b * a.units + u) * a.far_tiles + t;
+    const int is = sv.item_start[T_], ni = sv.n_items[T_];
+    const float ls = a.lse_s[(int64_t(b) * a.Hq + h) * a.N + tok];
+    float M = ls;
+    for (int k = 0; k < ni; ++k) M = fmaxf(M, a.part_lse[int64_t(is + k) * kRows + r]);
+    const float ws = fast_exp2(ls - M);
+    float L = ws;
+    T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D;
+    float o[PL];
+#pragma unroll
+    for (int e = 0; e < PL; ++e) o[e] = ws * Elem<T>::load(orow + lane + 64 * e);
+    for (int k = 0; k < ni; ++k) {
+      const float w = fast_exp2(a.part_lse[int64_t(is + k) * kRows + r] - M);
+      L += w;
+      const float* prow = a.part_o + (int64_t(is + k) * kRows + r) * D;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) o[e] = fmaf(w, prow[lane + 64 * e], o[e]);
+    }
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) Elem<T>::store(orow + lane + 64 * e, o[e] * inv);
+  }
+}
+
+// Sum of squared differences of this lane's channels.  Contraction is off so
+// that the difference is taken between the two rounded outputs (a fused
+// multiply-subtract would leave the rounding error of one product behind
+// even when both branches saw the same keys).
+template <int MD>
+SWI_DEV float sq_distance(const f32x16 (&x)[MD], const f32x16 (&y)[MD]) {
+#pragma clang fp contract(off)
+  float dd = 0.f;
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float e = x[md][i] - y[md][i];
+      dd += e * e;
+    }
+  return dd;
+}
+
+// ---------------------------------------------------------------------------
+// Both-branch mode: causal pass per tile, window keys first (snapshot), then
+// the far keys.  Grid (band_tiles, B*Hkv), heaviest tiles launched first.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, 1) void fused_kernel(PrefillArgs a) {
+  using Core = typename CoreSel<T, D>::type;
+  constexpr int MD = Core::MD;
+  __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
+  const int tile = a.band_tiles - 1 - int(blockIdx.x);
+  const int b = blockIdx.y / a.Hkv, kvh = blockIdx.y - b * a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane & 31, g = lane >> 5;
+  const int q0 = tile * a.tpt_band;
+  const int qlast = min(a.N - 1, q0 + a.tpt_band - 1);
+  const int r = wave * kQR + q;
+  const int slot = r / a.HK, hh = r - slot * a.HK;
+  const int tok = q0 + slot;
+  const bool valid = slot < a.tpt_band && tok < a.N;
+  const int h = kvh * a.HK + hh;
+  // phase A: window keys; phase B: far keys [0, tok-W]
+  const int loA = valid ? max(0, tok - a.W + 1) : 0, hiA = valid ? tok : -1;
+  const int loB = 0, hiB = valid ? tok - a.W : -1;
+  WaveBounds wa, wbb;
+  wa.init(valid, loA, hiA);
+  wbb.init(valid, loB, hiB);
+  const int kbA = (max(0, q0 - a.W + 1) / kBN) * kBN;
+  const int nA = (qlast - kbA) / kBN + 1;
+  const int nB = qlast >= a.W ? (qlast - a.W) / kBN + 1 : 0;
+
+  Core c;
+  c.init();
+  const T* Qp = static_cast<const T*>(a.Q);
+  c.load_q(valid ? Qp + ((int64_t(b) * a.N + tok) * a.Hq + h) * D : nullptr, g);
+  const T* Kb = static_cast<const T*>(a.K) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
+  const T* Vb = static_cast<const T*>(a.V) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
+  const int64_t rs = int64_t(a.Hkv) * D;
+  f32x16 snap[MD];
+  KVLoader<T, D, kThreads> ld;
+  ld.load(Kb, Vb, rs, kbA, a.N, tid);
+  for (int n = 0; n < nA + nB; ++n) {
+    const bool phaseB = n >= nA;
+    const int kb = phaseB ? (n - nA) * kBN : kbA + n * kBN;
+    if (n == nA) {  // window done: snapshot O_SWA
+      float lse_unused;
+      const float inv_s = finish_row(c.m, c.l, lse_unused);
+#pragma unroll
+      for (int md = 0; md < MD; ++md) snap[md] = c.acc[md] * inv_s;
+    }
+    __syncthreads();
+    ld.store(lds, tid);
+    __syncthreads();
+    if (n + 1 < nA + nB) {
+      const int nk = (n + 1 >= nA) ? (n + 1 - nA) * kBN : kbA + (n + 1) * kBN;
+      ld.load(Kb, Vb, rs, nk, a.N, tid);
+    }
+    if (!phaseB) {
+      if (wa.needed(kb)) c.block(lds, kb, wa.masked(kb), loA, hiA, a.sl2, q, g);
+    } else {
+      if (wbb.needed(kb)) c.block(lds, kb, wbb.masked(kb), loB, hiB, a.sl2, q, g);
+    }
+  }
+  float lse2;
+  const float inv = finish_row(c.m, c.l, lse2);
+  if (nB == 0) {
+#pragma unroll
+    for (int md = 0; md < MD; ++md) snap[md] = c.acc[md] * inv;
+  }
+  f32x16 full[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) full[md] = c.acc[md] * inv;
+  float dd = sq_distance<MD>(full, snap);
+  dd += __shfl_xor(dd, 32, kWave);
+  if (valid) {
+    const int gg = h / a.HG;
+    const bool full_sel = a.gate[(int64_t(b) * a.N + tok) * a.G + gg] != 0;
+    T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) full[md] = full_sel ? full[md] : snap[md];
+    store_row<MD>(orow, full, 1.f, g);
+    if (g == 0) a.diffp[(int64_t(b) * a.Hq + h) * a.N + tok] = dd;
+  }
+}
+
+// diff[b,t] = sum over heads (in head order) of the per-head distances
+__global__ __launch_bounds__(256) void diff_kernel(PrefillArgs a) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= int64_t(a.B) * a.N) return;
+  const int b = int(i / a.N), t = int(i - int64_t(b) * a.N);
+  float s = 0.f;
+  for (int h = 0; h < a.Hq; ++h) s += a.diffp[(int64_t(b) * a.Hq + h) * a.N + t];
+  a.diff[i] = s;
+}
+
+// ---------------------------------------------------------------------------
+static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool plan_prefill(const PrefillShape& sh, PrefillPlan* p) {
+  p->HK = sh.Hq / sh.Hkv;
+  p->HG = sh.Hq / sh.G;
+  p->hpu = p->HK < p->HG ? p->HK : p->HG;
+  p->units = sh.Hq / p->hpu;
+  p->tpt_band = kRows / p->HK;
+  p->tpt_far = kRows / p->hpu;
+  p->band_tiles = (sh.N + p->tpt_band - 1) / p->tpt_band;
+  p->far_tiles = (sh.N + p->tpt_far - 1) / p->tpt_far;
+  const long long nT = (long long)sh.B * p->units * p->far_tiles;
+  const long long max_items = kTargetItems + nT;
+  if (max_items > INT_MAX / kRows) return false;
+  p->max_items = int(max_items);
+  const size_t rowsN = size_t(sh.B) * sh.Hq * sh.N;
+  size_t off = 0;
+  p->off_lse = p->off_sched = p->off_part_o = p->off_part_lse = p->off_diffp = 0;
+  if (!sh.both_branch) {
+    p->off_lse = off;
+    off = align_up(off + rowsN * 4);
+    p->off_sched = off;
+    const size_t sched_ints = 2 + 2 * size_t(nT) + size_t(sh.B) * p->units + 1 + 2 * size_t(max_items);
+    off = align_up(off + sched_ints * 4);
+    p->off_part_o = off;
+    off = align_up(off + size_t(max_items) * kRows * sh.d * 4);
+    p->off_part_lse = off;
+    off = align_up(off + size_t(max_items) * kRows * 4);
+  } else {
+    p->off_diffp = off;
+    off = align_up(off + rowsN * 4);
+  }
+  p->bytes = off;
+  return true;
+}
+
+template <typename T, int D>
+static hipError_t run_prefill(const PrefillShape& sh, const PrefillPlan& p, PrefillArgs& a,
+                              hipStream_t s) {
+  if (!sh.both_branch) {
+    hipLaunchKernelGGL((band_kernel<T, D>), dim3(p.band_tiles, sh.B * sh.Hkv), dim3(kThreads),
+                       0, s, a);
+    hipLaunchKernelGGL(far_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, a);
+    hipLaunchKernelGGL((far_kernel<T, D>), dim3(p.max_items), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((merge_kernel<T, D>), dim3(1024), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((fused_kernel<T, D>), dim3(p.band_tiles, sh.B * sh.Hkv), dim3(kThreads),
+                       0, s, a);
+    const long long n = (long long)sh.B * sh.N;
+    hipLaunchKernelGGL(diff_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const void* Q,
+                          const void* K, const void* V, const uint8_t* gate, const int32_t* idx,
+                          const int32_t* cnt, void* O, float* diff, void* ws, hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  PrefillArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.gate = gate;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.lse_s = sh.both_branch ? nullptr : reinterpret_cast<float*>(w + p.off_lse);
+  a.sched = sh.both_branch ? nullptr : reinterpret_cast<int32_t*>(w + p.off_sched);
+  a.part_o = sh.both_branch ? nullptr : reinterpret_cast<float*>(w + p.off_part_o);
+  a.part_lse = sh.both_branch ? nullptr : reinterpret_cast<float*>(w + p.off_part_lse);
+  a.diffp = sh.both_branch ? reinterpret_cast<float*>(w + p.off_diffp) : nullptr;
+  a.diff = diff;
+  a.B = sh.B;
+  a.N = sh.N;
+  a.Hq = sh.Hq;
+  a.Hkv = sh.Hkv;
+  a.G = sh.G;
+  a.W = sh.W;
+  a.HK = p.HK;
+  a.HG = p.HG;
+  a.hpu = p.hpu;
+  a.units = p.units;
+  a.tpt_band = p.tpt_band;
+  a.tpt_far = p.tpt_far;
+  a.band_tiles = p.band_tiles;
+  a.far_tiles = p.far_tiles;
+  a.max_items = p.max_items;
+  a.sl2 = sh.scale * kLog2e;
+  if (sh.f32) {
+    if (sh.d == 64) return run_prefill<float, 64>(sh, p, a, s);
+    return run_prefill<float, 128>(sh, p, a, s);
+  }
+  if (sh.d == 64) return run_prefill<bf16_t, 64>(sh, p, a, s);
+  return run_prefill<bf16_t, 128>(sh, p, a, s);
+}
+
+}  // namespace swi

@@ -1,0 +1,225 @@
+"""GPU parity of the HIP library against the float64 CPU reference.
+
+Every test calls the C ABI through the thin binding, on seeded inputs that
+are fed unchanged (same stored bf16/fp32 values) to the reference."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sliding_window_attention_router_amd import synth
+from tests.gpu_util import TOL, TORCH_DTYPE, dev, diff_tolerance, ensure_built, host, max_abs, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_built()
+
+
+def swa():
+    import sliding_window_attention_router_amd as m
+
+    return m
+
+
+def _qkv(seed, B, N, Hq, Hkv, d, dtype):
+    rng = np.random.default_rng(seed)
+    mk = (lambda s: synth.round_bf16(rng.standard_normal(s, dtype=np.float32))) if dtype == "bf16" \
+        else (lambda s: rng.standard_normal(s, dtype=np.float32))
+    return mk((B, N, Hq, d)), mk((B, N, Hkv, d)), mk((B, N, Hkv, d))
+
+
+def _gpu_prefill(Q, K, V, gate, W, dtype, both=False):
+    td = TORCH_DTYPE[dtype]
+    O, diff = swa().prefill(dev(Q, td), dev(K, td), dev(V, td), dev(gate), W, both_branch=both)
+    torch.cuda.synchronize()
+    return host(O), (host(diff) if diff is not None else None)
+
+
+# ---------------------------------------------------------------- router
+def test_route_layer_bf16():
+    w = synth.layer()
+    say(f"route layer: H {w.H.shape}")
+    gate, idx, cnt, z = swa().route(dev(w.H, torch.bfloat16), dev(w.r, torch.bfloat16),
+                                     dev(w.bias), want_z=True)
+    torch.cuda.synchronize()
+    ref = oracle.route(w.H, w.r, w.bias)
+    g_gpu = gate.cpu().numpy()
+    far = ~ref["near"]
+    assert np.array_equal(g_gpu[far], ref["gate"][far])
+    assert max_abs(host(z), ref["z"]) < 1e-3
+    idx_ref, cnt_ref = oracle.compact(g_gpu)
+    c = cnt.cpu().numpy()
+    assert np.array_equal(c, cnt_ref)
+    ih = idx.cpu().numpy()
+    for b in range(ih.shape[0]):
+        for g in range(ih.shape[1]):
+            assert np.array_equal(ih[b, g, : c[b, g]], idx_ref[b, g, : c[b, g]])
+    dens = g_gpu.mean()
+    say(f"route layer: density {dens:.4f}, near-threshold tokens {int(ref['near'].sum())}")
+    assert 0.09 < dens < 0.17
+
+
+def test_route_f32_groups_unaligned_hidden():
+    rng = np.random.default_rng(21)
+    H = rng.standard_normal((2, 777, 100), dtype=np.float32)
+    r = (rng.standard_normal((100, 3), dtype=np.float32) * 0.1).astype(np.float32)
+    bias = np.array([0.0, -0.3, 0.4], np.float32)
+    gate, idx, cnt, z = swa().route(dev(H), dev(r), dev(bias), want_z=True)
+    torch.cuda.synchronize()
+    ref = oracle.route(H, r, bias)
+    far = ~ref["near"]
+    assert np.array_equal(gate.cpu().numpy()[far], ref["gate"][far])
+    assert max_abs(host(z), ref["z"]) < 1e-4
+
+
+@pytest.mark.parametrize("B,N,G,p", [(2, 1000, 3, 0.2), (1, 1, 1, 1.0), (1, 31, 2, 0.0),
+                                     (3, 33, 1, 1.0), (1, 32768, 1, 0.13), (1, 40000, 2, 0.5)])
+def test_compaction_given_gate(B, N, G, p):
+    rng = np.random.default_rng(N + G)
+    gate = (rng.random((B, N, G)) < p).astype(np.uint8)
+    _, idx, cnt, _ = swa().route(None, gate=dev(gate))
+    torch.cuda.synchronize()
+    idx_ref, cnt_ref = oracle.compact(gate)
+    c = cnt.cpu().numpy()
+    assert np.array_equal(c, cnt_ref)
+    ih = idx.cpu().numpy()
+    for b in range(B):
+        for g in range(G):
+            assert np.array_equal(ih[b, g, : c[b, g]], idx_ref[b, g, : c[b, g]])
+
+
+# ---------------------------------------------------------------- prefill
+@pytest.mark.parametrize("G", [2, 1])
+def test_prefill_tiny_f32(G):
+    w = synth.tiny(G=G)
+    O, _ = _gpu_prefill(w.Q, w.K, w.V, w.gate, w.W, "f32")
+    ref = oracle.prefill(w.Q, w.K, w.V, w.gate, w.W)["O"]
+    err = max_abs(O, ref)
+    say(f"tiny f32 G={G}: max-abs {err:.3e}")
+    assert err <= TOL["f32"]
+
+
+PREFILL_CASES = [
+    # B, N,   Hq, Hkv, G, d,  W,   p,   dtype
+    (1, 1000, 8, 2, 1, 128, 200, 0.2, "bf16"),   # GQA 4:1, ragged tail
+    (2, 777, 4, 4, 2, 64, 100, 0.3, "bf16"),     # MHA, two gate groups, d=64
+    (1, 530, 8, 1, 4, 128, 64, 0.5, "bf16"),     # gate groups inside one KV group
+    (1, 300, 2, 2, 2, 128, 512, 0.5, "bf16"),    # W > N
+    (1, 129, 4, 2, 1, 128, 64, 0.5, "bf16"),     # N just past a tile
+    (1, 5, 2, 1, 1, 64, 3, 0.5, "bf16"),         # N smaller than a block
+    (1, 400, 4, 2, 2, 128, 70, 0.4, "f32"),      # fp32 path, GQA
+]
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,G,d,W,p,dtype", PREFILL_CASES)
+def test_prefill_hard_gate(B, N, Hq, Hkv, G, d, W, p, dtype):
+    say(f"prefill case B={B} N={N} Hq={Hq} Hkv={Hkv} G={G} d={d} W={W} p={p} {dtype}")
+    Q, K, V = _qkv(N * 7 + d, B, N, Hq, Hkv, d, dtype)
+    gate = (np.random.default_rng(N).random((B, N, G)) < p).astype(np.uint8)
+    O, _ = _gpu_prefill(Q, K, V, gate, W, dtype)
+    ref = oracle.prefill(Q, K, V, gate, W)["O"]
+    err = max_abs(O, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("mode", ["zeros", "ones"])
+def test_prefill_gate_bounds(mode):
+    B, N, Hq, Hkv, G, d, W = 1, 700, 8, 2, 1, 128, 128
+    Q, K, V = _qkv(3, B, N, Hq, Hkv, d, "bf16")
+    gate = np.full((B, N, G), 1 if mode == "ones" else 0, np.uint8)
+    O, _ = _gpu_prefill(Q, K, V, gate, W, "bf16")
+    ref = oracle.prefill(Q, K, V, gate, W)["O"]
+    err = max_abs(O, ref)
+    say(f"gate all-{mode}: max-abs {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_prefill_window_one_is_v_exactly():
+    B, N, Hq, Hkv, G, d = 1, 300, 4, 2, 1, 128
+    Q, K, V = _qkv(4, B, N, Hq, Hkv, d, "bf16")
+    gate = np.zeros((B, N, G), np.uint8)
+    O, _ = _gpu_prefill(Q, K, V, gate, 1, "bf16")
+    for h in range(Hq):
+        assert np.array_equal(O[:, :, h], V[:, :, h // 2].astype(np.float64))
+
+
+def test_prefill_window_covering_sequence_is_gate_independent():
+    B, N, Hq, Hkv, G, d = 1, 250, 4, 1, 1, 128
+    Q, K, V = _qkv(5, B, N, Hq, Hkv, d, "bf16")
+    g0 = np.zeros((B, N, G), np.uint8)
+    g1 = np.ones((B, N, G), np.uint8)
+    O0, _ = _gpu_prefill(Q, K, V, g0, N, "bf16")
+    O1, _ = _gpu_prefill(Q, K, V, g1, N, "bf16")
+    assert max_abs(O0, O1) <= 2 * TOL["bf16"] and max_abs(O0, oracle.prefill(Q, K, V, g0, N)["O"]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("Hq,Hkv,G,W", [(4, 4, 1, 128), (8, 2, 2, 100)])
+def test_prefill_both_branch(Hq, Hkv, G, W):
+    B, N, d = 1, 600, 128
+    Q, K, V = _qkv(6, B, N, Hq, Hkv, d, "bf16")
+    rng = np.random.default_rng(7)
+    gate = np.stack([synth.structured_gate(rng, N, 0.3, 16, 64) for _ in range(G)], -1)[None]
+    O, diff = _gpu_prefill(Q, K, V, gate, W, "bf16", both=True)
+    ref = oracle.prefill(Q, K, V, gate, W, both_branch=True)
+    err = max_abs(O, ref["O"])
+    derr = np.abs(diff - ref["diff"])
+    tol = diff_tolerance(ref["diff"], Hq * d, TOL["bf16"])
+    say(f"both-branch: O max-abs {err:.3e}; diff max-abs {derr.max():.3e} "
+        f"(max rel {np.max(derr / np.maximum(ref['diff'], 1e-30)):.3e})")
+    assert err <= TOL["bf16"]
+    assert np.all(derr <= tol)
+    assert np.all(diff[:, :W] == 0.0)  # identical key sets before the window fills
+
+
+def test_prefill_deterministic():
+    B, N, Hq, Hkv, G, d, W = 1, 900, 8, 2, 1, 128, 128
+    Q, K, V = _qkv(8, B, N, Hq, Hkv, d, "bf16")
+    gate = (np.random.default_rng(9).random((B, N, G)) < 0.2).astype(np.uint8)
+    a, _ = _gpu_prefill(Q, K, V, gate, W, "bf16")
+    b, _ = _gpu_prefill(Q, K, V, gate, W, "bf16")
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- decode
+DECODE_CASES = [
+    # B, Lmax, Hq, Hkv, G, d, W, lens, dtype
+    (5, 700, 8, 2, 2, 128, 100, [700, 1, 99, 100, 350], "bf16"),
+    (3, 513, 8, 1, 4, 128, 64, [513, 200, 64], "bf16"),   # gate groups inside a KV group
+    (4, 300, 4, 4, 1, 64, 50, [300, 3, 51, 257], "bf16"),
+    (2, 260, 2, 1, 1, 128, 40, [260, 17], "f32"),
+]
+
+
+@pytest.mark.parametrize("B,Lmax,Hq,Hkv,G,d,W,lens,dtype", DECODE_CASES)
+def test_decode(B, Lmax, Hq, Hkv, G, d, W, lens, dtype):
+    say(f"decode case B={B} Lmax={Lmax} Hq={Hq} Hkv={Hkv} G={G} d={d} W={W} {dtype}")
+    rng = np.random.default_rng(Lmax)
+    mk = (lambda s: synth.round_bf16(rng.standard_normal(s, dtype=np.float32))) if dtype == "bf16" \
+        else (lambda s: rng.standard_normal(s, dtype=np.float32))
+    q, Kc, Vc = mk((B, Hq, d)), mk((B, Lmax, Hkv, d)), mk((B, Lmax, Hkv, d))
+    gate = (rng.random((B, G)) < 0.5).astype(np.uint8)
+    gate[0, :] = 1
+    lens = np.array(lens, np.int32)
+    td = TORCH_DTYPE[dtype]
+    o = swa().decode(dev(q, td), dev(Kc, td), dev(Vc, td), dev(lens), dev(gate), W)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q, Kc, Vc, lens, gate, W)["o"]
+    err = max_abs(host(o), ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+def test_decode_matches_prefill_last_row():
+    B, N, Hq, Hkv, G, d, W = 1, 640, 8, 2, 1, 128, 96
+    Q, K, V = _qkv(10, B, N, Hq, Hkv, d, "bf16")
+    for g in (0, 1):
+        gate = np.full((B, N, G), g, np.uint8)
+        O, _ = _gpu_prefill(Q, K, V, gate, W, "bf16")
+        o = swa().decode(dev(Q[:, -1], torch.bfloat16), dev(K, torch.bfloat16), dev(V, torch.bfloat16),
+                         dev(np.array([N], np.int32)), dev(gate[:, -1]), W)
+        torch.cuda.synchronize()
+        assert max_abs(host(o), O[:, -1]) <= 2 * TOL["bf16"]
