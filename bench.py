@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the SwiAttn routed hot path on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input:
+  router over the hidden states of a 32K-token sequence -> hard gate ->
+  compaction of the full-branch tokens -> routed prefill (window branch for
+  every row, far part of the full branch for the gathered rows, log-sum-exp
+  merge) at N=32768, 16 query / 4 KV heads, d=128, W=1024, bf16;
+  then one routed decode step for 64 sequences on a 32768-token shared bf16
+  KV cache (16/4 heads, d=128, W=1024, per-sequence gate Bernoulli(0.13)).
+
+The router inputs are H ~ N(0,1), r ~ N(0, 1/2048) and a bias set for a 13%
+full-branch fraction; the hidden rows are i.i.d., so the gate bits are
+i.i.d. Bernoulli(0.13).  Inputs are synthetic and seeded; they stand in for
+the evaluation data of the SwiAttn report, which needs trained weights.
+
+Prints ONE JSON line.  `value` is the routed prefill's useful TFLOP/s
+(4*d per attended (query head, key) pair at the realized gate, timed from
+the router to the merge); decode tokens/s and GB/s are reported beside it.
+`roofline` covers the kernel with the largest share of the step's time,
+timed with HIP events recorded on its launch stream inside the library.
+`cpu_baseline` times the float64 CPU reference on a bounded sample of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the CPU reference sample (0 = skip)")
+    ap.add_argument("--p", type=float, default=0.13, help="full-branch fraction")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ accounting
+def prefill_pairs(gate, W, Hq, G):
+    """Attended (query head, key) pairs: full rows see i+1 keys, window rows
+    min(i+1, W).  Returns (useful total, window part, far part)."""
+    B, N, _ = gate.shape
+    i = np.arange(N, dtype=np.int64)
+    band = np.minimum(i + 1, W)
+    far = np.maximum(i + 1 - W, 0)
+    tot_b = tot_f = 0
+    for h in range(Hq):
+        g = gate[:, :, h * G // Hq].astype(bool)
+        tot_b += int(band.sum()) * B
+        tot_f += int((far[None, :] * g).sum())
+    return tot_b + tot_f, tot_b, tot_f
+
+
+def decode_bytes(gate, cache_len, W, Hq, Hkv, d, elem=2):
+    """Algorithmic HBM bytes of one decode step: every attended key and value
+    row of a KV head is read once for its Hq/Hkv query heads, plus q and o."""
+    B, G = gate.shape
+    HK = Hq // Hkv
+    keys = 0
+    for b in range(B):
+        L = int(cache_len[b])
+        for kv in range(Hkv):
+            full = any(gate[b, (kv * HK + j) * G // Hq] for j in range(HK))
+            keys += L if full else min(L, W)
+    return keys * d * 2 * elem + B * Hq * d * 2 * elem, keys
+
+
+# ------------------------------------------------------------------ main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "the multi-GPU sharding is described but not implemented.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sliding_window_attention_router_amd as swa
+    from sliding_window_attention_router_amd import binding, synth
+
+    if not os.path.exists(binding.LIB_PATH):
+        from sliding_window_attention_router_amd import build
+
+        build.build()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    N, Hq, Hkv, d, W, hidden = 32768, 16, 4, 128, 1024, 2048
+    B_dec, L_dec = 64, 32768
+    t0 = time.time()
+    pre = synth.long_prefill(seed=3, N=N, Hq=Hq, Hkv=Hkv, d=d, W=W, p=args.p, with_router=True,
+                             hidden=hidden)
+    bf = torch.bfloat16
+    Q = torch.from_numpy(pre.Q).to(bf).to(dev)
+    K = torch.from_numpy(pre.K).to(bf).to(dev)
+    V = torch.from_numpy(pre.V).to(bf).to(dev)
+    H = torch.from_numpy(pre.H).to(bf).to(dev)
+    r = torch.from_numpy(pre.r).to(bf).to(dev)
+    bias = torch.from_numpy(pre.bias).to(dev)
+    dec = synth.decode_cache(seed=5, B=B_dec, Lmax=L_dec, Hq=Hq, Hkv=Hkv, d=d, W=W, p=args.p,
+                             device=dev)
+    q_d, Kc, Vc = dec["q"], dec["Kc"], dec["Vc"]
+    gate_d = torch.from_numpy(dec["gate"]).to(dev)
+    len_d = torch.from_numpy(dec["cache_len"]).to(dev)
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    G = 1
+    gate = torch.empty((1, N, G), dtype=torch.uint8, device=dev)
+    idx = torch.empty((1, G, N), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1, G), dtype=torch.int32, device=dev)
+    O = torch.empty_like(Q)
+    o_d = torch.empty_like(q_d)
+    ws_p = torch.empty(swa.prefill_workspace_size(1, N, Hq, Hkv, G, d, W), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(swa.decode_workspace_size(B_dec, L_dec, Hq, Hkv, G, d, W), dtype=torch.uint8,
+                       device=dev)
+
+    def new_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record()
+        return evs
+
+    def step(ev=None):
+        # ev: 11 events: [route start] + prefill stages 0..4 + decode stages 0..3 + [end]
+        if ev is not None:
+            ev[0].record()
+        swa.route(H, r, bias, out=(gate, idx, cnt))
+        swa.prefill(Q, K, V, gate, W, idx=idx, cnt=cnt, out=O, workspace=ws_p,
+                    events=ev[1:6] if ev is not None else None)
+        swa.decode(q_d, Kc, Vc, len_d, gate_d, W, out=o_d, workspace=ws_d,
+                   events=ev[6:10] if ev is not None else None)
+        if ev is not None:
+            ev[10].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evsets = [new_events(11) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(evsets[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    print(f"[bench] {args.steps} timed steps in {wall:.3f}s", file=sys.stderr, flush=True)
+
+    def avg(i, j):
+        return float(np.mean([e[i].elapsed_time(e[j]) for e in evsets]))
+
+    t = {
+        "route_compact": avg(0, 1),
+        "band": avg(1, 2),
+        "far_schedule": avg(2, 3),
+        "far": avg(3, 4),
+        "merge": avg(4, 5),
+        "decode_schedule": avg(6, 7),
+        "decode_splitk": avg(7, 8),
+        "decode_merge": avg(8, 9),
+    }
+    prefill_ms = avg(0, 5)
+    decode_ms = avg(6, 9)
+    step_ms = wall * 1e3 / args.steps
+
+    g_host = gate.cpu().numpy()
+    useful, band_pairs, far_pairs = prefill_pairs(g_host, W, Hq, G)
+    fl = 4.0 * d
+    prefill_tflops = useful * fl / (prefill_ms * 1e-3) / 1e12
+    dbytes, dkeys = decode_bytes(dec["gate"], dec["cache_len"], W, Hq, Hkv, d)
+    decode_gbs = dbytes / (decode_ms * 1e-3) / 1e9
+    decode_tok_s = B_dec / (decode_ms * 1e-3)
+
+    kern = {
+        "band": {"bound": "mfma", "work": band_pairs * fl, "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS},
+        "far": {"bound": "mfma", "work": far_pairs * fl, "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS},
+        "decode_splitk": {"bound": "hbm", "work": dbytes, "unit": "GB/s", "peak": HBM_PEAK_GBS},
+    }
+    rooflines = {}
+    for name, k in kern.items():
+        ms = t[name]
+        scale = 1e12 if k["unit"] == "TFLOP/s" else 1e9
+        ach = k["work"] / (ms * 1e-3) / scale
+        rooflines[name] = {"bound": k["bound"], "achieved": round(ach, 2), "peak": k["peak"],
+                           "unit": k["unit"], "frac": round(ach / k["peak"], 4), "ms": round(ms, 4),
+                           "traffic": None}
+    dominant = max(kern, key=lambda n: t[n])
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(pre, W, args.cpu_seconds)
+
+    realized_p = float(g_host.mean())
+    out = {
+        "metric": "routed prefill useful TFLOP/s + decode tok/s, N=32K W=1024, % roofline",
+        "value": round(prefill_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V/H and KV cache; router-made gate, i.i.d. Bernoulli(0.13))",
+        "config": {
+            "workload": "routed prefill N=32768 Hq=16 Hkv=4 d=128 W=1024 (router on hidden 2048) "
+                        "+ routed decode B=64 cache 32768 Hq=16 Hkv=4 d=128 W=1024",
+            "prefill": {"B": 1, "N": N, "Hq": Hq, "Hkv": Hkv, "d": d, "W": W, "hidden": hidden,
+                        "gate_density": round(realized_p, 5), "useful_pairs": useful,
+                        "useful_tflop": round(useful * fl / 1e12, 4), "ms": round(prefill_ms, 4),
+                        "frac_of_bf16_peak": round(prefill_tflops / BF16_PEAK_TFLOPS, 4)},
+            "decode": {"B": B_dec, "cache_len": L_dec, "Hq": Hq, "Hkv": Hkv, "d": d, "W": W,
+                       "full_sequences": int(dec["gate"].sum()), "attended_kv_rows": dkeys,
+                       "bytes": dbytes, "ms": round(decode_ms, 4),
+                       "tok_per_s": round(decode_tok_s, 1), "GB_per_s": round(decode_gbs, 1),
+                       "frac_of_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4)},
+        },
+        "kernel_ms": {k: round(v, 4) for k, v in t.items()},
+        "roofline": dict(rooflines[dominant], kernel=dominant),
+        "rooflines": rooflines,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(pre, W, budget_s):
+    """Float64 CPU reference on a bounded, evenly spaced sample of the
+    prefill rows (router over every token, then both branches' rows as the
+    gate picks them), scaled to useful TFLOP/s."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    Hq, d = pre.Q.shape[2], pre.Q.shape[3]
+    N = pre.Q.shape[1]
+    t0 = time.perf_counter()
+    rt = oracle.route(pre.H, pre.r, pre.bias)
+    gate = rt["gate"]
+    stride = 41  # coprime with every tile size: rows spread over all positions
+    rows_all = np.arange(0, N, stride)
+    rng = np.random.default_rng(0)
+    rng.shuffle(rows_all)
+    done, pairs = 0, 0
+    for s in range(0, rows_all.size, 16):
+        rows = np.sort(rows_all[s:s + 16])
+        oracle.prefill(pre.Q, pre.K, pre.V, gate, W, rows=rows)
+        for i in rows:
+            pairs += Hq * ((i + 1) if gate[0, i, 0] else min(i + 1, W))
+        done += rows.size
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(pairs * 4.0 * d / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"router over all {N} tokens + {done} evenly spaced prefill rows x {Hq} heads "
+                      f"({pairs} useful pairs) in {el:.1f}s, float64 numpy"}
+
+
+if __name__ == "__main__":
+    main()

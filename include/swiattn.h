@@ -157,6 +157,36 @@ int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t*
                    int d, int W, float scale, swiattn_dtype_t dtype, void* ws,
                    size_t ws_bytes, swiattn_stream_t stream);
 
+/*
+ * Stage timing (for profilers and benchmarks).  `events` holds up to six
+ * hipEvent_t handles created by the caller (stored as void*; NULL entries
+ * are skipped).  The _ex calls behave exactly like the plain ones and in
+ * addition record ev[i] on `stream` at stage boundary i:
+ *   prefill, hard-gate mode: 0 before the window kernel, 1 after it,
+ *     2 after the far-part schedule, 3 after the far kernel, 4 after the
+ *     merge;
+ *   prefill, both-branch mode: 0 before the fused kernel, 1 after it,
+ *     2 after the per-token head sum;
+ *   decode: 0 before the schedule, 1 after it, 2 after the split-K kernel,
+ *     3 after the merge.
+ * Passing events == NULL is the plain call.  Recording failures are
+ * reported as SWIATTN_ERR_HIP.
+ */
+typedef struct {
+  void* ev[6];
+} swiattn_events_t;
+
+int swiattn_prefill_ex(const void* Q, const void* K, const void* V, const uint8_t* gate,
+                       const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B,
+                       int N, int Hq, int Hkv, int G, int d, int W, float scale,
+                       swiattn_dtype_t dtype, unsigned flags, void* ws, size_t ws_bytes,
+                       swiattn_stream_t stream, const swiattn_events_t* events);
+
+int swiattn_decode_ex(const void* q, const void* Kc, const void* Vc, const int32_t* cache_len,
+                      const uint8_t* gate, void* o, int B, int Lmax, int Hq, int Hkv, int G,
+                      int d, int W, float scale, swiattn_dtype_t dtype, void* ws,
+                      size_t ws_bytes, swiattn_stream_t stream, const swiattn_events_t* events);
+
 /* Static text for an error code. */
 const char* swiattn_strerror(int code);
 

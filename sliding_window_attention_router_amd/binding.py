@@ -40,6 +40,8 @@ SYMBOLS = {
     "swiattn_prefill": (_i32, [_vp] * 8 + [_i32] * 7 + [_f32, _i32, _u32, _vp, _sz, _vp]),
     "swiattn_decode_workspace_size": (_sz, [_i32] * 8),
     "swiattn_decode": (_i32, [_vp] * 6 + [_i32] * 7 + [_f32, _i32, _vp, _sz, _vp]),
+    "swiattn_prefill_ex": (_i32, [_vp] * 8 + [_i32] * 7 + [_f32, _i32, _u32, _vp, _sz, _vp, _vp]),
+    "swiattn_decode_ex": (_i32, [_vp] * 6 + [_i32] * 7 + [_f32, _i32, _vp, _sz, _vp, _vp]),
     "swiattn_strerror": (ctypes.c_char_p, [_i32]),
     "swiattn_version": (ctypes.c_char_p, []),
 }
@@ -47,6 +49,24 @@ SYMBOLS = {
 
 class SwiAttnError(RuntimeError):
     pass
+
+
+class _Events(ctypes.Structure):
+    _fields_ = [("ev", ctypes.c_void_p * 6)]
+
+
+def _events(events):
+    """List of up to six torch.cuda.Event (or None) -> swiattn_events_t*.
+    Each event must have been recorded once so that it exists."""
+    if events is None:
+        return None
+    st = _Events()
+    for i, e in enumerate(events):
+        if e is not None:
+            if not e.cuda_event:
+                raise ValueError("record each event once before passing it (torch creates events lazily)")
+            st.ev[i] = e.cuda_event
+    return ctypes.byref(st)
 
 
 _lib = None
@@ -108,12 +128,13 @@ def _need(t, name, shape=None, dtype=None, device=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def route(H=None, r=None, bias=None, *, gate=None, want_z=False):
+def route(H=None, r=None, bias=None, *, gate=None, want_z=False, out=None):
     """Router logits, hard gate and compaction.
 
     H [B,N,hidden], r [hidden,G] (bf16 or fp32), bias [G] fp32 -> gate.
     Pass H=None and gate=[B,N,G] uint8 to only compact a given gate.
     Returns (gate uint8 [B,N,G], idx int32 [B,G,N], cnt int32 [B,G], z or None).
+    out: optional (gate, idx, cnt) tensors to write into.
     """
     L = lib()
     if H is None:
@@ -131,10 +152,16 @@ def route(H=None, r=None, bias=None, *, gate=None, want_z=False):
             raise ValueError("r must be [hidden, G]")
         G = r.shape[1]
         _need(bias, "bias", shape=(G,), dtype=torch.float32, device=dev)
-        gate = torch.empty((B, N, G), dtype=torch.uint8, device=dev)
+        gate = out[0] if out is not None else torch.empty((B, N, G), dtype=torch.uint8, device=dev)
+        _need(gate, "gate", shape=(B, N, G), dtype=torch.uint8, device=dev)
         z = torch.empty((B, N, G), dtype=torch.float32, device=dev) if want_z else None
-    idx = torch.empty((B, G, N), dtype=torch.int32, device=dev)
-    cnt = torch.empty((B, G), dtype=torch.int32, device=dev)
+    if out is not None:
+        idx, cnt = out[1], out[2]
+        _need(idx, "idx", shape=(B, G, N), dtype=torch.int32, device=dev)
+        _need(cnt, "cnt", shape=(B, G), dtype=torch.int32, device=dev)
+    else:
+        idx = torch.empty((B, G, N), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, G), dtype=torch.int32, device=dev)
     rc = L.swiattn_route(_p(H), _p(r), _p(bias), _p(gate), _p(z), _p(idx), _p(cnt),
                          B, N, hidden, G, code, _stream(dev))
     _check(rc, "swiattn_route")
@@ -160,12 +187,14 @@ def _workspace(nbytes, device, workspace):
 
 
 def prefill(Q, K, V, gate, W, *, idx=None, cnt=None, scale=None, both_branch=False,
-            out=None, diff=None, workspace=None):
+            out=None, diff=None, workspace=None, events=None):
     """Dual-branch prefill.  Q [B,N,Hq,d], K/V [B,N,Hkv,d], gate [B,N,G] uint8.
 
     In hard-gate mode the compacted positions (idx, cnt) from route() are
     used, or computed here by the library's compaction if not given.
     Returns (O [B,N,Hq,d], diff [B,N] fp32 or None).
+    events: optional torch.cuda.Event list recorded at the stage boundaries
+    documented for swiattn_prefill_ex.
     """
     L = lib()
     _need(Q, "Q")
@@ -200,17 +229,18 @@ def prefill(Q, K, V, gate, W, *, idx=None, cnt=None, scale=None, both_branch=Fal
     flags = FLAG_BOTH_BRANCH if both_branch else 0
     nbytes = int(L.swiattn_prefill_workspace_size(B, N, Hq, Hkv, G, d, W, code, flags))
     ws = _workspace(nbytes, dev, workspace)
-    rc = L.swiattn_prefill(_p(Q), _p(K), _p(V), _p(gate), _p(idx if not both_branch else None),
-                           _p(cnt if not both_branch else None), _p(out), _p(diff),
-                           B, N, Hq, Hkv, G, d, W, float(scale), code, flags,
-                           _p(ws), ws.numel(), _stream(dev))
+    rc = L.swiattn_prefill_ex(_p(Q), _p(K), _p(V), _p(gate), _p(idx if not both_branch else None),
+                              _p(cnt if not both_branch else None), _p(out), _p(diff),
+                              B, N, Hq, Hkv, G, d, W, float(scale), code, flags,
+                              _p(ws), ws.numel(), _stream(dev), _events(events))
     _check(rc, "swiattn_prefill")
     return out, diff
 
 
-def decode(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None, workspace=None):
+def decode(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None, workspace=None, events=None):
     """Routed decode.  q [B,Hq,d], Kc/Vc [B,Lmax,Hkv,d], cache_len int32 [B],
-    gate uint8 [B,G].  Returns o [B,Hq,d]."""
+    gate uint8 [B,G].  Returns o [B,Hq,d].  events: as for prefill, recorded
+    at the stage boundaries documented for swiattn_decode_ex."""
     L = lib()
     _need(q, "q")
     code = _dtype_code(q)
@@ -233,8 +263,8 @@ def decode(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None, workspace=Non
     _need(out, "out", shape=q.shape, dtype=q.dtype, device=dev)
     nbytes = int(L.swiattn_decode_workspace_size(B, Lmax, Hq, Hkv, G, d, W, code))
     ws = _workspace(nbytes, dev, workspace)
-    rc = L.swiattn_decode(_p(q), _p(Kc), _p(Vc), _p(cache_len), _p(gate), _p(out),
-                          B, Lmax, Hq, Hkv, G, d, W, float(scale), code, _p(ws), ws.numel(),
-                          _stream(dev))
+    rc = L.swiattn_decode_ex(_p(q), _p(Kc), _p(Vc), _p(cache_len), _p(gate), _p(out),
+                             B, Lmax, Hq, Hkv, G, d, W, float(scale), code, _p(ws), ws.numel(),
+                             _stream(dev), _events(events))
     _check(rc, "swiattn_decode")
     return out

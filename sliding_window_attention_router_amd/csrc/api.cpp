@@ -100,10 +100,11 @@ size_t swiattn_prefill_workspace_size(int B, int N, int Hq, int Hkv, int G, int 
   return p.bytes;
 }
 
-int swiattn_prefill(const void* Q, const void* K, const void* V, const uint8_t* gate,
-                    const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B, int N,
-                    int Hq, int Hkv, int G, int d, int W, float scale, swiattn_dtype_t dtype,
-                    unsigned flags, void* ws, size_t ws_bytes, swiattn_stream_t stream) {
+int swiattn_prefill_ex(const void* Q, const void* K, const void* V, const uint8_t* gate,
+                       const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B,
+                       int N, int Hq, int Hkv, int G, int d, int W, float scale,
+                       swiattn_dtype_t dtype, unsigned flags, void* ws, size_t ws_bytes,
+                       swiattn_stream_t stream, const swiattn_events_t* events) {
   swi::PrefillShape sh;
   swi::PrefillPlan p;
   const int rc = prefill_shape(B, N, Hq, Hkv, G, d, W, scale, dtype, flags, &sh, &p);
@@ -112,7 +113,16 @@ int swiattn_prefill(const void* Q, const void* K, const void* V, const uint8_t* 
   if (sh.both_branch ? !diff : (!idx || !cnt)) return SWIATTN_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.bytes) return SWIATTN_ERR_WORKSPACE;
   return hip_rc(swi::launch_prefill(sh, p, Q, K, V, gate, idx, cnt, O, diff, ws,
-                                    reinterpret_cast<hipStream_t>(stream)));
+                                    reinterpret_cast<hipStream_t>(stream),
+                                    events ? events->ev : nullptr));
+}
+
+int swiattn_prefill(const void* Q, const void* K, const void* V, const uint8_t* gate,
+                    const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B, int N,
+                    int Hq, int Hkv, int G, int d, int W, float scale, swiattn_dtype_t dtype,
+                    unsigned flags, void* ws, size_t ws_bytes, swiattn_stream_t stream) {
+  return swiattn_prefill_ex(Q, K, V, gate, idx, cnt, O, diff, B, N, Hq, Hkv, G, d, W, scale,
+                            dtype, flags, ws, ws_bytes, stream, nullptr);
 }
 
 size_t swiattn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int G, int d, int W,
@@ -123,10 +133,10 @@ size_t swiattn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int G, in
   return p.bytes;
 }
 
-int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t* cache_len,
-                   const uint8_t* gate, void* o, int B, int Lmax, int Hq, int Hkv, int G, int d,
-                   int W, float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
-                   swiattn_stream_t stream) {
+int swiattn_decode_ex(const void* q, const void* Kc, const void* Vc, const int32_t* cache_len,
+                      const uint8_t* gate, void* o, int B, int Lmax, int Hq, int Hkv, int G,
+                      int d, int W, float scale, swiattn_dtype_t dtype, void* ws,
+                      size_t ws_bytes, swiattn_stream_t stream, const swiattn_events_t* events) {
   swi::DecodeShape sh;
   swi::DecodePlan p;
   const int rc = decode_shape(B, Lmax, Hq, Hkv, G, d, W, scale, dtype, &sh, &p);
@@ -134,7 +144,16 @@ int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t*
   if (!q || !Kc || !Vc || !cache_len || !gate || !o) return SWIATTN_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.bytes) return SWIATTN_ERR_WORKSPACE;
   return hip_rc(swi::launch_decode(sh, p, q, Kc, Vc, cache_len, gate, o, ws,
-                                   reinterpret_cast<hipStream_t>(stream)));
+                                   reinterpret_cast<hipStream_t>(stream),
+                                   events ? events->ev : nullptr));
+}
+
+int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t* cache_len,
+                   const uint8_t* gate, void* o, int B, int Lmax, int Hq, int Hkv, int G, int d,
+                   int W, float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
+                   swiattn_stream_t stream) {
+  return swiattn_decode_ex(q, Kc, Vc, cache_len, gate, o, B, Lmax, Hq, Hkv, G, d, W, scale,
+                           dtype, ws, ws_bytes, stream, nullptr);
 }
 
 const char* swiattn_strerror(int code) {

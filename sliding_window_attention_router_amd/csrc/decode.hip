@@ -259,17 +259,25 @@ bool plan_decode(const DecodeShape& sh, DecodePlan* p) {
 
 template <typename T, int D>
 static hipError_t run_decode(const DecodeShape& sh, const DecodePlan& p, DecodeArgs& a,
-                             hipStream_t s) {
+                             hipStream_t s, void* const* ev) {
+  hipError_t e;
+  if ((e = mark(ev, 0, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(decode_schedule_kernel, dim3(1), dim3(kDecSchedThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = mark(ev, 1, s)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_kernel<T, D>), dim3(p.grid), dim3(kDecThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = mark(ev, 2, s)) != hipSuccess) return e;
   const int waves = sh.B * sh.Hq;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((waves + 3) / 4), dim3(256), 0, s, a);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return mark(ev, 3, s);
 }
 
 hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void* q,
                          const void* Kc, const void* Vc, const int32_t* cache_len,
-                         const uint8_t* gate, void* o, void* ws, hipStream_t s) {
+                         const uint8_t* gate, void* o, void* ws, hipStream_t s,
+                         void* const* ev) {
   char* w = static_cast<char*>(ws);
   DecodeArgs a;
   a.q = q;
@@ -292,11 +300,11 @@ hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void*
   a.max_items = p.max_items;
   a.sl2 = sh.scale * kLog2e;
   if (sh.f32) {
-    if (sh.d == 64) return run_decode<float, 64>(sh, p, a, s);
-    return run_decode<float, 128>(sh, p, a, s);
+    if (sh.d == 64) return run_decode<float, 64>(sh, p, a, s, ev);
+    return run_decode<float, 128>(sh, p, a, s, ev);
   }
-  if (sh.d == 64) return run_decode<bf16_t, 64>(sh, p, a, s);
-  return run_decode<bf16_t, 128>(sh, p, a, s);
+  if (sh.d == 64) return run_decode<bf16_t, 64>(sh, p, a, s, ev);
+  return run_decode<bf16_t, 128>(sh, p, a, s, ev);
 }
 
 }  // namespace swi

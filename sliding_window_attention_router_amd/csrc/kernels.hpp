@@ -36,9 +36,11 @@ struct PrefillPlan {
 };
 
 bool plan_prefill(const PrefillShape& sh, PrefillPlan* p);
+// ev: optional array of 6 hipEvent_t recorded at stage boundaries (may be null)
 hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const void* Q,
                           const void* K, const void* V, const uint8_t* gate, const int32_t* idx,
-                          const int32_t* cnt, void* O, float* diff, void* ws, hipStream_t s);
+                          const int32_t* cnt, void* O, float* diff, void* ws, hipStream_t s,
+                          void* const* ev);
 
 // ---- decode -------------------------------------------------------------
 struct DecodeShape {
@@ -56,6 +58,13 @@ struct DecodePlan {
 bool plan_decode(const DecodeShape& sh, DecodePlan* p);
 hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void* q,
                          const void* Kc, const void* Vc, const int32_t* cache_len,
-                         const uint8_t* gate, void* o, void* ws, hipStream_t s);
+                         const uint8_t* gate, void* o, void* ws, hipStream_t s,
+                         void* const* ev);
+
+// Record ev[i] on s if present; returns the first error.
+inline hipError_t mark(void* const* ev, int i, hipStream_t s) {
+  if (!ev || !ev[i]) return hipSuccess;
+  return hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
+}
 
 }  // namespace swi

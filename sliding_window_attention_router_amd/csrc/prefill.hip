@@ -506,25 +506,44 @@ bool plan_prefill(const PrefillShape& sh, PrefillPlan* p) {
 
 template <typename T, int D>
 static hipError_t run_prefill(const PrefillShape& sh, const PrefillPlan& p, PrefillArgs& a,
-                              hipStream_t s) {
+                              hipStream_t s, void* const* ev) {
+  hipError_t e;
+#define SWI_TRY(x)                    \
+  if ((e = (x)) != hipSuccess) return e;
   if (!sh.both_branch) {
+    SWI_TRY(mark(ev, 0, s));
     hipLaunchKernelGGL((band_kernel<T, D>), dim3(p.band_tiles, sh.B * sh.Hkv), dim3(kThreads),
                        0, s, a);
+    SWI_TRY(hipGetLastError());
+    SWI_TRY(mark(ev, 1, s));
     hipLaunchKernelGGL(far_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, a);
+    SWI_TRY(hipGetLastError());
+    SWI_TRY(mark(ev, 2, s));
     hipLaunchKernelGGL((far_kernel<T, D>), dim3(p.max_items), dim3(kThreads), 0, s, a);
+    SWI_TRY(hipGetLastError());
+    SWI_TRY(mark(ev, 3, s));
     hipLaunchKernelGGL((merge_kernel<T, D>), dim3(1024), dim3(256), 0, s, a);
+    SWI_TRY(hipGetLastError());
+    SWI_TRY(mark(ev, 4, s));
   } else {
+    SWI_TRY(mark(ev, 0, s));
     hipLaunchKernelGGL((fused_kernel<T, D>), dim3(p.band_tiles, sh.B * sh.Hkv), dim3(kThreads),
                        0, s, a);
+    SWI_TRY(hipGetLastError());
+    SWI_TRY(mark(ev, 1, s));
     const long long n = (long long)sh.B * sh.N;
     hipLaunchKernelGGL(diff_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, a);
+    SWI_TRY(hipGetLastError());
+    SWI_TRY(mark(ev, 2, s));
   }
-  return hipGetLastError();
+#undef SWI_TRY
+  return hipSuccess;
 }
 
 hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const void* Q,
                           const void* K, const void* V, const uint8_t* gate, const int32_t* idx,
-                          const int32_t* cnt, void* O, float* diff, void* ws, hipStream_t s) {
+                          const int32_t* cnt, void* O, float* diff, void* ws, hipStream_t s,
+                          void* const* ev) {
   char* w = static_cast<char*>(ws);
   PrefillArgs a;
   a.Q = Q;
@@ -557,11 +576,11 @@ hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const vo
   a.max_items = p.max_items;
   a.sl2 = sh.scale * kLog2e;
   if (sh.f32) {
-    if (sh.d == 64) return run_prefill<float, 64>(sh, p, a, s);
-    return run_prefill<float, 128>(sh, p, a, s);
+    if (sh.d == 64) return run_prefill<float, 64>(sh, p, a, s, ev);
+    return run_prefill<float, 128>(sh, p, a, s, ev);
   }
-  if (sh.d == 64) return run_prefill<bf16_t, 64>(sh, p, a, s);
-  return run_prefill<bf16_t, 128>(sh, p, a, s);
+  if (sh.d == 64) return run_prefill<bf16_t, 64>(sh, p, a, s, ev);
+  return run_prefill<bf16_t, 128>(sh, p, a, s, ev);
 }
 
 }  // namespace swi
