@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU reference sample (0 = skip)")
     ap.add_argument("--p", type=float, default=0.13, help="full-branch fraction")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this many MiB before the steps "
+                         "(a known-size reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -143,6 +146,14 @@ def main():
                    events=ev[6:10] if ev is not None else None)
         if ev is not None:
             ev[10].record()
+
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

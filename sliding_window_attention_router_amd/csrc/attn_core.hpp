@@ -10,7 +10,7 @@
 // O^T = V^T P^T, which lets P^T come straight from the score accumulators
 // (same lane <-> query mapping) and makes the per-query rescale a per-lane
 // multiply.  V is staged transposed in LDS so that an A operand (one
-// channel, 8 keys) is two 8-byte LDS reads.
+// channel, 8 keys) is a single 16-byte LDS read.
 //
 // The contraction index of an MFMA may be permuted freely as long as A and B
 // use the same permutation; the P^T / V^T operands use the permutation that
@@ -31,13 +31,19 @@ struct Lds;
 template <int D>
 struct Lds<bf16_t, D> {
   // K block [kBN][D]: row stride D*2+16 bytes puts consecutive keys 4 banks
-  // apart, so 16-byte operand reads of 16 lanes cover all 64 banks once.
+  // apart, so 16-byte operand reads of 8 consecutive lanes hit distinct banks.
   static constexpr int kKStride = D * 2 + 16;
-  // V block transposed [D][kBN]: row stride kBN*2+8 bytes (34 dwords) maps
-  // 32 consecutive channels onto distinct even banks for 8-byte reads.
-  static constexpr int kVStride = kBN * 2 + 8;
+  // V block transposed [D][kBN]: row stride kBN*2+16 bytes.  Inside each
+  // 16-key group the 4-key quarters are stored in the order 0,2,1,3, so the
+  // 8 keys an MFMA lane group needs (quarters g and g+2) are adjacent and
+  // one 16-byte read fetches them.
+  static constexpr int kVStride = kBN * 2 + 16;
   static constexpr int kKBytes = kBN * kKStride;
   static constexpr int kBytes = kKBytes + D * kVStride;
+  // byte offset of 4-key quarter kq (keys 4kq..4kq+3) inside a V^T row
+  SWI_DEV static constexpr int vq_offset(int kq) {
+    return ((kq & ~3) | ((kq & 1) << 1) | ((kq >> 1) & 1)) * 8;
+  }
 };
 template <int D>
 struct Lds<float, D> {
@@ -65,6 +71,10 @@ struct KVLoader<bf16_t, D, NT> {
   u32x4 kr[KPER];
   u32x4 vr[VPER][4];
 
+  // K piece u: key u / CPR, channels 8*(u % CPR): 16 consecutive lanes read
+  // one 256-byte row.  V piece u: key quarter u % 16 (4 keys), channels
+  // 8*(u / 16): the 16 lanes that write one V^T row together cover all its
+  // banks.
   SWI_DEV void load(const bf16_t* __restrict__ Kb, const bf16_t* __restrict__ Vb, int64_t rs,
                     int kb, int kend, int tid) {
 #pragma unroll
@@ -80,10 +90,10 @@ struct KVLoader<bf16_t, D, NT> {
 #pragma unroll
     for (int j = 0; j < VPER; ++j) {
       const int u = tid + NT * j;
-      const int kg = u / CPR, c = u - kg * CPR;
+      const int kq = u & 15, c = u >> 4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int kk = kb + 4 * kg + r;
+        const int kk = kb + 4 * kq + r;
         u32x4 v = {0u, 0u, 0u, 0u};
         if ((VU % NT == 0 || u < VU) && kk < kend)
           v = *reinterpret_cast<const u32x4*>(Vb + kk * rs + c * 8);
@@ -105,7 +115,8 @@ struct KVLoader<bf16_t, D, NT> {
     for (int j = 0; j < VPER; ++j) {
       const int u = tid + NT * j;
       if (VU % NT != 0 && u >= VU) continue;
-      const int kg = u / CPR, c = u - kg * CPR;
+      const int kq = u & 15, c = u >> 4;
+      const int col = L::vq_offset(kq);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t a0 = vr[j][0][e], a1 = vr[j][1][e], a2 = vr[j][2][e], a3 = vr[j][3][e];
@@ -113,8 +124,8 @@ struct KVLoader<bf16_t, D, NT> {
         u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
         u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
         const int ch = c * 8 + 2 * e;
-        *reinterpret_cast<u32x2*>(vt + ch * L::kVStride + kg * 8) = lo;
-        *reinterpret_cast<u32x2*>(vt + (ch + 1) * L::kVStride + kg * 8) = hi;
+        *reinterpret_cast<u32x2*>(vt + ch * L::kVStride + col) = lo;
+        *reinterpret_cast<u32x2*>(vt + (ch + 1) * L::kVStride + col) = hi;
       }
     }
   }
@@ -165,44 +176,56 @@ struct KVLoader<float, D, NT> {
 // ---------------------------------------------------------------------------
 // Online softmax update shared by both cores.  s[mt][i] holds the raw score
 // of key kb + 32*mt + 8*(i/4) + 4*g + i%4 for this lane's query.  On return
-// s holds the unnormalised probabilities, m/l are updated and the
-// accumulators rescaled.  Keys outside [lo, hi] are dropped when `masked`.
+// s holds the unnormalised probabilities exp2(sl2*s - m), l is updated and
+// the accumulators rescaled if m moved.  Keys outside [lo, hi] are dropped
+// when MASKED.
+//
+// m is the running maximum of sl2*score, kept lazily: it is only raised (and
+// the accumulators rescaled) when a block's maximum exceeds it by more than
+// kRescale, so a probability is at most 2^kRescale before the final
+// normalisation.  The result is the same softmax; only rounding differs.
 // ---------------------------------------------------------------------------
-template <int MD>
+constexpr float kRescale = 8.f;
+
+template <bool MASKED, int MD>
 SWI_DEV void online_softmax(f32x16 (&s)[2], f32x16 (&acc)[MD], float& m, float& l, int kb,
-                            bool masked, int lo, int hi, float sl2, int g) {
+                            int lo, int hi, float sl2, int g) {
   float mx = kNegInf;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float x = s[mt][i] * sl2;
-      if (masked) {
+      if (MASKED) {
         const int j = kb + mt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        if (j < lo || j > hi) x = kNegInf;
+        if (j < lo || j > hi) s[mt][i] = kNegInf;
       }
-      s[mt][i] = x;
-      mx = fmaxf(mx, x);
+      mx = fmaxf(mx, s[mt][i]);
     }
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-  const float mn = fmaxf(m, mx);
-  const float mu = (mn == kNegInf) ? 0.f : mn;
-  const float alpha = fast_exp2(m - mu);
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * sl2;
+  // raise m when the block maximum exceeds it by more than kRescale (and on
+  // the first block that has any key); wave-uniform skip otherwise
+  const bool raise = mx > m + kRescale;
+  if (__any(raise)) {
+    // lanes that do not raise keep m (which may still be -inf): alpha 1
+    const float alpha = raise ? fast_exp2(m - mx) : 1.f;  // 0 when m was -inf
+    if (raise) m = mx;
+    l *= alpha;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) acc[md] *= alpha;
+  }
+  const float mu = (m == kNegInf) ? 0.f : m;
   float ls = 0.f;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p = fast_exp2(s[mt][i] - mu);
+      const float p = fast_exp2(fmaf(s[mt][i], sl2, -mu));
       s[mt][i] = p;
       ls += p;
     }
   }
-  l = l * alpha + ls;
-  m = mn;
-#pragma unroll
-  for (int md = 0; md < MD; ++md) acc[md] *= alpha;
+  l += ls;
 }
 
 // ---------------------------------------------------------------------------
@@ -229,8 +252,8 @@ struct CoreBF16 {
     for (int ks = 0; ks < KS; ++ks)
       qreg[ks] = qrow ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + g * 8) : bf16x8{};
   }
-  SWI_DEV void block(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
-                     int g) {
+  template <bool MASKED>
+  SWI_DEV void block(const char* lds, int kb, int lo, int hi, float sl2, int q, int g) {
     f32x16 s[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -242,24 +265,29 @@ struct CoreBF16 {
         s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[mt], 0, 0, 0);
       }
     }
-    online_softmax<MD>(s, acc, m, l, kb, masked, lo, hi, sl2, g);
+    online_softmax<MASKED, MD>(s, acc, m, l, kb, lo, hi, sl2, g);
     bf16x8 pb[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[st][e] = bf16_t(s[st >> 1][(st & 1) * 8 + e]);
+    // k-step st covers keys 16st..16st+15; lane group g supplies quarters
+    // 4st+g and 4st+g+2, stored adjacently (Lds::vq_offset)
     const char* vt = lds + L::kKBytes;
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
-      const char* vp = vt + (md * 32 + q) * L::kVStride + g * 8;
+      const char* vp = vt + (md * 32 + q) * L::kVStride + g * 16;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(vp + st * 32);
-        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(vp + st * 32 + 16);
-        const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vp + st * 32);
         acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], acc[md], 0, 0, 0);
       }
     }
+  }
+  SWI_DEV void block(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
+                     int g) {
+    if (masked) block<true>(lds, kb, lo, hi, sl2, q, g);
+    else block<false>(lds, kb, lo, hi, sl2, q, g);
   }
 };
 
@@ -285,8 +313,8 @@ struct CoreF32 {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qreg[ks] = qrow ? qrow[ks * 2 + g] : 0.f;
   }
-  SWI_DEV void block(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
-                     int g) {
+  template <bool MASKED>
+  SWI_DEV void block(const char* lds, int kb, int lo, int hi, float sl2, int q, int g) {
     f32x16 s[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -296,7 +324,7 @@ struct CoreF32 {
       for (int ks = 0; ks < KS; ++ks)
         s[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kp[ks * 2], qreg[ks], s[mt], 0, 0, 0);
     }
-    online_softmax<MD>(s, acc, m, l, kb, masked, lo, hi, sl2, g);
+    online_softmax<MASKED, MD>(s, acc, m, l, kb, lo, hi, sl2, g);
     const char* vs = lds + L::kKBytes;
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
@@ -308,6 +336,11 @@ struct CoreF32 {
         acc[md] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[mt][i], acc[md], 0, 0, 0);
       }
     }
+  }
+  SWI_DEV void block(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
+                     int g) {
+    if (masked) block<true>(lds, kb, lo, hi, sl2, q, g);
+    else block<false>(lds, kb, lo, hi, sl2, q, g);
   }
 };
 

@@ -203,36 +203,76 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// one wave per (sequence, query head)
+// One workgroup per (sequence, query head): the four waves take every
+// fourth chunk, each keeps its own maximum and weighted sum, and the waves
+// are combined through LDS in a fixed order.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int PL = D / 64;  // adjacent channels per lane
+  __shared__ float sm[4], sl[4];
+  __shared__ float so[4][D];
   DecSched sv(a);
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= a.B * a.Hq) return;
-  const int lane = threadIdx.x & 63;
-  const int b = w / a.Hq, h = w - b * a.Hq;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = blockIdx.x / a.Hq, h = blockIdx.x - b * a.Hq;
   const int kvh = h / a.HK, r = h - kvh * a.HK;
   const int bk = b * a.Hkv + kvh;
   const int is = sv.item_start[bk], ni = sv.n_items[bk];
   float M = kNegInf;
-  for (int k = 0; k < ni; ++k) M = fmaxf(M, a.part_lse[int64_t(is + k) * a.HK + r]);
-  constexpr int PL = D / 64;
+  for (int k = w + 4 * lane; k < ni; k += 256) M = fmaxf(M, a.part_lse[int64_t(is + k) * a.HK + r]);
+  M = wave_max(M);
   float o[PL];
 #pragma unroll
   for (int e = 0; e < PL; ++e) o[e] = 0.f;
   float L = 0.f;
-  for (int k = 0; k < ni; ++k) {
-    const float pl = a.part_lse[int64_t(is + k) * a.HK + r];
-    const float wgt = pl == kNegInf ? 0.f : fast_exp2(pl - M);
-    L += wgt;
-    const float* prow = a.part_o + (int64_t(is + k) * a.HK + r) * D;
+  int k = w;
+  for (; k + 12 < ni; k += 16) {  // four chunks of this wave per step, loads in flight together
+    float lk[4], v[4][PL];
 #pragma unroll
-    for (int e = 0; e < PL; ++e) o[e] = fmaf(wgt, prow[lane + 64 * e], o[e]);
+    for (int j = 0; j < 4; ++j) {
+      const int64_t it = is + k + 4 * j;
+      lk[j] = a.part_lse[it * a.HK + r];
+#pragma unroll
+      for (int e = 0; e < PL; ++e) v[j][e] = a.part_o[(it * a.HK + r) * D + lane * PL + e];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float wt = lk[j] == kNegInf ? 0.f : fast_exp2(lk[j] - M);
+      L += wt;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) o[e] = fmaf(wt, v[j][e], o[e]);
+    }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  for (; k < ni; k += 4) {
+    const int64_t it = is + k;
+    const float lk = a.part_lse[it * a.HK + r];
+    const float wt = lk == kNegInf ? 0.f : fast_exp2(lk - M);
+    L += wt;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) o[e] = fmaf(wt, a.part_o[(it * a.HK + r) * D + lane * PL + e], o[e]);
+  }
+  if (lane == 0) {
+    sm[w] = M;
+    sl[w] = L;
+  }
+#pragma unroll
+  for (int e = 0; e < PL; ++e) so[w][lane * PL + e] = o[e];
+  __syncthreads();
+  if (w != 0) return;
+  const float Mt = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  float Lt = 0.f, ot[PL];
+#pragma unroll
+  for (int e = 0; e < PL; ++e) ot[e] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float f = sm[j] == kNegInf ? 0.f : fast_exp2(sm[j] - Mt);
+    Lt += f * sl[j];
+#pragma unroll
+    for (int e = 0; e < PL; ++e) ot[e] = fmaf(f, so[j][lane * PL + e], ot[e]);
+  }
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
   T* orow = static_cast<T*>(a.o) + (int64_t(b) * a.Hq + h) * D;
 #pragma unroll
-  for (int e = 0; e < PL; ++e) Elem<T>::store(orow + lane + 64 * e, o[e] * inv);
+  for (int e = 0; e < PL; ++e) Elem<T>::store(orow + lane * PL + e, ot[e] * inv);
 }
 
 static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
@@ -268,8 +308,7 @@ static hipError_t run_decode(const DecodeShape& sh, const DecodePlan& p, DecodeA
   hipLaunchKernelGGL((decode_kernel<T, D>), dim3(p.grid), dim3(kDecThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = mark(ev, 2, s)) != hipSuccess) return e;
-  const int waves = sh.B * sh.Hq;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((waves + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(sh.B * sh.Hq), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(ev, 3, s);
 }

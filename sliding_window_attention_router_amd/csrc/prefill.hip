@@ -6,13 +6,13 @@
 // query i is [i-W+1, i] (weimeta SWA glossary, section "详细解释"), the full
 // branch is causal [0, i].
 //
-// Hard-gate mode (three kernels after an on-device schedule):
+// Hard-gate mode (window kernel, on-device schedule, far kernel, merge):
 //   band_kernel   window branch for every row; writes O and the window
 //                 log-sum-exp (log2 units)
 //   far_kernel    for the gathered gate=1 rows only: the far keys [0, i-W]
 //                 (the full set minus the window), split into key chunks
-//   merge_kernel  log-sum-exp merge of window + far partials = O_FULL for
-//                 the gathered rows, written over their window output
+//   merge_kernel  log-sum-exp merge of window output + far chunks = O_FULL
+//                 for the gathered rows, written over their window output
 // The window and far key sets are disjoint and cover [0, i], so the merge is
 // the exact full softmax up to rounding.
 //
@@ -50,24 +50,45 @@ struct PrefillArgs {
   float* diff;      // [B,N]
   int B, N, Hq, Hkv, G, W;
   int HK, HG, hpu, units, tpt_band, tpt_far, band_tiles, far_tiles, max_items;
+  int cmax;   // width of the per-unit chunk tables
   float sl2;  // softmax scale * log2(e)
 };
 
-// schedule layout inside a.sched (int32):
-//   [0] total items  [1] blocks per chunk
-//   item_start[nT] | n_items[nT] | pair_start[nbu+1] | item_tile[max] | item_chunk[max]
+// Far-part schedule inside a.sched (int32):
+//   [0] total items  [1] 64-key blocks per chunk
+//   n_items[nT]            chunks of each tile (global tile index T)
+//   unit_base[nbu]         first item of each (batch, unit)
+//   first[nbu][cmax]       first tile of the unit that has a chunk c
+//   offset[nbu][cmax]      first item of chunk c inside the unit
+//   item_tile[max], item_chunk[max]
+// Items of a unit are ordered by (chunk, tile): consecutive items read the
+// same key range of the same KV head.
 struct SchedView {
-  int32_t *item_start, *n_items, *pair_start, *item_tile, *item_chunk;
+  int32_t *n_items, *unit_base, *first, *offset, *item_tile, *item_chunk;
   SWI_DEV SchedView(const PrefillArgs& a) {
     const int nT = a.B * a.units * a.far_tiles;
     const int nbu = a.B * a.units;
-    item_start = a.sched + 2;
-    n_items = item_start + nT;
-    pair_start = n_items + nT;
-    item_tile = pair_start + nbu + 1;
+    n_items = a.sched + 2;
+    unit_base = n_items + nT;
+    first = unit_base + nbu;
+    offset = first + nbu * a.cmax;
+    item_tile = offset + nbu * a.cmax;
     item_chunk = item_tile + a.max_items;
   }
+  // item holding chunk c of tile t of unit bu
+  SWI_DEV int item_of(int bu, int t, int c, int cmax) const {
+    return unit_base[bu] + offset[bu * cmax + c] + (t - first[bu * cmax + c]);
+  }
 };
+
+// Linear workgroup id -> logical work index so that each of the 8 XCDs (which
+// receive workgroups round-robin) runs one contiguous slice of the logical
+// order; returns -1 for padding workgroups.
+SWI_DEV int xcd_slice(int i, int total) {
+  const int per = (total + 7) / 8;
+  const int lin = (i & 7) * per + (i >> 3);
+  return ((i >> 3) < per && lin < total) ? lin : -1;
+}
 
 // Per-wave bounds used to skip blocks no row of the wave needs and to drop
 // the mask inside blocks every row of the wave fully covers.
@@ -94,8 +115,13 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void band_kernel(PrefillArgs a) {
   using Core = typename CoreSel<T, D>::type;
   __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
-  const int tile = blockIdx.x;
-  const int b = blockIdx.y / a.Hkv, kvh = blockIdx.y - b * a.Hkv;
+  // consecutive tiles of one KV head share most of their window: keep them
+  // on one XCD's L2
+  const int lin = xcd_slice(blockIdx.x, a.band_tiles * a.B * a.Hkv);
+  if (lin < 0) return;
+  const int tile = lin % a.band_tiles;
+  const int bk = lin / a.band_tiles;
+  const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane & 31, g = lane >> 5;
   const int q0 = tile * a.tpt_band;
@@ -175,17 +201,24 @@ SWI_DEV int block_excl_scan(int v, int* sh, int& total) {
 }
 
 __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs a) {
-  __shared__ int sh[33];
   __shared__ long long red[kSchedThreads / 64];
   SchedView sv(a);
   const int tid = threadIdx.x;
   const int nT = a.B * a.units * a.far_tiles;
-  const int per_b = a.units * a.far_tiles;
-  // pass 1: 64-key blocks of far work per tile
+  const int nbu = a.B * a.units;
+  const int TT = a.far_tiles;
+  // active tiles of a unit: ceil(cnt / tpt_far)
+  auto active = [&](int bu) {
+    const int b = bu / a.units, u = bu - b * a.units;
+    const int c = a.cnt[b * a.G + (u * a.hpu) / a.HG];
+    return (c + a.tpt_far - 1) / a.tpt_far;
+  };
+  // pass 1: 64-key blocks of far work per tile (non-decreasing along the
+  // active tiles of a unit, since gathered positions ascend)
   long long mine = 0;
   for (int T_ = tid; T_ < nT; T_ += kSchedThreads) {
-    const int b = T_ / per_b, rem = T_ - b * per_b;
-    const int u = rem / a.far_tiles, t = rem - u * a.far_tiles;
+    const int bu = T_ / TT, t = T_ - bu * TT;
+    const int b = bu / a.units, u = bu - b * a.units;
     const int g = (u * a.hpu) / a.HG;
     const int c = a.cnt[b * a.G + g];
     const int ntok = min(a.tpt_far, c - t * a.tpt_far);
@@ -204,52 +237,68 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
   long long total_blocks = 0;
   for (int w = 0; w < kSchedThreads / 64; ++w) total_blocks += red[w];
   const int cb = int(max<long long>(kMinChunkBlocks, (total_blocks + kTargetItems - 1) / kTargetItems));
-  // pass 2: chunks per tile and their exclusive prefix
-  int carry = 0;
-  for (int base = 0; base < nT; base += kSchedThreads) {
-    const int T_ = base + tid;
-    const int v = T_ < nT ? (sv.n_items[T_] + cb - 1) / cb : 0;
-    int tot;
-    const int ex = block_excl_scan(v, sh, tot);
-    if (T_ < nT) {
-      sv.item_start[T_] = carry + ex;
-      sv.n_items[T_] = v;
-    }
-    carry += tot;
-  }
-  // pass 3: item list
+  // pass 2: chunks per tile
+  for (int T_ = tid; T_ < nT; T_ += kSchedThreads) sv.n_items[T_] = (sv.n_items[T_] + cb - 1) / cb;
+  __syncthreads();
+  // pass 3: first tile holding chunk c (n_items steps up at tile t for the
+  // chunks in [n(t-1), n(t)))
   for (int T_ = tid; T_ < nT; T_ += kSchedThreads) {
-    const int s = sv.item_start[T_], n = sv.n_items[T_];
-    for (int k = 0; k < n; ++k) {
-      sv.item_tile[s + k] = T_;
-      sv.item_chunk[s + k] = k;
-    }
+    const int bu = T_ / TT, t = T_ - bu * TT;
+    const int n = sv.n_items[T_];
+    const int nprev = t > 0 ? sv.n_items[T_ - 1] : 0;
+    for (int c = nprev; c < n; ++c) sv.first[bu * a.cmax + c] = t;
   }
-  // gathered (row, head) pairs per (batch, unit), for the merge
+  __syncthreads();
+  // pass 4: per unit, offsets of its chunks (chunk c holds the active tiles
+  // from first[c] on), and the unit's item count
+  for (int bu = tid; bu < nbu; bu += kSchedThreads) {
+    const int nt = active(bu);
+    const int maxn = nt > 0 ? sv.n_items[bu * TT + nt - 1] : 0;
+    int run = 0;
+    for (int c = 0; c < maxn; ++c) {
+      sv.offset[bu * a.cmax + c] = run;
+      run += nt - sv.first[bu * a.cmax + c];
+    }
+    sv.unit_base[bu] = run;  // item count for now
+  }
+  __syncthreads();
   if (tid == 0) {
     int s = 0;
-    for (int bu = 0; bu < a.B * a.units; ++bu) {
-      const int b = bu / a.units, u = bu - b * a.units;
-      const int g = (u * a.hpu) / a.HG;
-      sv.pair_start[bu] = s;
-      s += a.cnt[b * a.G + g] * a.hpu;
+    for (int bu = 0; bu < nbu; ++bu) {
+      const int n = sv.unit_base[bu];
+      sv.unit_base[bu] = s;
+      s += n;
     }
-    sv.pair_start[a.B * a.units] = s;
-    a.sched[0] = carry;
+    a.sched[0] = s;
     a.sched[1] = cb;
+  }
+  __syncthreads();
+  // pass 5: item list
+  for (int T_ = tid; T_ < nT; T_ += kSchedThreads) {
+    const int bu = T_ / TT, t = T_ - bu * TT;
+    const int n = sv.n_items[T_];
+    for (int c = 0; c < n; ++c) {
+      const int it = sv.item_of(bu, t, c, a.cmax);
+      sv.item_tile[it] = T_;
+      sv.item_chunk[it] = c;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Far part of the full branch for gathered rows.  One workgroup per work
 // item (tile, chunk); grid = upper bound, idle workgroups exit at once.
+// A tile with a single chunk merges with the window result in place; the
+// chunks of longer tiles write normalised partials for merge_kernel.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void far_kernel(PrefillArgs a) {
   using Core = typename CoreSel<T, D>::type;
   __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
-  const int item = blockIdx.x;
-  if (item >= a.sched[0]) return;
+  // items are ordered by (unit, chunk, tile); an XCD takes a contiguous
+  // slice, so its resident workgroups read the same keys of one KV head
+  const int item = xcd_slice(blockIdx.x, a.sched[0]);
+  if (item < 0) return;
   SchedView sv(a);
   const int cb = a.sched[1];
   const int T_ = sv.item_tile[item], ch = sv.item_chunk[item];
@@ -295,64 +344,82 @@ __global__ __launch_bounds__(kThreads, 2) void far_kernel(PrefillArgs a) {
   }
   float lse2;
   const float inv = finish_row(c_.m, c_.l, lse2);
-  if (valid) {
+  if (!valid) return;
+  if (sv.n_items[T_] > 1) {  // the merge kernel combines the tile's chunks
     float* prow = a.part_o + (int64_t(item) * kRows + r) * D;
     store_row<Core::MD>(prow, c_.acc, inv, g);
     if (g == 0) a.part_lse[int64_t(item) * kRows + r] = lse2;
+    return;
   }
+  // single-chunk tile: merge with the window result right here
+  if (tok < a.W) return;
+  const float ls = a.lse_s[(int64_t(b) * a.Hq + h) * a.N + tok];
+  const float M = fmaxf(ls, lse2);
+  const float ws = fast_exp2(ls - M), wf = fast_exp2(lse2 - M);
+  T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D;
+  const float sf = inv * wf;
+#pragma unroll
+  for (int md = 0; md < Core::MD; ++md)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      c_.acc[md][i] = fmaf(c_.acc[md][i], sf, ws * Elem<T>::load(orow + acc_channel(md, i, g)));
+  store_row<Core::MD>(orow, c_.acc, 1.f / (ws + wf), g);
 }
 
 // ---------------------------------------------------------------------------
-// Merge for gathered rows: O_FULL = LSE-weighted window output + far
-// partials.  Persistent grid; one wave per gathered (row, head) pair.
+// Merge of multi-chunk far tiles: one workgroup per tile, lanes laid out as
+// in far_kernel (lane pair per row, 64 channels per lane).  O_FULL of a row
+// is the log-sum-exp weighted sum of its window output and its chunks'
+// partials, taken in chunk order.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(256) void merge_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) void merge_kernel(PrefillArgs a) {
+  constexpr int MD = D / 32;
   SchedView sv(a);
-  const int nbu = a.B * a.units;
-  const int total = sv.pair_start[nbu];
-  const int lane = threadIdx.x & 63;
-  const int nwaves = gridDim.x * (blockDim.x / 64);
-  constexpr int PL = D / 64;  // channels per lane
-  for (int p = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); p < total; p += nwaves) {
-    int lo = 0, hi = nbu - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sv.pair_start[mid] <= p) lo = mid;
-      else hi = mid - 1;
-    }
-    const int bu = lo;
-    const int b = bu / a.units, u = bu - b * a.units;
-    const int pp = p - sv.pair_start[bu];
-    const int gi = pp / a.hpu, hh = pp - gi * a.hpu;
-    const int g_gate = (u * a.hpu) / a.HG;
-    const int tok = a.idx[(int64_t(b) * a.G + g_gate) * a.N + gi];
-    if (tok < a.W) continue;  // far set empty: the window result is the full result
-    const int h = u * a.hpu + hh;
-    const int t = gi / a.tpt_far, slot = gi - t * a.tpt_far;
-    const int r = slot * a.hpu + hh;
-    const int T_ = (b * a.units + u) * a.far_tiles + t;
-    const int is = sv.item_start[T_], ni = sv.n_items[T_];
-    const float ls = a.lse_s[(int64_t(b) * a.Hq + h) * a.N + tok];
-    float M = ls;
-    for (int k = 0; k < ni; ++k) M = fmaxf(M, a.part_lse[int64_t(is + k) * kRows + r]);
-    const float ws = fast_exp2(ls - M);
-    float L = ws;
-    T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D;
-    float o[PL];
+  const int T_ = blockIdx.x;
+  const int ni = sv.n_items[T_];
+  if (ni < 2) return;
+  const int per_b = a.units * a.far_tiles;
+  const int b = T_ / per_b, rem = T_ - b * per_b;
+  const int u = rem / a.far_tiles, t = rem - u * a.far_tiles;
+  const int bu = b * a.units + u;
+  const int g_gate = (u * a.hpu) / a.HG;
+  const int c = a.cnt[b * a.G + g_gate];
+  const int ntok = min(a.tpt_far, c - t * a.tpt_far);
+  const int lane = threadIdx.x & 63, q = lane & 31, g = lane >> 5;
+  const int r = (threadIdx.x >> 6) * kQR + q;
+  const int slot = r / a.hpu, hh = r - slot * a.hpu;
+  if (slot >= ntok) return;
+  const int tok = a.idx[(int64_t(b) * a.G + g_gate) * a.N + t * a.tpt_far + slot];
+  if (tok < a.W) return;
+  const int h = u * a.hpu + hh;
+  const float ls = a.lse_s[(int64_t(b) * a.Hq + h) * a.N + tok];
+  float M = ls;
+  for (int k = 0; k < ni; ++k)
+    M = fmaxf(M, a.part_lse[int64_t(sv.item_of(bu, t, k, a.cmax)) * kRows + r]);
+  T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D;
+  float wsum = fast_exp2(ls - M);
+  f32x16 o[MD];
 #pragma unroll
-    for (int e = 0; e < PL; ++e) o[e] = ws * Elem<T>::load(orow + lane + 64 * e);
-    for (int k = 0; k < ni; ++k) {
-      const float w = fast_exp2(a.part_lse[int64_t(is + k) * kRows + r] - M);
-      L += w;
-      const float* prow = a.part_o + (int64_t(is + k) * kRows + r) * D;
+  for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int e = 0; e < PL; ++e) o[e] = fmaf(w, prow[lane + 64 * e], o[e]);
-    }
-    const float inv = 1.f / L;
+    for (int i = 0; i < 16; ++i) o[md][i] = wsum * Elem<T>::load(orow + acc_channel(md, i, g));
+  for (int k = 0; k < ni; ++k) {
+    const int it = sv.item_of(bu, t, k, a.cmax);
+    const float lk = a.part_lse[int64_t(it) * kRows + r];
+    const float w = lk == kNegInf ? 0.f : fast_exp2(lk - M);
+    wsum += w;
+    const float* prow = a.part_o + (int64_t(it) * kRows + r) * D;
 #pragma unroll
-    for (int e = 0; e < PL; ++e) Elem<T>::store(orow + lane + 64 * e, o[e] * inv);
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(prow + md * 32 + i4 * 8 + g * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[md][i4 * 4 + e] = fmaf(w, v[e], o[md][i4 * 4 + e]);
+      }
   }
+  store_row<MD>(orow, o, 1.f / wsum, g);
 }
 
 // Sum of squared differences of this lane's channels.  Contraction is off so
@@ -483,6 +550,8 @@ bool plan_prefill(const PrefillShape& sh, PrefillPlan* p) {
   const long long max_items = kTargetItems + nT;
   if (max_items > INT_MAX / kRows) return false;
   p->max_items = int(max_items);
+  // chunks per tile <= ceil(ceil(N / 64) / kMinChunkBlocks)
+  p->cmax = ((sh.N + kBN - 1) / kBN + kMinChunkBlocks - 1) / kMinChunkBlocks + 1;
   const size_t rowsN = size_t(sh.B) * sh.Hq * sh.N;
   size_t off = 0;
   p->off_lse = p->off_sched = p->off_part_o = p->off_part_lse = p->off_diffp = 0;
@@ -490,7 +559,8 @@ bool plan_prefill(const PrefillShape& sh, PrefillPlan* p) {
     p->off_lse = off;
     off = align_up(off + rowsN * 4);
     p->off_sched = off;
-    const size_t sched_ints = 2 + 2 * size_t(nT) + size_t(sh.B) * p->units + 1 + 2 * size_t(max_items);
+    const size_t nbu = size_t(sh.B) * p->units;
+    const size_t sched_ints = 2 + size_t(nT) + nbu + 2 * nbu * p->cmax + 2 * size_t(max_items);
     off = align_up(off + sched_ints * 4);
     p->off_part_o = off;
     off = align_up(off + size_t(max_items) * kRows * sh.d * 4);
@@ -512,17 +582,20 @@ static hipError_t run_prefill(const PrefillShape& sh, const PrefillPlan& p, Pref
   if ((e = (x)) != hipSuccess) return e;
   if (!sh.both_branch) {
     SWI_TRY(mark(ev, 0, s));
-    hipLaunchKernelGGL((band_kernel<T, D>), dim3(p.band_tiles, sh.B * sh.Hkv), dim3(kThreads),
-                       0, s, a);
+    const int band_total = p.band_tiles * sh.B * sh.Hkv;
+    hipLaunchKernelGGL((band_kernel<T, D>), dim3(8 * ((band_total + 7) / 8)), dim3(kThreads), 0,
+                       s, a);
     SWI_TRY(hipGetLastError());
     SWI_TRY(mark(ev, 1, s));
     hipLaunchKernelGGL(far_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, a);
     SWI_TRY(hipGetLastError());
     SWI_TRY(mark(ev, 2, s));
-    hipLaunchKernelGGL((far_kernel<T, D>), dim3(p.max_items), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((far_kernel<T, D>), dim3(8 * ((p.max_items + 7) / 8)), dim3(kThreads), 0,
+                       s, a);
     SWI_TRY(hipGetLastError());
     SWI_TRY(mark(ev, 3, s));
-    hipLaunchKernelGGL((merge_kernel<T, D>), dim3(1024), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((merge_kernel<T, D>), dim3(sh.B * p.units * p.far_tiles), dim3(kThreads), 0,
+                       s, a);
     SWI_TRY(hipGetLastError());
     SWI_TRY(mark(ev, 4, s));
   } else {
@@ -574,6 +647,7 @@ hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const vo
   a.band_tiles = p.band_tiles;
   a.far_tiles = p.far_tiles;
   a.max_items = p.max_items;
+  a.cmax = p.cmax;
   a.sl2 = sh.scale * kLog2e;
   if (sh.f32) {
     if (sh.d == 64) return run_prefill<float, 64>(sh, p, a, s, ev);

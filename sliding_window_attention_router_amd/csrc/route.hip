@@ -50,6 +50,57 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ H,
   }
 }
 
+// Single gate group, bf16/fp32 rows whose length is a multiple of the
+// 16-byte vector: each wave takes kTok tokens, every lane issues all of its
+// 16-byte loads (kTok rows x the vectors it owns) before reducing, and the
+// weight vectors a lane owns are loaded once.  Same per-lane order and xor
+// tree as route_kernel.
+constexpr int kTok = 4;
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void route_g1_kernel(const T* __restrict__ H,
+                                                       const T* __restrict__ r,
+                                                       const float* __restrict__ bias,
+                                                       uint8_t* __restrict__ gate,
+                                                       float* __restrict__ z_out, int64_t tokens,
+                                                       int hidden) {
+  constexpr int VEC = 16 / Elem<T>::kBytes;
+  const int lane = threadIdx.x & 63;
+  const int64_t tok0 = (int64_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6)) * kTok;
+  if (tok0 >= tokens) return;
+  u32x4 rv[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) rv[j] = *reinterpret_cast<const u32x4*>(r + int64_t(lane + 64 * j) * VEC);
+  u32x4 hv[kTok][NV];
+#pragma unroll
+  for (int t = 0; t < kTok; ++t)
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t tok = min(tok0 + t, tokens - 1);
+      hv[t][j] = *reinterpret_cast<const u32x4*>(H + tok * hidden + int64_t(lane + 64 * j) * VEC);
+    }
+  float acc[kTok];
+#pragma unroll
+  for (int t = 0; t < kTok; ++t) {
+    acc[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const T* hp = reinterpret_cast<const T*>(&hv[t][j]);
+      const T* rp = reinterpret_cast<const T*>(&rv[j]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[t] = fmaf(Elem<T>::load(hp + e), Elem<T>::load(rp + e), acc[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kTok; ++t) {
+    const float sum = wave_sum(acc[t]);
+    if (lane == 0 && tok0 + t < tokens) {
+      const float z = sum + bias[0];
+      gate[tok0 + t] = z > 0.f ? 1 : 0;
+      if (z_out) z_out[tok0 + t] = z;
+    }
+  }
+}
+
 // One 1024-thread block per (batch, gate group).  Each thread owns a
 // contiguous segment of positions, counts its routed tokens, a block-wide
 // exclusive prefix sum (wave shuffles + one LDS pass) gives each segment its
@@ -77,7 +128,19 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(const uint8_t*
     const int s0 = base + tid * seg;
     const int s1 = min(s0 + seg, N);
     uint32_t bits = 0;
-    for (int i = s0; i < s1; ++i) bits |= (gp[int64_t(i) * G] != 0 ? 1u : 0u) << (i - s0);
+    if (G == 1 && s1 - s0 == seg && ((reinterpret_cast<uintptr_t>(gp + s0) & 15) == 0)) {
+      // 32 gate bytes as two 16-byte loads
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(gp + s0);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(gp + s0 + 16);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t wd = k < 4 ? w0[k] : w1[k - 4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bits |= (((wd >> (8 * e)) & 0xffu) != 0 ? 1u : 0u) << (4 * k + e);
+      }
+    } else {
+      for (int i = s0; i < s1; ++i) bits |= (gp[int64_t(i) * G] != 0 ? 1u : 0u) << (i - s0);
+    }
     const int c = __popc(bits);
     // inclusive scan within the wave
     int incl = c;
@@ -118,6 +181,35 @@ hipError_t launch_route(const void* H, const void* r, const float* bias, uint8_t
                         hipStream_t s) {
   const int64_t tokens = int64_t(B) * N;
   const int wpb = 4;
+  const int VEC = f32 ? 4 : 8;
+  const bool aligned = (reinterpret_cast<uintptr_t>(H) & 15) == 0 && (reinterpret_cast<uintptr_t>(r) & 15) == 0;
+  if (G == 1 && aligned && hidden % (64 * VEC) == 0 && hidden / (64 * VEC) <= 8) {
+    const int nv = hidden / (64 * VEC);
+    dim3 g1(unsigned((tokens + wpb * kTok - 1) / (wpb * kTok)));
+#define SWI_ROUTE_G1(NVV)                                                                         \
+  case NVV:                                                                                       \
+    if (f32)                                                                                      \
+      hipLaunchKernelGGL((route_g1_kernel<float, NVV>), g1, dim3(64 * wpb), 0, s,                 \
+                         static_cast<const float*>(H), static_cast<const float*>(r), bias, gate,  \
+                         z_out, tokens, hidden);                                                  \
+    else                                                                                          \
+      hipLaunchKernelGGL((route_g1_kernel<bf16_t, NVV>), g1, dim3(64 * wpb), 0, s,                \
+                         static_cast<const bf16_t*>(H), static_cast<const bf16_t*>(r), bias,      \
+                         gate, z_out, tokens, hidden);                                            \
+    return hipGetLastError();
+    switch (nv) {
+      SWI_ROUTE_G1(1)
+      SWI_ROUTE_G1(2)
+      SWI_ROUTE_G1(3)
+      SWI_ROUTE_G1(4)
+      SWI_ROUTE_G1(5)
+      SWI_ROUTE_G1(6)
+      SWI_ROUTE_G1(7)
+      SWI_ROUTE_G1(8)
+      default: break;
+    }
+#undef SWI_ROUTE_G1
+  }
   dim3 grid(unsigned((tokens + wpb - 1) / wpb));
   if (f32)
     hipLaunchKernelGGL(route_kernel<float>, grid, dim3(64 * wpb), 0, s,
