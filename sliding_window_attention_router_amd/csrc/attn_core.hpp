@@ -55,8 +55,12 @@ struct Lds<float, D> {
 
 // ---------------------------------------------------------------------------
 // Global -> register -> LDS staging of one block of kBN keys of one KV head.
-// Rows at or beyond `kend` are zero-filled (never read from memory).
+// Rows at or beyond `kend` are read from row kend-1 instead (branch-free and
+// in bounds): every block that reaches past kend is processed with the key
+// mask, which gives those keys probability exactly 0, and 0 times a finite
+// value adds nothing.
 // ---------------------------------------------------------------------------
+SWI_DEV int clamp_row(int kk, int kend) { return kk < kend ? kk : kend - 1; }
 template <typename T, int D, int NT>
 struct KVLoader;
 
@@ -81,11 +85,9 @@ struct KVLoader<bf16_t, D, NT> {
     for (int j = 0; j < KPER; ++j) {
       const int u = tid + NT * j;
       const int key = u / CPR, c = u - key * CPR;
-      const int kk = kb + key;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if ((KU % NT == 0 || u < KU) && kk < kend)
-        v = *reinterpret_cast<const u32x4*>(Kb + kk * rs + c * 8);
-      kr[j] = v;
+      if (KU % NT != 0 && u >= KU) continue;
+      const int kk = clamp_row(kb + key, kend);
+      kr[j] = *reinterpret_cast<const u32x4*>(Kb + kk * rs + c * 8);
     }
 #pragma unroll
     for (int j = 0; j < VPER; ++j) {
@@ -93,11 +95,9 @@ struct KVLoader<bf16_t, D, NT> {
       const int kq = u & 15, c = u >> 4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int kk = kb + 4 * kq + r;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if ((VU % NT == 0 || u < VU) && kk < kend)
-          v = *reinterpret_cast<const u32x4*>(Vb + kk * rs + c * 8);
-        vr[j][r] = v;
+        if (VU % NT != 0 && u >= VU) continue;
+        const int kk = clamp_row(kb + 4 * kq + r, kend);
+        vr[j][r] = *reinterpret_cast<const u32x4*>(Vb + kk * rs + c * 8);
       }
     }
   }
@@ -146,14 +146,10 @@ struct KVLoader<float, D, NT> {
     for (int j = 0; j < KPER; ++j) {
       const int u = tid + NT * j;
       const int key = u / CPR, c = u - key * CPR;
-      const int kk = kb + key;
-      u32x4 k = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
-      if ((KU % NT == 0 || u < KU) && kk < kend) {
-        k = *reinterpret_cast<const u32x4*>(Kb + kk * rs + c * 4);
-        v = *reinterpret_cast<const u32x4*>(Vb + kk * rs + c * 4);
-      }
-      kr[j] = k;
-      vr[j] = v;
+      if (KU % NT != 0 && u >= KU) continue;
+      const int kk = clamp_row(kb + key, kend);
+      kr[j] = *reinterpret_cast<const u32x4*>(Kb + kk * rs + c * 4);
+      vr[j] = *reinterpret_cast<const u32x4*>(Vb + kk * rs + c * 4);
     }
   }
   SWI_DEV void store(char* lds, int tid) const {
