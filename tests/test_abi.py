@@ -1,0 +1,128 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point declared in include/swiattn.h, sizes workspaces, and rejects invalid
+arguments with the documented codes before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sliding_window_attention_router_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "swiattn.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, -1, -2, -3, -4
+BF16, F32 = 0, 1
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from sliding_window_attention_router_amd import build
+
+        build.build()
+    return binding.lib()
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swiattn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("swiattn_route", "swiattn_prefill", "swiattn_decode", "swiattn_prefill_workspace_size",
+              "swiattn_decode_workspace_size", "swiattn_strerror", "swiattn_prefill_ex", "swiattn_decode_ex"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in binding.SYMBOLS, f"{name} missing from the binding's table"
+
+
+def test_strerror_and_version(lib):
+    assert binding.strerror(OK) == "ok"
+    for c in (INVALID, UNSUPPORTED, WORKSPACE, HIP):
+        assert binding.strerror(c) not in ("ok", "unknown error code")
+    assert binding.strerror(-99) == "unknown error code"
+    assert lib.swiattn_version().decode().count(".") == 2
+
+
+def test_workspace_sizes(lib):
+    # valid shapes give a positive size; invalid ones give 0
+    assert lib.swiattn_prefill_workspace_size(1, 32768, 16, 4, 1, 128, 1024, BF16, 0) > 0
+    # both-branch mode needs only the per-(head, token) distances
+    assert lib.swiattn_prefill_workspace_size(1, 32768, 16, 16, 1, 128, 1024, BF16, 1) == 4 * 16 * 32768
+    assert lib.swiattn_prefill_workspace_size(0, 10, 2, 2, 1, 64, 4, BF16, 0) == 0
+    assert lib.swiattn_prefill_workspace_size(1, 10, 2, 2, 1, 96, 4, BF16, 0) == 0
+    assert lib.swiattn_decode_workspace_size(64, 32768, 16, 4, 1, 128, 1024, BF16) > 0
+    assert lib.swiattn_decode_workspace_size(64, 32768, 16, 5, 1, 128, 1024, BF16) == 0
+    # the size does not depend on the scale or the gate; it grows with N
+    a = lib.swiattn_prefill_workspace_size(1, 1000, 8, 2, 1, 128, 100, BF16, 0)
+    b = lib.swiattn_prefill_workspace_size(1, 2000, 8, 2, 1, 128, 100, BF16, 0)
+    assert 0 < a < b
+
+
+def _prefill(lib, **kw):
+    args = dict(Q=FAKE, K=FAKE, V=FAKE, gate=FAKE, idx=FAKE, cnt=FAKE, O=FAKE, diff=None,
+                B=1, N=100, Hq=4, Hkv=2, G=1, d=128, W=16, scale=0.088, dt=BF16, flags=0,
+                ws=FAKE, ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    a = args
+    return lib.swiattn_prefill(a["Q"], a["K"], a["V"], a["gate"], a["idx"], a["cnt"], a["O"], a["diff"],
+                               a["B"], a["N"], a["Hq"], a["Hkv"], a["G"], a["d"], a["W"], a["scale"],
+                               a["dt"], a["flags"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(W=0), INVALID), (dict(Hq=0), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID), (dict(G=3), INVALID), (dict(scale=0.0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=-1.0), INVALID), (dict(dt=7), INVALID),
+    (dict(flags=2), INVALID), (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(Hq=64, Hkv=1), UNSUPPORTED),                 # 64 query heads per KV head
+    (dict(Hq=12, Hkv=4, G=3), UNSUPPORTED),            # 3 heads per KV head, 4 per gate group
+    (dict(Hq=12, Hkv=3, G=3), OK),                     # 4 and 4 nest
+    (dict(Q=None), INVALID), (dict(K=None), INVALID), (dict(V=None), INVALID),
+    (dict(gate=None), INVALID), (dict(O=None), INVALID), (dict(idx=None), INVALID),
+    (dict(cnt=None), INVALID), (dict(flags=1, diff=None), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+])
+def test_prefill_rejects_invalid_arguments(lib, kw, code):
+    if code == OK:
+        # a valid shape: only check that it is accepted by the size query
+        assert lib.swiattn_prefill_workspace_size(1, 100, kw["Hq"], kw["Hkv"], kw["G"], 128, 16, BF16, 0) > 0
+        return
+    assert _prefill(lib, **kw) == code
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, Kc=FAKE, Vc=FAKE, lens=FAKE, gate=FAKE, o=FAKE, B=4, Lmax=100, Hq=4, Hkv=2, G=1,
+             d=128, W=16, scale=0.088, dt=BF16, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.swiattn_decode(a["q"], a["Kc"], a["Vc"], a["lens"], a["gate"], a["o"], a["B"], a["Lmax"],
+                              a["Hq"], a["Hkv"], a["G"], a["d"], a["W"], a["scale"], a["dt"], a["ws"],
+                              a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), INVALID), (dict(Lmax=0), INVALID), (dict(W=0), INVALID), (dict(Hkv=3), INVALID),
+    (dict(d=32), UNSUPPORTED), (dict(q=None), INVALID), (dict(lens=None), INVALID),
+    (dict(gate=None), INVALID), (dict(o=None), INVALID), (dict(ws=None), WORKSPACE),
+    (dict(ws_bytes=8), WORKSPACE), (dict(scale=0.0), INVALID),
+])
+def test_decode_rejects_invalid_arguments(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(G=0), dict(gate=None), dict(idx=None),
+                                dict(cnt=None), dict(r=None), dict(bias=None), dict(hidden=0), dict(dt=5)])
+def test_route_rejects_invalid_arguments(lib, kw):
+    a = dict(H=FAKE, r=FAKE, bias=FAKE, gate=FAKE, z=None, idx=FAKE, cnt=FAKE, B=1, N=10, hidden=64, G=1,
+             dt=BF16, stream=None)
+    a.update(kw)
+    rc = lib.swiattn_route(a["H"], a["r"], a["bias"], a["gate"], a["z"], a["idx"], a["cnt"], a["B"], a["N"],
+                           a["hidden"], a["G"], a["dt"], a["stream"])
+    assert rc == INVALID

@@ -1,0 +1,33 @@
+"""The benchmark's work accounting against closed forms (no GPU)."""
+import numpy as np
+
+import bench
+
+
+def test_prefill_pairs_closed_form():
+    N, W, Hq = 1000, 64, 4
+    for p in (0.0, 1.0):
+        gate = np.full((1, N, 1), int(p), np.uint8)
+        useful, band, far = bench.prefill_pairs(gate, W, Hq, 1)
+        # window part: sum_i min(i+1, W) = W(W+1)/2 + (N-W)W per head
+        assert band == Hq * (W * (W + 1) // 2 + (N - W) * W)
+        # far part with every row routed: sum_{i>=W} (i+1-W) = (N-W)(N-W+1)/2 per head
+        assert far == (Hq * (N - W) * (N - W + 1) // 2 if p else 0)
+        assert useful == band + far
+    # all-ones total equals the causal triangle
+    u, _, _ = bench.prefill_pairs(np.ones((1, N, 1), np.uint8), W, Hq, 1)
+    assert u == Hq * N * (N + 1) // 2
+    # two gate groups: heads follow their own group
+    gate = np.zeros((1, N, 2), np.uint8)
+    gate[0, :, 1] = 1
+    u2, b2, f2 = bench.prefill_pairs(gate, W, Hq, 2)
+    assert f2 == 2 * (N - W) * (N - W + 1) // 2 and b2 == band
+
+
+def test_decode_bytes_closed_form():
+    B, Hq, Hkv, d, W = 4, 16, 4, 128, 1024
+    lens = np.array([32768, 32768, 500, 1024])
+    gate = np.array([[1], [0], [1], [0]], np.uint8)
+    nbytes, keys = bench.decode_bytes(gate, lens, W, Hq, Hkv, d)
+    assert keys == Hkv * (32768 + 1024 + 500 + 1024)
+    assert nbytes == keys * d * 2 * 2 + B * Hq * d * 2 * 2

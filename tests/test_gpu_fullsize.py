@@ -1,0 +1,167 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times, checked on sampled rows the float64 reference computes one
+by one (plus invariants that hold at any size on every row)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sliding_window_attention_router_amd import synth
+from tests.gpu_util import TOL, dev, diff_tolerance, ensure_built, host, max_abs, say
+
+pytestmark = pytest.mark.gpu
+
+N32K, W = 32768, 1024
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_built()
+    yield
+    torch.cuda.empty_cache()
+
+
+def swa():
+    import sliding_window_attention_router_amd as m
+
+    return m
+
+
+def sample_rows(gate, seed, n_routed=96, n_window=96):
+    """Rows that exercise every code path: the first rows, the window edge,
+    the tail, and random routed / unrouted rows."""
+    N = gate.shape[1]
+    rng = np.random.default_rng(seed)
+    rows = set(range(0, 48)) | set(range(W - 24, W + 24)) | set(range(N - 24, N))
+    routed = np.flatnonzero(gate[0, :, 0])
+    plain = np.flatnonzero(gate[0, :, 0] == 0)
+    if routed.size:
+        rows |= set(rng.choice(routed, min(n_routed, routed.size), replace=False).tolist())
+    if plain.size:
+        rows |= set(rng.choice(plain, min(n_window, plain.size), replace=False).tolist())
+    # run boundaries of the gate
+    edges = np.flatnonzero(np.diff(gate[0, :, 0].astype(np.int8)) != 0)
+    rows |= set(rng.choice(edges, min(48, edges.size), replace=False).tolist()) if edges.size else set()
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+def f64(*arrays):
+    return [np.asarray(a, np.float64) for a in arrays]
+
+
+@pytest.mark.parametrize("mode", ["bernoulli", "zeros", "ones"])
+def test_long_prefill_32k(mode):
+    say(f"long prefill N=32768 GQA 16/4 gate={mode}")
+    w = synth.long_prefill(seed=3, gate_mode=mode)
+    bf = torch.bfloat16
+    Q, K, V = dev(w.Q, bf), dev(w.K, bf), dev(w.V, bf)
+    O, _ = swa().prefill(Q, K, V, dev(w.gate), W)
+    O2, _ = swa().prefill(Q, K, V, dev(w.gate), W)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2), "two runs differ"
+    Oh = host(O)
+    assert np.all(np.abs(Oh) <= np.abs(w.V).max() + 1e-2)  # softmax averages never leave the V range
+    rows = sample_rows(w.gate, 30)
+    Qd, Kd, Vd = f64(w.Q, w.K, w.V)
+    ref = oracle.prefill(Qd, Kd, Vd, w.gate, W, rows=rows)["O"]
+    err = max_abs(Oh[:, rows], ref)
+    say(f"  {rows.size} sampled rows x 16 heads: max-abs {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_layer_route_and_prefill_4k():
+    say("layer: router on hidden 2048 -> compaction -> prefill N=4096 MHA 16 heads")
+    w = synth.layer()
+    bf = torch.bfloat16
+    gate, idx, cnt, _ = swa().route(dev(w.H, bf), dev(w.r, bf), dev(w.bias))
+    O, _ = swa().prefill(dev(w.Q, bf), dev(w.K, bf), dev(w.V, bf), gate, w.W, idx=idx, cnt=cnt)
+    torch.cuda.synchronize()
+    g = gate.cpu().numpy()
+    rt = oracle.route(w.H, w.r, w.bias)
+    assert np.array_equal(g[~rt["near"]], rt["gate"][~rt["near"]])
+    rows = sample_rows(g, 31, 160, 160)
+    Qd, Kd, Vd = f64(w.Q, w.K, w.V)
+    ref = oracle.prefill(Qd, Kd, Vd, rt["gate"], w.W, rows=rows)["O"]
+    keep = ~rt["near"][0, rows, 0]  # rows whose decision is fixed
+    err = max_abs(host(O)[:, rows][:, keep], ref[:, keep])
+    say(f"  density {g.mean():.4f}; {rows.size} rows: max-abs {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("p", [0.30, 0.05])
+def test_structured_both_branch_32k(p):
+    say(f"structured routing p={p}: N=32768 MHA 16 heads, both-branch + hard-gate")
+    w = synth.structured(p)
+    bf = torch.bfloat16
+    Q, K, V, G = dev(w.Q, bf), dev(w.K, bf), dev(w.V, bf), dev(w.gate)
+    O, diff = swa().prefill(Q, K, V, G, W, both_branch=True)
+    Oh, _ = swa().prefill(Q, K, V, G, W)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.gate, 32, 48, 48)
+    Qd, Kd, Vd = f64(w.Q, w.K, w.V)
+    ref = oracle.prefill(Qd, Kd, Vd, w.gate, W, both_branch=True, rows=rows)
+    err = max_abs(host(O)[:, rows], ref["O"])
+    err_h = max_abs(host(Oh)[:, rows], ref["O"])
+    dg = host(diff)[:, rows]
+    derr = np.abs(dg - ref["diff"])
+    tol = diff_tolerance(ref["diff"], 16 * 128, TOL["bf16"])
+    say(f"  realized density {w.gate.mean():.4f}; {rows.size} rows: O max-abs {err:.3e} (hard-gate "
+        f"{err_h:.3e}); diff max-abs {derr.max():.3e}, max rel "
+        f"{np.max(derr / np.maximum(ref['diff'], 1e-30)):.3e}")
+    assert err <= TOL["bf16"] and err_h <= TOL["bf16"]
+    assert np.all(derr <= tol)
+    assert np.all(host(diff)[:, :W] == 0.0)
+
+
+def test_decode_64x32k():
+    say("decode: 64 sequences x 32768 cache, GQA 16/4, gate Bernoulli(0.13)")
+    d = synth.decode_cache(seed=5, device="cuda")
+    lens = dev(d["cache_len"])
+    gate = dev(d["gate"])
+    o = swa().decode(d["q"], d["Kc"], d["Vc"], lens, gate, W)
+    o2 = swa().decode(d["q"], d["Kc"], d["Vc"], lens, gate, W)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2), "two runs differ"
+    oh = host(o)
+    qh = host(d["q"])
+    errs = []
+    for b in range(d["q"].shape[0]):
+        L = int(d["cache_len"][b])
+        lo = 0 if d["gate"][b, 0] else max(0, L - W)
+        Kb = host(d["Kc"][b:b + 1, lo:L])
+        Vb = host(d["Vc"][b:b + 1, lo:L])
+        ref = oracle.decode(qh[b:b + 1], Kb, Vb, np.array([L - lo]), d["gate"][b:b + 1], W)["o"]
+        errs.append(max_abs(oh[b:b + 1], ref))
+    say(f"  full sequences {int(d['gate'].sum())}; max-abs over all 64 sequences {max(errs):.3e}")
+    assert max(errs) <= TOL["bf16"]
+    del d
+    torch.cuda.empty_cache()
+
+
+def test_decode_ragged_lengths():
+    say("decode: ragged cache lengths, 24 sequences, Lmax 8192")
+    rng = np.random.default_rng(7)
+    lens = rng.integers(1, 8193, 24).astype(np.int32)
+    lens[:4] = [1, 2, W, W + 1]
+    gate = (rng.random((24, 1)) < 0.5).astype(np.uint8)
+    d = synth.decode_cache(seed=6, B=24, Lmax=8192, cache_len=lens, gate=gate, device="cuda")
+    o = swa().decode(d["q"], d["Kc"], d["Vc"], dev(lens), dev(gate), W)
+    torch.cuda.synchronize()
+    ref = oracle.decode(host(d["q"]), host(d["Kc"]), host(d["Vc"]), lens, gate, W)["o"]
+    err = max_abs(host(o), ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_workspace_contents_do_not_leak():
+    """A workspace full of NaN bytes gives the same output as a fresh one."""
+    w = synth.long_prefill(seed=8, N=4096, p=0.2)
+    bf = torch.bfloat16
+    args = (dev(w.Q, bf), dev(w.K, bf), dev(w.V, bf), dev(w.gate), W)
+    n = swa().prefill_workspace_size(1, 4096, 16, 4, 1, 128, W)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")  # 0xFFFFFFFF is a NaN
+    O1, _ = swa().prefill(*args, workspace=ws)
+    O2, _ = swa().prefill(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+    assert not torch.isnan(O1.float()).any()
