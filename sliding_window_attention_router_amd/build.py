@@ -38,6 +38,7 @@ def flags():
         "-Wno-unused-function",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         f"-I{os.path.join(os.path.dirname(PKG), 'include')}",
+        *os.environ.get("SWIATTN_HIPCC_FLAGS", "").split(),
     ]
 
 

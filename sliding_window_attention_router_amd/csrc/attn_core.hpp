@@ -24,6 +24,9 @@
 namespace swi {
 
 constexpr int kBN = 64;  // keys per LDS block
+#ifndef SWI_MFMA_PRIO
+#define SWI_MFMA_PRIO 1  // wave issue priority inside MFMA sections
+#endif
 constexpr int kQR = 32;  // query rows per wave
 
 template <typename T, int D>
@@ -174,7 +177,7 @@ struct KVLoader<float, D, NT> {
 // of key kb + 32*mt + 8*(i/4) + 4*g + i%4 for this lane's query.  On return
 // s holds the unnormalised probabilities exp2(sl2*s - m), l is updated and
 // the accumulators rescaled if m moved.  Keys outside [lo, hi] are dropped
-// when MASKED.
+// when `masked` (wave-uniform).
 //
 // m is the running maximum of sl2*score, kept lazily: it is only raised (and
 // the accumulators rescaled) when a block's maximum exceeds it by more than
@@ -183,21 +186,25 @@ struct KVLoader<float, D, NT> {
 // ---------------------------------------------------------------------------
 constexpr float kRescale = 8.f;
 
-template <bool MASKED, int MD>
+template <int MD>
 SWI_DEV void online_softmax(f32x16 (&s)[2], f32x16 (&acc)[MD], float& m, float& l, int kb,
-                            int lo, int hi, float sl2, int g) {
-  float mx = kNegInf;
+                            bool masked, int lo, int hi, float sl2, int g) {
+  // Masking only rewrites the scores, in a wave-uniform branch, so masked
+  // and unmasked blocks share every other instruction and register.
+  if (masked) {
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (MASKED) {
+      for (int i = 0; i < 16; ++i) {
         const int j = kb + mt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
         if (j < lo || j > hi) s[mt][i] = kNegInf;
       }
-      mx = fmaxf(mx, s[mt][i]);
-    }
   }
+  float mx = kNegInf;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mt][i]);
   mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * sl2;
   // raise m when the block maximum exceeds it by more than kRescale (and on
   // the first block that has any key); wave-uniform skip otherwise
@@ -229,6 +236,7 @@ SWI_DEV void online_softmax(f32x16 (&s)[2], f32x16 (&acc)[MD], float& m, float& 
 // ---------------------------------------------------------------------------
 template <int D>
 struct CoreBF16 {
+  using T = bf16_t;
   using L = Lds<bf16_t, D>;
   static constexpr int KS = D / 16;  // k-steps of the score product
   static constexpr int MD = D / 32;  // 32-channel tiles of the output
@@ -248,9 +256,12 @@ struct CoreBF16 {
     for (int ks = 0; ks < KS; ++ks)
       qreg[ks] = qrow ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + g * 8) : bf16x8{};
   }
-  template <bool MASKED>
-  SWI_DEV void block(const char* lds, int kb, int lo, int hi, float sl2, int q, int g) {
+  SWI_DEV void block(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
+                     int g) {
     f32x16 s[2];
+    // Issue priority: a wave raises it for its MFMA sections, so the SIMD's
+    // other wave fills the VALU while the matrix pipe stays busy.
+    __builtin_amdgcn_s_setprio(SWI_MFMA_PRIO);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       s[mt] = f32x16{};
@@ -261,7 +272,8 @@ struct CoreBF16 {
         s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[mt], 0, 0, 0);
       }
     }
-    online_softmax<MASKED, MD>(s, acc, m, l, kb, lo, hi, sl2, g);
+    __builtin_amdgcn_s_setprio(0);
+    online_softmax<MD>(s, acc, m, l, kb, masked, lo, hi, sl2, g);
     bf16x8 pb[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st)
@@ -270,6 +282,7 @@ struct CoreBF16 {
     // k-step st covers keys 16st..16st+15; lane group g supplies quarters
     // 4st+g and 4st+g+2, stored adjacently (Lds::vq_offset)
     const char* vt = lds + L::kKBytes;
+    __builtin_amdgcn_s_setprio(SWI_MFMA_PRIO);
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
       const char* vp = vt + (md * 32 + q) * L::kVStride + g * 16;
@@ -279,12 +292,28 @@ struct CoreBF16 {
         acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], acc[md], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
-  SWI_DEV void block(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
-                     int g) {
-    if (masked) block<true>(lds, kb, lo, hi, sl2, q, g);
-    else block<false>(lds, kb, lo, hi, sl2, q, g);
+};
+
+// Array interface over a one-tile core (TPW = 1): the window and far kernels
+// are written for TPW row tiles per wave.
+template <typename C>
+struct OneTile {
+  using T = typename C::T;
+  using L = typename C::L;
+  static constexpr int TPW = 1;
+  static constexpr int MD = C::MD;
+  C c;
+  SWI_DEV void init() { c.init(); }
+  SWI_DEV void load_q(int, const T* qrow, int g) { c.load_q(qrow, g); }
+  SWI_DEV void block(const char* lds, int kb, bool masked, const int (&lo)[1], const int (&hi)[1],
+                     float sl2, int q, int g) {
+    c.block(lds, kb, masked, lo[0], hi[0], sl2, q, g);
   }
+  SWI_DEV f32x16 (&acc_of(int))[MD] { return c.acc; }
+  SWI_DEV float m_of(int) const { return c.m; }
+  SWI_DEV float l_of(int) const { return c.l; }
 };
 
 // ---------------------------------------------------------------------------
@@ -292,6 +321,7 @@ struct CoreBF16 {
 // ---------------------------------------------------------------------------
 template <int D>
 struct CoreF32 {
+  using T = float;
   using L = Lds<float, D>;
   static constexpr int KS = D / 2;
   static constexpr int MD = D / 32;
@@ -309,8 +339,8 @@ struct CoreF32 {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qreg[ks] = qrow ? qrow[ks * 2 + g] : 0.f;
   }
-  template <bool MASKED>
-  SWI_DEV void block(const char* lds, int kb, int lo, int hi, float sl2, int q, int g) {
+  SWI_DEV void block(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
+                     int g) {
     f32x16 s[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -320,7 +350,7 @@ struct CoreF32 {
       for (int ks = 0; ks < KS; ++ks)
         s[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kp[ks * 2], qreg[ks], s[mt], 0, 0, 0);
     }
-    online_softmax<MASKED, MD>(s, acc, m, l, kb, lo, hi, sl2, g);
+    online_softmax<MD>(s, acc, m, l, kb, masked, lo, hi, sl2, g);
     const char* vs = lds + L::kKBytes;
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
@@ -333,11 +363,6 @@ struct CoreF32 {
       }
     }
   }
-  SWI_DEV void block(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
-                     int g) {
-    if (masked) block<true>(lds, kb, lo, hi, sl2, q, g);
-    else block<false>(lds, kb, lo, hi, sl2, q, g);
-  }
 };
 
 template <typename T, int D>
@@ -349,6 +374,23 @@ struct CoreSel<bf16_t, D> {
 template <int D>
 struct CoreSel<float, D> {
   using type = CoreF32<D>;
+};
+
+// Row-tile configuration of the window and far kernels: 128 query rows per
+// workgroup, four waves of the one-tile core.
+template <typename T, int D>
+struct TileCfg;
+template <int D>
+struct TileCfg<bf16_t, D> {
+  using Core = OneTile<CoreBF16<D>>;
+  static constexpr int kWaves = 4;
+  static constexpr int kMinWG = 2;  // two workgroups per CU: 256 registers per wave
+};
+template <int D>
+struct TileCfg<float, D> {
+  using Core = OneTile<CoreF32<D>>;
+  static constexpr int kWaves = 4;
+  static constexpr int kMinWG = 1;
 };
 
 // Total row sum over the lane pair, the log2-domain normaliser, and 1/sum

@@ -28,8 +28,8 @@
 
 namespace swi {
 
-constexpr int kThreads = 256;      // 4 waves, 128 query rows per workgroup
-constexpr int kRows = 128;
+constexpr int kThreads = 256;      // merge / fused kernels: 4 waves x 32 rows
+constexpr int kRows = 128;          // query rows of every tile
 constexpr int kTargetItems = 2048;  // far work items aimed for per launch
 constexpr int kMinChunkBlocks = 8;  // far chunk is at least 8 x 64 keys
 constexpr int kSchedThreads = 1024;
@@ -107,13 +107,65 @@ struct WaveBounds {
   SWI_DEV bool masked(int kb) const { return kb < max_lo || kb + kBN - 1 > min_hi; }
 };
 
+// Union of the key intervals of the wave's live rows, for skipping blocks
+// and dropping the mask (see WaveBounds).
+template <int TPW>
+struct TileBounds {
+  int min_lo, max_hi;
+  WaveBounds wb;
+  SWI_DEV void init(const bool (&valid)[TPW], const int (&lo)[TPW], const int (&hi)[TPW]) {
+    int a = INT_MAX, b = -1, c = -1, d = INT_MAX;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const bool live = valid[t] && lo[t] <= hi[t];
+      a = min(a, live ? lo[t] : INT_MAX);
+      b = max(b, live ? hi[t] : -1);
+      c = max(c, valid[t] ? lo[t] : -1);
+      d = min(d, valid[t] ? hi[t] : INT_MAX);
+    }
+    min_lo = wave_min_i(a);
+    max_hi = wave_max_i(b);
+    wb.max_lo = wave_max_i(c);
+    wb.min_hi = wave_min_i(d);
+  }
+  SWI_DEV bool needed(int kb) const { return kb <= max_hi && kb + kBN - 1 >= min_lo; }
+  SWI_DEV bool masked(int kb) const { return wb.masked(kb); }
+};
+
+// Blocks kb0, kb0+64, ... (nb of them) of one KV head through the core, with
+// the global loads of the next two blocks in flight (two register stages,
+// used alternately) while a block is computed.
+template <typename Core, typename T, int D, int NT, int TPW>
+SWI_DEV void block_loop(Core& c, char* lds, const T* Kb, const T* Vb, int64_t rs, int kb0, int nb,
+                        int kend, const TileBounds<TPW>& tb, const int (&lo)[TPW],
+                        const int (&hi)[TPW], float sl2, int tid, int q, int g) {
+  KVLoader<T, D, NT> ld[2];
+  ld[0].load(Kb, Vb, rs, kb0, kend, tid);
+  if (nb > 1) ld[1].load(Kb, Vb, rs, kb0 + kBN, kend, tid);
+  for (int n = 0; n < nb; n += 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {  // stage j holds block n + j
+      const int m = n + j;
+      if (m >= nb) break;
+      const int kb = kb0 + m * kBN;
+      __syncthreads();
+      ld[j].store(lds, tid);
+      __syncthreads();
+      if (m + 2 < nb) ld[j].load(Kb, Vb, rs, kb + 2 * kBN, kend, tid);
+      if (tb.needed(kb)) c.block(lds, kb, tb.masked(kb), lo, hi, sl2, q, g);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Window branch over every row.  Grid (band_tiles, B*Hkv).  Rows of a tile
-// are tpt_band consecutive tokens x the HK query heads of one KV head.
+// Window branch over every row.  Rows of a tile are tpt_band consecutive
+// tokens x the HK query heads of one KV head (128 rows).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 2) void band_kernel(PrefillArgs a) {
-  using Core = typename CoreSel<T, D>::type;
+__global__ __launch_bounds__((TileCfg<T, D>::kWaves * 64), (TileCfg<T, D>::kMinWG)) void band_kernel(PrefillArgs a) {
+  using Core = typename TileCfg<T, D>::Core;
+  constexpr int NT = TileCfg<T, D>::kWaves * 64;
+  constexpr int TPW = Core::TPW;
   __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
   // consecutive tiles of one KV head share most of their window: keep them
   // on one XCD's L2
@@ -126,40 +178,40 @@ __global__ __launch_bounds__(kThreads, 2) void band_kernel(PrefillArgs a) {
   const int q = lane & 31, g = lane >> 5;
   const int q0 = tile * a.tpt_band;
   const int qlast = min(a.N - 1, q0 + a.tpt_band - 1);
-  const int r = wave * kQR + q;
-  const int slot = r / a.HK, hh = r - slot * a.HK;
-  const int tok = q0 + slot;
-  const bool valid = slot < a.tpt_band && tok < a.N;
-  const int h = kvh * a.HK + hh;
-  const int lo = valid ? max(0, tok - a.W + 1) : 0;
-  const int hi = valid ? tok : -1;
-  WaveBounds wb;
-  wb.init(valid, lo, hi);
-
+  int tok[TPW], h[TPW], lo[TPW], hi[TPW];
+  bool valid[TPW];
   Core c;
   c.init();
   const T* Qp = static_cast<const T*>(a.Q);
-  c.load_q(valid ? Qp + ((int64_t(b) * a.N + tok) * a.Hq + h) * D : nullptr, g);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int r = wave * (kQR * TPW) + t * kQR + q;
+    const int slot = r / a.HK, hh = r - slot * a.HK;
+    tok[t] = q0 + slot;
+    valid[t] = slot < a.tpt_band && tok[t] < a.N;
+    h[t] = kvh * a.HK + hh;
+    lo[t] = valid[t] ? max(0, tok[t] - a.W + 1) : 0;
+    hi[t] = valid[t] ? tok[t] : -1;
+    c.load_q(t, valid[t] ? Qp + ((int64_t(b) * a.N + tok[t]) * a.Hq + h[t]) * D : nullptr, g);
+  }
+  TileBounds<TPW> tb;
+  tb.init(valid, lo, hi);
 
   const T* Kb = static_cast<const T*>(a.K) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
   const T* Vb = static_cast<const T*>(a.V) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
   const int64_t rs = int64_t(a.Hkv) * D;
   const int kb0 = (max(0, q0 - a.W + 1) / kBN) * kBN;
-  KVLoader<T, D, kThreads> ld;
-  ld.load(Kb, Vb, rs, kb0, a.N, tid);
-  for (int kb = kb0; kb <= qlast; kb += kBN) {
-    __syncthreads();
-    ld.store(lds, tid);
-    __syncthreads();
-    if (kb + kBN <= qlast) ld.load(Kb, Vb, rs, kb + kBN, a.N, tid);
-    if (wb.needed(kb)) c.block(lds, kb, wb.masked(kb), lo, hi, a.sl2, q, g);
-  }
-  float lse2;
-  const float inv = finish_row(c.m, c.l, lse2);
-  if (valid) {
-    T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D;
-    store_row<Core::MD>(orow, c.acc, inv, g);
-    if (g == 0 && a.lse_s) a.lse_s[(int64_t(b) * a.Hq + h) * a.N + tok] = lse2;
+  block_loop<Core, T, D, NT>(c, lds, Kb, Vb, rs, kb0, (qlast - kb0) / kBN + 1, a.N, tb, lo, hi,
+                             a.sl2, tid, q, g);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    float lse2;
+    const float inv = finish_row(c.m_of(t), c.l_of(t), lse2);
+    if (valid[t]) {
+      T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok[t]) * a.Hq + h[t]) * D;
+      store_row<Core::MD>(orow, c.acc_of(t), inv, g);
+      if (g == 0 && a.lse_s) a.lse_s[(int64_t(b) * a.Hq + h[t]) * a.N + tok[t]] = lse2;
+    }
   }
 }
 
@@ -292,8 +344,10 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
 // chunks of longer tiles write normalised partials for merge_kernel.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 2) void far_kernel(PrefillArgs a) {
-  using Core = typename CoreSel<T, D>::type;
+__global__ __launch_bounds__((TileCfg<T, D>::kWaves * 64), (TileCfg<T, D>::kMinWG)) void far_kernel(PrefillArgs a) {
+  using Core = typename TileCfg<T, D>::Core;
+  constexpr int NT = TileCfg<T, D>::kWaves * 64;
+  constexpr int TPW = Core::TPW;
   __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
   // items are ordered by (unit, chunk, tile); an XCD takes a contiguous
   // slice, so its resident workgroups read the same keys of one KV head
@@ -304,66 +358,68 @@ __global__ __launch_bounds__(kThreads, 2) void far_kernel(PrefillArgs a) {
   const int T_ = sv.item_tile[item], ch = sv.item_chunk[item];
   const int per_b = a.units * a.far_tiles;
   const int b = T_ / per_b, rem = T_ - b * per_b;
-  const int u = rem / a.far_tiles, t = rem - u * a.far_tiles;
+  const int u = rem / a.far_tiles, t_ = rem - u * a.far_tiles;
   const int g_gate = (u * a.hpu) / a.HG;
   const int kvh = (u * a.hpu) / a.HK;
-  const int c = a.cnt[b * a.G + g_gate];
+  const int cnt = a.cnt[b * a.G + g_gate];
   const int32_t* ix = a.idx + (int64_t(b) * a.G + g_gate) * a.N;
-  const int ntok = min(a.tpt_far, c - t * a.tpt_far);
-  const int far_hi = ix[t * a.tpt_far + ntok - 1] - a.W;
+  const int ntok = min(a.tpt_far, cnt - t_ * a.tpt_far);
+  const int far_hi = ix[t_ * a.tpt_far + ntok - 1] - a.W;
   const int c0 = ch * cb * kBN;
   const int c1 = min(far_hi + 1, (ch + 1) * cb * kBN);  // keys [c0, c1)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane & 31, g = lane >> 5;
-  const int r = wave * kQR + q;
-  const int slot = r / a.hpu, hh = r - slot * a.hpu;
-  const bool valid = slot < ntok;
-  const int tok = valid ? ix[t * a.tpt_far + slot] : 0;
-  const int h = u * a.hpu + hh;
-  const int lo = c0;
-  const int hi = valid ? min(tok - a.W, c1 - 1) : -1;
-  WaveBounds wb;
-  wb.init(valid, lo, hi);
-
-  Core c_;
-  c_.init();
+  int r[TPW], tok[TPW], h[TPW], lo[TPW], hi[TPW];
+  bool valid[TPW];
+  Core c;
+  c.init();
   const T* Qp = static_cast<const T*>(a.Q);
-  c_.load_q(valid ? Qp + ((int64_t(b) * a.N + tok) * a.Hq + h) * D : nullptr, g);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    r[t] = wave * (kQR * TPW) + t * kQR + q;
+    const int slot = r[t] / a.hpu, hh = r[t] - slot * a.hpu;
+    valid[t] = slot < ntok;
+    tok[t] = valid[t] ? ix[t_ * a.tpt_far + slot] : 0;
+    h[t] = u * a.hpu + hh;
+    lo[t] = c0;
+    hi[t] = valid[t] ? min(tok[t] - a.W, c1 - 1) : -1;
+    c.load_q(t, valid[t] ? Qp + ((int64_t(b) * a.N + tok[t]) * a.Hq + h[t]) * D : nullptr, g);
+  }
+  TileBounds<TPW> tb;
+  tb.init(valid, lo, hi);
   const T* Kb = static_cast<const T*>(a.K) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
   const T* Vb = static_cast<const T*>(a.V) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
   const int64_t rs = int64_t(a.Hkv) * D;
-  KVLoader<T, D, kThreads> ld;
-  ld.load(Kb, Vb, rs, c0, c1, tid);
-  for (int kb = c0; kb < c1; kb += kBN) {
-    __syncthreads();
-    ld.store(lds, tid);
-    __syncthreads();
-    if (kb + kBN < c1) ld.load(Kb, Vb, rs, kb + kBN, c1, tid);
-    if (wb.needed(kb)) c_.block(lds, kb, wb.masked(kb), lo, hi, a.sl2, q, g);
-  }
-  float lse2;
-  const float inv = finish_row(c_.m, c_.l, lse2);
-  if (!valid) return;
-  if (sv.n_items[T_] > 1) {  // the merge kernel combines the tile's chunks
-    float* prow = a.part_o + (int64_t(item) * kRows + r) * D;
-    store_row<Core::MD>(prow, c_.acc, inv, g);
-    if (g == 0) a.part_lse[int64_t(item) * kRows + r] = lse2;
-    return;
-  }
-  // single-chunk tile: merge with the window result right here
-  if (tok < a.W) return;
-  const float ls = a.lse_s[(int64_t(b) * a.Hq + h) * a.N + tok];
-  const float M = fmaxf(ls, lse2);
-  const float ws = fast_exp2(ls - M), wf = fast_exp2(lse2 - M);
-  T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D;
-  const float sf = inv * wf;
+  block_loop<Core, T, D, NT>(c, lds, Kb, Vb, rs, c0, (c1 - c0 + kBN - 1) / kBN, c1, tb, lo, hi,
+                             a.sl2, tid, q, g);
+  const bool split = sv.n_items[T_] > 1;
 #pragma unroll
-  for (int md = 0; md < Core::MD; ++md)
+  for (int t = 0; t < TPW; ++t) {
+    float lse2;
+    const float inv = finish_row(c.m_of(t), c.l_of(t), lse2);
+    if (!valid[t]) continue;
+    auto& acc = c.acc_of(t);
+    if (split) {  // the merge kernel combines the tile's chunks
+      float* prow = a.part_o + (int64_t(item) * kRows + r[t]) * D;
+      store_row<Core::MD>(prow, acc, inv, g);
+      if (g == 0) a.part_lse[int64_t(item) * kRows + r[t]] = lse2;
+      continue;
+    }
+    // single-chunk tile: merge with the window result right here
+    if (tok[t] < a.W) continue;
+    const float ls = a.lse_s[(int64_t(b) * a.Hq + h[t]) * a.N + tok[t]];
+    const float M = fmaxf(ls, lse2);
+    const float ws = fast_exp2(ls - M), wf = fast_exp2(lse2 - M);
+    T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok[t]) * a.Hq + h[t]) * D;
+    const float sf = inv * wf;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      c_.acc[md][i] = fmaf(c_.acc[md][i], sf, ws * Elem<T>::load(orow + acc_channel(md, i, g)));
-  store_row<Core::MD>(orow, c_.acc, 1.f / (ws + wf), g);
+    for (int md = 0; md < Core::MD; ++md)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        acc[md][i] = fmaf(acc[md][i], sf, ws * Elem<T>::load(orow + acc_channel(md, i, g)));
+    store_row<Core::MD>(orow, acc, 1.f / (ws + wf), g);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -582,16 +638,15 @@ static hipError_t run_prefill(const PrefillShape& sh, const PrefillPlan& p, Pref
   if ((e = (x)) != hipSuccess) return e;
   if (!sh.both_branch) {
     SWI_TRY(mark(ev, 0, s));
+    constexpr int nt = TileCfg<T, D>::kWaves * 64;
     const int band_total = p.band_tiles * sh.B * sh.Hkv;
-    hipLaunchKernelGGL((band_kernel<T, D>), dim3(8 * ((band_total + 7) / 8)), dim3(kThreads), 0,
-                       s, a);
+    hipLaunchKernelGGL((band_kernel<T, D>), dim3(8 * ((band_total + 7) / 8)), dim3(nt), 0, s, a);
     SWI_TRY(hipGetLastError());
     SWI_TRY(mark(ev, 1, s));
     hipLaunchKernelGGL(far_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, a);
     SWI_TRY(hipGetLastError());
     SWI_TRY(mark(ev, 2, s));
-    hipLaunchKernelGGL((far_kernel<T, D>), dim3(8 * ((p.max_items + 7) / 8)), dim3(kThreads), 0,
-                       s, a);
+    hipLaunchKernelGGL((far_kernel<T, D>), dim3(8 * ((p.max_items + 7) / 8)), dim3(nt), 0, s, a);
     SWI_TRY(hipGetLastError());
     SWI_TRY(mark(ev, 3, s));
     hipLaunchKernelGGL((merge_kernel<T, D>), dim3(sh.B * p.units * p.far_tiles), dim3(kThreads), 0,
