@@ -136,16 +136,16 @@ def main():
         return evs
 
     def step(ev=None):
-        # ev: 11 events: [route start] + prefill stages 0..4 + decode stages 0..3 + [end]
+        # ev: 10 events: [route start] + prefill stages 0..4 + decode stages 0..2 + [end]
         if ev is not None:
             ev[0].record()
         swa.route(H, r, bias, out=(gate, idx, cnt))
         swa.prefill(Q, K, V, gate, W, idx=idx, cnt=cnt, out=O, workspace=ws_p,
                     events=ev[1:6] if ev is not None else None)
         swa.decode(q_d, Kc, Vc, len_d, gate_d, W, out=o_d, workspace=ws_d,
-                   events=ev[6:10] if ev is not None else None)
+                   events=ev[6:9] if ev is not None else None)
         if ev is not None:
-            ev[10].record()
+            ev[9].record()
 
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -158,7 +158,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evsets = [new_events(11) for _ in range(args.steps)]
+    evsets = [new_events(10) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
@@ -176,12 +176,11 @@ def main():
         "far_schedule": avg(2, 3),
         "far": avg(3, 4),
         "merge": avg(4, 5),
-        "decode_schedule": avg(6, 7),
-        "decode_splitk": avg(7, 8),
-        "decode_merge": avg(8, 9),
+        "decode_splitk": avg(6, 7),
+        "decode_merge": avg(7, 8),
     }
     prefill_ms = avg(0, 5)
-    decode_ms = avg(6, 9)
+    decode_ms = avg(6, 8)
     step_ms = wall * 1e3 / args.steps
 
     g_host = gate.cpu().numpy()

@@ -167,8 +167,7 @@ int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t*
  *     merge;
  *   prefill, both-branch mode: 0 before the fused kernel, 1 after it,
  *     2 after the per-token head sum;
- *   decode: 0 before the schedule, 1 after it, 2 after the split-K kernel,
- *     3 after the merge.
+ *   decode: 0 before the split-K kernel, 1 after it, 2 after the merge.
  * Passing events == NULL is the plain call.  Recording failures are
  * reported as SWIATTN_ERR_HIP.
  */

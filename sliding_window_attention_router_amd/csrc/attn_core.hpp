@@ -64,11 +64,21 @@ struct Lds<float, D> {
 // value adds nothing.
 // ---------------------------------------------------------------------------
 SWI_DEV int clamp_row(int kk, int kend) { return kk < kend ? kk : kend - 1; }
-template <typename T, int D, int NT>
+
+// kStream: the rows are read once (decode), so the loads carry the
+// non-temporal hint and do not displace reusable lines from the caches.
+template <bool kStream>
+SWI_DEV u32x4 load16(const void* p) {
+  const u32x4* v = static_cast<const u32x4*>(p);
+  if constexpr (kStream) return __builtin_nontemporal_load(v);
+  return *v;
+}
+
+template <typename T, int D, int NT, bool kStream = false>
 struct KVLoader;
 
-template <int D, int NT>
-struct KVLoader<bf16_t, D, NT> {
+template <int D, int NT, bool kStream>
+struct KVLoader<bf16_t, D, NT, kStream> {
   using L = Lds<bf16_t, D>;
   static constexpr int CPR = D / 8;  // 16-byte pieces per row
   static constexpr int KU = kBN * CPR;
@@ -90,7 +100,7 @@ struct KVLoader<bf16_t, D, NT> {
       const int key = u / CPR, c = u - key * CPR;
       if (KU % NT != 0 && u >= KU) continue;
       const int kk = clamp_row(kb + key, kend);
-      kr[j] = *reinterpret_cast<const u32x4*>(Kb + kk * rs + c * 8);
+      kr[j] = load16<kStream>(Kb + kk * rs + c * 8);
     }
 #pragma unroll
     for (int j = 0; j < VPER; ++j) {
@@ -100,7 +110,7 @@ struct KVLoader<bf16_t, D, NT> {
       for (int r = 0; r < 4; ++r) {
         if (VU % NT != 0 && u >= VU) continue;
         const int kk = clamp_row(kb + 4 * kq + r, kend);
-        vr[j][r] = *reinterpret_cast<const u32x4*>(Vb + kk * rs + c * 8);
+        vr[j][r] = load16<kStream>(Vb + kk * rs + c * 8);
       }
     }
   }
@@ -134,8 +144,8 @@ struct KVLoader<bf16_t, D, NT> {
   }
 };
 
-template <int D, int NT>
-struct KVLoader<float, D, NT> {
+template <int D, int NT, bool kStream>
+struct KVLoader<float, D, NT, kStream> {
   using L = Lds<float, D>;
   static constexpr int CPR = D / 4;
   static constexpr int KU = kBN * CPR;
@@ -151,8 +161,8 @@ struct KVLoader<float, D, NT> {
       const int key = u / CPR, c = u - key * CPR;
       if (KU % NT != 0 && u >= KU) continue;
       const int kk = clamp_row(kb + key, kend);
-      kr[j] = *reinterpret_cast<const u32x4*>(Kb + kk * rs + c * 4);
-      vr[j] = *reinterpret_cast<const u32x4*>(Vb + kk * rs + c * 4);
+      kr[j] = load16<kStream>(Kb + kk * rs + c * 4);
+      vr[j] = load16<kStream>(Vb + kk * rs + c * 4);
     }
   }
   SWI_DEV void store(char* lds, int tid) const {

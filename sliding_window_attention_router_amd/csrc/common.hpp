@@ -40,6 +40,21 @@ SWI_DEV int wave_min_i(int v) {
   for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
   return v;
 }
+SWI_DEV int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+// Inclusive prefix sum over the lanes of the wave.
+SWI_DEV int wave_incl_scan_i(int v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
 SWI_DEV int wave_max_i(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));

@@ -7,13 +7,19 @@
 // "详细解释").  The bytes read therefore depend on the gate: 32K keys for a
 // full sequence at a 32K cache, W keys otherwise.
 //
-// decode_schedule_kernel  (one workgroup) turns gates and cache lengths into
-//                         a list of (sequence, KV head, key chunk) items
-// decode_kernel           persistent single-wave workgroups; each walks its
-//                         items' key blocks with the next block's loads in
-//                         flight (also across item boundaries) and writes a
-//                         normalised partial output + log-sum-exp per item
-// decode_merge_kernel     log-sum-exp merge of a sequence's chunks
+// Work split (stream-K): the key range of each (sequence, KV head) pair is
+// cut into 64-key blocks, the blocks of all pairs are laid end to end, and
+// workgroup w of G takes the contiguous share [w*T/G, (w+1)*T/G) of the T
+// blocks.  Every workgroup reads the gates and cache lengths itself to find
+// T and its share, so no scheduling launch precedes the kernel; the shares
+// differ by at most one block.
+//
+// decode_kernel        single-wave workgroups; each walks its share with the
+//                      next block's loads in flight (also across pairs).  A
+//                      pair that lies wholly inside one share is finished and
+//                      written there; a pair cut by share boundaries leaves a
+//                      normalised partial output + log-sum-exp per piece
+// decode_merge_kernel  log-sum-exp merge of the pieces of each cut pair
 #include <climits>
 
 #include "attn_core.hpp"
@@ -21,9 +27,11 @@
 
 namespace swi {
 
-constexpr int kDecChunk = 256;       // keys per work item (4 blocks of 64)
-constexpr int kDecThreads = 64;      // one wave per workgroup
-constexpr int kDecSchedThreads = 1024;
+constexpr int kDecThreads = 64;  // one wave per workgroup
+constexpr int kDecGrid = 1024;   // four 35 KB workgroups per CU (LDS-bound)
+#ifndef SWI_DEC_STREAM
+#define SWI_DEC_STREAM true
+#endif
 
 struct DecodeArgs {
   const void* q;
@@ -32,23 +40,11 @@ struct DecodeArgs {
   const int32_t* cache_len;
   const uint8_t* gate;
   void* o;
-  int32_t* sched;   // [0] total, item_start[nbk] | n_items[nbk] | lo[nbk] | item_bk[max] | item_ch[max]
-  float* part_o;    // [max_items][HK][D]
-  float* part_lse;  // [max_items][HK]
-  int B, Lmax, Hq, Hkv, G, W, HK, HG, max_items;
+  int32_t* info;    // [0] T; per pair bk: [1+2bk] first block if cut else -1, [2+2bk] block count
+  float* part_o;    // [2*grid][HK][D] pieces of cut pairs, slot 2w (first piece of share w) or 2w+1
+  float* part_lse;  // [2*grid][HK]
+  int B, Lmax, Hq, Hkv, G, W, HK, HG;
   float sl2;
-};
-
-struct DecSched {
-  int32_t *item_start, *n_items, *lo, *item_bk, *item_ch;
-  SWI_DEV DecSched(const DecodeArgs& a) {
-    const int nbk = a.B * a.Hkv;
-    item_start = a.sched + 1;
-    n_items = item_start + nbk;
-    lo = n_items + nbk;
-    item_bk = lo + nbk;
-    item_ch = item_bk + a.max_items;
-  }
 };
 
 SWI_DEV int clamp_len(int L, int Lmax) { return L < 1 ? 1 : (L > Lmax ? Lmax : L); }
@@ -59,77 +55,62 @@ SWI_DEV int head_lo(const DecodeArgs& a, int b, int h, int L) {
   return full ? 0 : max(0, L - a.W);
 }
 
-__global__ __launch_bounds__(kDecSchedThreads) void decode_schedule_kernel(DecodeArgs a) {
-  __shared__ int sh[kDecSchedThreads / 64 + 1];
-  __shared__ int carry_s;
-  DecSched sv(a);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nbk = a.B * a.Hkv;
-  if (tid == 0) carry_s = 0;
-  __syncthreads();
-  for (int base = 0; base < nbk; base += kDecSchedThreads) {
-    const int bk = base + tid;
-    int n = 0, lo = 0;
-    if (bk < nbk) {
-      const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
-      const int L = clamp_len(a.cache_len[b], a.Lmax);
-      lo = INT_MAX;
-      for (int hh = 0; hh < a.HK; ++hh) lo = min(lo, head_lo(a, b, kvh * a.HK + hh, L));
-      n = (L - lo + kDecChunk - 1) / kDecChunk;
-    }
-    int incl = n;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
-    if (lane == 63) sh[wave] = incl;
-    __syncthreads();
-    if (wave == 0) {
-      const int nw = kDecSchedThreads / 64;
-      const int x = lane < nw ? sh[lane] : 0;
-      int w = x;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(w, o, 64);
-        if (lane >= o) w += t;
-      }
-      if (lane < nw) sh[lane] = w - x;
-      if (lane == nw - 1) sh[nw] = w;
-    }
-    __syncthreads();
-    const int start = carry_s + sh[wave] + incl - n;
-    if (bk < nbk) {
-      sv.item_start[bk] = start;
-      sv.n_items[bk] = n;
-      sv.lo[bk] = lo;
-      for (int k = 0; k < n; ++k) {
-        sv.item_bk[start + k] = bk;
-        sv.item_ch[start + k] = k;
-      }
-    }
-    __syncthreads();
-    if (tid == 0) carry_s += sh[kDecSchedThreads / 64];
-    __syncthreads();
-  }
-  if (tid == 0) a.sched[0] = carry_s;
+// Keys [lo, L) read for pair bk = (sequence, KV head): the union of the
+// ranges of its query heads.  Returns the number of 64-key blocks.
+SWI_DEV int pair_blocks(const DecodeArgs& a, int bk, int& L, int& lo) {
+  const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
+  L = clamp_len(a.cache_len[b], a.Lmax);
+  const int g0 = kvh * a.HK / a.HG, g1 = (kvh * a.HK + a.HK - 1) / a.HG;
+  bool full = false;
+  for (int gg = g0; gg <= g1; ++gg) full = full || a.gate[b * a.G + gg] != 0;
+  lo = full ? 0 : max(0, L - a.W);
+  return (L - lo + kBN - 1) / kBN;
 }
 
-template <typename T, int D>
-struct DecItem {
-  int b, kvh, L, c0, c1, nblk;
-  SWI_DEV void setup(const DecodeArgs& a, const DecSched& sv, int item) {
-    const int bk = sv.item_bk[item], ch = sv.item_ch[item];
+// First block of share w: floor(w*T/G).
+SWI_DEV int share_start(int w, int T, int G) { return int(int64_t(w) * T / G); }
+// The share that holds block x: the largest w with share_start(w) <= x.
+SWI_DEV int share_of(int x, int T, int G) {
+  return int(((int64_t(x) + 1) * G + T - 1) / T) - 1;
+}
+
+SWI_DEV int lane_of(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
+
+// 64 consecutive pairs, one per lane, with the inclusive prefix sum of their
+// block counts (absolute: carry holds the blocks of all earlier pairs).
+struct PairWindow {
+  int base, L, lo, incl;
+  SWI_DEV void fill(const DecodeArgs& a, int base_, int carry, int lane, int npairs) {
+    base = base_;
+    const int bk = base + lane;
+    int n = 0;
+    L = 1;
+    lo = 0;
+    if (bk < npairs) n = pair_blocks(a, bk, L, lo);
+    incl = wave_incl_scan_i(n) + carry;
+  }
+};
+
+// The blocks [blk0, blk1) of pair bk that fall into share [s, e).
+struct DecSeg {
+  int bk, b, kvh, L, lo, first, nb, blk0, blk1;
+  SWI_DEV void from(const DecodeArgs& a, const PairWindow& win, int j, int s, int e) {
+    bk = win.base + j;
     b = bk / a.Hkv;
     kvh = bk - b * a.Hkv;
-    L = clamp_len(a.cache_len[b], a.Lmax);
-    c0 = sv.lo[bk] + ch * kDecChunk;
-    c1 = min(L, c0 + kDecChunk);
-    nblk = (c1 - c0 + kBN - 1) / kBN;
+    L = lane_of(win.L, j);
+    lo = lane_of(win.lo, j);
+    const int incl = lane_of(win.incl, j);
+    nb = (L - lo + kBN - 1) / kBN;
+    first = incl - nb;
+    blk0 = max(s, first) - first;
+    blk1 = min(e, incl) - first;
   }
+  template <typename T, int D>
   SWI_DEV const T* kbase(const DecodeArgs& a) const {
     return static_cast<const T*>(a.Kc) + (int64_t(b) * a.Lmax * a.Hkv + kvh) * D;
   }
+  template <typename T, int D>
   SWI_DEV const T* vbase(const DecodeArgs& a) const {
     return static_cast<const T*>(a.Vc) + (int64_t(b) * a.Lmax * a.Hkv + kvh) * D;
   }
@@ -139,140 +120,179 @@ template <typename T, int D>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   using Core = typename CoreSel<T, D>::type;
   __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
-  const int total = a.sched[0];
-  int item = blockIdx.x;
-  if (item >= total) return;
-  DecSched sv(a);
   const int lane = threadIdx.x, q = lane & 31, g = lane >> 5;
+  const int npairs = a.B * a.Hkv;
+  const int G = gridDim.x, w = blockIdx.x;
+
+  // the blocks of all pairs (every workgroup counts them itself)
+  int tsum = 0;
+  for (int base = 0; base < npairs; base += 4 * kWave) {
+    int n[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int bk = base + k * kWave + lane;
+      int L, lo;
+      n[k] = bk < npairs ? pair_blocks(a, bk, L, lo) : 0;
+    }
+    tsum += n[0] + n[1] + n[2] + n[3];
+  }
+  const int total = wave_sum_i(tsum);
+  if (w == 0 && lane == 0) a.info[0] = total;
+  const int s = share_start(w, total, G), e = share_start(w + 1, total, G);
+  if (s >= e) return;
+
+  // the pair holding block s
+  PairWindow win;
+  int carry = 0, j = -1;
+  for (int base = 0; base < npairs; base += kWave) {
+    win.fill(a, base, carry, lane, npairs);
+    const uint64_t hit = __ballot(win.incl > s);
+    if (hit) {
+      j = __builtin_ctzll(hit);
+      break;
+    }
+    carry = lane_of(win.incl, kWave - 1);
+  }
+  if (j < 0) return;  // unreachable: s < T
+
   const bool valid = q < a.HK;
   const int64_t rs = int64_t(a.Hkv) * D;
-
-  DecItem<T, D> it;
-  it.setup(a, sv, item);
+  DecSeg cur;
+  cur.from(a, win, j, s, e);
   Core c;
-  int lo = 0, hi = -1;
-  auto begin_item = [&]() {
+  int lo_h = 0, hi = -1, wmax_lo = 0;
+  auto begin = [&]() {
     c.init();
-    const int h = it.kvh * a.HK + q;
-    const T* qp = static_cast<const T*>(a.q) + (int64_t(it.b) * a.Hq + h) * D;
+    const int h = cur.kvh * a.HK + q;
+    const T* qp = static_cast<const T*>(a.q) + (int64_t(cur.b) * a.Hq + h) * D;
     c.load_q(valid ? qp : nullptr, g);
-    lo = valid ? max(it.c0, head_lo(a, it.b, h, it.L)) : 0;
-    hi = valid ? it.c1 - 1 : -1;
+    lo_h = valid ? head_lo(a, cur.b, h, cur.L) : 0;
+    hi = valid ? cur.L - 1 : -1;
+    // heads of one KV head may start at different keys (window heads next
+    // to full ones): blocks before the latest start are masked
+    wmax_lo = wave_max_i(valid ? lo_h : -1);
   };
-  begin_item();
-  KVLoader<T, D, kDecThreads> ld;
-  ld.load(it.kbase(a), it.vbase(a), rs, it.c0, it.c1, lane);
-  int n = 0;
+  begin();
+  KVLoader<T, D, kDecThreads, SWI_DEC_STREAM> ld;
+  ld.load(cur.kbase<T, D>(a), cur.vbase<T, D>(a), rs, cur.lo + cur.blk0 * kBN, cur.L, lane);
+  int n = cur.blk0;
   while (true) {
-    // the block after this one, possibly in the next item
-    int nitem = item, nn = n + 1;
-    if (nn >= it.nblk) {
-      nitem = item + gridDim.x;
-      nn = 0;
+    // the block after this one, possibly the first block of the next pair
+    const bool seg_end = n + 1 >= cur.blk1;
+    const bool more = !seg_end || cur.first + cur.blk1 < e;
+    DecSeg nx = cur;
+    int nn = n + 1;
+    if (seg_end && more) {
+      if (++j == kWave) {
+        win.fill(a, win.base + kWave, lane_of(win.incl, kWave - 1), lane, npairs);
+        j = 0;
+      }
+      nx.from(a, win, j, s, e);
+      nn = nx.blk0;
     }
     __syncthreads();
     ld.store(lds, lane);
     __syncthreads();
-    DecItem<T, D> nx = it;
-    if (nitem < total) {
-      if (nitem != item) nx.setup(a, sv, nitem);
-      ld.load(nx.kbase(a), nx.vbase(a), rs, nx.c0 + nn * kBN, nx.c1, lane);
-    }
-    const int kb = it.c0 + n * kBN;
-    // rows of the wave may start later than the item (window heads sharing a
-    // KV head with a full head); the block beyond c1 is zero-filled
-    const int wmax_lo = wave_max_i(valid ? lo : -1);
-    const bool masked = kb < wmax_lo || kb + kBN > it.c1;
-    c.block(lds, kb, masked, lo, hi, a.sl2, q, g);
-    if (nn == 0) {  // item finished
-      float lse2;
-      const float inv = finish_row(c.m, c.l, lse2);
-      if (valid) {
-        float* prow = a.part_o + (int64_t(item) * a.HK + q) * D;
-        store_row<Core::MD>(prow, c.acc, inv, g);
-        if (g == 0) a.part_lse[int64_t(item) * a.HK + q] = lse2;
-      }
-      if (nitem >= total) break;
-      item = nitem;
-      it = nx;
-      begin_item();
-      n = 0;
-    } else {
+    if (more) ld.load(nx.kbase<T, D>(a), nx.vbase<T, D>(a), rs, nx.lo + nn * kBN, nx.L, lane);
+    const int kb = cur.lo + n * kBN;
+    const bool masked = kb < wmax_lo || kb + kBN > cur.L;
+    c.block(lds, kb, masked, lo_h, hi, a.sl2, q, g);
+    if (!seg_end) {
       n = nn;
+      continue;
     }
+    // pair piece finished: write the output, or a partial for the merge
+    float lse2;
+    const float inv = finish_row(c.m, c.l, lse2);
+    const bool whole = cur.blk0 == 0 && cur.blk1 == cur.nb;
+    if (whole) {
+      T* orow = static_cast<T*>(a.o) + (int64_t(cur.b) * a.Hq + cur.kvh * a.HK + q) * D;
+      if (valid) store_row<Core::MD>(orow, c.acc, inv, g);
+    } else {
+      const int slot = 2 * w + (cur.first + cur.blk0 == s ? 0 : 1);
+      if (valid) {
+        store_row<Core::MD>(a.part_o + (int64_t(slot) * a.HK + q) * D, c.acc, inv, g);
+        if (g == 0) a.part_lse[int64_t(slot) * a.HK + q] = lse2;
+      }
+    }
+    if (cur.blk0 == 0 && lane == 0) {  // the share that starts the pair describes it
+      a.info[1 + 2 * cur.bk] = whole ? -1 : cur.first;
+      a.info[2 + 2 * cur.bk] = cur.nb;
+    }
+    if (!more) break;
+    cur = nx;
+    begin();
+    n = nn;
   }
 }
 
-// One workgroup per (sequence, query head): the four waves take every
-// fourth chunk, each keeps its own maximum and weighted sum, and the waves
-// are combined through LDS in a fixed order.
+// One workgroup per pair cut by share boundaries.  Thread t merges output
+// elements 2t, 2t+1 (+512 ...) of the pair's [HK][D] block over its pieces
+// in share order (a fixed order, so the result does not depend on timing),
+// with the log-sum-exp rule: weights 2^(lse_k - max) on the normalised
+// piece outputs.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int PL = D / 64;  // adjacent channels per lane
-  __shared__ float sm[4], sl[4];
-  __shared__ float so[4][D];
-  DecSched sv(a);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int b = blockIdx.x / a.Hq, h = blockIdx.x - b * a.Hq;
-  const int kvh = h / a.HK, r = h - kvh * a.HK;
-  const int bk = b * a.Hkv + kvh;
-  const int is = sv.item_start[bk], ni = sv.n_items[bk];
-  float M = kNegInf;
-  for (int k = w + 4 * lane; k < ni; k += 256) M = fmaxf(M, a.part_lse[int64_t(is + k) * a.HK + r]);
-  M = wave_max(M);
-  float o[PL];
-#pragma unroll
-  for (int e = 0; e < PL; ++e) o[e] = 0.f;
-  float L = 0.f;
-  int k = w;
-  for (; k + 12 < ni; k += 16) {  // four chunks of this wave per step, loads in flight together
-    float lk[4], v[4][PL];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t it = is + k + 4 * j;
-      lk[j] = a.part_lse[it * a.HK + r];
-#pragma unroll
-      for (int e = 0; e < PL; ++e) v[j][e] = a.part_o[(it * a.HK + r) * D + lane * PL + e];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float wt = lk[j] == kNegInf ? 0.f : fast_exp2(lk[j] - M);
-      L += wt;
-#pragma unroll
-      for (int e = 0; e < PL; ++e) o[e] = fmaf(wt, v[j][e], o[e]);
-    }
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int G) {
+  __shared__ int slots[kDecGrid];
+  const int bk = blockIdx.x;
+  const int first = a.info[1 + 2 * bk];
+  if (first < 0) return;
+  const int nb = a.info[2 + 2 * bk], total = a.info[0];
+  const int w0 = share_of(first, total, G), w1 = share_of(first + nb - 1, total, G);
+  const int np = w1 - w0 + 1;
+  // piece in share w0: its first or its second slot; later shares start
+  // inside the pair, so their piece is their first slot (empty shares,
+  // possible when there are fewer blocks than workgroups, hold none)
+  for (int k = threadIdx.x; k < np; k += 256) {
+    const int w = w0 + k;
+    int sl = 2 * w;
+    if (k == 0) sl += share_start(w0, total, G) == first ? 0 : 1;
+    else if (share_start(w, total, G) == share_start(w + 1, total, G)) sl = -1;
+    slots[k] = sl;
   }
-  for (; k < ni; k += 4) {
-    const int64_t it = is + k;
-    const float lk = a.part_lse[it * a.HK + r];
-    const float wt = lk == kNegInf ? 0.f : fast_exp2(lk - M);
-    L += wt;
-#pragma unroll
-    for (int e = 0; e < PL; ++e) o[e] = fmaf(wt, a.part_o[(it * a.HK + r) * D + lane * PL + e], o[e]);
-  }
-  if (lane == 0) {
-    sm[w] = M;
-    sl[w] = L;
-  }
-#pragma unroll
-  for (int e = 0; e < PL; ++e) so[w][lane * PL + e] = o[e];
   __syncthreads();
-  if (w != 0) return;
-  const float Mt = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
-  float Lt = 0.f, ot[PL];
+  const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
+  T* obase = static_cast<T*>(a.o) + (int64_t(b) * a.Hq + kvh * a.HK) * D;
+  // pieces are read in batches of kBatch with all loads in flight; the
+  // running maximum is raised once per batch
+  constexpr int kBatch = 16;
+  for (int e0 = 2 * threadIdx.x; e0 < a.HK * D; e0 += 512) {
+    const int r = e0 / D;
+    float M = kNegInf, Ls = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int k0 = 0; k0 < np; k0 += kBatch) {
+      float lk[kBatch];
+      float2 v[kBatch];
 #pragma unroll
-  for (int e = 0; e < PL; ++e) ot[e] = 0.f;
+      for (int j = 0; j < kBatch; ++j) {
+        const int sl = k0 + j < np ? slots[k0 + j] : -1;
+        lk[j] = kNegInf;
+        v[j] = make_float2(0.f, 0.f);
+        if (sl >= 0) {
+          lk[j] = a.part_lse[int64_t(sl) * a.HK + r];
+          v[j] = *reinterpret_cast<const float2*>(a.part_o + int64_t(sl) * a.HK * D + e0);
+        }
+      }
+      float mb = M;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float f = sm[j] == kNegInf ? 0.f : fast_exp2(sm[j] - Mt);
-    Lt += f * sl[j];
+      for (int j = 0; j < kBatch; ++j) mb = fmaxf(mb, lk[j]);
+      if (mb == kNegInf) continue;
+      const float sc = M == kNegInf ? 0.f : fast_exp2(M - mb);
+      Ls *= sc;
+      o0 *= sc;
+      o1 *= sc;
 #pragma unroll
-    for (int e = 0; e < PL; ++e) ot[e] = fmaf(f, so[j][lane * PL + e], ot[e]);
+      for (int j = 0; j < kBatch; ++j) {
+        const float wt = lk[j] == kNegInf ? 0.f : fast_exp2(lk[j] - mb);
+        Ls += wt;
+        o0 = fmaf(wt, v[j].x, o0);
+        o1 = fmaf(wt, v[j].y, o1);
+      }
+      M = mb;
+    }
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    Elem<T>::store(obase + e0, o0 * inv);
+    Elem<T>::store(obase + e0 + 1, o1 * inv);
   }
-  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-  T* orow = static_cast<T*>(a.o) + (int64_t(b) * a.Hq + h) * D;
-#pragma unroll
-  for (int e = 0; e < PL; ++e) Elem<T>::store(orow + lane * PL + e, ot[e] * inv);
 }
 
 static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
@@ -280,19 +300,17 @@ static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 bool plan_decode(const DecodeShape& sh, DecodePlan* p) {
   p->HK = sh.Hq / sh.Hkv;
   p->HG = sh.Hq / sh.G;
-  p->chunk = kDecChunk;
-  const long long max_items = (long long)sh.B * sh.Hkv * ((sh.Lmax + kDecChunk - 1) / kDecChunk);
-  if (max_items > INT_MAX / 64) return false;
-  p->max_items = int(max_items);
-  p->grid = int(max_items < 1024 ? max_items : 1024);
-  const int nbk = sh.B * sh.Hkv;
+  const long long npairs = (long long)sh.B * sh.Hkv;
+  const long long tmax = npairs * ((sh.Lmax + kBN - 1) / kBN);  // T can not exceed this
+  if (tmax > INT_MAX / 4 || npairs > INT_MAX / 4) return false;
+  p->grid = int(tmax < kDecGrid ? tmax : kDecGrid);
   size_t off = 0;
-  p->off_sched = off;
-  off = align_up(off + (1 + 3 * size_t(nbk) + 2 * size_t(max_items)) * 4);
+  p->off_info = off;
+  off = align_up(off + (1 + 2 * size_t(npairs)) * 4);
   p->off_part_o = off;
-  off = align_up(off + size_t(max_items) * p->HK * sh.d * 4);
+  off = align_up(off + 2 * size_t(p->grid) * p->HK * sh.d * 4);
   p->off_part_lse = off;
-  off = align_up(off + size_t(max_items) * p->HK * 4);
+  off = align_up(off + 2 * size_t(p->grid) * p->HK * 4);
   p->bytes = off;
   return true;
 }
@@ -302,15 +320,12 @@ static hipError_t run_decode(const DecodeShape& sh, const DecodePlan& p, DecodeA
                              hipStream_t s, void* const* ev) {
   hipError_t e;
   if ((e = mark(ev, 0, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_schedule_kernel, dim3(1), dim3(kDecSchedThreads), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = mark(ev, 1, s)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_kernel<T, D>), dim3(p.grid), dim3(kDecThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = mark(ev, 2, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(sh.B * sh.Hq), dim3(256), 0, s, a);
+  if ((e = mark(ev, 1, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(sh.B * sh.Hkv), dim3(256), 0, s, a, p.grid);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return mark(ev, 3, s);
+  return mark(ev, 2, s);
 }
 
 hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void* q,
@@ -325,7 +340,7 @@ hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void*
   a.cache_len = cache_len;
   a.gate = gate;
   a.o = o;
-  a.sched = reinterpret_cast<int32_t*>(w + p.off_sched);
+  a.info = reinterpret_cast<int32_t*>(w + p.off_info);
   a.part_o = reinterpret_cast<float*>(w + p.off_part_o);
   a.part_lse = reinterpret_cast<float*>(w + p.off_part_lse);
   a.B = sh.B;
@@ -336,7 +351,6 @@ hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void*
   a.W = sh.W;
   a.HK = p.HK;
   a.HG = p.HG;
-  a.max_items = p.max_items;
   a.sl2 = sh.scale * kLog2e;
   if (sh.f32) {
     if (sh.d == 64) return run_decode<float, 64>(sh, p, a, s, ev);

@@ -51,10 +51,8 @@ struct DecodeShape {
 };
 struct DecodePlan {
   int HK, HG;
-  int chunk;      // keys per work item
-  int max_items;  // B * Hkv * ceil(Lmax / chunk)
-  int grid;       // persistent workgroups
-  size_t off_sched, off_part_o, off_part_lse, bytes;
+  int grid;       // workgroups of the split-K kernel (one share of the key blocks each)
+  size_t off_info, off_part_o, off_part_lse, bytes;
 };
 bool plan_decode(const DecodeShape& sh, DecodePlan* p);
 hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void* q,

@@ -191,6 +191,10 @@ DECODE_CASES = [
     (3, 513, 8, 1, 4, 128, 64, [513, 200, 64], "bf16"),   # gate groups inside a KV group
     (4, 300, 4, 4, 1, 64, 50, [300, 3, 51, 257], "bf16"),
     (2, 260, 2, 1, 1, 128, 40, [260, 17], "f32"),
+    # more blocks' worth of workgroups than blocks: some key-block shares are empty
+    (40, 200, 4, 2, 1, 128, 32, [int(x) for x in np.random.default_rng(11).integers(1, 61, 40)], "bf16"),
+    # 400 (sequence, KV head) pairs, ragged: pairs cut across several shares
+    (100, 2048, 8, 4, 2, 64, 300, [int(x) for x in np.random.default_rng(12).integers(1, 2049, 100)], "bf16"),
 ]
 
 
