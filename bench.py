@@ -18,13 +18,18 @@ Prints ONE JSON line.  `value` is the routed prefill's useful TFLOP/s
 (4*d per attended (query head, key) pair at the realized gate, timed from
 the router to the merge); decode tokens/s and GB/s are reported beside it.
 `roofline` covers the kernel with the largest share of the step's time,
-timed with HIP events recorded on its launch stream inside the library.
+timed with HIP events recorded on its launch stream inside the library;
+its `traffic` (HBM bytes per launch) comes from the committed rocprofv3
+counter summary under profiles/ and is null when the kernel sources have
+changed since those counters were taken.
 `cpu_baseline` times the float64 CPU reference on a bounded sample of the
 same workload.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import math
 import os
@@ -35,6 +40,13 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# rocprofv3 counter summary of this benchmark (FETCH_SIZE / WRITE_SIZE per
+# dispatch, scaled by the counts of a plain copy of known size)
+PROFILE = os.path.join(ROOT, "profiles", "kernels_prefill32k_decode64x32k.md")
+# bench kernel key -> kernel function name in the profile
+PROFILE_NAMES = {"band": "band_kernel", "far": "far_kernel", "decode_splitk": "decode_kernel"}
 
 
 def parse():
@@ -79,6 +91,36 @@ def decode_bytes(gate, cache_len, W, Hq, Hkv, d, elem=2):
             full = any(gate[b, (kv * HK + j) * G // Hq] for j in range(HK))
             keys += L if full else min(L, W)
     return keys * d * 2 * elem + B * Hq * d * 2 * elem, keys
+
+
+def kernel_source_hash():
+    """sha256 over the kernel sources, file by file in byte order of their paths."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "sliding_window_attention_router_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(path=PROFILE):
+    """HBM bytes per launch by kernel name, from the committed counter
+    summary; empty when the summary was taken on other kernel sources."""
+    if not os.path.exists(path):
+        return {}
+    text = open(path, encoding="utf-8").read()
+    m = [ln for ln in text.splitlines() if ln.startswith("kernel sources sha256:")]
+    if not m or m[0].split(":", 1)[1].strip().strip("`") != kernel_source_hash():
+        return {}
+    out = {}
+    section = text.split("## HBM traffic", 1)[-1].split("\n## ", 1)[0] if "## HBM traffic" in text else ""
+    for ln in section.splitlines():
+        cells = [c.strip().strip("`") for c in ln.strip().strip("|").split("|")]
+        if len(cells) >= 5 and cells[0] in PROFILE_NAMES.values():
+            try:
+                out[cells[0]] = float(cells[4])
+            except ValueError:
+                pass
+    return out
 
 
 # ------------------------------------------------------------------ main
@@ -197,13 +239,14 @@ def main():
         "decode_splitk": {"bound": "hbm", "work": dbytes, "unit": "GB/s", "peak": HBM_PEAK_GBS},
     }
     rooflines = {}
+    traffic = profiled_traffic()
     for name, k in kern.items():
         ms = t[name]
         scale = 1e12 if k["unit"] == "TFLOP/s" else 1e9
         ach = k["work"] / (ms * 1e-3) / scale
         rooflines[name] = {"bound": k["bound"], "achieved": round(ach, 2), "peak": k["peak"],
                            "unit": k["unit"], "frac": round(ach / k["peak"], 4), "ms": round(ms, 4),
-                           "traffic": None}
+                           "traffic": traffic.get(PROFILE_NAMES[name])}
     dominant = max(kern, key=lambda n: t[n])
 
     cpu = None
