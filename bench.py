@@ -46,7 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # dispatch, scaled by the counts of a plain copy of known size)
 PROFILE = os.path.join(ROOT, "profiles", "kernels_prefill32k_decode64x32k.md")
 # bench kernel key -> kernel function name in the profile
-PROFILE_NAMES = {"band": "band_kernel", "far": "far_kernel", "decode_splitk": "decode_kernel"}
+PROFILE_NAMES = {"attn": "attn_kernel", "decode_splitk": "decode_kernel"}
 
 
 def parse():
@@ -178,16 +178,16 @@ def main():
         return evs
 
     def step(ev=None):
-        # ev: 10 events: [route start] + prefill stages 0..4 + decode stages 0..2 + [end]
+        # ev: 9 events: [route start] + prefill stages 0..3 + decode stages 0..2 + [end]
         if ev is not None:
             ev[0].record()
         swa.route(H, r, bias, out=(gate, idx, cnt))
         swa.prefill(Q, K, V, gate, W, idx=idx, cnt=cnt, out=O, workspace=ws_p,
-                    events=ev[1:6] if ev is not None else None)
+                    events=ev[1:5] if ev is not None else None)
         swa.decode(q_d, Kc, Vc, len_d, gate_d, W, out=o_d, workspace=ws_d,
-                   events=ev[6:9] if ev is not None else None)
+                   events=ev[5:8] if ev is not None else None)
         if ev is not None:
-            ev[9].record()
+            ev[8].record()
 
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -200,7 +200,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evsets = [new_events(10) for _ in range(args.steps)]
+    evsets = [new_events(9) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
@@ -214,15 +214,14 @@ def main():
 
     t = {
         "route_compact": avg(0, 1),
-        "band": avg(1, 2),
-        "far_schedule": avg(2, 3),
-        "far": avg(3, 4),
-        "merge": avg(4, 5),
-        "decode_splitk": avg(6, 7),
-        "decode_merge": avg(7, 8),
+        "far_schedule": avg(1, 2),
+        "attn": avg(2, 3),
+        "merge": avg(3, 4),
+        "decode_splitk": avg(5, 6),
+        "decode_merge": avg(6, 7),
     }
-    prefill_ms = avg(0, 5)
-    decode_ms = avg(6, 8)
+    prefill_ms = avg(0, 4)
+    decode_ms = avg(5, 7)
     step_ms = wall * 1e3 / args.steps
 
     g_host = gate.cpu().numpy()
@@ -234,8 +233,7 @@ def main():
     decode_tok_s = B_dec / (decode_ms * 1e-3)
 
     kern = {
-        "band": {"bound": "mfma", "work": band_pairs * fl, "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS},
-        "far": {"bound": "mfma", "work": far_pairs * fl, "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS},
+        "attn": {"bound": "mfma", "work": useful * fl, "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS},
         "decode_splitk": {"bound": "hbm", "work": dbytes, "unit": "GB/s", "peak": HBM_PEAK_GBS},
     }
     rooflines = {}

@@ -148,8 +148,10 @@ size_t swiattn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int G, in
  *   gate   [B,G]           uint8  hard gate of the new token
  *   o      [B,Hq,d]        dtype  out
  *   The full branch reads keys [0, L-1], the window branch the last
- *   min(W, L) keys.  Work is split over key chunks on the device from the
- *   gate and L (no host synchronisation) and merged by log-sum-exp.
+ *   min(W, L) keys.  Work is split into equal shares of 64-key blocks on
+ *   the device from the gate and L (no host synchronisation); pieces of a
+ *   (sequence, KV head) range cut by share boundaries are merged by
+ *   log-sum-exp.
  * Errors: as swiattn_prefill.
  */
 int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t* cache_len,
@@ -162,9 +164,9 @@ int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t*
  * hipEvent_t handles created by the caller (stored as void*; NULL entries
  * are skipped).  The _ex calls behave exactly like the plain ones and in
  * addition record ev[i] on `stream` at stage boundary i:
- *   prefill, hard-gate mode: 0 before the window kernel, 1 after it,
- *     2 after the far-part schedule, 3 after the far kernel, 4 after the
- *     merge;
+ *   prefill, hard-gate mode: 0 before the far-part schedule, 1 after it,
+ *     2 after the attention kernel (window tiles and far chunks), 3 after
+ *     the merge;
  *   prefill, both-branch mode: 0 before the fused kernel, 1 after it,
  *     2 after the per-token head sum;
  *   decode: 0 before the split-K kernel, 1 after it, 2 after the merge.

@@ -6,13 +6,17 @@
 // query i is [i-W+1, i] (weimeta SWA glossary, section "详细解释"), the full
 // branch is causal [0, i].
 //
-// Hard-gate mode (window kernel, on-device schedule, far kernel, merge):
-//   band_kernel   window branch for every row; writes O and the window
-//                 log-sum-exp (log2 units)
-//   far_kernel    for the gathered gate=1 rows only: the far keys [0, i-W]
-//                 (the full set minus the window), split into key chunks
-//   merge_kernel  log-sum-exp merge of window output + far chunks = O_FULL
-//                 for the gathered rows, written over their window output
+// Hard-gate mode (on-device schedule, one attention launch, merge):
+//   far_schedule_kernel  cuts the far keys of the gathered gate=1 rows into
+//                        work items
+//   attn_kernel          far items first: for the gathered rows only, the
+//                        far keys [0, i-W] (the full set minus the window)
+//                        of one key chunk, written as normalised partials;
+//                        then window tiles: the window branch for every
+//                        row, written to O with its log-sum-exp (log2)
+//   merge_kernel         log-sum-exp merge of window output + far chunks =
+//                        O_FULL for the gathered rows, written over their
+//                        window output
 // The window and far key sets are disjoint and cover [0, i], so the merge is
 // the exact full softmax up to rounding.
 //
@@ -50,6 +54,7 @@ struct PrefillArgs {
   float* diff;      // [B,N]
   int B, N, Hq, Hkv, G, W;
   int HK, HG, hpu, units, tpt_band, tpt_far, band_tiles, far_tiles, max_items;
+  int far_grid;  // workgroups of attn_kernel reserved for far items (multiple of 8)
   int cmax;   // width of the per-unit chunk tables
   float sl2;  // softmax scale * log2(e)
 };
@@ -162,15 +167,10 @@ SWI_DEV void block_loop(Core& c, char* lds, const T* Kb, const T* Vb, int64_t rs
 // tokens x the HK query heads of one KV head (128 rows).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__((TileCfg<T, D>::kWaves * 64), (TileCfg<T, D>::kMinWG)) void band_kernel(PrefillArgs a) {
+SWI_DEV void band_tile(const PrefillArgs& a, char* lds, int lin) {
   using Core = typename TileCfg<T, D>::Core;
   constexpr int NT = TileCfg<T, D>::kWaves * 64;
   constexpr int TPW = Core::TPW;
-  __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
-  // consecutive tiles of one KV head share most of their window: keep them
-  // on one XCD's L2
-  const int lin = xcd_slice(blockIdx.x, a.band_tiles * a.B * a.Hkv);
-  if (lin < 0) return;
   const int tile = lin % a.band_tiles;
   const int bk = lin / a.band_tiles;
   const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
@@ -344,15 +344,10 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
 // chunks of longer tiles write normalised partials for merge_kernel.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__((TileCfg<T, D>::kWaves * 64), (TileCfg<T, D>::kMinWG)) void far_kernel(PrefillArgs a) {
+SWI_DEV void far_item(const PrefillArgs& a, char* lds, int item) {
   using Core = typename TileCfg<T, D>::Core;
   constexpr int NT = TileCfg<T, D>::kWaves * 64;
   constexpr int TPW = Core::TPW;
-  __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
-  // items are ordered by (unit, chunk, tile); an XCD takes a contiguous
-  // slice, so its resident workgroups read the same keys of one KV head
-  const int item = xcd_slice(blockIdx.x, a.sched[0]);
-  if (item < 0) return;
   SchedView sv(a);
   const int cb = a.sched[1];
   const int T_ = sv.item_tile[item], ch = sv.item_chunk[item];
@@ -393,39 +388,42 @@ __global__ __launch_bounds__((TileCfg<T, D>::kWaves * 64), (TileCfg<T, D>::kMinW
   const int64_t rs = int64_t(a.Hkv) * D;
   block_loop<Core, T, D, NT>(c, lds, Kb, Vb, rs, c0, (c1 - c0 + kBN - 1) / kBN, c1, tb, lo, hi,
                              a.sl2, tid, q, g);
-  const bool split = sv.n_items[T_] > 1;
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     float lse2;
     const float inv = finish_row(c.m_of(t), c.l_of(t), lse2);
     if (!valid[t]) continue;
-    auto& acc = c.acc_of(t);
-    if (split) {  // the merge kernel combines the tile's chunks
-      float* prow = a.part_o + (int64_t(item) * kRows + r[t]) * D;
-      store_row<Core::MD>(prow, acc, inv, g);
-      if (g == 0) a.part_lse[int64_t(item) * kRows + r[t]] = lse2;
-      continue;
-    }
-    // single-chunk tile: merge with the window result right here
-    if (tok[t] < a.W) continue;
-    const float ls = a.lse_s[(int64_t(b) * a.Hq + h[t]) * a.N + tok[t]];
-    const float M = fmaxf(ls, lse2);
-    const float ws = fast_exp2(ls - M), wf = fast_exp2(lse2 - M);
-    T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok[t]) * a.Hq + h[t]) * D;
-    const float sf = inv * wf;
-#pragma unroll
-    for (int md = 0; md < Core::MD; ++md)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        acc[md][i] = fmaf(acc[md][i], sf, ws * Elem<T>::load(orow + acc_channel(md, i, g)));
-    store_row<Core::MD>(orow, acc, 1.f / (ws + wf), g);
+    float* prow = a.part_o + (int64_t(item) * kRows + r[t]) * D;
+    store_row<Core::MD>(prow, c.acc_of(t), inv, g);
+    if (g == 0) a.part_lse[int64_t(item) * kRows + r[t]] = lse2;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Merge of multi-chunk far tiles: one workgroup per tile, lanes laid out as
-// in far_kernel (lane pair per row, 64 channels per lane).  O_FULL of a row
-// is the log-sum-exp weighted sum of its window output and its chunks'
+// Window tiles and far items in one launch.  Workgroups [0, far_grid) take
+// far items (an XCD takes a contiguous slice of the (unit, chunk, tile)
+// order, so its resident workgroups read the same keys of one KV head);
+// the rest take window tiles (consecutive tiles of one KV head share most
+// of their window, so they too stay on one XCD's L2).  Workgroups start in
+// index order, so the long far items start first and the shorter window
+// tiles fill the tail of the launch.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__((TileCfg<T, D>::kWaves * 64), (TileCfg<T, D>::kMinWG)) void attn_kernel(PrefillArgs a) {
+  __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
+  if (int(blockIdx.x) < a.far_grid) {
+    const int item = xcd_slice(blockIdx.x, a.sched[0]);
+    if (item >= 0) far_item<T, D>(a, lds, item);
+    return;
+  }
+  const int lin = xcd_slice(blockIdx.x - a.far_grid, a.band_tiles * a.B * a.Hkv);
+  if (lin >= 0) band_tile<T, D>(a, lds, lin);
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the far tiles: one workgroup per tile, lanes laid out as in the
+// far items (lane pair per row, 64 channels per lane).  O_FULL of a row is
+// the log-sum-exp weighted sum of its window output and its chunks'
 // partials, taken in chunk order.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
@@ -434,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(PrefillArgs a) {
   SchedView sv(a);
   const int T_ = blockIdx.x;
   const int ni = sv.n_items[T_];
-  if (ni < 2) return;
+  if (ni < 1) return;
   const int per_b = a.units * a.far_tiles;
   const int b = T_ / per_b, rem = T_ - b * per_b;
   const int u = rem / a.far_tiles, t = rem - u * a.far_tiles;
@@ -638,21 +636,19 @@ static hipError_t run_prefill(const PrefillShape& sh, const PrefillPlan& p, Pref
   if ((e = (x)) != hipSuccess) return e;
   if (!sh.both_branch) {
     SWI_TRY(mark(ev, 0, s));
-    constexpr int nt = TileCfg<T, D>::kWaves * 64;
-    const int band_total = p.band_tiles * sh.B * sh.Hkv;
-    hipLaunchKernelGGL((band_kernel<T, D>), dim3(8 * ((band_total + 7) / 8)), dim3(nt), 0, s, a);
-    SWI_TRY(hipGetLastError());
-    SWI_TRY(mark(ev, 1, s));
     hipLaunchKernelGGL(far_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, a);
     SWI_TRY(hipGetLastError());
-    SWI_TRY(mark(ev, 2, s));
-    hipLaunchKernelGGL((far_kernel<T, D>), dim3(8 * ((p.max_items + 7) / 8)), dim3(nt), 0, s, a);
+    SWI_TRY(mark(ev, 1, s));
+    constexpr int nt = TileCfg<T, D>::kWaves * 64;
+    const int band_total = p.band_tiles * sh.B * sh.Hkv;
+    hipLaunchKernelGGL((attn_kernel<T, D>), dim3(a.far_grid + 8 * ((band_total + 7) / 8)), dim3(nt), 0,
+                       s, a);
     SWI_TRY(hipGetLastError());
-    SWI_TRY(mark(ev, 3, s));
+    SWI_TRY(mark(ev, 2, s));
     hipLaunchKernelGGL((merge_kernel<T, D>), dim3(sh.B * p.units * p.far_tiles), dim3(kThreads), 0,
                        s, a);
     SWI_TRY(hipGetLastError());
-    SWI_TRY(mark(ev, 4, s));
+    SWI_TRY(mark(ev, 3, s));
   } else {
     SWI_TRY(mark(ev, 0, s));
     hipLaunchKernelGGL((fused_kernel<T, D>), dim3(p.band_tiles, sh.B * sh.Hkv), dim3(kThreads),
@@ -702,6 +698,7 @@ hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const vo
   a.band_tiles = p.band_tiles;
   a.far_tiles = p.far_tiles;
   a.max_items = p.max_items;
+  a.far_grid = 8 * ((p.max_items + 7) / 8);
   a.cmax = p.cmax;
   a.sl2 = sh.scale * kLog2e;
   if (sh.f32) {

@@ -36,11 +36,11 @@ def test_decode_bytes_closed_form():
 def test_profiled_traffic_is_tied_to_the_kernel_sources(tmp_path):
     """Counter figures are reported only for the sources they were taken on."""
     table = ("## HBM traffic\n\n| kernel | dispatches | FETCH KiB | WRITE KiB | HBM bytes/launch | work |\n"
-             "|---|---|---|---|---|---|\n| `far_kernel` | 4 | 1.0 | 2.0 | 12345 | x |\n\n"
-             "## MFMA use\n\n| `far_kernel` | 1 | 2 | 3 | 999 | 5 |\n")
+             "|---|---|---|---|---|---|\n| `attn_kernel` | 4 | 1.0 | 2.0 | 12345 | x |\n\n"
+             "## MFMA use\n\n| `attn_kernel` | 1 | 2 | 3 | 999 | 5 |\n")
     good = tmp_path / "good.md"
     good.write_text(f"kernel sources sha256: `{bench.kernel_source_hash()}`\n\n" + table)
-    assert bench.profiled_traffic(str(good)) == {"far_kernel": 12345.0}
+    assert bench.profiled_traffic(str(good)) == {"attn_kernel": 12345.0}
     stale = tmp_path / "stale.md"
     stale.write_text("kernel sources sha256: `" + "0" * 64 + "`\n\n" + table)
     assert bench.profiled_traffic(str(stale)) == {}
