@@ -92,25 +92,55 @@ struct KVLoader<bf16_t, D, NT, kStream> {
   // one 256-byte row.  V piece u: key quarter u % 16 (4 keys), channels
   // 8*(u / 16): the 16 lanes that write one V^T row together cover all its
   // banks.
+  //
+  // Addressing: the block's first row is wave-uniform (scalar base), each
+  // piece adds a fixed per-lane 32-bit byte offset.  Only a block that
+  // reaches past kend (wave-uniform test) pays for the clamp.  The streaming
+  // (decode) loader keeps the per-row form, which measured faster there.
   SWI_DEV void load(const bf16_t* __restrict__ Kb, const bf16_t* __restrict__ Vb, int64_t rs,
                     int kb, int kend, int tid) {
+    const char* kp = reinterpret_cast<const char*>(Kb + int64_t(kb) * rs);
+    const char* vp = reinterpret_cast<const char*>(Vb + int64_t(kb) * rs);
+    const uint32_t rb = uint32_t(rs) * 2u;  // bytes per row
+    const int last = kend - 1 - kb;         // last readable row of the block
+    if (!kStream && kb + kBN <= kend) {
+      // piece j of lane tid: row tid/CPR + j*NT/CPR, column tid%CPR (K);
+      // rows 4*(tid%16) + r, columns tid/16 + j*NT/16 (V).  The j and r
+      // parts are uniform and go into the scalar base.
+      static_assert(NT % CPR == 0 && NT % 16 == 0, "lane layout");
+      const uint32_t k_lane = uint32_t(tid / CPR) * rb + uint32_t(tid % CPR) * 16u;
+      const uint32_t v_lane = uint32_t(4 * (tid & 15)) * rb + uint32_t(tid >> 4) * 16u;
 #pragma unroll
-    for (int j = 0; j < KPER; ++j) {
-      const int u = tid + NT * j;
-      const int key = u / CPR, c = u - key * CPR;
-      if (KU % NT != 0 && u >= KU) continue;
-      const int kk = clamp_row(kb + key, kend);
-      kr[j] = load16<kStream>(Kb + kk * rs + c * 8);
-    }
+      for (int j = 0; j < KPER; ++j) {
+        if (KU % NT != 0 && tid + NT * j >= KU) continue;
+        kr[j] = load16<kStream>(kp + size_t(j * (NT / CPR)) * rb + k_lane);
+      }
 #pragma unroll
-    for (int j = 0; j < VPER; ++j) {
-      const int u = tid + NT * j;
-      const int kq = u & 15, c = u >> 4;
+      for (int j = 0; j < VPER; ++j) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (VU % NT != 0 && u >= VU) continue;
-        const int kk = clamp_row(kb + 4 * kq + r, kend);
-        vr[j][r] = load16<kStream>(Vb + kk * rs + c * 8);
+        for (int r = 0; r < 4; ++r) {
+          if (VU % NT != 0 && tid + NT * j >= VU) continue;
+          vr[j][r] = load16<kStream>(vp + (size_t(r) * rb + size_t(j * (NT / 16)) * 16u) + v_lane);
+        }
+      }    } else {
+#pragma unroll
+      for (int j = 0; j < KPER; ++j) {
+        const int u = tid + NT * j;
+        const int key = u / CPR, c = u - key * CPR;
+        if (KU % NT != 0 && u >= KU) continue;
+        const int kk = min(key, last);
+        kr[j] = load16<kStream>(kp + (int64_t(kk) * rb + c * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < VPER; ++j) {
+        const int u = tid + NT * j;
+        const int kq = u & 15, c = u >> 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (VU % NT != 0 && u >= VU) continue;
+          const int kk = min(4 * kq + r, last);
+          vr[j][r] = load16<kStream>(vp + (int64_t(kk) * rb + c * 16));
+        }
       }
     }
   }
@@ -215,7 +245,7 @@ SWI_DEV void online_softmax(f32x16 (&s)[2], f32x16 (&acc)[MD], float& m, float& 
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mt][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * sl2;
+  mx = fmaxf(mx, xor32(mx)) * sl2;
   // raise m when the block maximum exceeds it by more than kRescale (and on
   // the first block that has any key); wave-uniform skip otherwise
   const bool raise = mx > m + kRescale;
@@ -406,7 +436,7 @@ struct TileCfg<float, D> {
 // Total row sum over the lane pair, the log2-domain normaliser, and 1/sum
 // (0 for a row that saw no key).
 SWI_DEV float finish_row(float m, float l, float& lse2) {
-  const float lt = l + __shfl_xor(l, 32, kWave);
+  const float lt = l + xor32(l);
   lse2 = lt > 0.f ? m + fast_log2(lt) : kNegInf;
   return lt > 0.f ? 1.f / lt : 0.f;
 }

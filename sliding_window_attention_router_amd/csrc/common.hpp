@@ -25,6 +25,16 @@ using bf16_t = __bf16;
 SWI_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 SWI_DEV float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Value of lane l ^ 32 (the other half of the wave), through the gfx950
+// v_permlane32_swap (a VALU op, no LDS round trip): swapping the upper half
+// of one copy with the lower half of another leaves lane l's partner value
+// in the second result for l < 32 and in the first for l >= 32.
+SWI_DEV float xor32(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
+}
+
 SWI_DEV float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

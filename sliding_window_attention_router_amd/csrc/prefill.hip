@@ -34,7 +34,7 @@ namespace swi {
 
 constexpr int kThreads = 256;      // merge / fused kernels: 4 waves x 32 rows
 constexpr int kRows = 128;          // query rows of every tile
-constexpr int kTargetItems = 2048;  // far work items aimed for per launch
+constexpr int kTargetItems = 1024;  // far work items aimed for per launch
 constexpr int kMinChunkBlocks = 8;  // far chunk is at least 8 x 64 keys
 constexpr int kSchedThreads = 1024;
 
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(PrefillArgs a) {
 #pragma unroll
   for (int md = 0; md < MD; ++md) full[md] = c.acc[md] * inv;
   float dd = sq_distance<MD>(full, snap);
-  dd += __shfl_xor(dd, 32, kWave);
+  dd += xor32(dd);
   if (valid) {
     const int gg = h / a.HG;
     const bool full_sel = a.gate[(int64_t(b) * a.N + tok) * a.G + gg] != 0;
