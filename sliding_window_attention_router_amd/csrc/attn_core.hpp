@@ -336,6 +336,139 @@ struct CoreBF16 {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Direct (DMA) staging for bf16: gfx950's global_load_lds_dwordx4 copies 16
+// bytes per lane from global memory straight into LDS (lane i of a wave
+// writes bytes [16i, 16i+16) after the wave-uniform destination), so a K/V
+// block needs no registers and no LDS store instructions.  Each 1 KB copy
+// covers 1024 / (2D) whole rows; the lane -> source mapping is free, which
+// is used to XOR-swizzle the 16-byte chunks of every row:
+//   K: chunk c of key row k is stored at chunk position c ^ (k & 7), so the
+//      8 rows read by 8 consecutive lanes (same chunk) hit distinct banks;
+//   V: chunk c of key row k is stored at c ^ ((k & 3) << 1), so the four
+//      rows of one transposing read (below) hit distinct banks.
+// V^T operands come from ds_read_b64_tr_b16: within each group of 16
+// lanes, source lane 4r + k supplies four 16-bit values and destination
+// lane 4k + e receives value e of source lanes k, 4 + k, 8 + k, 12 + k (as
+// its elements 0..3).  Pointing source lane 4r + k at channels
+// [c0 + 4k, c0 + 4k + 4) of key row r therefore gives lane i the channel
+// c0 + i for four consecutive keys: one half of an MFMA A operand.
+// ---------------------------------------------------------------------------
+#define SWI_GLOBAL(p) ((__attribute__((address_space(1))) void*)(p))
+#define SWI_LOCAL(p) ((__attribute__((address_space(3))) void*)(p))
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct LdsDma {
+  static constexpr int kRowB = 2 * D;  // bytes per key row
+  static constexpr int kKBytes = kBN * kRowB;
+  static constexpr int kBytes = 2 * kKBytes;  // K block, then V block
+  SWI_DEV static constexpr int k_pos(int key, int chunk) {
+    return key * kRowB + ((chunk ^ (key & 7)) << 4);
+  }
+  SWI_DEV static constexpr int v_pos(int key, int chunk) {
+    return kKBytes + key * kRowB + ((chunk ^ ((key & 3) << 1)) << 4);
+  }
+};
+
+template <int D, int NT>
+struct KVDma {
+  using L = LdsDma<D>;
+  static constexpr int kCopies = L::kKBytes / 1024;  // 1 KB copies per matrix
+  static constexpr int kPer = kCopies / (NT / 64);   // per wave
+  static_assert(kCopies % (NT / 64) == 0, "copies per wave");
+  // Copy rows kb .. kb+63 (rows at or past kend read row kend-1) into buf.
+  SWI_DEV static void issue(char* buf, const bf16_t* Kb, const bf16_t* Vb, int64_t rs, int kb,
+                            int kend, int tid) {
+    const int wave = tid >> 6, lane = tid & 63;
+    const char* kp = reinterpret_cast<const char*>(Kb + int64_t(kb) * rs);
+    const char* vp = reinterpret_cast<const char*>(Vb + int64_t(kb) * rs);
+    const uint32_t rb = uint32_t(rs) * 2u;
+    const int last = kend - 1 - kb;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int m = wave * kPer + i;
+      const int byte = m * 1024 + lane * 16;
+      const int row = byte / L::kRowB, p = (byte % L::kRowB) >> 4;
+      const uint32_t src = uint32_t(min(row, last)) * rb;
+      __builtin_amdgcn_global_load_lds(SWI_GLOBAL(kp + src + uint32_t((p ^ (row & 7)) << 4)),
+                                       SWI_LOCAL(buf + m * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(SWI_GLOBAL(vp + src + uint32_t((p ^ ((row & 3) << 1)) << 4)),
+                                       SWI_LOCAL(buf + L::kKBytes + m * 1024), 16, 0, 0);
+    }
+  }
+};
+
+// bf16 core reading the DMA layout (same arithmetic as CoreBF16).
+template <int D>
+struct CoreBF16Dma {
+  using T = bf16_t;
+  using L = LdsDma<D>;
+  static constexpr int KS = D / 16;
+  static constexpr int MD = D / 32;
+  bf16x8 qreg[KS];
+  f32x16 acc[MD];
+  float m, l;
+
+  SWI_DEV void init() {
+    m = kNegInf;
+    l = 0.f;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) acc[md] = f32x16{};
+  }
+  SWI_DEV void load_q(const bf16_t* qrow, int g) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qreg[ks] = qrow ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + g * 8) : bf16x8{};
+  }
+  SWI_DEV void block(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
+                     int g) {
+    f32x16 s[2];
+    __builtin_amdgcn_s_setprio(SWI_MFMA_PRIO);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      s[mt] = f32x16{};
+      bf16x8 a[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        a[ks] = *reinterpret_cast<const bf16x8*>(lds + L::k_pos(mt * 32 + q, ks * 2 + g));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qreg[ks], s[mt], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    online_softmax<MD>(s, acc, m, l, kb, masked, lo, hi, sl2, g);
+    bf16x8 pb[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[st][e] = bf16_t(s[st >> 1][(st & 1) * 8 + e]);
+    // k-step st, lane group g holds keys 16st + 4g + {0..3} (slots 0..3) and
+    // 16st + 8 + 4g + {0..3} (slots 4..7) of P^T; fetch V^T to match
+    const int lane = threadIdx.x & 63;
+    const int r = (lane >> 2) & 3, k = lane & 3, hh = (lane >> 4) & 1;
+    __builtin_amdgcn_s_setprio(SWI_MFMA_PRIO);
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const int chunk = md * 4 + 2 * hh + (k >> 1);
+      const char* vp = lds + L::v_pos(4 * g + r, chunk) + (k & 1) * 8;
+      bf16x8 a[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vp + 16 * st * L::kRowB));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vp + (16 * st + 8) * L::kRowB));
+        a[st] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st], pb[st], acc[md], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  }
+};
+
 // Array interface over a one-tile core (TPW = 1): the window and far kernels
 // are written for TPW row tiles per wave.
 template <typename C>
@@ -422,13 +555,15 @@ template <typename T, int D>
 struct TileCfg;
 template <int D>
 struct TileCfg<bf16_t, D> {
-  using Core = OneTile<CoreBF16<D>>;
+  using Core = OneTile<CoreBF16Dma<D>>;
+  static constexpr bool kDma = true;
   static constexpr int kWaves = 4;
   static constexpr int kMinWG = 2;  // two workgroups per CU: 256 registers per wave
 };
 template <int D>
 struct TileCfg<float, D> {
   using Core = OneTile<CoreF32<D>>;
+  static constexpr bool kDma = false;
   static constexpr int kWaves = 4;
   static constexpr int kMinWG = 1;
 };

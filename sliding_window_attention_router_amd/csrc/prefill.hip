@@ -141,7 +141,7 @@ struct TileBounds {
 // the global loads of the next two blocks in flight (two register stages,
 // used alternately) while a block is computed.
 template <typename Core, typename T, int D, int NT, int TPW>
-SWI_DEV void block_loop(Core& c, char* lds, const T* Kb, const T* Vb, int64_t rs, int kb0, int nb,
+SWI_DEV void block_loop_regs(Core& c, char* lds, const T* Kb, const T* Vb, int64_t rs, int kb0, int nb,
                         int kend, const TileBounds<TPW>& tb, const int (&lo)[TPW],
                         const int (&hi)[TPW], float sl2, int tid, int q, int g) {
   KVLoader<T, D, NT> ld[2];
@@ -162,12 +162,58 @@ SWI_DEV void block_loop(Core& c, char* lds, const T* Kb, const T* Vb, int64_t rs
   }
 }
 
+// The same with DMA staging (bf16): block m is copied into buffer m%2 while
+// block m-1 is computed from the other one.  The barrier at the top of each
+// step waits for this wave's copies of block m (the compiler's fence waits
+// for them) and for every wave to be done with block m-1, whose buffer the
+// next copy then overwrites.
+template <typename Core, int D, int NT, int TPW>
+SWI_DEV void block_loop_dma(Core& c, char* buf0, char* buf1, const bf16_t* Kb, const bf16_t* Vb,
+                            int64_t rs, int kb0, int nb, int kend, const TileBounds<TPW>& tb,
+                            const int (&lo)[TPW], const int (&hi)[TPW], float sl2, int tid, int q,
+                            int g) {
+  using Dma = KVDma<D, NT>;
+  Dma::issue(buf0, Kb, Vb, rs, kb0, kend, tid);
+  for (int n = 0; n < nb; n += 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = n + j;
+      if (m >= nb) break;
+      char* cur = j == 0 ? buf0 : buf1;
+      char* nxt = j == 0 ? buf1 : buf0;
+      __syncthreads();
+      if (m + 1 < nb) Dma::issue(nxt, Kb, Vb, rs, kb0 + (m + 1) * kBN, kend, tid);
+      const int kb = kb0 + m * kBN;
+      if (tb.needed(kb)) c.block(cur, kb, tb.masked(kb), lo, hi, sl2, q, g);
+    }
+  }
+}
+
+template <typename Core, typename T, int D, int NT, int TPW>
+SWI_DEV void block_loop(Core& c, char* buf0, char* buf1, const T* Kb, const T* Vb, int64_t rs,
+                        int kb0, int nb, int kend, const TileBounds<TPW>& tb, const int (&lo)[TPW],
+                        const int (&hi)[TPW], float sl2, int tid, int q, int g) {
+  if constexpr (TileCfg<T, D>::kDma)
+    block_loop_dma<Core, D, NT>(c, buf0, buf1, Kb, Vb, rs, kb0, nb, kend, tb, lo, hi, sl2, tid, q, g);
+  else
+    block_loop_regs<Core, T, D, NT>(c, buf0, Kb, Vb, rs, kb0, nb, kend, tb, lo, hi, sl2, tid, q, g);
+}
+
+// LDS of the window / far work: two DMA buffers (bf16) or one staging
+// buffer (float32)
+template <typename T, int D>
+struct TileLds {
+  static constexpr bool kDma = TileCfg<T, D>::kDma;
+  static constexpr int kBuf0 = kDma ? LdsDma<D>::kBytes : Lds<T, D>::kBytes;
+  static constexpr int kBuf1 = kDma ? LdsDma<D>::kBytes : 16;
+};
+
 // ---------------------------------------------------------------------------
 // Window branch over every row.  Rows of a tile are tpt_band consecutive
 // tokens x the HK query heads of one KV head (128 rows).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-SWI_DEV void band_tile(const PrefillArgs& a, char* lds, int lin) {
+SWI_DEV void band_tile(const PrefillArgs& a, char* buf0, char* buf1, int lin) {
   using Core = typename TileCfg<T, D>::Core;
   constexpr int NT = TileCfg<T, D>::kWaves * 64;
   constexpr int TPW = Core::TPW;
@@ -201,7 +247,7 @@ SWI_DEV void band_tile(const PrefillArgs& a, char* lds, int lin) {
   const T* Vb = static_cast<const T*>(a.V) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
   const int64_t rs = int64_t(a.Hkv) * D;
   const int kb0 = (max(0, q0 - a.W + 1) / kBN) * kBN;
-  block_loop<Core, T, D, NT>(c, lds, Kb, Vb, rs, kb0, (qlast - kb0) / kBN + 1, a.N, tb, lo, hi,
+  block_loop<Core, T, D, NT>(c, buf0, buf1, Kb, Vb, rs, kb0, (qlast - kb0) / kBN + 1, a.N, tb, lo, hi,
                              a.sl2, tid, q, g);
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
@@ -344,7 +390,7 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
 // chunks of longer tiles write normalised partials for merge_kernel.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-SWI_DEV void far_item(const PrefillArgs& a, char* lds, int item) {
+SWI_DEV void far_item(const PrefillArgs& a, char* buf0, char* buf1, int item) {
   using Core = typename TileCfg<T, D>::Core;
   constexpr int NT = TileCfg<T, D>::kWaves * 64;
   constexpr int TPW = Core::TPW;
@@ -386,7 +432,7 @@ SWI_DEV void far_item(const PrefillArgs& a, char* lds, int item) {
   const T* Kb = static_cast<const T*>(a.K) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
   const T* Vb = static_cast<const T*>(a.V) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
   const int64_t rs = int64_t(a.Hkv) * D;
-  block_loop<Core, T, D, NT>(c, lds, Kb, Vb, rs, c0, (c1 - c0 + kBN - 1) / kBN, c1, tb, lo, hi,
+  block_loop<Core, T, D, NT>(c, buf0, buf1, Kb, Vb, rs, c0, (c1 - c0 + kBN - 1) / kBN, c1, tb, lo, hi,
                              a.sl2, tid, q, g);
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
@@ -410,14 +456,15 @@ SWI_DEV void far_item(const PrefillArgs& a, char* lds, int item) {
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__((TileCfg<T, D>::kWaves * 64), (TileCfg<T, D>::kMinWG)) void attn_kernel(PrefillArgs a) {
-  __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
+  __shared__ __align__(16) char buf0[TileLds<T, D>::kBuf0];
+  __shared__ __align__(16) char buf1[TileLds<T, D>::kBuf1];
   if (int(blockIdx.x) < a.far_grid) {
     const int item = xcd_slice(blockIdx.x, a.sched[0]);
-    if (item >= 0) far_item<T, D>(a, lds, item);
+    if (item >= 0) far_item<T, D>(a, buf0, buf1, item);
     return;
   }
   const int lin = xcd_slice(blockIdx.x - a.far_grid, a.band_tiles * a.B * a.Hkv);
-  if (lin >= 0) band_tile<T, D>(a, lds, lin);
+  if (lin >= 0) band_tile<T, D>(a, buf0, buf1, lin);
 }
 
 // ---------------------------------------------------------------------------
