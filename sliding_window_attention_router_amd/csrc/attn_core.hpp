@@ -399,13 +399,45 @@ struct KVDma {
   }
 };
 
-// bf16 core reading the DMA layout (same arithmetic as CoreBF16).
+// LDS reads of the DMA layout are issued from inline assembly with explicit
+// waits.  The compiler cannot tell that the transposing reads touch only
+// the buffer that is not being filled, and would otherwise wait for the
+// copies of the next block before every read of the current one.  Byte
+// address = wave-invariant per-lane part (register) + compile-time offset.
+template <int OFF>
+SWI_DEV bf16x8 lds_read_b128(uint32_t addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+SWI_DEV s16x4 lds_read_tr16(uint32_t addr) {
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// Wait for every outstanding LDS read; tying the operands orders their uses
+// after the wait.
+template <typename V, int N>
+SWI_DEV void lds_wait(V (&v)[N]) {
+  static_assert(N == 8, "eight operands per group");
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                 "+v"(v[6]), "+v"(v[7]));
+}
+SWI_DEV uint32_t lds_addr(const char* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
+}
+
+// bf16 core reading the DMA layout (same arithmetic as CoreBF16).  Operand
+// reads run one group of eight ahead of the MFMAs that use them.
 template <int D>
 struct CoreBF16Dma {
   using T = bf16_t;
   using L = LdsDma<D>;
   static constexpr int KS = D / 16;
   static constexpr int MD = D / 32;
+  static_assert(KS == 8 || KS == 4, "head dim 64 or 128");
   bf16x8 qreg[KS];
   f32x16 acc[MD];
   float m, l;
@@ -421,20 +453,60 @@ struct CoreBF16Dma {
     for (int ks = 0; ks < KS; ++ks)
       qreg[ks] = qrow ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + g * 8) : bf16x8{};
   }
+
+  // K operands of key tile MT: 8 reads (KS = 8) or the KS reads of both tiles
+  template <int MT>
+  SWI_DEV static void read_k(const uint32_t (&ka)[KS], bf16x8 (&a)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int mt = KS == 8 ? MT : i / KS, ks = i % KS;
+      a[i] = [&]() {
+        if (mt == 0) return lds_read_b128<0>(ka[ks]);
+        return lds_read_b128<32 * L::kRowB>(ka[ks]);
+      }();
+    }
+  }
+  // V^T operands of output tile md: st = 0..3, two transposing reads each
+  template <int MDI>
+  SWI_DEV static void read_v(uint32_t va, s16x4 (&v)[8]) {
+    v[0] = lds_read_tr16<L::kKBytes + 0 * L::kRowB>(va);
+    v[1] = lds_read_tr16<L::kKBytes + 8 * L::kRowB>(va);
+    v[2] = lds_read_tr16<L::kKBytes + 16 * L::kRowB>(va);
+    v[3] = lds_read_tr16<L::kKBytes + 24 * L::kRowB>(va);
+    v[4] = lds_read_tr16<L::kKBytes + 32 * L::kRowB>(va);
+    v[5] = lds_read_tr16<L::kKBytes + 40 * L::kRowB>(va);
+    v[6] = lds_read_tr16<L::kKBytes + 48 * L::kRowB>(va);
+    v[7] = lds_read_tr16<L::kKBytes + 56 * L::kRowB>(va);
+  }
+
   SWI_DEV void block(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
                      int g) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t base = lds_addr(lds);
+    // per-lane parts of the addresses (key row q of a tile, chunk 2ks+g)
+    uint32_t ka[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = base + L::k_pos(q, ks * 2 + g);
     f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    bf16x8 a0[8], a1[8];
+    read_k<0>(ka, a0);
+    lds_wait(a0);
+    if (KS == 8) read_k<1>(ka, a1);
     __builtin_amdgcn_s_setprio(SWI_MFMA_PRIO);
+    if (KS == 8) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = f32x16{};
-      bf16x8 a[KS];
+      for (int ks = 0; ks < 8; ++ks)
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[ks], qreg[ks], s[0], 0, 0, 0);
+      lds_wait(a1);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        a[ks] = *reinterpret_cast<const bf16x8*>(lds + L::k_pos(mt * 32 + q, ks * 2 + g));
+      for (int ks = 0; ks < 8; ++ks)
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[ks], qreg[ks], s[1], 0, 0, 0);
+    } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qreg[ks], s[mt], 0, 0, 0);
+      for (int i = 0; i < 8; ++i)
+        s[i / KS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], qreg[i % KS], s[i / KS], 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(0);
     online_softmax<MD>(s, acc, m, l, kb, masked, lo, hi, sl2, g);
@@ -444,26 +516,29 @@ struct CoreBF16Dma {
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[st][e] = bf16_t(s[st >> 1][(st & 1) * 8 + e]);
     // k-step st, lane group g holds keys 16st + 4g + {0..3} (slots 0..3) and
-    // 16st + 8 + 4g + {0..3} (slots 4..7) of P^T; fetch V^T to match
-    const int lane = threadIdx.x & 63;
+    // 16st + 8 + 4g + {0..3} (slots 4..7) of P^T; the transposing reads
+    // fetch V^T to match (source lane 4r + k of each 16-lane group points at
+    // key row 4g + r, channels c0 + 4k .. c0 + 4k + 3)
     const int r = (lane >> 2) & 3, k = lane & 3, hh = (lane >> 4) & 1;
+    uint32_t va[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+      va[md] = base + (L::v_pos(4 * g + r, md * 4 + 2 * hh + (k >> 1)) - L::kKBytes) + (k & 1) * 8;
+    s16x4 v0[8], v1[8];
+    read_v<0>(va[0], v0);
     __builtin_amdgcn_s_setprio(SWI_MFMA_PRIO);
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
-      const int chunk = md * 4 + 2 * hh + (k >> 1);
-      const char* vp = lds + L::v_pos(4 * g + r, chunk) + (k & 1) * 8;
-      bf16x8 a[4];
+      s16x4(&cur)[8] = (md & 1) ? v1 : v0;
+      s16x4(&nxt)[8] = (md & 1) ? v0 : v1;
+      lds_wait(cur);
+      if (md + 1 < MD) read_v<0>(va[md + 1], nxt);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(vp + 16 * st * L::kRowB));
-        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(vp + (16 * st + 8) * L::kRowB));
-        a[st] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(cur[2 * st], cur[2 * st + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], acc[md], 0, 0, 0);
       }
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st], pb[st], acc[md], 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(0);
   }

@@ -162,11 +162,11 @@ SWI_DEV void block_loop_regs(Core& c, char* lds, const T* Kb, const T* Vb, int64
   }
 }
 
-// The same with DMA staging (bf16): block m is copied into buffer m%2 while
-// block m-1 is computed from the other one.  The barrier at the top of each
-// step waits for this wave's copies of block m (the compiler's fence waits
-// for them) and for every wave to be done with block m-1, whose buffer the
-// next copy then overwrites.
+// The same with DMA staging (bf16): block m+1 is copied into buffer (m+1)%2
+// while block m is computed from the other one.  The wait + barrier at the
+// top of each step makes block m's copies (from every wave) visible and
+// ensures every wave is done with block m-1, whose buffer the next copy
+// then overwrites.
 template <typename Core, int D, int NT, int TPW>
 SWI_DEV void block_loop_dma(Core& c, char* buf0, char* buf1, const bf16_t* Kb, const bf16_t* Vb,
                             int64_t rs, int kb0, int nb, int kend, const TileBounds<TPW>& tb,
@@ -181,6 +181,10 @@ SWI_DEV void block_loop_dma(Core& c, char* buf0, char* buf1, const bf16_t* Kb, c
       if (m >= nb) break;
       char* cur = j == 0 ? buf0 : buf1;
       char* nxt = j == 0 ? buf1 : buf0;
+      // this wave's copies of block m have landed (the core's LDS reads are
+      // invisible to the compiler's wait insertion, so wait explicitly),
+      // then every wave's
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (m + 1 < nb) Dma::issue(nxt, Kb, Vb, rs, kb0 + (m + 1) * kBN, kend, tid);
       const int kb = kb0 + m * kBN;
