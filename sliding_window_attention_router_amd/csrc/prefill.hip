@@ -48,7 +48,7 @@ struct PrefillArgs {
   const int32_t* cnt;
   float* lse_s;     // [B,Hq,N] window-branch normaliser, log2 units
   int32_t* sched;   // far schedule (layout in far_schedule_kernel)
-  float* part_o;    // [max_items][kRows][D]
+  void* part_o;     // [max_items][kRows][D], input type (normalised far partials)
   float* part_lse;  // [max_items][kRows]
   float* diffp;     // [B,Hq,N]
   float* diff;      // [B,N]
@@ -93,6 +93,13 @@ SWI_DEV int xcd_slice(int i, int total) {
   const int per = (total + 7) / 8;
   const int lin = (i & 7) * per + (i >> 3);
   return ((i >> 3) < per && lin < total) ? lin : -1;
+}
+
+// Four consecutive values as float.
+SWI_DEV f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+SWI_DEV f32x4 load4(const bf16_t* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{float(v[0]), float(v[1]), float(v[2]), float(v[3])};
 }
 
 // Per-wave bounds used to skip blocks no row of the wave needs and to drop
@@ -443,7 +450,7 @@ SWI_DEV void far_item(const PrefillArgs& a, char* buf0, char* buf1, int item) {
     float lse2;
     const float inv = finish_row(c.m_of(t), c.l_of(t), lse2);
     if (!valid[t]) continue;
-    float* prow = a.part_o + (int64_t(item) * kRows + r[t]) * D;
+    T* prow = static_cast<T*>(a.part_o) + (int64_t(item) * kRows + r[t]) * D;
     store_row<Core::MD>(prow, c.acc_of(t), inv, g);
     if (g == 0) a.part_lse[int64_t(item) * kRows + r[t]] = lse2;
   }
@@ -509,17 +516,18 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(PrefillArgs a) {
   for (int md = 0; md < MD; ++md)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[md][i] = wsum * Elem<T>::load(orow + acc_channel(md, i, g));
+#pragma unroll 2
   for (int k = 0; k < ni; ++k) {
     const int it = sv.item_of(bu, t, k, a.cmax);
     const float lk = a.part_lse[int64_t(it) * kRows + r];
     const float w = lk == kNegInf ? 0.f : fast_exp2(lk - M);
     wsum += w;
-    const float* prow = a.part_o + (int64_t(it) * kRows + r) * D;
+    const T* prow = static_cast<const T*>(a.part_o) + (int64_t(it) * kRows + r) * D;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(prow + md * 32 + i4 * 8 + g * 4);
+        const f32x4 v = load4(prow + md * 32 + i4 * 8 + g * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[md][i4 * 4 + e] = fmaf(w, v[e], o[md][i4 * 4 + e]);
       }
@@ -668,7 +676,7 @@ bool plan_prefill(const PrefillShape& sh, PrefillPlan* p) {
     const size_t sched_ints = 2 + size_t(nT) + nbu + 2 * nbu * p->cmax + 2 * size_t(max_items);
     off = align_up(off + sched_ints * 4);
     p->off_part_o = off;
-    off = align_up(off + size_t(max_items) * kRows * sh.d * 4);
+    off = align_up(off + size_t(max_items) * kRows * sh.d * (sh.f32 ? 4 : 2));
     p->off_part_lse = off;
     off = align_up(off + size_t(max_items) * kRows * 4);
   } else {
@@ -730,7 +738,7 @@ hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const vo
   a.cnt = cnt;
   a.lse_s = sh.both_branch ? nullptr : reinterpret_cast<float*>(w + p.off_lse);
   a.sched = sh.both_branch ? nullptr : reinterpret_cast<int32_t*>(w + p.off_sched);
-  a.part_o = sh.both_branch ? nullptr : reinterpret_cast<float*>(w + p.off_part_o);
+  a.part_o = sh.both_branch ? nullptr : static_cast<void*>(w + p.off_part_o);
   a.part_lse = sh.both_branch ? nullptr : reinterpret_cast<float*>(w + p.off_part_lse);
   a.diffp = sh.both_branch ? reinterpret_cast<float*>(w + p.off_diffp) : nullptr;
   a.diff = diff;
