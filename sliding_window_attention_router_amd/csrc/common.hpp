@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+
 #define SWI_DEV __device__ __forceinline__
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -35,25 +37,44 @@ SWI_DEV float xor32(float v) {
   return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
 }
 
+// Wave-wide reductions on the DPP network (VALU only, no LDS round trip):
+// combine within quads, half-rows and rows of 16 lanes, then across rows
+// (row_bcast15 into rows 1 and 3, row_bcast31 into rows 2 and 3); lane 63
+// ends with the total, which is returned to every lane.  Lanes a step does
+// not update read the identity.  The combining order is fixed.
+template <int CTRL, int ROWS = 0xF>
+SWI_DEV int dpp_src(int v, int identity) {
+  return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROWS, 0xF, false);
+}
+template <typename Op>
+SWI_DEV int wave_reduce(int v, int identity, Op op) {
+  v = op(v, dpp_src<0xB1>(v, identity));        // quad_perm [1,0,3,2]
+  v = op(v, dpp_src<0x4E>(v, identity));        // quad_perm [2,3,0,1]
+  v = op(v, dpp_src<0x141>(v, identity));       // row_half_mirror
+  v = op(v, dpp_src<0x140>(v, identity));       // row_mirror
+  v = op(v, dpp_src<0x142, 0xA>(v, identity));  // row_bcast15
+  v = op(v, dpp_src<0x143, 0xC>(v, identity));  // row_bcast31
+  return __builtin_amdgcn_readlane(v, 63);
+}
 SWI_DEV float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return __int_as_float(wave_reduce(__float_as_int(v), __float_as_int(-__builtin_huge_valf()),
+                                    [](int a, int b) {
+                                      return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+                                    }));
 }
 SWI_DEV float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return __int_as_float(wave_reduce(__float_as_int(v), 0, [](int a, int b) {
+    return __float_as_int(__int_as_float(a) + __int_as_float(b));
+  }));
 }
 SWI_DEV int wave_min_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce(v, INT_MAX, [](int a, int b) { return min(a, b); });
+}
+SWI_DEV int wave_max_i(int v) {
+  return wave_reduce(v, INT_MIN, [](int a, int b) { return max(a, b); });
 }
 SWI_DEV int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, 0, [](int a, int b) { return a + b; });
 }
 // Inclusive prefix sum over the lanes of the wave.
 SWI_DEV int wave_incl_scan_i(int v) {
@@ -63,11 +84,6 @@ SWI_DEV int wave_incl_scan_i(int v) {
     const int t = __shfl_up(v, o, kWave);
     if (lane >= o) v += t;
   }
-  return v;
-}
-SWI_DEV int wave_max_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
   return v;
 }
 
