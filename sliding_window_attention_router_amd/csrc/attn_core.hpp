@@ -342,11 +342,15 @@ struct CoreBF16 {
 // writes bytes [16i, 16i+16) after the wave-uniform destination), so a K/V
 // block needs no registers and no LDS store instructions.  Each 1 KB copy
 // covers 1024 / (2D) whole rows; the lane -> source mapping is free, which
-// is used to XOR-swizzle the 16-byte chunks of every row:
-//   K: chunk c of key row k is stored at chunk position c ^ (k & 7), so the
-//      8 rows read by 8 consecutive lanes (same chunk) hit distinct banks;
-//   V: chunk c of key row k is stored at c ^ ((k & 3) << 1), so the four
-//      rows of one transposing read (below) hit distinct banks.
+// is used to XOR-swizzle the 16-byte chunks of every row so that the
+// operand reads hit distinct banks (64 banks of 4 bytes: a 128-bit read is
+// served 16 lanes at a time, a 64-bit read 32 lanes at a time):
+//   K: the 16 lanes of a read take 16 consecutive key rows at one chunk;
+//      chunk c of row k is stored at c ^ (k & 15) (d = 128) or
+//      c ^ ((k >> 1) & 7) (d = 64, two rows per 256 bytes);
+//   V: 32 lanes of a transposing read take 4 rows x 4 chunks; chunk c of
+//      row k is stored at c ^ ((k & 3) << 2) (d = 128) or
+//      c ^ (((k >> 1) & 1) << 2) (d = 64).
 // V^T operands come from ds_read_b64_tr_b16: within each group of 16
 // lanes, source lane 4r + k supplies four 16-bit values and destination
 // lane 4k + e receives value e of source lanes k, 4 + k, 8 + k, 12 + k (as
@@ -363,11 +367,15 @@ struct LdsDma {
   static constexpr int kRowB = 2 * D;  // bytes per key row
   static constexpr int kKBytes = kBN * kRowB;
   static constexpr int kBytes = 2 * kKBytes;  // K block, then V block
+  SWI_DEV static constexpr int k_swz(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
+  SWI_DEV static constexpr int v_swz(int key) {
+    return D == 128 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2);
+  }
   SWI_DEV static constexpr int k_pos(int key, int chunk) {
-    return key * kRowB + ((chunk ^ (key & 7)) << 4);
+    return key * kRowB + ((chunk ^ k_swz(key)) << 4);
   }
   SWI_DEV static constexpr int v_pos(int key, int chunk) {
-    return kKBytes + key * kRowB + ((chunk ^ ((key & 3) << 1)) << 4);
+    return kKBytes + key * kRowB + ((chunk ^ v_swz(key)) << 4);
   }
 };
 
@@ -391,9 +399,9 @@ struct KVDma {
       const int byte = m * 1024 + lane * 16;
       const int row = byte / L::kRowB, p = (byte % L::kRowB) >> 4;
       const uint32_t src = uint32_t(min(row, last)) * rb;
-      __builtin_amdgcn_global_load_lds(SWI_GLOBAL(kp + src + uint32_t((p ^ (row & 7)) << 4)),
+      __builtin_amdgcn_global_load_lds(SWI_GLOBAL(kp + src + uint32_t((p ^ L::k_swz(row)) << 4)),
                                        SWI_LOCAL(buf + m * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(SWI_GLOBAL(vp + src + uint32_t((p ^ ((row & 3) << 1)) << 4)),
+      __builtin_amdgcn_global_load_lds(SWI_GLOBAL(vp + src + uint32_t((p ^ L::v_swz(row)) << 4)),
                                        SWI_LOCAL(buf + L::kKBytes + m * 1024), 16, 0, 0);
     }
   }
