@@ -433,6 +433,16 @@ SWI_DEV void lds_wait(V (&v)[N]) {
                : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
                  "+v"(v[6]), "+v"(v[7]));
 }
+// The same, placed after the MFMA chain that produced `after` (an input
+// only, to order the wait behind that chain in the instruction stream).
+template <typename V, int N>
+SWI_DEV void lds_wait_after(V (&v)[N], float after) {
+  static_assert(N == 8, "eight operands per group");
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                 "+v"(v[6]), "+v"(v[7])
+               : "v"(after));
+}
 SWI_DEV uint32_t lds_addr(const char* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
@@ -507,7 +517,7 @@ struct CoreBF16Dma {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[ks], qreg[ks], s[0], 0, 0, 0);
-      lds_wait(a1);
+      lds_wait_after(a1, s[0][0]);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[ks], qreg[ks], s[1], 0, 0, 0);
