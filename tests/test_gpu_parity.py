@@ -111,6 +111,8 @@ PREFILL_CASES = [
     (1, 129, 4, 2, 1, 128, 64, 0.5, "bf16"),     # N just past a tile
     (1, 5, 2, 1, 1, 64, 3, 0.5, "bf16"),         # N smaller than a block
     (1, 400, 4, 2, 2, 128, 70, 0.4, "f32"),      # fp32 path, GQA
+    (1, 2100, 16, 4, 1, 64, 256, 0.2, "bf16"),   # d=64 GQA 4:1, many window blocks and far chunks
+    (2, 1500, 8, 2, 1, 128, 300, 0.3, "bf16"),   # two sequences: per-sequence K/V copy offsets
 ]
 
 
