@@ -447,6 +447,13 @@ SWI_DEV uint32_t lds_addr(const char* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
 
+// Called by a core's block() right after its score MFMAs, when the query
+// registers are free for the rest of the block (used to start loading the
+// next tile's queries).
+struct NoHook {
+  SWI_DEV void operator()() const {}
+};
+
 // bf16 core reading the DMA layout (same arithmetic as CoreBF16).  Operand
 // reads run one group of eight ahead of the MFMAs that use them.
 template <int D>
@@ -497,8 +504,9 @@ struct CoreBF16Dma {
     v[7] = lds_read_tr16<L::kKBytes + 56 * L::kRowB>(va);
   }
 
+  template <typename F = NoHook>
   SWI_DEV void block(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
-                     int g) {
+                     int g, F&& after_scores = F()) {
     const int lane = threadIdx.x & 63;
     const uint32_t base = lds_addr(lds);
     // per-lane parts of the addresses (key row q of a tile, chunk 2ks+g)
@@ -527,6 +535,7 @@ struct CoreBF16Dma {
         s[i / KS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], qreg[i % KS], s[i / KS], 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(0);
+    after_scores();
     online_softmax<MD>(s, acc, m, l, kb, masked, lo, hi, sl2, g);
     bf16x8 pb[4];
 #pragma unroll
@@ -576,6 +585,11 @@ struct OneTile {
   SWI_DEV void block(const char* lds, int kb, bool masked, const int (&lo)[1], const int (&hi)[1],
                      float sl2, int q, int g) {
     c.block(lds, kb, masked, lo[0], hi[0], sl2, q, g);
+  }
+  template <typename F>
+  SWI_DEV void block_hook(const char* lds, int kb, bool masked, int lo, int hi, float sl2, int q,
+                          int g, F&& after_scores) {
+    c.block(lds, kb, masked, lo, hi, sl2, q, g, after_scores);
   }
   SWI_DEV f32x16 (&acc_of(int))[MD] { return c.acc; }
   SWI_DEV float m_of(int) const { return c.m; }

@@ -33,7 +33,7 @@ struct PrefillPlan {
   int far_tiles;  // per (b, unit): ceil(N / tpt_far)
   int max_items;  // upper bound on far work items
   int cmax;       // bound on chunks per far tile (+1)
-  size_t off_lse, off_sched, off_part_o, off_part_lse, off_diffp, bytes;
+  size_t off_lse, off_sched, off_queue, off_part_o, off_part_lse, off_diffp, bytes;
 };
 
 bool plan_prefill(const PrefillShape& sh, PrefillPlan* p);

@@ -25,6 +25,7 @@
 // the far keys to O_FULL, and writes gate ? O_FULL : O_SWA and the
 // per-(head, token) squared distance; diff_kernel sums it over heads
 // (the regulariser paragraph of the same section uses this distance).
+#include <atomic>
 #include <climits>
 
 #include "attn_core.hpp"
@@ -52,9 +53,11 @@ struct PrefillArgs {
   float* part_lse;  // [max_items][kRows]
   float* diffp;     // [B,Hq,N]
   float* diff;      // [B,N]
+  int* queue;       // [8] window-tile queue positions (zeroed by the schedule kernel)
   int B, N, Hq, Hkv, G, W;
   int HK, HG, hpu, units, tpt_band, tpt_far, band_tiles, far_tiles, max_items;
   int far_grid;  // workgroups of attn_kernel reserved for far items (multiple of 8)
+  int band_grid; // workgroups of attn_kernel that work off the window-tile queues
   int cmax;   // width of the per-unit chunk tables
   float sl2;  // softmax scale * log2(e)
 };
@@ -371,6 +374,7 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
     sv.unit_base[bu] = run;  // item count for now
   }
   __syncthreads();
+  if (tid < 8) a.queue[tid] = 0;
   if (tid == 0) {
     int s = 0;
     for (int bu = 0; bu < nbu; ++bu) {
@@ -457,6 +461,151 @@ SWI_DEV void far_item(const PrefillArgs& a, char* buf0, char* buf1, int item) {
 }
 
 // ---------------------------------------------------------------------------
+// Persistent window workers (DMA path).  The window tiles are split into 8
+// queues, queue x holding the x-th eighth of the tiles (consecutive tiles of
+// one KV head, which share most of their keys in that XCD's L2); a worker
+// takes tiles from the queue of its XCD and moves on to the others when it
+// runs dry.  Every position of every queue is handed out once (atomic
+// counters, zeroed by the schedule kernel that precedes the launch).
+// Across tiles the block stream continues without a pipeline restart: the
+// next tile id is claimed a tile ahead and published two blocks before the
+// current tile ends, the copy of its first K/V block is issued during the
+// last block of the current tile, and its queries are loaded right after
+// that block's score MFMAs.
+// ---------------------------------------------------------------------------
+struct TileQueue {
+  int n, per;
+  SWI_DEV int len(int x) const { return min(per, max(0, n - x * per)); }
+};
+// One thread: the next tile, from queue x or, once x is drained, the others.
+// The counters are shared by workgroups on all XCDs, whose L2 caches are
+// not coherent with each other: the increments are made at system scope,
+// which performs them past the L2s.
+SWI_DEV int grab_tile(int* queue, const TileQueue& tq, int& x) {
+  for (int k = 0; k < 8; ++k) {
+    const int p = __hip_atomic_fetch_add(queue + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (p < tq.len(x)) return x * tq.per + p;
+    x = (x + 1) & 7;
+  }
+  return -1;
+}
+
+// Window tile lin: tpt_band consecutive tokens x the HK heads of one KV head.
+struct BandTile {
+  int b, kvh, q0, kb0, nb;
+  SWI_DEV void set(const PrefillArgs& a, int lin) {
+    const int tile = lin % a.band_tiles, bk = lin / a.band_tiles;
+    b = bk / a.Hkv;
+    kvh = bk - b * a.Hkv;
+    q0 = tile * a.tpt_band;
+    const int qlast = min(a.N - 1, q0 + a.tpt_band - 1);
+    kb0 = (max(0, q0 - a.W + 1) / kBN) * kBN;
+    nb = (qlast - kb0) / kBN + 1;
+  }
+};
+
+template <typename T, int D>
+SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
+  using Core = typename TileCfg<T, D>::Core;
+  constexpr int NT = TileCfg<T, D>::kWaves * 64;
+  using Dma = KVDma<D, NT>;
+  __shared__ int s_next;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane & 31, g = lane >> 5;
+  TileQueue tq;
+  tq.n = a.band_tiles * a.B * a.Hkv;
+  tq.per = (tq.n + 7) / 8;
+  int qx = blockIdx.x & 7;  // workgroups are dealt to the 8 XCDs in turn
+  if (tid == 0) s_next = grab_tile(a.queue, tq, qx);
+  __syncthreads();
+  int lin = __builtin_amdgcn_readfirstlane(s_next);
+  if (lin < 0) return;
+  // this lane's row inside any tile
+  const int r = wave * kQR + q, slot = r / a.HK, hh = r - slot * a.HK;
+  const T* Qp = static_cast<const T*>(a.Q);
+  const int64_t rs = int64_t(a.Hkv) * D;
+  auto qrow = [&](const BandTile& t) -> const T* {
+    const int tok = t.q0 + slot;
+    const bool v = slot < a.tpt_band && tok < a.N;
+    return v ? Qp + ((int64_t(t.b) * a.N + tok) * a.Hq + t.kvh * a.HK + hh) * D : nullptr;
+  };
+  auto kv_off = [&](const BandTile& t) { return (int64_t(t.b) * a.N * a.Hkv + t.kvh) * D; };
+  BandTile t;
+  t.set(a, lin);
+  Core c;
+  c.init();
+  c.load_q(0, qrow(t), g);
+  Dma::issue(buf0, static_cast<const T*>(a.K) + kv_off(t), static_cast<const T*>(a.V) + kv_off(t), rs,
+             t.kb0, a.N, tid);
+  int s = 0;  // blocks streamed so far: block s sits in buffer s % 2
+  int next_raw = -1;
+  if (tid == 0) next_raw = grab_tile(a.queue, tq, qx);
+  bool q_pref = false;
+  while (true) {
+    const int tok = t.q0 + slot;
+    const bool valid = slot < a.tpt_band && tok < a.N;
+    const int lo = valid ? max(0, tok - a.W + 1) : 0, hi = valid ? tok : -1;
+    TileBounds<1> tb;
+    {
+      const bool v1[1] = {valid};
+      const int l1[1] = {lo}, h1[1] = {hi};
+      tb.init(v1, l1, h1);
+    }
+    const T* Kb = static_cast<const T*>(a.K) + kv_off(t);
+    const T* Vb = static_cast<const T*>(a.V) + kv_off(t);
+    // the next id is published at step pub and read one barrier later
+    const int pub = t.nb >= 2 ? t.nb - 2 : 0;
+    const int rd = t.nb >= 2 ? pub + 1 : 0;
+    int nlin = -1;
+    BandTile nt;
+    nt.set(a, 0);
+    for (int n = 0; n < t.nb; ++n, ++s) {
+      char* cur = (s & 1) ? buf1 : buf0;
+      char* nxt = (s & 1) ? buf0 : buf1;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (n == pub && tid == 0) s_next = next_raw;
+      if (t.nb < 2) __syncthreads();
+      if (n == rd) {
+        nlin = __builtin_amdgcn_readfirstlane(s_next);
+        if (nlin >= 0) nt.set(a, nlin);
+        // claim the tile after that one now, so that the claim is back long
+        // before its id is published
+        if (tid == 0 && nlin >= 0) next_raw = grab_tile(a.queue, tq, qx);
+      }
+      if (n + 1 < t.nb)
+        Dma::issue(nxt, Kb, Vb, rs, t.kb0 + (n + 1) * kBN, a.N, tid);
+      else if (nlin >= 0)
+        Dma::issue(nxt, static_cast<const T*>(a.K) + kv_off(nt), static_cast<const T*>(a.V) + kv_off(nt),
+                   rs, nt.kb0, a.N, tid);
+      const int kb = t.kb0 + n * kBN;
+      if (!tb.needed(kb)) continue;
+      // last block of the tile: the next tile's queries follow its scores
+      const bool pre = n + 1 == t.nb && nlin >= 0;
+      c.block_hook(cur, kb, tb.masked(kb), lo, hi, a.sl2, q, g, [&]() {
+        if (pre) c.c.load_q(qrow(nt), g);
+      });
+      q_pref = q_pref || pre;
+    }
+    // tile finished: output and window normaliser
+    float lse2;
+    const float inv = finish_row(c.m_of(0), c.l_of(0), lse2);
+    if (valid) {
+      const int h = t.kvh * a.HK + hh;
+      T* orow = static_cast<T*>(a.O) + ((int64_t(t.b) * a.N + tok) * a.Hq + h) * D;
+      store_row<Core::MD>(orow, c.acc_of(0), inv, g);
+      if (g == 0 && a.lse_s) a.lse_s[(int64_t(t.b) * a.Hq + h) * a.N + tok] = lse2;
+    }
+    if (nlin < 0) break;
+    lin = nlin;
+    t = nt;
+    c.init();
+    if (!q_pref) c.load_q(0, qrow(t), g);
+    q_pref = false;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Window tiles and far items in one launch.  Workgroups [0, far_grid) take
 // far items (an XCD takes a contiguous slice of the (unit, chunk, tile)
 // order, so its resident workgroups read the same keys of one KV head);
@@ -474,8 +623,12 @@ __global__ __launch_bounds__((TileCfg<T, D>::kWaves * 64), (TileCfg<T, D>::kMinW
     if (item >= 0) far_item<T, D>(a, buf0, buf1, item);
     return;
   }
-  const int lin = xcd_slice(blockIdx.x - a.far_grid, a.band_tiles * a.B * a.Hkv);
-  if (lin >= 0) band_tile<T, D>(a, buf0, buf1, lin);
+  if constexpr (TileCfg<T, D>::kDma) {
+    band_worker<T, D>(a, buf0, buf1);
+  } else {
+    const int lin = xcd_slice(blockIdx.x - a.far_grid, a.band_tiles * a.B * a.Hkv);
+    if (lin >= 0) band_tile<T, D>(a, buf0, buf1, lin);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -650,6 +803,23 @@ __global__ __launch_bounds__(256) void diff_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Compute units of the current device (queried once per device).
+static hipError_t compute_units(int* n) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cache[dev].load() > 0) {
+    *n = cache[dev].load();
+    return hipSuccess;
+  }
+  e = hipDeviceGetAttribute(n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (*n < 1) *n = 1;
+  if (dev >= 0 && dev < 64) cache[dev].store(*n);
+  return hipSuccess;
+}
+
 bool plan_prefill(const PrefillShape& sh, PrefillPlan* p) {
   p->HK = sh.Hq / sh.Hkv;
   p->HG = sh.Hq / sh.G;
@@ -667,7 +837,7 @@ bool plan_prefill(const PrefillShape& sh, PrefillPlan* p) {
   p->cmax = ((sh.N + kBN - 1) / kBN + kMinChunkBlocks - 1) / kMinChunkBlocks + 1;
   const size_t rowsN = size_t(sh.B) * sh.Hq * sh.N;
   size_t off = 0;
-  p->off_lse = p->off_sched = p->off_part_o = p->off_part_lse = p->off_diffp = 0;
+  p->off_lse = p->off_sched = p->off_queue = p->off_part_o = p->off_part_lse = p->off_diffp = 0;
   if (!sh.both_branch) {
     p->off_lse = off;
     off = align_up(off + rowsN * 4);
@@ -675,6 +845,8 @@ bool plan_prefill(const PrefillShape& sh, PrefillPlan* p) {
     const size_t nbu = size_t(sh.B) * p->units;
     const size_t sched_ints = 2 + size_t(nT) + nbu + 2 * nbu * p->cmax + 2 * size_t(max_items);
     off = align_up(off + sched_ints * 4);
+    p->off_queue = off;
+    off = align_up(off + 8 * 4);
     p->off_part_o = off;
     off = align_up(off + size_t(max_items) * kRows * sh.d * (sh.f32 ? 4 : 2));
     p->off_part_lse = off;
@@ -700,7 +872,15 @@ static hipError_t run_prefill(const PrefillShape& sh, const PrefillPlan& p, Pref
     SWI_TRY(mark(ev, 1, s));
     constexpr int nt = TileCfg<T, D>::kWaves * 64;
     const int band_total = p.band_tiles * sh.B * sh.Hkv;
-    hipLaunchKernelGGL((attn_kernel<T, D>), dim3(a.far_grid + 8 * ((band_total + 7) / 8)), dim3(nt), 0,
+    if (TileCfg<T, D>::kDma) {  // resident window workers: kMinWG per CU
+      int cus = 0;
+      SWI_TRY(compute_units(&cus));
+      const int workers = TileCfg<T, D>::kMinWG * cus;
+      a.band_grid = band_total < workers ? band_total : workers;
+    } else {
+      a.band_grid = band_total;
+    }
+    hipLaunchKernelGGL((attn_kernel<T, D>), dim3(a.far_grid + 8 * ((a.band_grid + 7) / 8)), dim3(nt), 0,
                        s, a);
     SWI_TRY(hipGetLastError());
     SWI_TRY(mark(ev, 2, s));
@@ -738,6 +918,7 @@ hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const vo
   a.cnt = cnt;
   a.lse_s = sh.both_branch ? nullptr : reinterpret_cast<float*>(w + p.off_lse);
   a.sched = sh.both_branch ? nullptr : reinterpret_cast<int32_t*>(w + p.off_sched);
+  a.queue = sh.both_branch ? nullptr : reinterpret_cast<int*>(w + p.off_queue);
   a.part_o = sh.both_branch ? nullptr : static_cast<void*>(w + p.off_part_o);
   a.part_lse = sh.both_branch ? nullptr : reinterpret_cast<float*>(w + p.off_part_lse);
   a.diffp = sh.both_branch ? reinterpret_cast<float*>(w + p.off_diffp) : nullptr;
