@@ -399,10 +399,13 @@ struct KVDma {
       const int byte = m * 1024 + lane * 16;
       const int row = byte / L::kRowB, p = (byte % L::kRowB) >> 4;
       const uint32_t src = uint32_t(min(row, last)) * rb;
-      __builtin_amdgcn_global_load_lds(SWI_GLOBAL(kp + src + uint32_t((p ^ L::k_swz(row)) << 4)),
-                                       SWI_LOCAL(buf + m * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(SWI_GLOBAL(vp + src + uint32_t((p ^ L::v_swz(row)) << 4)),
-                                       SWI_LOCAL(buf + L::kKBytes + m * 1024), 16, 0, 0);
+      // one 32-bit lane offset per address: the copies then use the
+      // scalar-base + offset form (one VGPR per address instead of two)
+      const uint32_t ko = src + uint32_t((p ^ L::k_swz(row)) << 4);
+      const uint32_t vo = src + uint32_t((p ^ L::v_swz(row)) << 4);
+      __builtin_amdgcn_global_load_lds(SWI_GLOBAL(kp + ko), SWI_LOCAL(buf + m * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(SWI_GLOBAL(vp + vo), SWI_LOCAL(buf + L::kKBytes + m * 1024), 16,
+                                       0, 0);
     }
   }
 };

@@ -72,7 +72,7 @@ struct PrefillArgs {
 // Items of a unit are ordered by (chunk, tile): consecutive items read the
 // same key range of the same KV head.
 struct SchedView {
-  int32_t *n_items, *unit_base, *first, *offset, *item_tile, *item_chunk;
+  int32_t *n_items, *unit_base, *first, *offset, *item_tile, *item_chunk, *merge_base, *merge_tile;
   SWI_DEV SchedView(const PrefillArgs& a) {
     const int nT = a.B * a.units * a.far_tiles;
     const int nbu = a.B * a.units;
@@ -82,6 +82,8 @@ struct SchedView {
     offset = first + nbu * a.cmax;
     item_tile = offset + nbu * a.cmax;
     item_chunk = item_tile + a.max_items;
+    merge_base = item_chunk + a.max_items;  // per unit; merge_base[nbu]: total
+    merge_tile = merge_base + nbu + 1;
   }
   // item holding chunk c of tile t of unit bu
   SWI_DEV int item_of(int bu, int t, int c, int cmax) const {
@@ -98,8 +100,15 @@ SWI_DEV int xcd_slice(int i, int total) {
   return ((i >> 3) < per && lin < total) ? lin : -1;
 }
 
-// Four consecutive values as float.
+// Four consecutive values as float, and back.
 SWI_DEV f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+SWI_DEV void store4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+SWI_DEV void store4(bf16_t* p, f32x4 v) {
+  bf16x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = bf16_t(v[e]);
+  *reinterpret_cast<bf16x4*>(p) = o;
+}
 SWI_DEV f32x4 load4(const bf16_t* p) {
   const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
   return f32x4{float(v[0]), float(v[1]), float(v[2]), float(v[3])};
@@ -372,6 +381,8 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
       run += nt - sv.first[bu * a.cmax + c];
     }
     sv.unit_base[bu] = run;  // item count for now
+    // tiles with chunks: the unit's active tiles from first[0] on
+    sv.merge_base[bu] = maxn > 0 ? nt - sv.first[bu * a.cmax] : 0;  // count for now
   }
   __syncthreads();
   if (tid < 8) a.queue[tid] = 0;
@@ -384,6 +395,13 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
     }
     a.sched[0] = s;
     a.sched[1] = cb;
+    int m = 0;
+    for (int bu = 0; bu < nbu; ++bu) {
+      const int n = sv.merge_base[bu];
+      sv.merge_base[bu] = m;
+      m += n;
+    }
+    sv.merge_base[nbu] = m;
   }
   __syncthreads();
   // pass 5: item list
@@ -395,6 +413,8 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
       sv.item_tile[it] = T_;
       sv.item_chunk[it] = c;
     }
+    // the merge list: tiles with chunks, unit by unit
+    if (n > 0) sv.merge_tile[sv.merge_base[bu] + t - sv.first[bu * a.cmax]] = T_;
   }
 }
 
@@ -632,60 +652,76 @@ __global__ __launch_bounds__((TileCfg<T, D>::kWaves * 64), (TileCfg<T, D>::kMinW
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the far tiles: one workgroup per tile, lanes laid out as in the
-// far items (lane pair per row, 64 channels per lane).  O_FULL of a row is
-// the log-sum-exp weighted sum of its window output and its chunks'
-// partials, taken in chunk order.
+// Merge of the far tiles.  Work units are (tile with chunks, quarter of its
+// rows), taken from the schedule's list by a fixed grid; 8 threads share a
+// row, each with D/8 consecutive channels, so that many independent loads
+// are in flight (one thread per row walking its chunks one after another
+// left the kernel bound by load latency).  O_FULL of a row is the
+// log-sum-exp weighted sum of its window output and its chunks' partials,
+// taken in chunk order.
 // ---------------------------------------------------------------------------
+constexpr int kMergeThreads = 256;
+constexpr int kMergeTPR = 8;  // threads per row
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(PrefillArgs a) {
-  constexpr int MD = D / 32;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(PrefillArgs a) {
+  constexpr int kRowsWG = kMergeThreads / kMergeTPR;  // rows per work unit
+  constexpr int kParts = kRows / kRowsWG;
+  constexpr int CPT = D / kMergeTPR;  // channels per thread
   SchedView sv(a);
-  const int T_ = blockIdx.x;
-  const int ni = sv.n_items[T_];
-  if (ni < 1) return;
-  const int per_b = a.units * a.far_tiles;
-  const int b = T_ / per_b, rem = T_ - b * per_b;
-  const int u = rem / a.far_tiles, t = rem - u * a.far_tiles;
-  const int bu = b * a.units + u;
-  const int g_gate = (u * a.hpu) / a.HG;
-  const int c = a.cnt[b * a.G + g_gate];
-  const int ntok = min(a.tpt_far, c - t * a.tpt_far);
-  const int lane = threadIdx.x & 63, q = lane & 31, g = lane >> 5;
-  const int r = (threadIdx.x >> 6) * kQR + q;
-  const int slot = r / a.hpu, hh = r - slot * a.hpu;
-  if (slot >= ntok) return;
-  const int tok = a.idx[(int64_t(b) * a.G + g_gate) * a.N + t * a.tpt_far + slot];
-  if (tok < a.W) return;
-  const int h = u * a.hpu + hh;
-  const float ls = a.lse_s[(int64_t(b) * a.Hq + h) * a.N + tok];
-  float M = ls;
-  for (int k = 0; k < ni; ++k)
-    M = fmaxf(M, a.part_lse[int64_t(sv.item_of(bu, t, k, a.cmax)) * kRows + r]);
-  T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D;
-  float wsum = fast_exp2(ls - M);
-  f32x16 o[MD];
+  const int nm = sv.merge_base[a.B * a.units];
+  const int rr = threadIdx.x / kMergeTPR, c0 = (threadIdx.x % kMergeTPR) * CPT;
+  for (int w = blockIdx.x; w < nm * kParts; w += gridDim.x) {
+    const int T_ = sv.merge_tile[w / kParts];
+    const int r = (w % kParts) * kRowsWG + rr;
+    const int ni = sv.n_items[T_];
+    const int per_b = a.units * a.far_tiles;
+    const int b = T_ / per_b, rem = T_ - b * per_b;
+    const int u = rem / a.far_tiles, t = rem - u * a.far_tiles;
+    const int bu = b * a.units + u;
+    const int g_gate = (u * a.hpu) / a.HG;
+    const int c = a.cnt[b * a.G + g_gate];
+    const int ntok = min(a.tpt_far, c - t * a.tpt_far);
+    const int slot = r / a.hpu, hh = r - slot * a.hpu;
+    if (slot >= ntok) continue;
+    const int tok = a.idx[(int64_t(b) * a.G + g_gate) * a.N + t * a.tpt_far + slot];
+    if (tok < a.W) continue;
+    const int h = u * a.hpu + hh;
+    const float ls = a.lse_s[(int64_t(b) * a.Hq + h) * a.N + tok];
+    float M = ls;
+    for (int k = 0; k < ni; ++k)
+      M = fmaxf(M, a.part_lse[int64_t(sv.item_of(bu, t, k, a.cmax)) * kRows + r]);
+    T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D + c0;
+    float wsum = fast_exp2(ls - M);
+    float o[CPT];
 #pragma unroll
-  for (int md = 0; md < MD; ++md)
+    for (int i4 = 0; i4 < CPT / 4; ++i4) {
+      const f32x4 v = load4(orow + i4 * 4);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[md][i] = wsum * Elem<T>::load(orow + acc_channel(md, i, g));
+      for (int e = 0; e < 4; ++e) o[i4 * 4 + e] = wsum * v[e];
+    }
 #pragma unroll 2
-  for (int k = 0; k < ni; ++k) {
-    const int it = sv.item_of(bu, t, k, a.cmax);
-    const float lk = a.part_lse[int64_t(it) * kRows + r];
-    const float w = lk == kNegInf ? 0.f : fast_exp2(lk - M);
-    wsum += w;
-    const T* prow = static_cast<const T*>(a.part_o) + (int64_t(it) * kRows + r) * D;
+    for (int k = 0; k < ni; ++k) {
+      const int it = sv.item_of(bu, t, k, a.cmax);
+      const float lk = a.part_lse[int64_t(it) * kRows + r];
+      const float wk = lk == kNegInf ? 0.f : fast_exp2(lk - M);
+      wsum += wk;
+      const T* prow = static_cast<const T*>(a.part_o) + (int64_t(it) * kRows + r) * D + c0;
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
+      for (int i4 = 0; i4 < CPT / 4; ++i4) {
+        const f32x4 v = load4(prow + i4 * 4);
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 v = load4(prow + md * 32 + i4 * 8 + g * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[md][i4 * 4 + e] = fmaf(w, v[e], o[md][i4 * 4 + e]);
+        for (int e = 0; e < 4; ++e) o[i4 * 4 + e] = fmaf(wk, v[e], o[i4 * 4 + e]);
       }
+    }
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int i4 = 0; i4 < CPT / 4; ++i4) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = o[i4 * 4 + e] * inv;
+      store4(orow + i4 * 4, v);
+    }
   }
-  store_row<MD>(orow, o, 1.f / wsum, g);
 }
 
 // Sum of squared differences of this lane's channels.  Contraction is off so
@@ -843,7 +879,8 @@ bool plan_prefill(const PrefillShape& sh, PrefillPlan* p) {
     off = align_up(off + rowsN * 4);
     p->off_sched = off;
     const size_t nbu = size_t(sh.B) * p->units;
-    const size_t sched_ints = 2 + size_t(nT) + nbu + 2 * nbu * p->cmax + 2 * size_t(max_items);
+    const size_t sched_ints =
+        2 + size_t(nT) + nbu + 2 * nbu * p->cmax + 2 * size_t(max_items) + nbu + 1 + size_t(nT);
     off = align_up(off + sched_ints * 4);
     p->off_queue = off;
     off = align_up(off + 8 * 4);
@@ -884,8 +921,11 @@ static hipError_t run_prefill(const PrefillShape& sh, const PrefillPlan& p, Pref
                        s, a);
     SWI_TRY(hipGetLastError());
     SWI_TRY(mark(ev, 2, s));
-    hipLaunchKernelGGL((merge_kernel<T, D>), dim3(sh.B * p.units * p.far_tiles), dim3(kThreads), 0,
-                       s, a);
+    {
+      int cus = 0;
+      SWI_TRY(compute_units(&cus));
+      hipLaunchKernelGGL((merge_kernel<T, D>), dim3(4 * cus), dim3(kMergeThreads), 0, s, a);
+    }
     SWI_TRY(hipGetLastError());
     SWI_TRY(mark(ev, 3, s));
   } else {
