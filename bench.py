@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU reference sample (0 = skip)")
     ap.add_argument("--p", type=float, default=0.13, help="full-branch fraction")
+    ap.add_argument("--both-steps", type=int, default=3,
+                    help="timed runs of the both-branch prefill (after the timed steps; 0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB before the steps "
                          "(a known-size reference for hardware byte counters)")
@@ -247,6 +249,8 @@ def main():
                            "traffic": traffic.get(PROFILE_NAMES[name])}
     dominant = max(kern, key=lambda n: t[n])
 
+    both = both_branch_run(swa, Q, K, V, gate, W, args.both_steps) if args.both_steps > 0 else None
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(pre, W, args.cpu_seconds)
@@ -277,6 +281,7 @@ def main():
                        "bytes": dbytes, "ms": round(decode_ms, 4),
                        "tok_per_s": round(decode_tok_s, 1), "GB_per_s": round(decode_gbs, 1),
                        "frac_of_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4)},
+            "both_branch": both,
         },
         "kernel_ms": {k: round(v, 4) for k, v in t.items()},
         "roofline": dict(rooflines[dominant], kernel=dominant),
@@ -284,6 +289,41 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def both_branch_run(swa, Q, K, V, gate, W, steps):
+    """Both-branch prefill on the same inputs (outside the timed steps): every
+    row takes both branches and the per-token distance is written.  Useful
+    work is the full causal branch (the window branch's keys are a subset of
+    it): 4*d*Hq*sum_i (i+1) FLOP."""
+    import torch
+    B, N, Hq, d = Q.shape
+    dev = Q.device
+    G = gate.shape[2]
+    ws = torch.empty(swa.prefill_workspace_size(B, N, Hq, K.shape[2], G, d, W, both_branch=True),
+                     dtype=torch.uint8, device=dev)
+    O = torch.empty_like(Q)
+    diff = torch.empty((B, N), dtype=torch.float32, device=dev)
+    swa.prefill(Q, K, V, gate, W, both_branch=True, out=O, diff=diff, workspace=ws)
+    torch.cuda.synchronize()
+    sets = []
+    for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        for e in ev:
+            e.record()
+        sets.append(ev)
+    torch.cuda.synchronize()
+    for ev in sets:
+        swa.prefill(Q, K, V, gate, W, both_branch=True, out=O, diff=diff, workspace=ws, events=ev)
+    torch.cuda.synchronize()
+    stage = [float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in sets])) for i in range(4)]
+    ms = sum(stage)
+    flop = 4.0 * d * Hq * B * N * (N + 1) / 2
+    return {"ms": round(ms, 4), "useful_tflop": round(flop / 1e12, 4),
+            "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "kernel_ms": {"far_schedule": round(stage[0], 4), "attn": round(stage[1], 4),
+                          "merge": round(stage[2], 4), "diff": round(stage[3], 4)}}
 
 
 def cpu_baseline(pre, W, budget_s):

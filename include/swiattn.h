@@ -109,7 +109,9 @@ size_t swiattn_prefill_workspace_size(int B, int N, int Hq, int Hkv, int G, int 
  *   O     [B,N,Hq,d]   dtype   out: gate ? O_FULL : O_SWA, every row written
  *   diff  [B,N]        float   out, both-branch mode only (else may be
  *                              NULL): sum over heads and channels of
- *                              (O_FULL - O_SWA)^2 in float32
+ *                              (O_FULL - O_SWA)^2 in float32, with O_SWA
+ *                              as stored (rounded to dtype) and O_FULL
+ *                              before rounding; exactly 0 for rows i < W
  *   W >= 1 (W >= N makes the two branches identical); scale > 0 is the
  *   softmax scale (1/sqrt(d) for standard attention).
  *   ws, ws_bytes: device workspace of at least
@@ -117,8 +119,9 @@ size_t swiattn_prefill_workspace_size(int B, int N, int Hq, int Hkv, int G, int 
  *
  * Hard-gate mode runs the window branch for every row, the far part
  * [0, i-W] of the full branch only for gathered gate=1 rows, and merges the
- * two key sets by their log-sum-exp.  Both-branch mode runs one causal pass
- * per query tile that snapshots the window result on the way.
+ * two key sets by their log-sum-exp.  Both-branch mode runs the same
+ * stages with every row taking the far part; its merge also writes the
+ * distance and keeps O_SWA where the gate is 0.
  * Errors: INVALID_ARG (sizes < 1, NULL pointers, Hq % Hkv, Hq % G, scale),
  * UNSUPPORTED (d, group nesting, Hq/Hkv > 32), WORKSPACE.
  */
@@ -167,8 +170,8 @@ int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t*
  *   prefill, hard-gate mode: 0 before the far-part schedule, 1 after it,
  *     2 after the attention kernel (window tiles and far chunks), 3 after
  *     the merge;
- *   prefill, both-branch mode: 0 before the fused kernel, 1 after it,
- *     2 after the per-token head sum;
+ *   prefill, both-branch mode: the same four, and 4 after the per-token
+ *     head sum of the distance;
  *   decode: 0 before the split-K kernel, 1 after it, 2 after the merge.
  * Passing events == NULL is the plain call.  Recording failures are
  * reported as SWIATTN_ERR_HIP.

@@ -27,10 +27,11 @@ struct PrefillPlan {
   int HG;         // query heads per gate group
   int hpu;        // heads per far unit: min(HK, HG)
   int units;      // far units per sequence: Hq / hpu
-  int tpt_band;   // tokens per band / fused tile: 128 / HK
+  int tpt_band;   // tokens per window tile: 128 / HK
   int tpt_far;    // gathered tokens per far tile: 128 / hpu
   int band_tiles; // ceil(N / tpt_band)
   int far_tiles;  // per (b, unit): ceil(N / tpt_far)
+  int target_items;  // far work items aimed for
   int max_items;  // upper bound on far work items
   int cmax;       // bound on chunks per far tile (+1)
   size_t off_lse, off_sched, off_queue, off_part_o, off_part_lse, off_diffp, bytes;

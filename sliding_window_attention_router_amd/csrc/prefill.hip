@@ -20,11 +20,12 @@
 // The window and far key sets are disjoint and cover [0, i], so the merge is
 // the exact full softmax up to rounding.
 //
-// Both-branch mode (fused_kernel): one causal pass per query tile that
-// walks the window keys first, snapshots O_SWA in registers, continues over
-// the far keys to O_FULL, and writes gate ? O_FULL : O_SWA and the
-// per-(head, token) squared distance; diff_kernel sums it over heads
-// (the regulariser paragraph of the same section uses this distance).
+// Both-branch mode: the same launches with every row taking the full
+// branch (no compaction: the far tiles are consecutive positions).  The
+// merge then also writes the per-(head, token) squared distance between
+// O_FULL and O_SWA, and replaces the window output only where the gate is
+// 1; diff_kernel sums the distance over heads (the regulariser paragraph
+// of the same section uses this distance).
 #include <atomic>
 #include <climits>
 
@@ -33,9 +34,9 @@
 
 namespace swi {
 
-constexpr int kThreads = 256;      // merge / fused kernels: 4 waves x 32 rows
-constexpr int kRows = 128;          // query rows of every tile
-constexpr int kTargetItems = 1024;  // far work items aimed for per launch
+constexpr int kRows = 128;  // query rows of every tile
+constexpr int kTargetItems = 1024;      // far work items aimed for per launch (hard gate)
+constexpr int kTargetItemsAll = 4096;   // the same when every row takes the full branch
 constexpr int kMinChunkBlocks = 8;  // far chunk is at least 8 x 64 keys
 constexpr int kSchedThreads = 1024;
 
@@ -51,7 +52,7 @@ struct PrefillArgs {
   int32_t* sched;   // far schedule (layout in far_schedule_kernel)
   void* part_o;     // [max_items][kRows][D], input type (normalised far partials)
   float* part_lse;  // [max_items][kRows]
-  float* diffp;     // [B,Hq,N]
+  float* diffp;     // [B,Hq,N] per-head squared distance (both-branch mode)
   float* diff;      // [B,N]
   int* queue;       // [8] window-tile queue positions (zeroed by the schedule kernel)
   int B, N, Hq, Hkv, G, W;
@@ -59,8 +60,19 @@ struct PrefillArgs {
   int far_grid;  // workgroups of attn_kernel reserved for far items (multiple of 8)
   int band_grid; // workgroups of attn_kernel that work off the window-tile queues
   int cmax;   // width of the per-unit chunk tables
+  int all_rows;      // both-branch mode: every row takes the full branch (no idx/cnt)
+  int target_items;  // far work items aimed for
   float sl2;  // softmax scale * log2(e)
 };
+
+// The rows that take the full branch, per gate group: the compacted gate=1
+// positions (hard gate), or every position (both-branch mode).
+SWI_DEV int far_count(const PrefillArgs& a, int b, int g) {
+  return a.all_rows ? a.N : a.cnt[b * a.G + g];
+}
+SWI_DEV int far_pos(const PrefillArgs& a, int b, int g, int k) {
+  return a.all_rows ? k : a.idx[(int64_t(b) * a.G + g) * a.N + k];
+}
 
 // Far-part schedule inside a.sched (int32):
 //   [0] total items  [1] 64-key blocks per chunk
@@ -279,7 +291,8 @@ SWI_DEV void band_tile(const PrefillArgs& a, char* buf0, char* buf1, int lin) {
     if (valid[t]) {
       T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok[t]) * a.Hq + h[t]) * D;
       store_row<Core::MD>(orow, c.acc_of(t), inv, g);
-      if (g == 0 && a.lse_s) a.lse_s[(int64_t(b) * a.Hq + h[t]) * a.N + tok[t]] = lse2;
+      if (g == 0) a.lse_s[(int64_t(b) * a.Hq + h[t]) * a.N + tok[t]] = lse2;
+      if (g == 0 && a.diffp) a.diffp[(int64_t(b) * a.Hq + h[t]) * a.N + tok[t]] = 0.f;
     }
   }
 }
@@ -290,7 +303,7 @@ SWI_DEV void band_tile(const PrefillArgs& a, char* buf0, char* buf1, int lin) {
 // (heads that share both the KV head and the gate group).  Its far keys are
 // [0, t_last - W] where t_last is its largest token; the tile is cut into
 // chunks of `cb` 64-key blocks, cb chosen so that the launch has about
-// kTargetItems chunks in total.
+// target_items chunks in total.
 // ---------------------------------------------------------------------------
 SWI_DEV int block_excl_scan(int v, int* sh, int& total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -331,7 +344,7 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
   // active tiles of a unit: ceil(cnt / tpt_far)
   auto active = [&](int bu) {
     const int b = bu / a.units, u = bu - b * a.units;
-    const int c = a.cnt[b * a.G + (u * a.hpu) / a.HG];
+    const int c = far_count(a, b, (u * a.hpu) / a.HG);
     return (c + a.tpt_far - 1) / a.tpt_far;
   };
   // pass 1: 64-key blocks of far work per tile (non-decreasing along the
@@ -341,11 +354,11 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
     const int bu = T_ / TT, t = T_ - bu * TT;
     const int b = bu / a.units, u = bu - b * a.units;
     const int g = (u * a.hpu) / a.HG;
-    const int c = a.cnt[b * a.G + g];
+    const int c = far_count(a, b, g);
     const int ntok = min(a.tpt_far, c - t * a.tpt_far);
     int blocks = 0;
     if (ntok > 0) {
-      const int tlast = a.idx[(int64_t(b) * a.G + g) * a.N + t * a.tpt_far + ntok - 1];
+      const int tlast = far_pos(a, b, g, t * a.tpt_far + ntok - 1);
       const int fh = tlast - a.W;
       if (fh >= 0) blocks = fh / kBN + 1;
     }
@@ -357,7 +370,7 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
   __syncthreads();
   long long total_blocks = 0;
   for (int w = 0; w < kSchedThreads / 64; ++w) total_blocks += red[w];
-  const int cb = int(max<long long>(kMinChunkBlocks, (total_blocks + kTargetItems - 1) / kTargetItems));
+  const int cb = int(max<long long>(kMinChunkBlocks, (total_blocks + a.target_items - 1) / a.target_items));
   // pass 2: chunks per tile
   for (int T_ = tid; T_ < nT; T_ += kSchedThreads) sv.n_items[T_] = (sv.n_items[T_] + cb - 1) / cb;
   __syncthreads();
@@ -437,10 +450,9 @@ SWI_DEV void far_item(const PrefillArgs& a, char* buf0, char* buf1, int item) {
   const int u = rem / a.far_tiles, t_ = rem - u * a.far_tiles;
   const int g_gate = (u * a.hpu) / a.HG;
   const int kvh = (u * a.hpu) / a.HK;
-  const int cnt = a.cnt[b * a.G + g_gate];
-  const int32_t* ix = a.idx + (int64_t(b) * a.G + g_gate) * a.N;
+  const int cnt = far_count(a, b, g_gate);
   const int ntok = min(a.tpt_far, cnt - t_ * a.tpt_far);
-  const int far_hi = ix[t_ * a.tpt_far + ntok - 1] - a.W;
+  const int far_hi = far_pos(a, b, g_gate, t_ * a.tpt_far + ntok - 1) - a.W;
   const int c0 = ch * cb * kBN;
   const int c1 = min(far_hi + 1, (ch + 1) * cb * kBN);  // keys [c0, c1)
 
@@ -456,7 +468,7 @@ SWI_DEV void far_item(const PrefillArgs& a, char* buf0, char* buf1, int item) {
     r[t] = wave * (kQR * TPW) + t * kQR + q;
     const int slot = r[t] / a.hpu, hh = r[t] - slot * a.hpu;
     valid[t] = slot < ntok;
-    tok[t] = valid[t] ? ix[t_ * a.tpt_far + slot] : 0;
+    tok[t] = valid[t] ? far_pos(a, b, g_gate, t_ * a.tpt_far + slot) : 0;
     h[t] = u * a.hpu + hh;
     lo[t] = c0;
     hi[t] = valid[t] ? min(tok[t] - a.W, c1 - 1) : -1;
@@ -497,15 +509,23 @@ struct TileQueue {
   int n, per;
   SWI_DEV int len(int x) const { return min(per, max(0, n - x * per)); }
 };
-// One thread: the next tile, from queue x or, once x is drained, the others.
-// The counters are shared by workgroups on all XCDs, whose L2 caches are
-// not coherent with each other: the increments are made at system scope,
-// which performs them past the L2s.
-SWI_DEV int grab_tile(int* queue, const TileQueue& tq, int& x) {
+// Claims on the tile queues (one thread).  The counters are shared by
+// workgroups on all XCDs, whose L2 caches are not coherent with each other:
+// the increments are made at system scope, which performs them past the
+// L2s, and their results take a memory round trip.  A claim is therefore
+// split: claim() issues the increment on queue x and returns the raw
+// position without waiting for it; resolve(), a block or more later (the
+// block barriers have drained the increment by then), turns it into a tile,
+// or, if queue x ran dry, claims from the other queues in turn (waiting).
+SWI_DEV int claim(int* queue, int x) {
+  return __hip_atomic_fetch_add(queue + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+SWI_DEV int resolve(int* queue, const TileQueue& tq, int& x, int p) {
   for (int k = 0; k < 8; ++k) {
-    const int p = __hip_atomic_fetch_add(queue + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     if (p < tq.len(x)) return x * tq.per + p;
+    if (k == 7) break;
     x = (x + 1) & 7;
+    p = claim(queue, x);
   }
   return -1;
 }
@@ -536,7 +556,7 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
   tq.n = a.band_tiles * a.B * a.Hkv;
   tq.per = (tq.n + 7) / 8;
   int qx = blockIdx.x & 7;  // workgroups are dealt to the 8 XCDs in turn
-  if (tid == 0) s_next = grab_tile(a.queue, tq, qx);
+  if (tid == 0) s_next = resolve(a.queue, tq, qx, claim(a.queue, qx));
   __syncthreads();
   int lin = __builtin_amdgcn_readfirstlane(s_next);
   if (lin < 0) return;
@@ -558,8 +578,8 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
   Dma::issue(buf0, static_cast<const T*>(a.K) + kv_off(t), static_cast<const T*>(a.V) + kv_off(t), rs,
              t.kb0, a.N, tid);
   int s = 0;  // blocks streamed so far: block s sits in buffer s % 2
-  int next_raw = -1;
-  if (tid == 0) next_raw = grab_tile(a.queue, tq, qx);
+  int next_raw = 0;  // thread 0: raw position of the pending claim on queue qx
+  if (tid == 0) next_raw = claim(a.queue, qx);
   bool q_pref = false;
   while (true) {
     const int tok = t.q0 + slot;
@@ -584,14 +604,14 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
       char* nxt = (s & 1) ? buf0 : buf1;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (n == pub && tid == 0) s_next = next_raw;
+      if (n == pub && tid == 0) s_next = resolve(a.queue, tq, qx, next_raw);
       if (t.nb < 2) __syncthreads();
       if (n == rd) {
         nlin = __builtin_amdgcn_readfirstlane(s_next);
         if (nlin >= 0) nt.set(a, nlin);
-        // claim the tile after that one now, so that the claim is back long
-        // before its id is published
-        if (tid == 0 && nlin >= 0) next_raw = grab_tile(a.queue, tq, qx);
+        // claim the tile after that one now; it is resolved when the next
+        // tile publishes it
+        if (tid == 0 && nlin >= 0) next_raw = claim(a.queue, qx);
       }
       if (n + 1 < t.nb)
         Dma::issue(nxt, Kb, Vb, rs, t.kb0 + (n + 1) * kBN, a.N, tid);
@@ -614,7 +634,8 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
       const int h = t.kvh * a.HK + hh;
       T* orow = static_cast<T*>(a.O) + ((int64_t(t.b) * a.N + tok) * a.Hq + h) * D;
       store_row<Core::MD>(orow, c.acc_of(0), inv, g);
-      if (g == 0 && a.lse_s) a.lse_s[(int64_t(t.b) * a.Hq + h) * a.N + tok] = lse2;
+      if (g == 0) a.lse_s[(int64_t(t.b) * a.Hq + h) * a.N + tok] = lse2;
+      if (g == 0 && a.diffp) a.diffp[(int64_t(t.b) * a.Hq + h) * a.N + tok] = 0.f;
     }
     if (nlin < 0) break;
     lin = nlin;
@@ -651,6 +672,20 @@ __global__ __launch_bounds__((TileCfg<T, D>::kWaves * 64), (TileCfg<T, D>::kMinW
   }
 }
 
+// Sum of squared differences of n channels.  Contraction is off so that
+// each difference is taken between the two rounded values.
+template <int n>
+SWI_DEV float sq_distance(const float (&x)[n], const float (&y)[n]) {
+#pragma clang fp contract(off)
+  float dd = 0.f;
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+    const float e = x[i] - y[i];
+    dd += e * e;
+  }
+  return dd;
+}
+
 // ---------------------------------------------------------------------------
 // Merge of the far tiles.  Work units are (tile with chunks, quarter of its
 // rows), taken from the schedule's list by a fixed grid; 8 threads share a
@@ -658,7 +693,9 @@ __global__ __launch_bounds__((TileCfg<T, D>::kWaves * 64), (TileCfg<T, D>::kMinW
 // are in flight (one thread per row walking its chunks one after another
 // left the kernel bound by load latency).  O_FULL of a row is the
 // log-sum-exp weighted sum of its window output and its chunks' partials,
-// taken in chunk order.
+// taken in chunk order.  In both-branch mode every row is merged: the
+// per-head squared distance between O_FULL and the window output is
+// written, and O_FULL replaces the window output only where the gate is 1.
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 256;
 constexpr int kMergeTPR = 8;  // threads per row
@@ -679,11 +716,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PrefillArgs a) {
     const int u = rem / a.far_tiles, t = rem - u * a.far_tiles;
     const int bu = b * a.units + u;
     const int g_gate = (u * a.hpu) / a.HG;
-    const int c = a.cnt[b * a.G + g_gate];
+    const int c = far_count(a, b, g_gate);
     const int ntok = min(a.tpt_far, c - t * a.tpt_far);
     const int slot = r / a.hpu, hh = r - slot * a.hpu;
+    // (the 8 threads of a row take every branch together)
     if (slot >= ntok) continue;
-    const int tok = a.idx[(int64_t(b) * a.G + g_gate) * a.N + t * a.tpt_far + slot];
+    const int tok = far_pos(a, b, g_gate, t * a.tpt_far + slot);
     if (tok < a.W) continue;
     const int h = u * a.hpu + hh;
     const float ls = a.lse_s[(int64_t(b) * a.Hq + h) * a.N + tok];
@@ -692,12 +730,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PrefillArgs a) {
       M = fmaxf(M, a.part_lse[int64_t(sv.item_of(bu, t, k, a.cmax)) * kRows + r]);
     T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D + c0;
     float wsum = fast_exp2(ls - M);
-    float o[CPT];
+    float os[CPT], o[CPT];
 #pragma unroll
     for (int i4 = 0; i4 < CPT / 4; ++i4) {
       const f32x4 v = load4(orow + i4 * 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[i4 * 4 + e] = wsum * v[e];
+      for (int e = 0; e < 4; ++e) {
+        os[i4 * 4 + e] = v[e];
+        o[i4 * 4 + e] = wsum * v[e];
+      }
     }
 #pragma unroll 2
     for (int k = 0; k < ni; ++k) {
@@ -715,114 +756,23 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PrefillArgs a) {
     }
     const float inv = 1.f / wsum;
 #pragma unroll
-    for (int i4 = 0; i4 < CPT / 4; ++i4) {
-      f32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = o[i4 * 4 + e] * inv;
-      store4(orow + i4 * 4, v);
+    for (int e = 0; e < CPT; ++e) o[e] *= inv;
+    bool write = true;
+    if (a.diffp) {
+      // squared distance to the window output, summed over the row's 8
+      // threads (lanes 8k .. 8k+7 of the wave) in a fixed order
+      float dd = sq_distance<CPT>(o, os);
+      dd += __shfl_xor(dd, 1, kMergeTPR);
+      dd += __shfl_xor(dd, 2, kMergeTPR);
+      dd += __shfl_xor(dd, 4, kMergeTPR);
+      if (c0 == 0) a.diffp[(int64_t(b) * a.Hq + h) * a.N + tok] = dd;
+      write = a.gate[(int64_t(b) * a.N + tok) * a.G + h / a.HG] != 0;
     }
-  }
-}
-
-// Sum of squared differences of this lane's channels.  Contraction is off so
-// that the difference is taken between the two rounded outputs (a fused
-// multiply-subtract would leave the rounding error of one product behind
-// even when both branches saw the same keys).
-template <int MD>
-SWI_DEV float sq_distance(const f32x16 (&x)[MD], const f32x16 (&y)[MD]) {
-#pragma clang fp contract(off)
-  float dd = 0.f;
+    if (write) {
 #pragma unroll
-  for (int md = 0; md < MD; ++md)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = x[md][i] - y[md][i];
-      dd += e * e;
+      for (int i4 = 0; i4 < CPT / 4; ++i4)
+        store4(orow + i4 * 4, f32x4{o[i4 * 4], o[i4 * 4 + 1], o[i4 * 4 + 2], o[i4 * 4 + 3]});
     }
-  return dd;
-}
-
-// ---------------------------------------------------------------------------
-// Both-branch mode: causal pass per tile, window keys first (snapshot), then
-// the far keys.  Grid (band_tiles, B*Hkv), heaviest tiles launched first.
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 1) void fused_kernel(PrefillArgs a) {
-  using Core = typename CoreSel<T, D>::type;
-  constexpr int MD = Core::MD;
-  __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
-  const int tile = a.band_tiles - 1 - int(blockIdx.x);
-  const int b = blockIdx.y / a.Hkv, kvh = blockIdx.y - b * a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = lane & 31, g = lane >> 5;
-  const int q0 = tile * a.tpt_band;
-  const int qlast = min(a.N - 1, q0 + a.tpt_band - 1);
-  const int r = wave * kQR + q;
-  const int slot = r / a.HK, hh = r - slot * a.HK;
-  const int tok = q0 + slot;
-  const bool valid = slot < a.tpt_band && tok < a.N;
-  const int h = kvh * a.HK + hh;
-  // phase A: window keys; phase B: far keys [0, tok-W]
-  const int loA = valid ? max(0, tok - a.W + 1) : 0, hiA = valid ? tok : -1;
-  const int loB = 0, hiB = valid ? tok - a.W : -1;
-  WaveBounds wa, wbb;
-  wa.init(valid, loA, hiA);
-  wbb.init(valid, loB, hiB);
-  const int kbA = (max(0, q0 - a.W + 1) / kBN) * kBN;
-  const int nA = (qlast - kbA) / kBN + 1;
-  const int nB = qlast >= a.W ? (qlast - a.W) / kBN + 1 : 0;
-
-  Core c;
-  c.init();
-  const T* Qp = static_cast<const T*>(a.Q);
-  c.load_q(valid ? Qp + ((int64_t(b) * a.N + tok) * a.Hq + h) * D : nullptr, g);
-  const T* Kb = static_cast<const T*>(a.K) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
-  const T* Vb = static_cast<const T*>(a.V) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
-  const int64_t rs = int64_t(a.Hkv) * D;
-  f32x16 snap[MD];
-  KVLoader<T, D, kThreads> ld;
-  ld.load(Kb, Vb, rs, kbA, a.N, tid);
-  for (int n = 0; n < nA + nB; ++n) {
-    const bool phaseB = n >= nA;
-    const int kb = phaseB ? (n - nA) * kBN : kbA + n * kBN;
-    if (n == nA) {  // window done: snapshot O_SWA
-      float lse_unused;
-      const float inv_s = finish_row(c.m, c.l, lse_unused);
-#pragma unroll
-      for (int md = 0; md < MD; ++md) snap[md] = c.acc[md] * inv_s;
-    }
-    __syncthreads();
-    ld.store(lds, tid);
-    __syncthreads();
-    if (n + 1 < nA + nB) {
-      const int nk = (n + 1 >= nA) ? (n + 1 - nA) * kBN : kbA + (n + 1) * kBN;
-      ld.load(Kb, Vb, rs, nk, a.N, tid);
-    }
-    if (!phaseB) {
-      if (wa.needed(kb)) c.block(lds, kb, wa.masked(kb), loA, hiA, a.sl2, q, g);
-    } else {
-      if (wbb.needed(kb)) c.block(lds, kb, wbb.masked(kb), loB, hiB, a.sl2, q, g);
-    }
-  }
-  float lse2;
-  const float inv = finish_row(c.m, c.l, lse2);
-  if (nB == 0) {
-#pragma unroll
-    for (int md = 0; md < MD; ++md) snap[md] = c.acc[md] * inv;
-  }
-  f32x16 full[MD];
-#pragma unroll
-  for (int md = 0; md < MD; ++md) full[md] = c.acc[md] * inv;
-  float dd = sq_distance<MD>(full, snap);
-  dd += xor32(dd);
-  if (valid) {
-    const int gg = h / a.HG;
-    const bool full_sel = a.gate[(int64_t(b) * a.N + tok) * a.G + gg] != 0;
-    T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D;
-#pragma unroll
-    for (int md = 0; md < MD; ++md) full[md] = full_sel ? full[md] : snap[md];
-    store_row<MD>(orow, full, 1.f, g);
-    if (g == 0) a.diffp[(int64_t(b) * a.Hq + h) * a.N + tok] = dd;
   }
 }
 
@@ -866,29 +816,29 @@ bool plan_prefill(const PrefillShape& sh, PrefillPlan* p) {
   p->band_tiles = (sh.N + p->tpt_band - 1) / p->tpt_band;
   p->far_tiles = (sh.N + p->tpt_far - 1) / p->tpt_far;
   const long long nT = (long long)sh.B * p->units * p->far_tiles;
-  const long long max_items = kTargetItems + nT;
+  p->target_items = sh.both_branch ? kTargetItemsAll : kTargetItems;
+  const long long max_items = p->target_items + nT;
   if (max_items > INT_MAX / kRows) return false;
   p->max_items = int(max_items);
   // chunks per tile <= ceil(ceil(N / 64) / kMinChunkBlocks)
   p->cmax = ((sh.N + kBN - 1) / kBN + kMinChunkBlocks - 1) / kMinChunkBlocks + 1;
   const size_t rowsN = size_t(sh.B) * sh.Hq * sh.N;
   size_t off = 0;
-  p->off_lse = p->off_sched = p->off_queue = p->off_part_o = p->off_part_lse = p->off_diffp = 0;
-  if (!sh.both_branch) {
-    p->off_lse = off;
-    off = align_up(off + rowsN * 4);
-    p->off_sched = off;
-    const size_t nbu = size_t(sh.B) * p->units;
-    const size_t sched_ints =
-        2 + size_t(nT) + nbu + 2 * nbu * p->cmax + 2 * size_t(max_items) + nbu + 1 + size_t(nT);
-    off = align_up(off + sched_ints * 4);
-    p->off_queue = off;
-    off = align_up(off + 8 * 4);
-    p->off_part_o = off;
-    off = align_up(off + size_t(max_items) * kRows * sh.d * (sh.f32 ? 4 : 2));
-    p->off_part_lse = off;
-    off = align_up(off + size_t(max_items) * kRows * 4);
-  } else {
+  p->off_lse = off;
+  off = align_up(off + rowsN * 4);
+  p->off_sched = off;
+  const size_t nbu = size_t(sh.B) * p->units;
+  const size_t sched_ints =
+      2 + size_t(nT) + nbu + 2 * nbu * p->cmax + 2 * size_t(max_items) + nbu + 1 + size_t(nT);
+  off = align_up(off + sched_ints * 4);
+  p->off_queue = off;
+  off = align_up(off + 8 * 4);
+  p->off_part_o = off;
+  off = align_up(off + size_t(max_items) * kRows * sh.d * (sh.f32 ? 4 : 2));
+  p->off_part_lse = off;
+  off = align_up(off + size_t(max_items) * kRows * 4);
+  p->off_diffp = 0;
+  if (sh.both_branch) {
     p->off_diffp = off;
     off = align_up(off + rowsN * 4);
   }
@@ -902,42 +852,32 @@ static hipError_t run_prefill(const PrefillShape& sh, const PrefillPlan& p, Pref
   hipError_t e;
 #define SWI_TRY(x)                    \
   if ((e = (x)) != hipSuccess) return e;
-  if (!sh.both_branch) {
-    SWI_TRY(mark(ev, 0, s));
-    hipLaunchKernelGGL(far_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, a);
-    SWI_TRY(hipGetLastError());
-    SWI_TRY(mark(ev, 1, s));
-    constexpr int nt = TileCfg<T, D>::kWaves * 64;
-    const int band_total = p.band_tiles * sh.B * sh.Hkv;
-    if (TileCfg<T, D>::kDma) {  // resident window workers: kMinWG per CU
-      int cus = 0;
-      SWI_TRY(compute_units(&cus));
-      const int workers = TileCfg<T, D>::kMinWG * cus;
-      a.band_grid = band_total < workers ? band_total : workers;
-    } else {
-      a.band_grid = band_total;
-    }
-    hipLaunchKernelGGL((attn_kernel<T, D>), dim3(a.far_grid + 8 * ((a.band_grid + 7) / 8)), dim3(nt), 0,
-                       s, a);
-    SWI_TRY(hipGetLastError());
-    SWI_TRY(mark(ev, 2, s));
-    {
-      int cus = 0;
-      SWI_TRY(compute_units(&cus));
-      hipLaunchKernelGGL((merge_kernel<T, D>), dim3(4 * cus), dim3(kMergeThreads), 0, s, a);
-    }
-    SWI_TRY(hipGetLastError());
-    SWI_TRY(mark(ev, 3, s));
+  SWI_TRY(mark(ev, 0, s));
+  hipLaunchKernelGGL(far_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, a);
+  SWI_TRY(hipGetLastError());
+  SWI_TRY(mark(ev, 1, s));
+  constexpr int nt = TileCfg<T, D>::kWaves * 64;
+  const int band_total = p.band_tiles * sh.B * sh.Hkv;
+  int cus = 0;
+  SWI_TRY(compute_units(&cus));
+  if (TileCfg<T, D>::kDma) {  // resident window workers: kMinWG per CU
+    const int workers = TileCfg<T, D>::kMinWG * cus;
+    a.band_grid = band_total < workers ? band_total : workers;
   } else {
-    SWI_TRY(mark(ev, 0, s));
-    hipLaunchKernelGGL((fused_kernel<T, D>), dim3(p.band_tiles, sh.B * sh.Hkv), dim3(kThreads),
-                       0, s, a);
-    SWI_TRY(hipGetLastError());
-    SWI_TRY(mark(ev, 1, s));
+    a.band_grid = band_total;
+  }
+  hipLaunchKernelGGL((attn_kernel<T, D>), dim3(a.far_grid + 8 * ((a.band_grid + 7) / 8)), dim3(nt), 0,
+                     s, a);
+  SWI_TRY(hipGetLastError());
+  SWI_TRY(mark(ev, 2, s));
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3(4 * cus), dim3(kMergeThreads), 0, s, a);
+  SWI_TRY(hipGetLastError());
+  SWI_TRY(mark(ev, 3, s));
+  if (sh.both_branch) {
     const long long n = (long long)sh.B * sh.N;
     hipLaunchKernelGGL(diff_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, a);
     SWI_TRY(hipGetLastError());
-    SWI_TRY(mark(ev, 2, s));
+    SWI_TRY(mark(ev, 4, s));
   }
 #undef SWI_TRY
   return hipSuccess;
@@ -956,12 +896,14 @@ hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const vo
   a.gate = gate;
   a.idx = idx;
   a.cnt = cnt;
-  a.lse_s = sh.both_branch ? nullptr : reinterpret_cast<float*>(w + p.off_lse);
-  a.sched = sh.both_branch ? nullptr : reinterpret_cast<int32_t*>(w + p.off_sched);
-  a.queue = sh.both_branch ? nullptr : reinterpret_cast<int*>(w + p.off_queue);
-  a.part_o = sh.both_branch ? nullptr : static_cast<void*>(w + p.off_part_o);
-  a.part_lse = sh.both_branch ? nullptr : reinterpret_cast<float*>(w + p.off_part_lse);
+  a.lse_s = reinterpret_cast<float*>(w + p.off_lse);
+  a.sched = reinterpret_cast<int32_t*>(w + p.off_sched);
+  a.queue = reinterpret_cast<int*>(w + p.off_queue);
+  a.part_o = static_cast<void*>(w + p.off_part_o);
+  a.part_lse = reinterpret_cast<float*>(w + p.off_part_lse);
   a.diffp = sh.both_branch ? reinterpret_cast<float*>(w + p.off_diffp) : nullptr;
+  a.all_rows = sh.both_branch ? 1 : 0;
+  a.target_items = p.target_items;
   a.diff = diff;
   a.B = sh.B;
   a.N = sh.N;
