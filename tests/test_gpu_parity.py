@@ -177,6 +177,40 @@ def test_prefill_both_branch(Hq, Hkv, G, W):
     assert np.all(diff[:, :W] == 0.0)  # identical key sets before the window fills
 
 
+BOTH_CASES = [
+    # B, N, Hq, Hkv, G, d, W, dtype
+    (2, 300, 4, 2, 2, 64, 50, "f32"),      # float32 path; window output stored exactly
+    (2, 700, 8, 1, 4, 64, 64, "bf16"),     # gate groups inside a KV group (2 heads per unit)
+    (1, 600, 4, 2, 1, 128, 1000, "bf16"),  # W > N: no row has far keys, diff all 0
+    (1, 1000, 8, 4, 2, 128, 333, "bf16"),  # ragged N and W
+]
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,G,d,W,dtype", BOTH_CASES)
+def test_prefill_both_branch_shapes(B, N, Hq, Hkv, G, d, W, dtype):
+    Q, K, V = _qkv(13, B, N, Hq, Hkv, d, dtype)
+    gate = (np.random.default_rng(14).random((B, N, G)) < 0.3).astype(np.uint8)
+    O, diff = _gpu_prefill(Q, K, V, gate, W, dtype, both=True)
+    ref = oracle.prefill(Q, K, V, gate, W, both_branch=True)
+    err = max_abs(O, ref["O"])
+    derr = np.abs(diff - ref["diff"])
+    tol = diff_tolerance(ref["diff"], Hq * d, TOL[dtype])
+    say(f"both-branch {dtype} B={B} N={N} Hq={Hq} Hkv={Hkv} G={G} d={d} W={W}: O max-abs {err:.3e}; "
+        f"diff max-abs {derr.max():.3e}")
+    assert err <= TOL[dtype]
+    assert np.all(derr <= tol)
+    assert np.all(diff[:, :min(W, N)] == 0.0)
+
+
+def test_prefill_both_branch_deterministic():
+    B, N, Hq, Hkv, G, d, W = 1, 900, 8, 2, 1, 128, 128
+    Q, K, V = _qkv(15, B, N, Hq, Hkv, d, "bf16")
+    gate = (np.random.default_rng(16).random((B, N, G)) < 0.2).astype(np.uint8)
+    a, da = _gpu_prefill(Q, K, V, gate, W, "bf16", both=True)
+    b, db = _gpu_prefill(Q, K, V, gate, W, "bf16", both=True)
+    assert np.array_equal(a, b) and np.array_equal(da, db)
+
+
 def test_prefill_deterministic():
     B, N, Hq, Hkv, G, d, W = 1, 900, 8, 2, 1, 128, 128
     Q, K, V = _qkv(8, B, N, Hq, Hkv, d, "bf16")
