@@ -23,7 +23,8 @@ Pins: every function below is checked by the CPU tests against something
 other than itself (the printed W=4 table, W>=N equals causal attention,
 W=1 returns V, all-ones / all-zeros gates against torch's CPU
 scaled_dot_product_attention in float64, a pure-Python brute force on tiny
-inputs, closed forms for the router, decode equal to the last prefill row).
+inputs, closed forms for the router, decode equal to the last prefill row,
+hand-computed values and exact ratios for the regulariser).
 No function here is parity-unpinned.
 """
 from __future__ import annotations
@@ -38,6 +39,8 @@ __all__ = [
     "attend_rows",
     "prefill",
     "decode",
+    "softplus",
+    "regularizer",
 ]
 
 NEAR_THRESHOLD = 1e-5
@@ -266,3 +269,36 @@ def decode(q, Kc, Vc, cache_len, gate, W, scale=None):
                                  np.asarray(Vc[b, : i + 1, kv]), [lo], [hi], scale)
             o[b, h], lse[b, h] = ob[0], lb[0]
     return {"o": o, "lse": lse}
+
+
+# ---------------------------------------------------------------------------
+# Adaptive regulariser  ([SwiAttn] section 2, adaptive regulariser paragraph)
+# ---------------------------------------------------------------------------
+def softplus(x):
+    """log(1 + e^x), evaluated as max(x, 0) + log1p(e^-|x|) (no overflow)."""
+    x = np.asarray(x, np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def regularizer(z, nll, diff, gamma_base=1e-3, eps=0.1, alpha=100.0):
+    """Per-token adaptive regulariser of one layer.
+
+    [SwiAttn] section 2, adaptive regulariser paragraph: the loss of token t
+    is gamma_t * softplus(R(h_t)) with the weight
+    gamma_t = gamma_base / (eps + NLL(t) + alpha * ||o_FULL - o_SWA||^2),
+    and the hyperparameters gamma_base = 1e-3, eps = 0.1, alpha = 100.
+
+    z     [B,N,G]  router logits R(h_t) (the values route() thresholds)
+    nll   [B,N]    the token's negative log-likelihood (an input here)
+    diff  [B,N]    ||o_FULL - o_SWA||^2 of the token (prefill's both-branch
+                   output: summed over heads and channels)
+    Returns L [B,N,G] float64.
+
+    Reading: with G > 1 gate groups (the pages have one router per token)
+    every group's logit is weighted by the token's gamma, which uses the
+    distance summed over all heads.  The pages' loss is this value per token
+    and layer; how it is reduced over tokens and layers is not part of it.
+    """
+    z = np.asarray(z, np.float64)
+    gamma = gamma_base / (eps + np.asarray(nll, np.float64) + alpha * np.asarray(diff, np.float64))
+    return gamma[..., None] * softplus(z)

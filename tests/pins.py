@@ -244,6 +244,42 @@ def check_compact():
             assert np.all(idx[b, g, len(pos):] == -1)
 
 
+def check_regularizer_hand_values():
+    """[SwiAttn] section 2, adaptive regulariser: values worked by hand with
+    gamma_base = 1e-3, eps = 0.1, alpha = 100.
+      z = 0, NLL = 0.9, d = 0:      gamma = 1e-3 / 1.0 = 1e-3, softplus(0) = ln 2
+      z = 0, NLL = 0, d = 0.009:    alpha*d = 0.9, the same gamma and value
+      z = ln(e - 1), NLL = 1.9:     softplus = ln e = 1, gamma = 1e-3 / 2
+      z = 50:                       softplus(50) = 50 + ln(1 + e^-50) = 50 to double precision
+      z = -50:                      softplus(-50) = ln(1 + e^-50) = e^-50 (1 - e^-50/2 ...)
+      z = 800:                      softplus(800) = 800 (no overflow)"""
+    z = np.array([0.0, 0.0, math.log(math.e - 1.0), 50.0, -50.0, 800.0])
+    nll = np.array([0.9, 0.0, 1.9, 0.9, 0.9, 0.9])
+    d = np.array([0.0, 0.009, 0.0, 0.0, 0.0, 0.0])
+    L = ref.regularizer(z[None, :, None], nll[None], d[None])[0, :, 0]
+    want = [1e-3 * math.log(2.0), 1e-3 * math.log(2.0), 5e-4, 1e-3 * 50.0,
+            1e-3 * math.exp(-50.0), 1e-3 * 800.0]
+    for got, w in zip(L, want):
+        assert abs(got - w) <= 1e-12 * abs(w), (got, w)
+
+
+def check_regularizer_ratios():
+    """gamma is inversely proportional to eps + NLL + alpha*d, so
+    L(d) / L(0) = (eps + NLL) / (eps + NLL + alpha d) for any logit, L scales
+    with gamma_base, and every gate group of a token shares one gamma."""
+    rng = np.random.default_rng(21)
+    z = rng.normal(0.0, 3.0, (2, 40, 3))
+    nll = rng.uniform(0.0, 5.0, (2, 40))
+    d = rng.uniform(0.0, 0.2, (2, 40))
+    L = ref.regularizer(z, nll, d)
+    L0 = ref.regularizer(z, nll, np.zeros_like(d))
+    assert np.allclose(L / L0, ((0.1 + nll) / (0.1 + nll + 100.0 * d))[..., None], rtol=1e-12, atol=0)
+    assert np.allclose(ref.regularizer(z, nll, d, gamma_base=3e-3), 3.0 * L, rtol=1e-12, atol=0)
+    # ratio across groups of one token = ratio of the softplus values
+    sp = np.log1p(np.exp(z[..., 1])) / np.log1p(np.exp(z[..., 0]))
+    assert np.allclose(L[..., 1] / L[..., 0], sp, rtol=1e-12, atol=0)
+
+
 ALL_PINS = [
     check_w4_key_ranges,
     check_w4_attention_weights,
@@ -257,4 +293,6 @@ ALL_PINS = [
     check_convex_hull,
     check_router_closed_form,
     check_compact,
+    check_regularizer_hand_values,
+    check_regularizer_ratios,
 ]

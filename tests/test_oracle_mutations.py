@@ -77,3 +77,32 @@ def test_router_mutants_caught(monkeypatch):
         monkeypatch.setattr(ref, "route", m)
         with pytest.raises(AssertionError):
             pins.check_router_closed_form()
+
+
+def test_regularizer_mutants_caught(monkeypatch):
+    def alpha_on_nll(z, nll, diff, gamma_base=1e-3, eps=0.1, alpha=100.0):
+        g = gamma_base / (eps + alpha * np.asarray(nll) + np.asarray(diff))
+        return g[..., None] * ref.softplus(z)
+
+    def no_eps(z, nll, diff, gamma_base=1e-3, eps=0.1, alpha=100.0):
+        g = gamma_base / (np.asarray(nll) + alpha * np.asarray(diff))
+        return g[..., None] * ref.softplus(z)
+
+    def sigmoid_not_softplus(z, nll, diff, gamma_base=1e-3, eps=0.1, alpha=100.0):
+        g = gamma_base / (eps + np.asarray(nll) + alpha * np.asarray(diff))
+        return g[..., None] / (1.0 + np.exp(-np.asarray(z, np.float64)))
+
+    def gamma_multiplies(z, nll, diff, gamma_base=1e-3, eps=0.1, alpha=100.0):
+        g = gamma_base * (eps + np.asarray(nll) + alpha * np.asarray(diff))
+        return g[..., None] * ref.softplus(z)
+
+    def naive_softplus(x):
+        with np.errstate(over="ignore"):
+            return np.log(1.0 + np.exp(np.asarray(x, np.float64)))
+
+    for m in (alpha_on_nll, no_eps, sigmoid_not_softplus, gamma_multiplies):
+        monkeypatch.setattr(ref, "regularizer", m)
+        assert _run_all_pins() > 0, m.__name__
+    monkeypatch.undo()
+    monkeypatch.setattr(ref, "softplus", naive_softplus)
+    assert _run_all_pins() > 0, "naive softplus"
