@@ -249,7 +249,8 @@ def main():
                            "traffic": traffic.get(PROFILE_NAMES[name])}
     dominant = max(kern, key=lambda n: t[n])
 
-    both = both_branch_run(swa, Q, K, V, gate, W, args.both_steps) if args.both_steps > 0 else None
+    both = (both_branch_run(swa, Q, K, V, gate, W, args.both_steps, H, r, bias)
+            if args.both_steps > 0 else None)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -291,11 +292,14 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def both_branch_run(swa, Q, K, V, gate, W, steps):
+def both_branch_run(swa, Q, K, V, gate, W, steps, H, r, bias):
     """Both-branch prefill on the same inputs (outside the timed steps): every
-    row takes both branches and the per-token distance is written.  Useful
-    work is the full causal branch (the window branch's keys are a subset of
-    it): 4*d*Hq*sum_i (i+1) FLOP."""
+    row takes both branches and the per-token distance is written; then the
+    adaptive regulariser on that distance, the router's logits and a seeded
+    synthetic NLL (uniform in [0, 6]).  Useful work of the prefill is the
+    full causal branch (the window branch's keys are a subset of it):
+    4*d*Hq*sum_i (i+1) FLOP; the regulariser moves 16 bytes per token and
+    gate group."""
     import torch
     B, N, Hq, d = Q.shape
     dev = Q.device
@@ -304,26 +308,35 @@ def both_branch_run(swa, Q, K, V, gate, W, steps):
                      dtype=torch.uint8, device=dev)
     O = torch.empty_like(Q)
     diff = torch.empty((B, N), dtype=torch.float32, device=dev)
+    z = swa.route(H, r, bias, want_z=True)[3]
+    nll = torch.from_numpy(np.random.default_rng(17).uniform(0.0, 6.0, (B, N)).astype(np.float32)).to(dev)
+    loss = torch.empty_like(z)
     swa.prefill(Q, K, V, gate, W, both_branch=True, out=O, diff=diff, workspace=ws)
+    swa.regularizer(z, nll, diff, out=loss)
     torch.cuda.synchronize()
     sets = []
     for _ in range(steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         for e in ev:
             e.record()
         sets.append(ev)
     torch.cuda.synchronize()
     for ev in sets:
-        swa.prefill(Q, K, V, gate, W, both_branch=True, out=O, diff=diff, workspace=ws, events=ev)
+        swa.prefill(Q, K, V, gate, W, both_branch=True, out=O, diff=diff, workspace=ws, events=ev[:5])
+        swa.regularizer(z, nll, diff, out=loss)
+        ev[5].record()
     torch.cuda.synchronize()
-    stage = [float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in sets])) for i in range(4)]
-    ms = sum(stage)
+    stage = [float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in sets])) for i in range(5)]
+    ms = sum(stage[:4])
     flop = 4.0 * d * Hq * B * N * (N + 1) / 2
+    reg_bytes = 4 * (2 * z.numel() + 2 * B * N)
     return {"ms": round(ms, 4), "useful_tflop": round(flop / 1e12, 4),
             "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
             "frac_of_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "kernel_ms": {"far_schedule": round(stage[0], 4), "attn": round(stage[1], 4),
-                          "merge": round(stage[2], 4), "diff": round(stage[3], 4)}}
+                          "merge": round(stage[2], 4), "diff": round(stage[3], 4)},
+            "regularizer": {"ms": round(stage[4], 4), "bytes": reg_bytes,
+                            "GB_per_s": round(reg_bytes / (stage[4] * 1e-3) / 1e9, 1)}}
 
 
 def cpu_baseline(pre, W, budget_s):

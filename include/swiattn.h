@@ -89,6 +89,29 @@ int swiattn_route(const void* H, const void* r, const float* bias, uint8_t* gate
                   int G, swiattn_dtype_t dtype, swiattn_stream_t stream);
 
 /*
+ * swiattn_regularizer - adaptive regulariser of one layer, per token.
+ * (SwiAttn report, section 2, adaptive regulariser paragraph.)
+ *
+ *   z     [B,N,G]  float  router logits R(h_t) (swiattn_route's z_out)
+ *   nll   [B,N]    float  the token's negative log-likelihood
+ *   diff  [B,N]    float  ||o_FULL - o_SWA||^2 of the token (swiattn_prefill's
+ *                         both-branch output)
+ *   loss  [B,N,G]  float  out: gamma_t * softplus(z) with
+ *                         gamma_t = gamma_base / (eps + nll + alpha * diff)
+ *
+ * The pages use gamma_base = 1e-3, eps = 0.1, alpha = 100.  Every group's
+ * logit of a token shares the token's gamma.  Computed in float32;
+ * softplus(x) = max(x, 0) + log1p(e^-|x|).  Device pointers, caller-owned;
+ * loss must not overlap the inputs.  NLL and diff are expected to be >= 0
+ * (the denominator is then at least eps).
+ * Errors: INVALID_ARG for B, N, G < 1, a NULL pointer, eps <= 0, alpha < 0
+ * or a non-finite parameter.
+ */
+int swiattn_regularizer(const float* z, const float* nll, const float* diff, float* loss, int B,
+                        int N, int G, float gamma_base, float eps, float alpha,
+                        swiattn_stream_t stream);
+
+/*
  * swiattn_prefill_workspace_size - bytes of device workspace that
  * swiattn_prefill needs for these sizes (an upper bound over every gate).
  * Returns 0 if the arguments are invalid.

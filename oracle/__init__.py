@@ -10,6 +10,8 @@ from .swiattn_ref import (  # noqa: F401
     decode,
     full_key_range,
     prefill,
+    regularizer,
     route,
+    softplus,
     swa_key_range,
 )

@@ -12,5 +12,6 @@ from .binding import (  # noqa: F401
     lib,
     prefill,
     prefill_workspace_size,
+    regularizer,
     route,
 )

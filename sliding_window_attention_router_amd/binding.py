@@ -19,6 +19,7 @@ __all__ = [
     "SwiAttnError",
     "lib",
     "route",
+    "regularizer",
     "prefill",
     "decode",
     "prefill_workspace_size",
@@ -42,6 +43,7 @@ SYMBOLS = {
     "swiattn_decode": (_i32, [_vp] * 6 + [_i32] * 7 + [_f32, _i32, _vp, _sz, _vp]),
     "swiattn_prefill_ex": (_i32, [_vp] * 8 + [_i32] * 7 + [_f32, _i32, _u32, _vp, _sz, _vp, _vp]),
     "swiattn_decode_ex": (_i32, [_vp] * 6 + [_i32] * 7 + [_f32, _i32, _vp, _sz, _vp, _vp]),
+    "swiattn_regularizer": (_i32, [_vp] * 4 + [_i32] * 3 + [_f32] * 3 + [_vp]),
     "swiattn_strerror": (ctypes.c_char_p, [_i32]),
     "swiattn_version": (ctypes.c_char_p, []),
 }
@@ -166,6 +168,23 @@ def route(H=None, r=None, bias=None, *, gate=None, want_z=False, out=None):
                          B, N, hidden, G, code, _stream(dev))
     _check(rc, "swiattn_route")
     return gate, idx, cnt, z
+
+
+def regularizer(z, nll, diff, *, gamma_base=1e-3, eps=0.1, alpha=100.0, out=None):
+    """Adaptive regulariser per token: gamma_base / (eps + nll + alpha*diff)
+    * softplus(z).  z [B,N,G] (router logits), nll [B,N], diff [B,N] (the
+    both-branch distance), all float32 on one device.  Returns loss [B,N,G]."""
+    _need(z, "z", dtype=torch.float32)
+    B, N, G = z.shape
+    dev = z.device
+    _need(nll, "nll", shape=(B, N), dtype=torch.float32, device=dev)
+    _need(diff, "diff", shape=(B, N), dtype=torch.float32, device=dev)
+    loss = out if out is not None else torch.empty((B, N, G), dtype=torch.float32, device=dev)
+    _need(loss, "loss", shape=(B, N, G), dtype=torch.float32, device=dev)
+    rc = lib().swiattn_regularizer(_p(z), _p(nll), _p(diff), _p(loss), B, N, G, float(gamma_base),
+                                   float(eps), float(alpha), _stream(dev))
+    _check(rc, "swiattn_regularizer")
+    return loss
 
 
 def prefill_workspace_size(B, N, Hq, Hkv, G, d, W, dtype=torch.bfloat16, both_branch=False):

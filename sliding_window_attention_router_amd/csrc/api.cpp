@@ -92,6 +92,20 @@ int swiattn_route(const void* H, const void* r, const float* bias, uint8_t* gate
   return hip_rc(swi::launch_compact(gate, idx, cnt, B, N, G, s));
 }
 
+int swiattn_regularizer(const float* z, const float* nll, const float* diff, float* loss, int B,
+                        int N, int G, float gamma_base, float eps, float alpha,
+                        swiattn_stream_t stream) {
+  if (B < 1 || N < 1 || G < 1) return SWIATTN_ERR_INVALID_ARG;
+  if (!z || !nll || !diff || !loss) return SWIATTN_ERR_INVALID_ARG;
+  // eps > 0 and alpha >= 0 keep the weight's denominator positive for
+  // non-negative NLL and distance; NaN fails every comparison
+  if (!(eps > 0.f) || !(alpha >= 0.f) || !(gamma_base == gamma_base) ||
+      !(eps < 3.4e38f) || !(alpha < 3.4e38f) || !(gamma_base < 3.4e38f && gamma_base > -3.4e38f))
+    return SWIATTN_ERR_INVALID_ARG;
+  return hip_rc(swi::launch_regularizer(z, nll, diff, loss, B, N, G, gamma_base, eps, alpha,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t swiattn_prefill_workspace_size(int B, int N, int Hq, int Hkv, int G, int d, int W,
                                       swiattn_dtype_t dtype, unsigned flags) {
   swi::PrefillShape sh;

@@ -13,6 +13,11 @@ hipError_t launch_route(const void* H, const void* r, const float* bias, uint8_t
 hipError_t launch_compact(const uint8_t* gate, int32_t* idx, int32_t* cnt, int B, int N, int G,
                           hipStream_t s);
 
+// ---- adaptive regulariser ----------------------------------------------
+hipError_t launch_regularizer(const float* z, const float* nll, const float* diff, float* loss,
+                              int B, int N, int G, float gamma_base, float eps, float alpha,
+                              hipStream_t s);
+
 // ---- prefill ------------------------------------------------------------
 struct PrefillShape {
   int B, N, Hq, Hkv, G, d, W;

@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("swiattn_route", "swiattn_prefill", "swiattn_decode", "swiattn_prefill_workspace_size",
-              "swiattn_decode_workspace_size", "swiattn_strerror", "swiattn_prefill_ex", "swiattn_decode_ex"):
+              "swiattn_decode_workspace_size", "swiattn_strerror", "swiattn_prefill_ex", "swiattn_decode_ex",
+              "swiattn_regularizer"):
         assert n in names
 
 
@@ -128,4 +129,16 @@ def test_route_rejects_invalid_arguments(lib, kw):
     a.update(kw)
     rc = lib.swiattn_route(a["H"], a["r"], a["bias"], a["gate"], a["z"], a["idx"], a["cnt"], a["B"], a["N"],
                            a["hidden"], a["G"], a["dt"], a["stream"])
+    assert rc == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(G=0), dict(z=None), dict(nll=None), dict(diff=None),
+                                dict(loss=None), dict(eps=0.0), dict(eps=-1.0), dict(alpha=-1.0),
+                                dict(eps=float("nan")), dict(alpha=float("inf")), dict(gamma_base=float("nan"))])
+def test_regularizer_rejects_invalid_arguments(lib, kw):
+    a = dict(z=FAKE, nll=FAKE, diff=FAKE, loss=FAKE, B=1, N=10, G=1, gamma_base=1e-3, eps=0.1, alpha=100.0,
+             stream=None)
+    a.update(kw)
+    rc = lib.swiattn_regularizer(a["z"], a["nll"], a["diff"], a["loss"], a["B"], a["N"], a["G"],
+                                 a["gamma_base"], a["eps"], a["alpha"], a["stream"])
     assert rc == INVALID

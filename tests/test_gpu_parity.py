@@ -211,6 +211,60 @@ def test_prefill_both_branch_deterministic():
     assert np.array_equal(a, b) and np.array_equal(da, db)
 
 
+# ---------------------------------------------------------------- regulariser
+@pytest.mark.parametrize("B,N,G", [(2, 1000, 3), (1, 1, 1), (1, 32768, 1), (3, 777, 2)])
+def test_regularizer(B, N, G):
+    rng = np.random.default_rng(31 + N)
+    z = rng.normal(0.0, 4.0, (B, N, G)).astype(np.float32)
+    z.reshape(-1)[:6] = [0.0, 800.0, -800.0, 50.0, -50.0, -100.0][: z.size]
+    nll = rng.uniform(0.0, 8.0, (B, N)).astype(np.float32)
+    diff = (rng.random((B, N)) < 0.5) * rng.exponential(0.05, (B, N))
+    diff = diff.astype(np.float32)
+    loss = host(swa().regularizer(dev(z), dev(nll), dev(diff)))
+    ref = oracle.regularizer(z, nll, diff)
+    err = np.abs(loss - ref)
+    say(f"regularizer B={B} N={N} G={G}: max rel {np.max(err / np.maximum(ref, 1e-30)):.2e}")
+    # float32: a few roundings of the weight and of softplus; denormal
+    # softplus values (z below about -87) keep an absolute bound
+    assert np.all(err <= 2e-6 * ref + 1e-40)
+    # other hyperparameters are passed through
+    loss2 = host(swa().regularizer(dev(z), dev(nll), dev(diff), gamma_base=2e-3, eps=0.5, alpha=10.0))
+    ref2 = oracle.regularizer(z, nll, diff, gamma_base=2e-3, eps=0.5, alpha=10.0)
+    assert np.all(np.abs(loss2 - ref2) <= 2e-6 * ref2 + 1e-40)
+
+
+def test_regularizer_after_both_branch_layer():
+    """Router logits -> both-branch prefill distance -> regulariser, against
+    the same chain in the oracle (synthetic NLL)."""
+    B, N, Hq, Hkv, G, d, W, hidden = 1, 1500, 8, 2, 1, 64, 200, 256
+    w = synth.long_prefill(seed=33, B=B, N=N, Hq=Hq, Hkv=Hkv, d=d, W=W, p=0.3, G=G, with_router=True,
+                           hidden=hidden)
+    bf = torch.bfloat16
+    gate, idx, cnt, z = swa().route(dev(w.H, bf), dev(w.r, bf), dev(w.bias), want_z=True)
+    O, diff = swa().prefill(dev(w.Q, bf), dev(w.K, bf), dev(w.V, bf), gate, W, both_branch=True)
+    nll = np.random.default_rng(34).uniform(0.0, 6.0, (B, N)).astype(np.float32)
+    loss = host(swa().regularizer(z, dev(nll), diff))
+    # the oracle chain runs on its own router output (the distance does not
+    # depend on the gate)
+    rz = oracle.route(w.H, w.r, w.bias)
+    rp = oracle.prefill(w.Q, w.K, w.V, rz["gate"], W, both_branch=True)
+    ref = oracle.regularizer(rz["z"], nll, rp["diff"])
+    # the distance is within diff_tolerance of the oracle's, so the weight's
+    # relative error is at most alpha * tol / (eps + NLL + alpha * diff); the
+    # logits are within 1e-3 (float32 accumulation), and softplus changes by
+    # at most that much relatively (d log softplus(z) / dz = sigmoid(z) /
+    # softplus(z) <= 1)
+    tol_d = diff_tolerance(rp["diff"], Hq * d, TOL["bf16"])
+    den = 0.1 + nll + 100.0 * rp["diff"]
+    # rows before the window fills have distance exactly 0 on both sides
+    tol_d[:, :W] = 0.0
+    assert np.all(host(diff)[:, :W] == 0.0)
+    rel = (100.0 * tol_d / den)[..., None] + 2e-3
+    err = np.abs(loss - ref)
+    say(f"regulariser after both-branch: max rel {np.max(err / ref):.2e} (bound {rel.max():.2e})")
+    assert np.all(err <= rel * ref + 1e-30)
+
+
 def test_prefill_deterministic():
     B, N, Hq, Hkv, G, d, W = 1, 900, 8, 2, 1, 128, 128
     Q, K, V = _qkv(8, B, N, Hq, Hkv, d, "bf16")
