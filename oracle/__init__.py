@@ -8,6 +8,7 @@ from .swiattn_ref import (  # noqa: F401
     attend_rows,
     compact,
     decode,
+    decode_step,
     full_key_range,
     prefill,
     regularizer,

@@ -41,6 +41,7 @@ __all__ = [
     "decode",
     "softplus",
     "regularizer",
+    "decode_step",
 ]
 
 NEAR_THRESHOLD = 1e-5
@@ -269,6 +270,46 @@ def decode(q, Kc, Vc, cache_len, gate, W, scale=None):
                                  np.asarray(Vc[b, : i + 1, kv]), [lo], [hi], scale)
             o[b, h], lse[b, h] = ob[0], lb[0]
     return {"o": o, "lse": lse}
+
+
+# ---------------------------------------------------------------------------
+# Serving decode step  ([SwiAttn] section 2: router per token, shared cache)
+# ---------------------------------------------------------------------------
+def decode_step(Hn, r, bias, q, k, v, Kc, Vc, cache_len, W, scale=None):
+    """One serving step: route the new tokens, append their keys and values
+    to the shared cache, then decode.
+
+    [SwiAttn] section 2: the router decides per token, from its hidden state,
+    which branch it takes, and in decode both branches read one KV cache, so
+    the new token's key and value are appended whatever the gate says.
+
+    Hn [B,hidden] hidden states of the new tokens, r [hidden,G], bias [G];
+    q [B,Hq,d]; k, v [B,Hkv,d] the new tokens' keys and values;
+    Kc, Vc [B,Lmax,Hkv,d] and cache_len [B] the cache before the step (not
+    modified: copies are returned).
+    Returns dict gate [B,G], z [B,G], Kc, Vc, cache_len (after the step),
+    o [B,Hq,d], lse [B,Hq].
+
+    Reading: the new token of sequence b goes to position cache_len[b] and
+    the length grows by one; the query then sits at that position, as in
+    decode().  A sequence whose cache is already full (cache_len = Lmax) is
+    not appended and decodes over the cache as it stands.
+    """
+    Hn = np.asarray(Hn)
+    rt = route(Hn[:, None, :], r, bias)
+    gate = rt["gate"][:, 0, :]
+    Kc = np.array(Kc, copy=True)
+    Vc = np.array(Vc, copy=True)
+    L = np.array(cache_len, dtype=np.int64, copy=True)
+    Lmax = Kc.shape[1]
+    for b in range(L.shape[0]):
+        if L[b] < Lmax:
+            Kc[b, L[b]] = k[b]
+            Vc[b, L[b]] = v[b]
+            L[b] += 1
+    out = decode(q, Kc, Vc, L, gate, W, scale)
+    return {"gate": gate, "z": rt["z"][:, 0, :], "Kc": Kc, "Vc": Vc, "cache_len": L,
+            "o": out["o"], "lse": out["lse"]}
 
 
 # ---------------------------------------------------------------------------

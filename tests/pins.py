@@ -280,6 +280,57 @@ def check_regularizer_ratios():
     assert np.allclose(L[..., 1] / L[..., 0], sp, rtol=1e-12, atol=0)
 
 
+def check_decode_step_rebuilds_prefill():
+    """Serving a sequence token by token from an empty cache (route the new
+    token's hidden state, append its key and value, decode) reproduces the
+    prefill rows of the whole sequence with the gates the router gives each
+    token; the cache then holds exactly the sequence's keys and values."""
+    rng = np.random.default_rng(41)
+    B, N, Hq, Hkv, d, W, hidden, G = 2, 24, 4, 2, 8, 5, 16, 1
+    Q, K, V = _rand_qkv(42, B, N, Hq, Hkv, d)
+    H = rng.standard_normal((B, N, hidden))
+    r = rng.standard_normal((hidden, G)) / 4.0
+    bias = np.array([0.0])
+    gates = ref.route(H, r, bias)["gate"]
+    assert 0 < gates.sum() < B * N  # both branches occur
+    pre = ref.prefill(Q, K, V, gates, W)["O"]
+    Kc = np.full((B, N, Hkv, d), 7.0)
+    Vc = np.full((B, N, Hkv, d), -7.0)
+    L = np.zeros(B, np.int64)
+    for t in range(N):
+        st = ref.decode_step(H[:, t], r, bias, Q[:, t], K[:, t], V[:, t], Kc, Vc, L, W)
+        Kc, Vc, L = st["Kc"], st["Vc"], st["cache_len"]
+        assert np.array_equal(L, np.full(B, t + 1))
+        assert np.array_equal(st["gate"], gates[:, t])
+        np.testing.assert_allclose(st["o"], pre[:, t], rtol=0, atol=1e-13)
+    assert np.array_equal(Kc, K) and np.array_equal(Vc, V)
+
+
+def check_decode_step_ragged_and_full():
+    """Each sequence appends at its own length; a full cache is left as it is
+    and decodes over its Lmax keys (the same as decode() on it)."""
+    rng = np.random.default_rng(43)
+    B, Lmax, Hq, Hkv, d, W, hidden, G = 3, 10, 2, 1, 4, 3, 6, 2
+    Kc = rng.standard_normal((B, Lmax, Hkv, d))
+    Vc = rng.standard_normal((B, Lmax, Hkv, d))
+    L0 = np.array([3, Lmax, 0])
+    q = rng.standard_normal((B, Hq, d))
+    k = rng.standard_normal((B, Hkv, d))
+    v = rng.standard_normal((B, Hkv, d))
+    Hn = rng.standard_normal((B, hidden))
+    r = rng.standard_normal((hidden, G))
+    bias = np.zeros(G)
+    st = ref.decode_step(Hn, r, bias, q, k, v, Kc, Vc, L0, W)
+    assert list(st["cache_len"]) == [4, Lmax, 1]
+    assert np.array_equal(st["Kc"][0, 3], k[0]) and np.array_equal(st["Vc"][2, 0], v[2])
+    assert np.array_equal(st["Kc"][1], Kc[1]) and np.array_equal(st["Vc"][1], Vc[1])
+    mask = np.ones((B, Lmax), bool)
+    mask[0, 3] = mask[2, 0] = False
+    assert np.array_equal(st["Kc"][mask], Kc[mask])
+    want = ref.decode(q[1:2], Kc[1:2], Vc[1:2], [Lmax], st["gate"][1:2], W)["o"]
+    np.testing.assert_allclose(st["o"][1:2], want, rtol=0, atol=0)
+
+
 ALL_PINS = [
     check_w4_key_ranges,
     check_w4_attention_weights,
@@ -295,4 +346,6 @@ ALL_PINS = [
     check_compact,
     check_regularizer_hand_values,
     check_regularizer_ratios,
+    check_decode_step_rebuilds_prefill,
+    check_decode_step_ragged_and_full,
 ]

@@ -106,3 +106,35 @@ def test_regularizer_mutants_caught(monkeypatch):
     monkeypatch.undo()
     monkeypatch.setattr(ref, "softplus", naive_softplus)
     assert _run_all_pins() > 0, "naive softplus"
+
+
+def test_decode_step_mutants_caught(monkeypatch):
+    real_decode, real_route = ref.decode, ref.route
+
+    def step_with(append_at, grow, route_row=0):
+        def step(Hn, r, bias, q, k, v, Kc, Vc, cache_len, W, scale=None):
+            Hn = np.asarray(Hn)
+            rt = real_route(np.roll(Hn, route_row, axis=0)[:, None, :], r, bias)
+            gate = rt["gate"][:, 0, :]
+            Kc, Vc = np.array(Kc, copy=True), np.array(Vc, copy=True)
+            L = np.array(cache_len, dtype=np.int64, copy=True)
+            for b in range(L.shape[0]):
+                if L[b] < Kc.shape[1]:
+                    p = min(max(append_at(L[b]), 0), Kc.shape[1] - 1)
+                    Kc[b, p], Vc[b, p] = k[b], v[b]
+                    L[b] += grow
+            Ld = np.maximum(L, 1)
+            out = real_decode(q, Kc, Vc, Ld, gate, W, scale)
+            return {"gate": gate, "z": rt["z"][:, 0, :], "Kc": Kc, "Vc": Vc, "cache_len": L,
+                    "o": out["o"], "lse": out["lse"]}
+        return step
+
+    mutants = {
+        "append_one_past": step_with(lambda L: L + 1, 1),
+        "append_over_last": step_with(lambda L: L - 1, 1),
+        "no_length_growth": step_with(lambda L: L, 0),
+        "routes_other_token": step_with(lambda L: L, 1, route_row=1),
+    }
+    for name, m in mutants.items():
+        monkeypatch.setattr(ref, "decode_step", m)
+        assert _run_all_pins() > 0, name
