@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU reference sample (0 = skip)")
     ap.add_argument("--p", type=float, default=0.13, help="full-branch fraction")
+    ap.add_argument("--serve-steps", type=int, default=5,
+                    help="timed serving decode steps (route + append + decode; after the timed steps; 0 = skip)")
     ap.add_argument("--both-steps", type=int, default=3,
                     help="timed runs of the both-branch prefill (after the timed steps; 0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -251,6 +253,8 @@ def main():
 
     both = (both_branch_run(swa, Q, K, V, gate, W, args.both_steps, H, r, bias)
             if args.both_steps > 0 else None)
+    serve = (serve_run(swa, q_d, Kc, Vc, len_d, r, bias, W, args.serve_steps)
+             if args.serve_steps > 0 else None)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -283,6 +287,7 @@ def main():
                        "tok_per_s": round(decode_tok_s, 1), "GB_per_s": round(decode_gbs, 1),
                        "frac_of_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4)},
             "both_branch": both,
+            "serving_step": serve,
         },
         "kernel_ms": {k: round(v, 4) for k, v in t.items()},
         "roofline": dict(rooflines[dominant], kernel=dominant),
@@ -290,6 +295,50 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def serve_run(swa, q, Kc, Vc, cache_len, r, bias, W, steps):
+    """Serving decode steps on the decode workload's cache (outside the timed
+    steps): each routes 64 new tokens (hidden states drawn from a seeded
+    N(0,1), router as in the prefill), appends their keys and values at
+    position L-1 of the full cache (the lengths are set to L-1 before each
+    step) and decodes over L keys.  Timed with events around the whole call."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv = Kc.shape[2]
+    dev = q.device
+    hidden = r.shape[0]
+    gen = torch.Generator(device=dev).manual_seed(23)
+    Hn = torch.randn(B, hidden, generator=gen, device=dev).to(r.dtype)
+    k = torch.randn(B, Hkv, d, generator=gen, device=dev).to(q.dtype)
+    v = torch.randn(B, Hkv, d, generator=gen, device=dev).to(q.dtype)
+    before = (cache_len - 1).to(torch.int32)
+    L = before.clone()
+    o = torch.empty_like(q)
+    gate = torch.empty((B, r.shape[1]), dtype=torch.uint8, device=dev)
+    G = r.shape[1]
+    ws = torch.empty(swa.decode_workspace_size(B, Kc.shape[1], Hq, Hkv, G, d, W), dtype=torch.uint8,
+                     device=dev)
+    swa.decode_step(Hn, r, bias, q, k, v, Kc, Vc, L, W, gate=gate, out=o, workspace=ws)
+    times = []
+    for _ in range(steps):
+        L.copy_(before)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        swa.decode_step(Hn, r, bias, q, k, v, Kc, Vc, L, W, gate=gate, out=o, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.mean(times))
+    g = gate.cpu().numpy()
+    lens = L.cpu().numpy()
+    dbytes, keys = decode_bytes(g, lens, W, Hq, Hkv, d)
+    byts = dbytes + B * hidden * 2 + 2 * B * Hkv * d * 2  # + router input + appended rows
+    return {"B": B, "cache_len_after": int(lens.max()), "hidden": hidden,
+            "full_sequences": int(g.sum()), "attended_kv_rows": keys, "bytes": byts,
+            "ms": round(ms, 4), "tok_per_s": round(B / (ms * 1e-3), 1),
+            "GB_per_s": round(byts / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def both_branch_run(swa, Q, K, V, gate, W, steps, H, r, bias):

@@ -186,6 +186,38 @@ int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t*
                    size_t ws_bytes, swiattn_stream_t stream);
 
 /*
+ * swiattn_decode_step - one serving step: route the new tokens, append
+ * their keys and values to the shared cache, decode.
+ * (SwiAttn report, section 2: router per token; in decode both branches
+ * read one KV cache, so every new token is appended whatever its gate.)
+ *
+ *   Hn     [B,hidden]      dtype  the new tokens' hidden states (router input)
+ *   r      [hidden,G]      dtype  router weight;  bias [G] float
+ *   q      [B,Hq,d]        dtype  the new tokens' queries
+ *   k, v   [B,Hkv,d]       dtype  the new tokens' keys and values
+ *   Kc, Vc [B,Lmax,Hkv,d]  dtype  in/out: linear cache
+ *   cache_len [B]          int32  in/out: L per sequence before the step,
+ *                                 0 <= L <= Lmax; the new token goes to
+ *                                 position L and L becomes L + 1.  A full
+ *                                 cache (L = Lmax) is not appended and its
+ *                                 sequence decodes over the cache as it is;
+ *                                 a value below 0 is taken as 0
+ *   gate   [B,G]           uint8  out: the new tokens' hard gate (as
+ *                                 swiattn_route with N = 1)
+ *   o      [B,Hq,d]        dtype  out: as swiattn_decode after the append
+ *   ws, ws_bytes: as swiattn_decode (swiattn_decode_workspace_size).
+ * Runs the router, the append and the decode on `stream`, in that order,
+ * with no host synchronisation.
+ * Errors: as swiattn_decode, plus INVALID_ARG for hidden < 1 or a NULL
+ * router or k/v pointer.
+ */
+int swiattn_decode_step(const void* Hn, const void* r, const float* bias, const void* q,
+                        const void* k, const void* v, void* Kc, void* Vc, int32_t* cache_len,
+                        uint8_t* gate, void* o, int B, int Lmax, int hidden, int Hq, int Hkv, int G,
+                        int d, int W, float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
+                        swiattn_stream_t stream);
+
+/*
  * Stage timing (for profilers and benchmarks).  `events` holds up to six
  * hipEvent_t handles created by the caller (stored as void*; NULL entries
  * are skipped).  The _ex calls behave exactly like the plain ones and in

@@ -22,6 +22,7 @@ __all__ = [
     "regularizer",
     "prefill",
     "decode",
+    "decode_step",
     "prefill_workspace_size",
     "decode_workspace_size",
     "strerror",
@@ -44,6 +45,7 @@ SYMBOLS = {
     "swiattn_prefill_ex": (_i32, [_vp] * 8 + [_i32] * 7 + [_f32, _i32, _u32, _vp, _sz, _vp, _vp]),
     "swiattn_decode_ex": (_i32, [_vp] * 6 + [_i32] * 7 + [_f32, _i32, _vp, _sz, _vp, _vp]),
     "swiattn_regularizer": (_i32, [_vp] * 4 + [_i32] * 3 + [_f32] * 3 + [_vp]),
+    "swiattn_decode_step": (_i32, [_vp] * 11 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp]),
     "swiattn_strerror": (ctypes.c_char_p, [_i32]),
     "swiattn_version": (ctypes.c_char_p, []),
 }
@@ -287,3 +289,48 @@ def decode(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None, workspace=Non
                              _stream(dev), _events(events))
     _check(rc, "swiattn_decode")
     return out
+
+
+def decode_step(Hn, r, bias, q, k, v, Kc, Vc, cache_len, W, *, scale=None, gate=None, out=None,
+                workspace=None):
+    """One serving step: route the new tokens (Hn [B,hidden], r [hidden,G],
+    bias [G] fp32), append k, v [B,Hkv,d] to the cache Kc/Vc [B,Lmax,Hkv,d]
+    at position cache_len[b] (int32 [B], advanced in place), then decode q
+    [B,Hq,d] over the updated cache.  Returns (o [B,Hq,d], gate uint8 [B,G])."""
+    L = lib()
+    _need(q, "q")
+    code = _dtype_code(q)
+    B, Hq, d = q.shape
+    dev = q.device
+    _need(Hn, "Hn", dtype=q.dtype, device=dev)
+    if Hn.dim() != 2 or Hn.shape[0] != B:
+        raise ValueError("Hn must be [B,hidden]")
+    hidden = Hn.shape[1]
+    _need(r, "r", dtype=q.dtype, device=dev)
+    if r.dim() != 2 or r.shape[0] != hidden:
+        raise ValueError("r must be [hidden,G]")
+    G = r.shape[1]
+    _need(bias, "bias", shape=(G,), dtype=torch.float32, device=dev)
+    _need(Kc, "Kc", dtype=q.dtype, device=dev)
+    if Kc.dim() != 4 or Kc.shape[0] != B or Kc.shape[3] != d:
+        raise ValueError("Kc must be [B,Lmax,Hkv,d]")
+    Lmax, Hkv = Kc.shape[1], Kc.shape[2]
+    _need(Vc, "Vc", shape=Kc.shape, dtype=q.dtype, device=dev)
+    _need(k, "k", shape=(B, Hkv, d), dtype=q.dtype, device=dev)
+    _need(v, "v", shape=(B, Hkv, d), dtype=q.dtype, device=dev)
+    _need(cache_len, "cache_len", shape=(B,), dtype=torch.int32, device=dev)
+    if gate is None:
+        gate = torch.empty((B, G), dtype=torch.uint8, device=dev)
+    _need(gate, "gate", shape=(B, G), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", shape=q.shape, dtype=q.dtype, device=dev)
+    nbytes = int(L.swiattn_decode_workspace_size(B, Lmax, Hq, Hkv, G, d, W, code))
+    ws = _workspace(nbytes, dev, workspace)
+    rc = L.swiattn_decode_step(_p(Hn), _p(r), _p(bias), _p(q), _p(k), _p(v), _p(Kc), _p(Vc),
+                               _p(cache_len), _p(gate), _p(out), B, Lmax, hidden, Hq, Hkv, G, d, W,
+                               float(scale), code, _p(ws), ws.numel(), _stream(dev))
+    _check(rc, "swiattn_decode_step")
+    return out, gate

@@ -170,6 +170,23 @@ int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t*
                            dtype, ws, ws_bytes, stream, nullptr);
 }
 
+int swiattn_decode_step(const void* Hn, const void* r, const float* bias, const void* q,
+                        const void* k, const void* v, void* Kc, void* Vc, int32_t* cache_len,
+                        uint8_t* gate, void* o, int B, int Lmax, int hidden, int Hq, int Hkv, int G,
+                        int d, int W, float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
+                        swiattn_stream_t stream) {
+  swi::DecodeShape sh;
+  swi::DecodePlan p;
+  const int rc = decode_shape(B, Lmax, Hq, Hkv, G, d, W, scale, dtype, &sh, &p);
+  if (rc != SWIATTN_OK) return rc;
+  if (hidden < 1) return SWIATTN_ERR_INVALID_ARG;
+  if (!Hn || !r || !bias || !q || !k || !v || !Kc || !Vc || !cache_len || !gate || !o)
+    return SWIATTN_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < p.bytes) return SWIATTN_ERR_WORKSPACE;
+  return hip_rc(swi::launch_decode_step(sh, p, Hn, r, bias, hidden, q, k, v, Kc, Vc, cache_len,
+                                        gate, o, ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
 const char* swiattn_strerror(int code) {
   switch (code) {
     case SWIATTN_OK: return "ok";

@@ -360,4 +360,46 @@ hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void*
   return run_decode<bf16_t, 128>(sh, p, a, s, ev);
 }
 
+// ---------------------------------------------------------------------------
+// Serving step: the new token's key and value rows go to position
+// L = cache_len[b] of its sequence's cache and the length becomes L + 1
+// (SwiAttn report, section 2: both branches read one cache, so every token
+// is appended whatever its gate).  A length below 0 is taken as 0; a full
+// cache (L >= Lmax) is left as it is.  One workgroup per sequence copies the
+// Hkv*d-element rows in 16-byte pieces, then one thread stores the length
+// (every thread has read it before the barrier).
+// ---------------------------------------------------------------------------
+constexpr int kAppendThreads = 256;
+
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(const uint4* k, const uint4* v, uint4* Kc,
+                                                                uint4* Vc, int32_t* cache_len, int Lmax,
+                                                                int row16) {
+  const int b = blockIdx.x;
+  const int L = max(cache_len[b], 0);
+  if (L < Lmax) {
+    const int64_t dst = (int64_t(b) * Lmax + L) * row16;
+    const int64_t src = int64_t(b) * row16;
+    for (int i = threadIdx.x; i < row16; i += kAppendThreads) {
+      Kc[dst + i] = k[src + i];
+      Vc[dst + i] = v[src + i];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && L < Lmax) cache_len[b] = L + 1;
+}
+
+hipError_t launch_decode_step(const DecodeShape& sh, const DecodePlan& p, const void* Hn,
+                              const void* r, const float* bias, int hidden, const void* q,
+                              const void* k, const void* v, void* Kc, void* Vc, int32_t* cache_len,
+                              uint8_t* gate, void* o, void* ws, hipStream_t s) {
+  hipError_t e = launch_route(Hn, r, bias, gate, nullptr, sh.B, 1, hidden, sh.G, sh.f32, s);
+  if (e != hipSuccess) return e;
+  const int row16 = sh.Hkv * sh.d * (sh.f32 ? 4 : 2) / 16;
+  hipLaunchKernelGGL(append_kernel, dim3(sh.B), dim3(kAppendThreads), 0, s,
+                     static_cast<const uint4*>(k), static_cast<const uint4*>(v), static_cast<uint4*>(Kc),
+                     static_cast<uint4*>(Vc), cache_len, sh.Lmax, row16);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_decode(sh, p, q, Kc, Vc, cache_len, gate, o, ws, s, nullptr);
+}
+
 }  // namespace swi

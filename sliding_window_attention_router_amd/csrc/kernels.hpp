@@ -65,6 +65,11 @@ hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void*
                          const void* Kc, const void* Vc, const int32_t* cache_len,
                          const uint8_t* gate, void* o, void* ws, hipStream_t s,
                          void* const* ev);
+// route of the new tokens (N = 1), append of their K/V rows, decode
+hipError_t launch_decode_step(const DecodeShape& sh, const DecodePlan& p, const void* Hn,
+                              const void* r, const float* bias, int hidden, const void* q,
+                              const void* k, const void* v, void* Kc, void* Vc, int32_t* cache_len,
+                              uint8_t* gate, void* o, void* ws, hipStream_t s);
 
 // Record ev[i] on s if present; returns the first error.
 inline hipError_t mark(void* const* ev, int i, hipStream_t s) {

@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("swiattn_route", "swiattn_prefill", "swiattn_decode", "swiattn_prefill_workspace_size",
               "swiattn_decode_workspace_size", "swiattn_strerror", "swiattn_prefill_ex", "swiattn_decode_ex",
-              "swiattn_regularizer"):
+              "swiattn_regularizer", "swiattn_decode_step"):
         assert n in names
 
 
@@ -142,3 +142,18 @@ def test_regularizer_rejects_invalid_arguments(lib, kw):
     rc = lib.swiattn_regularizer(a["z"], a["nll"], a["diff"], a["loss"], a["B"], a["N"], a["G"],
                                  a["gamma_base"], a["eps"], a["alpha"], a["stream"])
     assert rc == INVALID
+
+
+@pytest.mark.parametrize("kw,code", [(dict(B=0), INVALID), (dict(hidden=0), INVALID), (dict(Hn=None), INVALID),
+                                     (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(cache_len=None), INVALID),
+                                     (dict(gate=None), INVALID), (dict(d=96), UNSUPPORTED), (dict(ws=None), WORKSPACE)])
+def test_decode_step_rejects_invalid_arguments(lib, kw, code):
+    a = dict(Hn=FAKE, r=FAKE, bias=FAKE, q=FAKE, k=FAKE, v=FAKE, Kc=FAKE, Vc=FAKE, cache_len=FAKE, gate=FAKE,
+             o=FAKE, B=2, Lmax=100, hidden=64, Hq=4, Hkv=2, G=1, d=128, W=16, scale=0.1, dt=BF16, ws=FAKE,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    rc = lib.swiattn_decode_step(a["Hn"], a["r"], a["bias"], a["q"], a["k"], a["v"], a["Kc"], a["Vc"],
+                                 a["cache_len"], a["gate"], a["o"], a["B"], a["Lmax"], a["hidden"], a["Hq"],
+                                 a["Hkv"], a["G"], a["d"], a["W"], a["scale"], a["dt"], a["ws"], a["ws_bytes"],
+                                 a["stream"])
+    assert rc == code

@@ -307,6 +307,72 @@ def test_decode(B, Lmax, Hq, Hkv, G, d, W, lens, dtype):
     assert err <= TOL[dtype]
 
 
+STEP_CASES = [
+    # B, Lmax, Hq, Hkv, G, d, W, hidden, lens (before the step), dtype
+    (6, 300, 8, 2, 2, 128, 64, 128, [0, 1, 150, 299, 300, 64], "bf16"),
+    (3, 200, 4, 4, 1, 64, 30, 96, [199, 17, 0], "f32"),
+]
+
+
+@pytest.mark.parametrize("B,Lmax,Hq,Hkv,G,d,W,hidden,lens,dtype", STEP_CASES)
+def test_decode_step(B, Lmax, Hq, Hkv, G, d, W, hidden, lens, dtype):
+    rng = np.random.default_rng(51 + B)
+    rnd = (lambda *sh: synth.round_bf16(rng.standard_normal(sh, dtype=np.float32))) if dtype == "bf16" \
+        else (lambda *sh: rng.standard_normal(sh, dtype=np.float32))
+    Kc, Vc = rnd(B, Lmax, Hkv, d), rnd(B, Lmax, Hkv, d)
+    q, k, v = rnd(B, Hq, d), rnd(B, Hkv, d), rnd(B, Hkv, d)
+    Hn = rnd(B, hidden)
+    r = (rnd(hidden, G) / np.sqrt(hidden)).astype(np.float32)
+    if dtype == "bf16":
+        r = synth.round_bf16(r)
+    bias = np.zeros(G, np.float32)
+    L0 = np.array(lens, np.int32)
+    td = TORCH_DTYPE[dtype]
+    Kg, Vg, Lg = dev(Kc, td), dev(Vc, td), dev(L0)
+    o, gate = swa().decode_step(dev(Hn, td), dev(r, td), dev(bias), dev(q, td), dev(k, td), dev(v, td),
+                                Kg, Vg, Lg, W)
+    ref = oracle.decode_step(Hn, r, bias, q, k, v, Kc, Vc, L0, W)
+    near = np.abs(ref["z"]) < 1e-5
+    g = gate.cpu().numpy()
+    assert np.array_equal(g[~near], ref["gate"][~near])
+    assert np.array_equal(Lg.cpu().numpy(), ref["cache_len"])
+    assert np.array_equal(host(Kg), ref["Kc"]) and np.array_equal(host(Vg), ref["Vc"])
+    ok = ~near.any(axis=1)
+    err = max_abs(host(o)[ok], ref["o"][ok])
+    say(f"decode step {dtype} B={B} lens={lens}: o max-abs {err:.3e}, near-threshold sequences {int((~ok).sum())}")
+    assert err <= TOL[dtype]
+
+
+def test_decode_step_serves_a_sequence():
+    """Token-by-token serving from an empty cache reproduces the prefill rows
+    of the whole sequence (gates from the router on each token)."""
+    B, N, Hq, Hkv, G, d, W, hidden = 3, 80, 8, 2, 1, 128, 24, 64
+    w = synth.long_prefill(seed=52, B=B, N=N, Hq=Hq, Hkv=Hkv, d=d, W=W, p=0.3, G=G, with_router=True,
+                           hidden=hidden)
+    rz = oracle.route(w.H, w.r, w.bias)
+    assert not rz["near"].any()  # no token within 1e-5 of the threshold for this seed
+    ref = oracle.prefill(w.Q, w.K, w.V, rz["gate"], W)["O"]
+    bf = torch.bfloat16
+    Kc = torch.zeros((B, N, Hkv, d), dtype=bf, device="cuda")
+    Vc = torch.zeros_like(Kc)
+    L = torch.zeros(B, dtype=torch.int32, device="cuda")
+    H, Q, K, V = dev(w.H, bf), dev(w.Q, bf), dev(w.K, bf), dev(w.V, bf)
+    r, bias = dev(w.r, bf), dev(w.bias)
+    outs, gates = [], []
+    for t in range(N):
+        o, g = swa().decode_step(H[:, t].contiguous(), r, bias, Q[:, t].contiguous(), K[:, t].contiguous(),
+                                 V[:, t].contiguous(), Kc, Vc, L, W)
+        outs.append(host(o))
+        gates.append(g.cpu().numpy())
+    O = np.stack(outs, 1)
+    assert np.array_equal(np.stack(gates, 1), rz["gate"])
+    assert np.array_equal(L.cpu().numpy(), np.full(B, N))
+    assert np.array_equal(host(Kc), w.K) and np.array_equal(host(Vc), w.V)
+    err = max_abs(O, ref)
+    say(f"served {N} tokens x {B} sequences: max-abs vs prefill rows {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 def test_decode_matches_prefill_last_row():
     B, N, Hq, Hkv, G, d, W = 1, 640, 8, 2, 1, 128, 96
     Q, K, V = _qkv(10, B, N, Hq, Hkv, d, "bf16")
