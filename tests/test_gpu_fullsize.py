@@ -69,6 +69,33 @@ def test_long_prefill_32k(mode):
     assert err <= TOL["bf16"]
 
 
+def test_long_prefill_128k():
+    """The longest context the pages discuss: N=131072 with their window
+    recommendation W=4096, GQA 16/4, gate Bernoulli(0.13)."""
+    N, Wl = 131072, 4096
+    say(f"long prefill N={N} W={Wl} GQA 16/4 gate Bernoulli(0.13)")
+    w = synth.long_prefill(seed=9, N=N, W=Wl)
+    bf = torch.bfloat16
+    Q, K, V = dev(w.Q, bf), dev(w.K, bf), dev(w.V, bf)
+    O, _ = swa().prefill(Q, K, V, dev(w.gate), Wl)
+    O2, _ = swa().prefill(Q, K, V, dev(w.gate), Wl)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2), "two runs differ"
+    Oh = host(O)
+    del O, O2, Q, K, V
+    assert np.all(np.abs(Oh) <= np.abs(w.V).max() + 1e-2)
+    rng = np.random.default_rng(10)
+    routed = np.flatnonzero(w.gate[0, :, 0])
+    plain = np.flatnonzero(w.gate[0, :, 0] == 0)
+    rows = set(range(0, 8)) | set(range(Wl - 8, Wl + 8)) | set(range(N - 8, N))
+    rows |= set(rng.choice(routed, 16, replace=False).tolist()) | set(rng.choice(plain, 16, replace=False).tolist())
+    rows = np.array(sorted(rows))
+    ref = oracle.prefill(w.Q, w.K, w.V, w.gate, Wl, rows=rows)["O"]
+    err = max_abs(Oh[:, rows], ref)
+    say(f"  {rows.size} sampled rows x 16 heads: max-abs {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 def test_layer_route_and_prefill_4k():
     say("layer: router on hidden 2048 -> compaction -> prefill N=4096 MHA 16 heads")
     w = synth.layer()
