@@ -202,6 +202,47 @@ def test_prefill_both_branch_shapes(B, N, Hq, Hkv, G, d, W, dtype):
     assert np.all(diff[:, :min(W, N)] == 0.0)
 
 
+@pytest.mark.parametrize("N,W", [(1, 1), (2, 1), (65, 64), (64, 64)])
+def test_prefill_both_branch_degenerate(N, W):
+    """Single tokens, a window of one key (row i's far part is [0, i-1]), and
+    a sequence that is one key longer than the window."""
+    B, Hq, Hkv, G, d = 1, 4, 2, 2, 64
+    Q, K, V = _qkv(17, B, N, Hq, Hkv, d, "bf16")
+    gate = (np.arange(N * G).reshape(1, N, G) % 3 == 0).astype(np.uint8)
+    O, diff = _gpu_prefill(Q, K, V, gate, W, "bf16", both=True)
+    ref = oracle.prefill(Q, K, V, gate, W, both_branch=True)
+    assert max_abs(O, ref["O"]) <= TOL["bf16"]
+    assert np.all(np.abs(diff - ref["diff"]) <= diff_tolerance(ref["diff"], Hq * d, TOL["bf16"]))
+    assert np.all(diff[:, :min(W, N)] == 0.0)
+    if N > W:
+        assert np.all(diff[:, W:] > 0.0)  # the far keys change the full-branch output
+
+
+def test_decode_step_one_slot_cache():
+    """Lmax = 1: the first token fills the cache, a second step finds it full."""
+    B, Lmax, Hq, Hkv, G, d, W, hidden = 2, 1, 4, 2, 1, 128, 1, 64
+    rng = np.random.default_rng(61)
+    rnd = lambda *sh: synth.round_bf16(rng.standard_normal(sh, dtype=np.float32))
+    Kc, Vc = np.zeros((B, Lmax, Hkv, d), np.float32), np.zeros((B, Lmax, Hkv, d), np.float32)
+    q, k, v, Hn = rnd(B, Hq, d), rnd(B, Hkv, d), rnd(B, Hkv, d), rnd(B, hidden)
+    r = synth.round_bf16(rnd(hidden, G) / 8.0)
+    bias = np.zeros(G, np.float32)
+    bf = torch.bfloat16
+    Kg, Vg, Lg = dev(Kc, bf), dev(Vc, bf), dev(np.zeros(B, np.int32))
+    o, _ = swa().decode_step(dev(Hn, bf), dev(r, bf), dev(bias), dev(q, bf), dev(k, bf), dev(v, bf),
+                             Kg, Vg, Lg, W)
+    ref = oracle.decode_step(Hn, r, bias, q, k, v, Kc, Vc, np.zeros(B, np.int32), W)
+    assert np.array_equal(Lg.cpu().numpy(), [1, 1])
+    assert max_abs(host(o), ref["o"]) <= TOL["bf16"]
+    # the cache is full now: nothing is appended, the output is the decode over it
+    k2, v2 = rnd(B, Hkv, d), rnd(B, Hkv, d)
+    o2, _ = swa().decode_step(dev(Hn, bf), dev(r, bf), dev(bias), dev(q, bf), dev(k2, bf), dev(v2, bf),
+                              Kg, Vg, Lg, W)
+    assert np.array_equal(Lg.cpu().numpy(), [1, 1])
+    assert np.array_equal(host(Kg), ref["Kc"]) and np.array_equal(host(Vg), ref["Vc"])
+    assert max_abs(host(o2), ref["o"]) <= TOL["bf16"]
+
+
 def test_prefill_both_branch_deterministic():
     B, N, Hq, Hkv, G, d, W = 1, 900, 8, 2, 1, 128, 128
     Q, K, V = _qkv(15, B, N, Hq, Hkv, d, "bf16")
