@@ -5,6 +5,7 @@ CPU-baseline leg may import this package.  It shares no code with the HIP
 library and imports nothing from it.
 """
 from .swiattn_ref import (  # noqa: F401
+    anchor_key_range,
     attend_rows,
     compact,
     decode,

@@ -35,6 +35,7 @@ __all__ = [
     "route",
     "compact",
     "swa_key_range",
+    "anchor_key_range",
     "full_key_range",
     "attend_rows",
     "prefill",
@@ -112,6 +113,23 @@ def swa_key_range(i, W):
     return max(0, i - W + 1), i
 
 
+def anchor_key_range(i, W, A):
+    """Global anchors of the window branch: the first A keys of the sequence,
+    which every query sees in addition to its window, minus the keys its
+    window already holds -> inclusive [0, min(A, i-W+1) - 1] (empty, hi < lo,
+    when A = 0 or the window reaches position 0).
+
+    [Glossary] section "SWA 落地的四个常见坑", pitfall 1, fix (2): the keys
+    of the first 256 tokens are listed on their own, every query also
+    attends to them, and they take no part in the sliding.
+    Reading: an anchor is a key like any other in the window branch's
+    softmax (one key set, window union anchors); anchors are causal like the
+    window (the window starts at or before i, so the anchors end before it);
+    the full branch already sees them."""
+    lo, _ = swa_key_range(i, W)
+    return 0, min(A, lo) - 1
+
+
 def full_key_range(i):
     """Full branch key set of query position i: every key up to and including
     i -> inclusive [0, i].
@@ -125,13 +143,16 @@ def full_key_range(i):
 # ---------------------------------------------------------------------------
 # Softmax attention over an explicit key interval per row
 # ---------------------------------------------------------------------------
-def attend_rows(q, K, V, lo, hi, scale):
-    """Softmax attention of each query row over its own inclusive key interval.
+def attend_rows(q, K, V, lo, hi, scale, lo2=None, hi2=None):
+    """Softmax attention of each query row over its own inclusive key interval
+    (and, if given, a second interval disjoint from it: one key set, their
+    union).
 
     q [R,d], K [L,d], V [L,dv], lo/hi int [R] (lo <= hi)  ->
       O   float64 [R,dv]  sum_j p_j v_j / sum_j p_j,  p_j = exp(s_j - max s)
       lse float64 [R]     log sum_j exp(s_j)
-    with s_j = scale * <q, k_j> for lo <= j <= hi.
+    with s_j = scale * <q, k_j> for lo <= j <= hi (or lo2 <= j <= hi2; a row
+    with hi2 < lo2 has no second interval).
     """
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -139,6 +160,10 @@ def attend_rows(q, K, V, lo, hi, scale):
     lo = np.asarray(lo, dtype=np.int64)
     hi = np.asarray(hi, dtype=np.int64)
     R = q.shape[0]
+    two = lo2 is not None
+    if two:
+        lo2 = np.broadcast_to(np.asarray(lo2, dtype=np.int64), (R,))
+        hi2 = np.broadcast_to(np.asarray(hi2, dtype=np.int64), (R,))
     O = np.empty((R, V.shape[1]), dtype=np.float64)
     lse = np.empty(R, dtype=np.float64)
     if R == 0:
@@ -151,9 +176,16 @@ def attend_rows(q, K, V, lo, hi, scale):
         sel = order[start : start + n]
         kmax = int(hi[sel].max()) + 1
         kmin = int(lo[sel].min())
+        if two:
+            live2 = hi2[sel] >= lo2[sel]
+            if live2.any():
+                kmin = min(kmin, int(lo2[sel][live2].min()))
+                kmax = max(kmax, int(hi2[sel][live2].max()) + 1)
         j = np.arange(kmin, kmax)
         s = scale * (q[sel] @ K[kmin:kmax].T)
         mask = (j[None, :] >= lo[sel, None]) & (j[None, :] <= hi[sel, None])
+        if two:
+            mask |= (j[None, :] >= lo2[sel, None]) & (j[None, :] <= hi2[sel, None])
         s = np.where(mask, s, -np.inf)
         m = s.max(axis=1, keepdims=True)
         p = np.exp(s - m)
@@ -174,7 +206,7 @@ def _head_maps(Hq, Hkv, G):
 # ---------------------------------------------------------------------------
 # Prefill: both branches on shared Q/K/V, gated combination
 # ---------------------------------------------------------------------------
-def prefill(Q, K, V, gate, W, scale=None, both_branch=False, rows=None):
+def prefill(Q, K, V, gate, W, scale=None, both_branch=False, rows=None, anchors=0):
     """Dual-branch attention forward over a prefix.
 
     [SwiAttn] section 2, dual-branch paragraph: both branches use the same Q,
@@ -188,6 +220,8 @@ def prefill(Q, K, V, gate, W, scale=None, both_branch=False, rows=None):
 
     Q [B,N,Hq,d], K/V [B,N,Hkv,d], gate [B,N,G] (0/1)
     rows: optional sorted token positions to evaluate (default all N)
+    anchors: A >= 0 global anchor keys added to the window branch
+             (anchor_key_range); 0 is plain SWA
     ->  dict
       O     float64 [B,R,Hq,d]
       lse   float64 [B,R,Hq]      natural-log normaliser of the chosen branch
@@ -213,7 +247,9 @@ def prefill(Q, K, V, gate, W, scale=None, both_branch=False, rows=None):
         Of = np.empty((B, R, Hq, dv))
         Os = np.empty((B, R, Hq, dv))
     sw = np.array([swa_key_range(int(i), W) for i in rows], dtype=np.int64).reshape(R, 2)
+    an = np.array([anchor_key_range(int(i), W, anchors) for i in rows], dtype=np.int64).reshape(R, 2)
     fu = np.array([full_key_range(int(i)) for i in rows], dtype=np.int64).reshape(R, 2)
+    none = np.array([0, -1], dtype=np.int64)  # no second interval
     for b in range(B):
         for h in range(Hq):
             kv, g = h // hk, h // hg
@@ -221,14 +257,18 @@ def prefill(Q, K, V, gate, W, scale=None, both_branch=False, rows=None):
             sig = gate[b, rows, g] != 0
             if both_branch:
                 o_f, l_f = attend_rows(qh, K[b, :, kv], V[b, :, kv], fu[:, 0], fu[:, 1], scale)
-                o_s, l_s = attend_rows(qh, K[b, :, kv], V[b, :, kv], sw[:, 0], sw[:, 1], scale)
+                o_s, l_s = attend_rows(qh, K[b, :, kv], V[b, :, kv], sw[:, 0], sw[:, 1], scale,
+                                       an[:, 0], an[:, 1])
                 Of[b, :, h], Os[b, :, h] = o_f, o_s
                 O[b, :, h] = np.where(sig[:, None], o_f, o_s)
                 lse[b, :, h] = np.where(sig, l_f, l_s)
             else:
                 lo = np.where(sig, fu[:, 0], sw[:, 0])
                 hi = np.where(sig, fu[:, 1], sw[:, 1])
-                O[b, :, h], lse[b, :, h] = attend_rows(qh, K[b, :, kv], V[b, :, kv], lo, hi, scale)
+                lo2 = np.where(sig, none[0], an[:, 0])
+                hi2 = np.where(sig, none[1], an[:, 1])
+                O[b, :, h], lse[b, :, h] = attend_rows(qh, K[b, :, kv], V[b, :, kv], lo, hi, scale,
+                                                       lo2, hi2)
     out = {"O": O, "lse": lse}
     if both_branch:
         out["O_full"], out["O_swa"] = Of, Os
@@ -239,7 +279,7 @@ def prefill(Q, K, V, gate, W, scale=None, both_branch=False, rows=None):
 # ---------------------------------------------------------------------------
 # Decode: one new query per sequence against the shared KV cache
 # ---------------------------------------------------------------------------
-def decode(q, Kc, Vc, cache_len, gate, W, scale=None):
+def decode(q, Kc, Vc, cache_len, gate, W, scale=None, anchors=0):
     """One decode step per sequence, both branches reading one KV cache.
 
     [SwiAttn] section 2: in decode the two branches share the KV cache.
@@ -250,6 +290,8 @@ def decode(q, Kc, Vc, cache_len, gate, W, scale=None):
 
     q [B,Hq,d], Kc/Vc [B,Lmax,Hkv,d], cache_len int [B] (1 <= L <= Lmax),
     gate [B,G]  ->  dict  o float64 [B,Hq,d], lse float64 [B,Hq]
+    anchors: A >= 0 global anchor keys of the window branch (anchor_key_range
+    at position L-1); the anchors stay in the linear cache like every key.
     """
     q = np.asarray(q)
     gate = np.asarray(gate)
@@ -265,9 +307,12 @@ def decode(q, Kc, Vc, cache_len, gate, W, scale=None):
         i = int(cache_len[b]) - 1
         for h in range(Hq):
             kv, g = h // hk, h // hg
-            lo, hi = full_key_range(i) if gate[b, g] else swa_key_range(i, W)
+            if gate[b, g]:
+                (lo, hi), (lo2, hi2) = full_key_range(i), (0, -1)
+            else:
+                (lo, hi), (lo2, hi2) = swa_key_range(i, W), anchor_key_range(i, W, anchors)
             ob, lb = attend_rows(q[b, h][None, :], np.asarray(Kc[b, : i + 1, kv]),
-                                 np.asarray(Vc[b, : i + 1, kv]), [lo], [hi], scale)
+                                 np.asarray(Vc[b, : i + 1, kv]), [lo], [hi], scale, [lo2], [hi2])
             o[b, h], lse[b, h] = ob[0], lb[0]
     return {"o": o, "lse": lse}
 
@@ -275,7 +320,7 @@ def decode(q, Kc, Vc, cache_len, gate, W, scale=None):
 # ---------------------------------------------------------------------------
 # Serving decode step  ([SwiAttn] section 2: router per token, shared cache)
 # ---------------------------------------------------------------------------
-def decode_step(Hn, r, bias, q, k, v, Kc, Vc, cache_len, W, scale=None):
+def decode_step(Hn, r, bias, q, k, v, Kc, Vc, cache_len, W, scale=None, anchors=0):
     """One serving step: route the new tokens, append their keys and values
     to the shared cache, then decode.
 
@@ -307,7 +352,7 @@ def decode_step(Hn, r, bias, q, k, v, Kc, Vc, cache_len, W, scale=None):
             Kc[b, L[b]] = k[b]
             Vc[b, L[b]] = v[b]
             L[b] += 1
-    out = decode(q, Kc, Vc, L, gate, W, scale)
+    out = decode(q, Kc, Vc, L, gate, W, scale, anchors)
     return {"gate": gate, "z": rt["z"][:, 0, :], "Kc": Kc, "Vc": Vc, "cache_len": L,
             "o": out["o"], "lse": out["lse"]}
 

@@ -153,8 +153,10 @@ def check_decode_equals_last_prefill_row():
         np.testing.assert_allclose(dec[b], pre, rtol=0, atol=1e-13)
 
 
-def brute_force(Q, K, V, gate, W, scale):
-    """Independent pure-Python evaluation: explicit loops, math.exp."""
+def brute_force(Q, K, V, gate, W, scale, A=0):
+    """Independent pure-Python evaluation: explicit loops, math.exp.  The
+    window branch's keys are chosen by a membership test: causal, and either
+    among the W newest or among the first A of the sequence."""
     B, N, Hq, d = Q.shape
     Hkv, G = K.shape[2], gate.shape[2]
     Of = np.zeros(Q.shape)
@@ -164,7 +166,8 @@ def brute_force(Q, K, V, gate, W, scale):
             kv = h * Hkv // Hq
             for i in range(N):
                 for which, out in (("full", Of), ("swa", Os)):
-                    keys = [j for j in range(N) if j <= i and (which == "full" or i - j < W)]
+                    keys = [j for j in range(N)
+                            if j <= i and (which == "full" or i - j < W or j < A)]
                     s = [scale * sum(Q[b, i, h, c] * K[b, j, kv, c] for c in range(d)) for j in keys]
                     mx = max(s)
                     w = [math.exp(x - mx) for x in s]
@@ -190,6 +193,80 @@ def check_brute_force_tiny():
     dflt = ref.prefill(Q, K, V, gate, W)["O"]
     O_bf2, _ = brute_force(Q, K, V, gate, W, 1.0 / math.sqrt(d))
     np.testing.assert_allclose(dflt, O_bf2, rtol=0, atol=1e-12)
+
+
+def check_anchors_brute_force():
+    """Global anchors ([Glossary] pitfall 1, fix 2): every query also sees the
+    first A keys, each key once.  Against the membership-test brute force,
+    for anchors inside, overlapping and beyond the window."""
+    B, N, Hq, Hkv, d, W = 1, 13, 4, 2, 3, 4
+    Q, K, V = _rand_qkv(31, B, N, Hq, Hkv, d)
+    gate = (np.random.default_rng(32).random((B, N, 2)) < 0.5).astype(np.uint8)
+    for A in (1, 3, 6, 20):
+        O_bf, diff_bf = brute_force(Q, K, V, gate, W, 0.9, A=A)
+        out = ref.prefill(Q, K, V, gate, W, scale=0.9, both_branch=True, anchors=A)
+        np.testing.assert_allclose(out["O"], O_bf, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(out["diff"], diff_bf, rtol=1e-12, atol=1e-14)
+        hard = ref.prefill(Q, K, V, gate, W, scale=0.9, anchors=A)["O"]
+        np.testing.assert_allclose(hard, O_bf, rtol=0, atol=1e-12)
+
+
+def check_anchors_closed_form():
+    """W = 1 with A anchors and q = 0: row i >= A averages the anchors and
+    itself, (v_0 + ... + v_{A-1} + v_i) / (A + 1); row i < A averages
+    v_0..v_i (its anchors end where its window starts)."""
+    N, A = 10, 3
+    Q = np.zeros((1, N, 1, N))
+    K = np.random.default_rng(33).standard_normal((1, N, 1, N))
+    V = np.eye(N)[None, :, None, :]
+    out = ref.prefill(Q, K, V, np.zeros((1, N, 1), np.uint8), W=1, anchors=A)["O"][0, :, 0]
+    expect = np.zeros((N, N))
+    for i in range(N):
+        if i >= A:
+            expect[i, :A] = 1.0 / (A + 1)
+            expect[i, i] = 1.0 / (A + 1)
+        else:
+            expect[i, : i + 1] = 1.0 / (i + 1)
+    np.testing.assert_allclose(out, expect, rtol=0, atol=1e-15)
+
+
+def check_anchors_against_sdpa_and_cover():
+    """Gate all zeros with anchors equals torch's float64 attention under the
+    mask causal & (band | first A keys); W + A >= N turns the window branch
+    into full causal attention (diff 0 everywhere); rows i < W + A have the
+    full key set in both branches (diff exactly 0), later rows do not."""
+    B, N, Hq, Hkv, d, W, A = 1, 80, 4, 2, 8, 16, 8
+    Q, K, V = _rand_qkv(34, B, N, Hq, Hkv, d)
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    mask = (j <= i) & ((j > i - W) | (j < A))
+    zeros = ref.prefill(Q, K, V, np.zeros((B, N, 1), np.uint8), W=W, anchors=A)["O"]
+    np.testing.assert_allclose(zeros, _torch_sdpa(Q, K, V, mask), rtol=0, atol=1e-12)
+    out = ref.prefill(Q, K, V, np.zeros((B, N, 1), np.uint8), W=W, both_branch=True, anchors=A)
+    assert np.all(out["diff"][:, : W + A] == 0.0)
+    assert np.all(out["diff"][:, W + A:] > 0.0)
+    cover = ref.prefill(Q, K, V, np.zeros((B, N, 1), np.uint8), W=50, both_branch=True, anchors=30)
+    assert np.all(cover["diff"] == 0.0)
+    np.testing.assert_allclose(cover["O"], _torch_sdpa(Q, K, V, j <= i), rtol=0, atol=1e-12)
+
+
+def check_anchored_decode_equals_last_prefill_row():
+    """Decode with anchors at cache length L reproduces anchored prefill row
+    L-1 (the anchors are the first A entries of the same linear cache)."""
+    B, Lmax, Hq, Hkv, d, W, A = 3, 60, 4, 2, 8, 12, 5
+    Q, K, V = _rand_qkv(35, B, Lmax, Hq, Hkv, d)
+    lens = np.array([60, 16, 7])
+    gate = np.array([[0], [0], [1]], np.uint8)
+    q = np.stack([Q[b, lens[b] - 1] for b in range(B)])
+    dec = ref.decode(q, K, V, lens, gate, W, anchors=A)["o"]
+    for b in range(B):
+        L = lens[b]
+        g = np.broadcast_to(gate[b], (1, L, 1)).astype(np.uint8)
+        pre = ref.prefill(Q[b:b + 1, :L], K[b:b + 1, :L], V[b:b + 1, :L], g, W, anchors=A)["O"][0, L - 1]
+        np.testing.assert_allclose(dec[b], pre, rtol=0, atol=1e-13)
+    # a window sequence past W + A differs from its anchor-free decode
+    plain = ref.decode(q, K, V, lens, gate, W)["o"]
+    assert not np.allclose(dec[0], plain[0])
 
 
 def check_convex_hull():
@@ -348,4 +425,8 @@ ALL_PINS = [
     check_regularizer_ratios,
     check_decode_step_rebuilds_prefill,
     check_decode_step_ragged_and_full,
+    check_anchors_brute_force,
+    check_anchors_closed_form,
+    check_anchors_against_sdpa_and_cover,
+    check_anchored_decode_equals_last_prefill_row,
 ]

@@ -9,24 +9,24 @@ from tests import pins
 _attend = ref.attend_rows
 
 
-def _attend_no_scale(q, K, V, lo, hi, scale):
-    return _attend(q, K, V, lo, hi, 1.0)
+def _attend_no_scale(q, K, V, lo, hi, scale, lo2=None, hi2=None):
+    return _attend(q, K, V, lo, hi, 1.0, lo2, hi2)
 
 
-def _attend_transposed_kv(q, K, V, lo, hi, scale):
-    return _attend(q, V, K, lo, hi, scale)
+def _attend_transposed_kv(q, K, V, lo, hi, scale, lo2=None, hi2=None):
+    return _attend(q, V, K, lo, hi, scale, lo2, hi2)
 
 
-def _attend_unnormalised(q, K, V, lo, hi, scale):
-    O, lse = _attend(q, K, V, lo, hi, scale)
+def _attend_unnormalised(q, K, V, lo, hi, scale, lo2=None, hi2=None):
+    O, lse = _attend(q, K, V, lo, hi, scale, lo2, hi2)
     n = (np.asarray(hi) - np.asarray(lo) + 1)[:, None]
     return O * n, lse
 
 
-def _attend_drop_last_key(q, K, V, lo, hi, scale):
+def _attend_drop_last_key(q, K, V, lo, hi, scale, lo2=None, hi2=None):
     hi = np.asarray(hi)
     lo = np.asarray(lo)
-    return _attend(q, K, V, lo, np.maximum(lo, hi - 1), scale)
+    return _attend(q, K, V, lo, np.maximum(lo, hi - 1), scale, lo2, hi2)
 
 
 MUTANTS = {
@@ -40,6 +40,16 @@ MUTANTS = {
     "k_and_v_swapped": ("attend_rows", _attend_transposed_kv),
     "unnormalised_weights": ("attend_rows", _attend_unnormalised),
     "drops_newest_key": ("attend_rows", _attend_drop_last_key),
+    # anchors not cut at the window start: early rows see future anchor keys
+    "anchors_not_causal": ("anchor_key_range", lambda i, W, A: (0, A - 1)),
+    # one anchor key too many
+    "anchors_one_too_many": ("anchor_key_range",
+                             lambda i, W, A: (0, min(A, max(0, i - W + 1)) - (0 if A else 1))),
+    # anchors that slide with the window (the A keys before it, not the first A)
+    "anchors_slide": ("anchor_key_range",
+                      lambda i, W, A: (max(0, i - W + 1 - A), max(0, i - W + 1) - 1)),
+    # anchors ignored altogether
+    "anchors_ignored": ("anchor_key_range", lambda i, W, A: (0, -1)),
 }
 
 
