@@ -246,6 +246,42 @@ int swiattn_decode_ex(const void* q, const void* Kc, const void* Vc, const int32
                       int d, int W, float scale, swiattn_dtype_t dtype, void* ws,
                       size_t ws_bytes, swiattn_stream_t stream, const swiattn_events_t* events);
 
+/*
+ * swiattn_prefill_anchored / swiattn_decode_anchored - the same calls with
+ * global anchors in the window branch.
+ * (weimeta glossary "滑窗注意力 Sliding Window Attention 是什么？", section
+ * "SWA 落地的四个常见坑", pitfall 1, fix 2: the keys of the first tokens of
+ * the document, 256 there, are listed apart and every query attends to them
+ * in addition to its window, outside the sliding.)
+ *
+ *   anchors  A >= 0: the window-branch key set of query i becomes
+ *            [0, min(A, i-W+1) - 1] union [max(0, i-W+1), i], every key
+ *            once, in one softmax.  The full branch is unchanged ([0, i]
+ *            already holds the anchors).  A = 0 is exactly swiattn_prefill /
+ *            swiattn_decode; A >= N (prefill) or A >= Lmax (decode) is
+ *            treated as N or Lmax.
+ *   Every other argument, the workspace (same size queries: anchors need
+ *   no extra space), the outputs and the events are those of
+ *   swiattn_prefill_ex / swiattn_decode_ex (events may be NULL).
+ *   Prefill: gate=1 rows take the far part [A, i-W] (empty when i-W < A);
+ *   in both-branch mode diff is exactly 0 for rows i < W + A.
+ *   Decode: a window head of a sequence with L = cache_len reads its anchors
+ *   [0, min(A, L-W) - 1] from the same linear cache.
+ * Errors: as swiattn_prefill / swiattn_decode, plus INVALID_ARG for A < 0.
+ */
+int swiattn_prefill_anchored(const void* Q, const void* K, const void* V, const uint8_t* gate,
+                             const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B,
+                             int N, int Hq, int Hkv, int G, int d, int W, int anchors,
+                             float scale, swiattn_dtype_t dtype, unsigned flags, void* ws,
+                             size_t ws_bytes, swiattn_stream_t stream,
+                             const swiattn_events_t* events);
+
+int swiattn_decode_anchored(const void* q, const void* Kc, const void* Vc,
+                            const int32_t* cache_len, const uint8_t* gate, void* o, int B,
+                            int Lmax, int Hq, int Hkv, int G, int d, int W, int anchors,
+                            float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
+                            swiattn_stream_t stream, const swiattn_events_t* events);
+
 /* Static text for an error code. */
 const char* swiattn_strerror(int code);
 

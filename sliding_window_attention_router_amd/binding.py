@@ -46,6 +46,8 @@ SYMBOLS = {
     "swiattn_decode_ex": (_i32, [_vp] * 6 + [_i32] * 7 + [_f32, _i32, _vp, _sz, _vp, _vp]),
     "swiattn_regularizer": (_i32, [_vp] * 4 + [_i32] * 3 + [_f32] * 3 + [_vp]),
     "swiattn_decode_step": (_i32, [_vp] * 11 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp]),
+    "swiattn_prefill_anchored": (_i32, [_vp] * 8 + [_i32] * 8 + [_f32, _i32, _u32, _vp, _sz, _vp, _vp]),
+    "swiattn_decode_anchored": (_i32, [_vp] * 6 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp, _vp]),
     "swiattn_strerror": (ctypes.c_char_p, [_i32]),
     "swiattn_version": (ctypes.c_char_p, []),
 }
@@ -208,8 +210,10 @@ def _workspace(nbytes, device, workspace):
 
 
 def prefill(Q, K, V, gate, W, *, idx=None, cnt=None, scale=None, both_branch=False,
-            out=None, diff=None, workspace=None, events=None):
+            out=None, diff=None, workspace=None, events=None, anchors=0):
     """Dual-branch prefill.  Q [B,N,Hq,d], K/V [B,N,Hkv,d], gate [B,N,G] uint8.
+    anchors: global anchor keys of the window branch (swiattn_prefill_anchored);
+    0 calls swiattn_prefill_ex.
 
     In hard-gate mode the compacted positions (idx, cnt) from route() are
     used, or computed here by the library's compaction if not given.
@@ -250,18 +254,26 @@ def prefill(Q, K, V, gate, W, *, idx=None, cnt=None, scale=None, both_branch=Fal
     flags = FLAG_BOTH_BRANCH if both_branch else 0
     nbytes = int(L.swiattn_prefill_workspace_size(B, N, Hq, Hkv, G, d, W, code, flags))
     ws = _workspace(nbytes, dev, workspace)
-    rc = L.swiattn_prefill_ex(_p(Q), _p(K), _p(V), _p(gate), _p(idx if not both_branch else None),
-                              _p(cnt if not both_branch else None), _p(out), _p(diff),
-                              B, N, Hq, Hkv, G, d, W, float(scale), code, flags,
-                              _p(ws), ws.numel(), _stream(dev), _events(events))
+    ptrs = (_p(Q), _p(K), _p(V), _p(gate), _p(idx if not both_branch else None),
+            _p(cnt if not both_branch else None), _p(out), _p(diff))
+    if anchors:
+        rc = L.swiattn_prefill_anchored(*ptrs, B, N, Hq, Hkv, G, d, W, int(anchors), float(scale),
+                                        code, flags, _p(ws), ws.numel(), _stream(dev),
+                                        _events(events))
+    else:
+        rc = L.swiattn_prefill_ex(*ptrs, B, N, Hq, Hkv, G, d, W, float(scale), code, flags,
+                                  _p(ws), ws.numel(), _stream(dev), _events(events))
     _check(rc, "swiattn_prefill")
     return out, diff
 
 
-def decode(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None, workspace=None, events=None):
+def decode(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None, workspace=None, events=None,
+           anchors=0):
     """Routed decode.  q [B,Hq,d], Kc/Vc [B,Lmax,Hkv,d], cache_len int32 [B],
     gate uint8 [B,G].  Returns o [B,Hq,d].  events: as for prefill, recorded
-    at the stage boundaries documented for swiattn_decode_ex."""
+    at the stage boundaries documented for swiattn_decode_ex.  anchors: global
+    anchor keys of the window branch (swiattn_decode_anchored); 0 calls
+    swiattn_decode_ex."""
     L = lib()
     _need(q, "q")
     code = _dtype_code(q)
@@ -284,9 +296,13 @@ def decode(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None, workspace=Non
     _need(out, "out", shape=q.shape, dtype=q.dtype, device=dev)
     nbytes = int(L.swiattn_decode_workspace_size(B, Lmax, Hq, Hkv, G, d, W, code))
     ws = _workspace(nbytes, dev, workspace)
-    rc = L.swiattn_decode_ex(_p(q), _p(Kc), _p(Vc), _p(cache_len), _p(gate), _p(out),
-                             B, Lmax, Hq, Hkv, G, d, W, float(scale), code, _p(ws), ws.numel(),
-                             _stream(dev), _events(events))
+    ptrs = (_p(q), _p(Kc), _p(Vc), _p(cache_len), _p(gate), _p(out))
+    if anchors:
+        rc = L.swiattn_decode_anchored(*ptrs, B, Lmax, Hq, Hkv, G, d, W, int(anchors), float(scale),
+                                       code, _p(ws), ws.numel(), _stream(dev), _events(events))
+    else:
+        rc = L.swiattn_decode_ex(*ptrs, B, Lmax, Hq, Hkv, G, d, W, float(scale), code, _p(ws),
+                                 ws.numel(), _stream(dev), _events(events))
     _check(rc, "swiattn_decode")
     return out
 

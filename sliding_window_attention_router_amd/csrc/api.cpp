@@ -43,6 +43,7 @@ int prefill_shape(int B, int N, int Hq, int Hkv, int G, int d, int W, float scal
   sh->G = G;
   sh->d = d;
   sh->W = W;
+  sh->A = 0;
   sh->scale = scale;
   sh->f32 = dt == SWIATTN_F32;
   sh->both_branch = (flags & SWIATTN_FLAG_BOTH_BRANCH) != 0;
@@ -63,6 +64,7 @@ int decode_shape(int B, int Lmax, int Hq, int Hkv, int G, int d, int W, float sc
   sh->G = G;
   sh->d = d;
   sh->W = W;
+  sh->A = 0;
   sh->scale = scale;
   sh->f32 = dt == SWIATTN_F32;
   if (!swi::plan_decode(*sh, plan)) return SWIATTN_ERR_UNSUPPORTED;
@@ -114,15 +116,18 @@ size_t swiattn_prefill_workspace_size(int B, int N, int Hq, int Hkv, int G, int 
   return p.bytes;
 }
 
-int swiattn_prefill_ex(const void* Q, const void* K, const void* V, const uint8_t* gate,
-                       const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B,
-                       int N, int Hq, int Hkv, int G, int d, int W, float scale,
-                       swiattn_dtype_t dtype, unsigned flags, void* ws, size_t ws_bytes,
-                       swiattn_stream_t stream, const swiattn_events_t* events) {
+int swiattn_prefill_anchored(const void* Q, const void* K, const void* V, const uint8_t* gate,
+                             const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B,
+                             int N, int Hq, int Hkv, int G, int d, int W, int anchors,
+                             float scale, swiattn_dtype_t dtype, unsigned flags, void* ws,
+                             size_t ws_bytes, swiattn_stream_t stream,
+                             const swiattn_events_t* events) {
   swi::PrefillShape sh;
   swi::PrefillPlan p;
   const int rc = prefill_shape(B, N, Hq, Hkv, G, d, W, scale, dtype, flags, &sh, &p);
   if (rc != SWIATTN_OK) return rc;
+  if (anchors < 0) return SWIATTN_ERR_INVALID_ARG;
+  sh.A = anchors < N ? anchors : N;
   if (!Q || !K || !V || !gate || !O) return SWIATTN_ERR_INVALID_ARG;
   if (sh.both_branch ? !diff : (!idx || !cnt)) return SWIATTN_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.bytes) return SWIATTN_ERR_WORKSPACE;
@@ -131,12 +136,21 @@ int swiattn_prefill_ex(const void* Q, const void* K, const void* V, const uint8_
                                     events ? events->ev : nullptr));
 }
 
+int swiattn_prefill_ex(const void* Q, const void* K, const void* V, const uint8_t* gate,
+                       const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B,
+                       int N, int Hq, int Hkv, int G, int d, int W, float scale,
+                       swiattn_dtype_t dtype, unsigned flags, void* ws, size_t ws_bytes,
+                       swiattn_stream_t stream, const swiattn_events_t* events) {
+  return swiattn_prefill_anchored(Q, K, V, gate, idx, cnt, O, diff, B, N, Hq, Hkv, G, d, W, 0,
+                                  scale, dtype, flags, ws, ws_bytes, stream, events);
+}
+
 int swiattn_prefill(const void* Q, const void* K, const void* V, const uint8_t* gate,
                     const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B, int N,
                     int Hq, int Hkv, int G, int d, int W, float scale, swiattn_dtype_t dtype,
                     unsigned flags, void* ws, size_t ws_bytes, swiattn_stream_t stream) {
-  return swiattn_prefill_ex(Q, K, V, gate, idx, cnt, O, diff, B, N, Hq, Hkv, G, d, W, scale,
-                            dtype, flags, ws, ws_bytes, stream, nullptr);
+  return swiattn_prefill_anchored(Q, K, V, gate, idx, cnt, O, diff, B, N, Hq, Hkv, G, d, W, 0,
+                                  scale, dtype, flags, ws, ws_bytes, stream, nullptr);
 }
 
 size_t swiattn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int G, int d, int W,
@@ -147,14 +161,17 @@ size_t swiattn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int G, in
   return p.bytes;
 }
 
-int swiattn_decode_ex(const void* q, const void* Kc, const void* Vc, const int32_t* cache_len,
-                      const uint8_t* gate, void* o, int B, int Lmax, int Hq, int Hkv, int G,
-                      int d, int W, float scale, swiattn_dtype_t dtype, void* ws,
-                      size_t ws_bytes, swiattn_stream_t stream, const swiattn_events_t* events) {
+int swiattn_decode_anchored(const void* q, const void* Kc, const void* Vc,
+                            const int32_t* cache_len, const uint8_t* gate, void* o, int B,
+                            int Lmax, int Hq, int Hkv, int G, int d, int W, int anchors,
+                            float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
+                            swiattn_stream_t stream, const swiattn_events_t* events) {
   swi::DecodeShape sh;
   swi::DecodePlan p;
   const int rc = decode_shape(B, Lmax, Hq, Hkv, G, d, W, scale, dtype, &sh, &p);
   if (rc != SWIATTN_OK) return rc;
+  if (anchors < 0) return SWIATTN_ERR_INVALID_ARG;
+  sh.A = anchors < Lmax ? anchors : Lmax;
   if (!q || !Kc || !Vc || !cache_len || !gate || !o) return SWIATTN_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.bytes) return SWIATTN_ERR_WORKSPACE;
   return hip_rc(swi::launch_decode(sh, p, q, Kc, Vc, cache_len, gate, o, ws,
@@ -162,12 +179,20 @@ int swiattn_decode_ex(const void* q, const void* Kc, const void* Vc, const int32
                                    events ? events->ev : nullptr));
 }
 
+int swiattn_decode_ex(const void* q, const void* Kc, const void* Vc, const int32_t* cache_len,
+                      const uint8_t* gate, void* o, int B, int Lmax, int Hq, int Hkv, int G,
+                      int d, int W, float scale, swiattn_dtype_t dtype, void* ws,
+                      size_t ws_bytes, swiattn_stream_t stream, const swiattn_events_t* events) {
+  return swiattn_decode_anchored(q, Kc, Vc, cache_len, gate, o, B, Lmax, Hq, Hkv, G, d, W, 0,
+                                 scale, dtype, ws, ws_bytes, stream, events);
+}
+
 int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t* cache_len,
                    const uint8_t* gate, void* o, int B, int Lmax, int Hq, int Hkv, int G, int d,
                    int W, float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
                    swiattn_stream_t stream) {
-  return swiattn_decode_ex(q, Kc, Vc, cache_len, gate, o, B, Lmax, Hq, Hkv, G, d, W, scale,
-                           dtype, ws, ws_bytes, stream, nullptr);
+  return swiattn_decode_anchored(q, Kc, Vc, cache_len, gate, o, B, Lmax, Hq, Hkv, G, d, W, 0,
+                                 scale, dtype, ws, ws_bytes, stream, nullptr);
 }
 
 int swiattn_decode_step(const void* Hn, const void* r, const float* bias, const void* q,

@@ -20,6 +20,12 @@
 //                      written there; a pair cut by share boundaries leaves a
 //                      normalised partial output + log-sum-exp per piece
 // decode_merge_kernel  log-sum-exp merge of the pieces of each cut pair
+//
+// Global anchors (weimeta SWA glossary, section "SWA 落地的四个常见坑",
+// pitfall 1, fix 2): with A > 0 a window head also reads the first
+// min(A, L-W) keys of the cache.  A pair with a window head then starts with
+// anchor blocks [0, 64 na) (masked to each head's anchors) before its main
+// range; the masks keep the two key sets of a head disjoint.
 #include <climits>
 
 #include "attn_core.hpp"
@@ -44,6 +50,7 @@ struct DecodeArgs {
   float* part_o;    // [2*grid][HK][D] pieces of cut pairs, slot 2w (first piece of share w) or 2w+1
   float* part_lse;  // [2*grid][HK]
   int B, Lmax, Hq, Hkv, G, W, HK, HG;
+  int A;  // global anchor keys of the window branch (0 = none)
   float sl2;
 };
 
@@ -56,15 +63,21 @@ SWI_DEV int head_lo(const DecodeArgs& a, int b, int h, int L) {
 }
 
 // Keys [lo, L) read for pair bk = (sequence, KV head): the union of the
-// ranges of its query heads.  Returns the number of 64-key blocks.
-SWI_DEV int pair_blocks(const DecodeArgs& a, int bk, int& L, int& lo) {
+// ranges of its query heads; na anchor blocks precede them when a head of
+// the pair is a window head.  Returns the number of 64-key blocks.
+SWI_DEV int pair_blocks(const DecodeArgs& a, int bk, int& L, int& lo, int& na) {
   const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
   L = clamp_len(a.cache_len[b], a.Lmax);
   const int g0 = kvh * a.HK / a.HG, g1 = (kvh * a.HK + a.HK - 1) / a.HG;
-  bool full = false;
-  for (int gg = g0; gg <= g1; ++gg) full = full || a.gate[b * a.G + gg] != 0;
+  bool full = false, win = false;
+  for (int gg = g0; gg <= g1; ++gg) {
+    const bool f = a.gate[b * a.G + gg] != 0;
+    full = full || f;
+    win = win || !f;
+  }
   lo = full ? 0 : max(0, L - a.W);
-  return (L - lo + kBN - 1) / kBN;
+  na = win ? (min(a.A, max(0, L - a.W)) + kBN - 1) / kBN : 0;
+  return na + (L - lo + kBN - 1) / kBN;
 }
 
 // First block of share w: floor(w*T/G).
@@ -79,33 +92,37 @@ SWI_DEV int lane_of(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
 // 64 consecutive pairs, one per lane, with the inclusive prefix sum of their
 // block counts (absolute: carry holds the blocks of all earlier pairs).
 struct PairWindow {
-  int base, L, lo, incl;
+  int base, L, lo, na, incl;
   SWI_DEV void fill(const DecodeArgs& a, int base_, int carry, int lane, int npairs) {
     base = base_;
     const int bk = base + lane;
     int n = 0;
     L = 1;
     lo = 0;
-    if (bk < npairs) n = pair_blocks(a, bk, L, lo);
+    na = 0;
+    if (bk < npairs) n = pair_blocks(a, bk, L, lo, na);
     incl = wave_incl_scan_i(n) + carry;
   }
 };
 
-// The blocks [blk0, blk1) of pair bk that fall into share [s, e).
+// The blocks [blk0, blk1) of pair bk that fall into share [s, e).  Block n
+// of the pair is anchor block n for n < na, else main block n - na.
 struct DecSeg {
-  int bk, b, kvh, L, lo, first, nb, blk0, blk1;
+  int bk, b, kvh, L, lo, na, first, nb, blk0, blk1;
   SWI_DEV void from(const DecodeArgs& a, const PairWindow& win, int j, int s, int e) {
     bk = win.base + j;
     b = bk / a.Hkv;
     kvh = bk - b * a.Hkv;
     L = lane_of(win.L, j);
     lo = lane_of(win.lo, j);
+    na = lane_of(win.na, j);
     const int incl = lane_of(win.incl, j);
-    nb = (L - lo + kBN - 1) / kBN;
+    nb = na + (L - lo + kBN - 1) / kBN;
     first = incl - nb;
     blk0 = max(s, first) - first;
     blk1 = min(e, incl) - first;
   }
+  SWI_DEV int kb(int n) const { return n < na ? n * kBN : lo + (n - na) * kBN; }
   template <typename T, int D>
   SWI_DEV const T* kbase(const DecodeArgs& a) const {
     return static_cast<const T*>(a.Kc) + (int64_t(b) * a.Lmax * a.Hkv + kvh) * D;
@@ -131,8 +148,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int bk = base + k * kWave + lane;
-      int L, lo;
-      n[k] = bk < npairs ? pair_blocks(a, bk, L, lo) : 0;
+      int L, lo, na;
+      n[k] = bk < npairs ? pair_blocks(a, bk, L, lo, na) : 0;
     }
     tsum += n[0] + n[1] + n[2] + n[3];
   }
@@ -160,7 +177,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   DecSeg cur;
   cur.from(a, win, j, s, e);
   Core c;
-  int lo_h = 0, hi = -1, wmax_lo = 0;
+  int lo_h = 0, hi = -1, ahi = -1, wmax_lo = 0;
   auto begin = [&]() {
     c.init();
     const int h = cur.kvh * a.HK + q;
@@ -168,13 +185,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     c.load_q(valid ? qp : nullptr, g);
     lo_h = valid ? head_lo(a, cur.b, h, cur.L) : 0;
     hi = valid ? cur.L - 1 : -1;
+    // a window head's anchors [0, ahi] end where its window starts; a full
+    // head (lo_h = 0) has none
+    ahi = valid ? min(a.A, lo_h) - 1 : -1;
     // heads of one KV head may start at different keys (window heads next
     // to full ones): blocks before the latest start are masked
     wmax_lo = wave_max_i(valid ? lo_h : -1);
   };
   begin();
   KVLoader<T, D, kDecThreads, SWI_DEC_STREAM> ld;
-  ld.load(cur.kbase<T, D>(a), cur.vbase<T, D>(a), rs, cur.lo + cur.blk0 * kBN, cur.L, lane);
+  ld.load(cur.kbase<T, D>(a), cur.vbase<T, D>(a), rs, cur.kb(cur.blk0), cur.L, lane);
   int n = cur.blk0;
   while (true) {
     // the block after this one, possibly the first block of the next pair
@@ -193,10 +213,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     __syncthreads();
     ld.store(lds, lane);
     __syncthreads();
-    if (more) ld.load(nx.kbase<T, D>(a), nx.vbase<T, D>(a), rs, nx.lo + nn * kBN, nx.L, lane);
-    const int kb = cur.lo + n * kBN;
-    const bool masked = kb < wmax_lo || kb + kBN > cur.L;
-    c.block(lds, kb, masked, lo_h, hi, a.sl2, q, g);
+    if (more) ld.load(nx.kbase<T, D>(a), nx.vbase<T, D>(a), rs, nx.kb(nn), nx.L, lane);
+    const int kb = cur.kb(n);
+    const bool anc = n < cur.na;  // wave-uniform
+    const bool masked = anc || kb < wmax_lo || kb + kBN > cur.L;
+    c.block(lds, kb, masked, anc ? 0 : lo_h, anc ? ahi : hi, a.sl2, q, g);
     if (!seg_end) {
       n = nn;
       continue;
@@ -349,6 +370,7 @@ hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void*
   a.Hkv = sh.Hkv;
   a.G = sh.G;
   a.W = sh.W;
+  a.A = sh.A;
   a.HK = p.HK;
   a.HG = p.HG;
   a.sl2 = sh.scale * kLog2e;

@@ -21,6 +21,7 @@ hipError_t launch_regularizer(const float* z, const float* nll, const float* dif
 // ---- prefill ------------------------------------------------------------
 struct PrefillShape {
   int B, N, Hq, Hkv, G, d, W;
+  int A;  // global anchor keys of the window branch (0 = none)
   float scale;
   bool f32;
   bool both_branch;
@@ -52,6 +53,7 @@ hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const vo
 // ---- decode -------------------------------------------------------------
 struct DecodeShape {
   int B, Lmax, Hq, Hkv, G, d, W;
+  int A;  // global anchor keys of the window branch (0 = none)
   float scale;
   bool f32;
 };

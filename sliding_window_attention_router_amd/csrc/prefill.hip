@@ -20,6 +20,14 @@
 // The window and far key sets are disjoint and cover [0, i], so the merge is
 // the exact full softmax up to rounding.
 //
+// Global anchors (weimeta SWA glossary, section "SWA 落地的四个常见坑",
+// pitfall 1, fix 2): with A > 0 every window-branch query also sees the
+// first A keys of its sequence, [0, min(A, i-W+1) - 1].  A window tile then
+// walks the anchor blocks before its window blocks (the two masks keep each
+// row's key sets disjoint, so a block that falls in both segments is simply
+// visited twice with different keys), and the far part of a gate=1 row
+// shrinks to [A, i-W].
+//
 // Both-branch mode: the same launches with every row taking the full
 // branch (no compaction: the far tiles are consecutive positions).  The
 // merge then also writes the per-(head, token) squared distance between
@@ -56,6 +64,7 @@ struct PrefillArgs {
   float* diff;      // [B,N]
   int* queue;       // [8] window-tile queue positions (zeroed by the schedule kernel)
   int B, N, Hq, Hkv, G, W;
+  int A;  // global anchor keys of the window branch (0 = none)
   int HK, HG, hpu, units, tpt_band, tpt_far, band_tiles, far_tiles, max_items;
   int far_grid;  // workgroups of attn_kernel reserved for far items (multiple of 8)
   int band_grid; // workgroups of attn_kernel that work off the window-tile queues
@@ -259,7 +268,7 @@ SWI_DEV void band_tile(const PrefillArgs& a, char* buf0, char* buf1, int lin) {
   const int q = lane & 31, g = lane >> 5;
   const int q0 = tile * a.tpt_band;
   const int qlast = min(a.N - 1, q0 + a.tpt_band - 1);
-  int tok[TPW], h[TPW], lo[TPW], hi[TPW];
+  int tok[TPW], h[TPW], lo[TPW], hi[TPW], alo[TPW], ahi[TPW];
   bool valid[TPW];
   Core c;
   c.init();
@@ -273,6 +282,8 @@ SWI_DEV void band_tile(const PrefillArgs& a, char* buf0, char* buf1, int lin) {
     h[t] = kvh * a.HK + hh;
     lo[t] = valid[t] ? max(0, tok[t] - a.W + 1) : 0;
     hi[t] = valid[t] ? tok[t] : -1;
+    alo[t] = 0;
+    ahi[t] = valid[t] ? min(a.A, lo[t]) - 1 : -1;  // anchors end where the window starts
     c.load_q(t, valid[t] ? Qp + ((int64_t(b) * a.N + tok[t]) * a.Hq + h[t]) * D : nullptr, g);
   }
   TileBounds<TPW> tb;
@@ -281,6 +292,14 @@ SWI_DEV void band_tile(const PrefillArgs& a, char* buf0, char* buf1, int lin) {
   const T* Kb = static_cast<const T*>(a.K) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
   const T* Vb = static_cast<const T*>(a.V) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
   const int64_t rs = int64_t(a.Hkv) * D;
+  // anchor blocks first (the last row of the tile has the most anchors)
+  const int na = (min(a.A, max(0, qlast - a.W + 1)) + kBN - 1) / kBN;
+  if (na > 0) {
+    TileBounds<TPW> tba;
+    tba.init(valid, alo, ahi);
+    block_loop<Core, T, D, NT>(c, buf0, buf1, Kb, Vb, rs, 0, na, a.N, tba, alo, ahi, a.sl2, tid, q, g);
+    __syncthreads();  // every wave is done with the staging buffers
+  }
   const int kb0 = (max(0, q0 - a.W + 1) / kBN) * kBN;
   block_loop<Core, T, D, NT>(c, buf0, buf1, Kb, Vb, rs, kb0, (qlast - kb0) / kBN + 1, a.N, tb, lo, hi,
                              a.sl2, tid, q, g);
@@ -359,8 +378,8 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
     int blocks = 0;
     if (ntok > 0) {
       const int tlast = far_pos(a, b, g, t * a.tpt_far + ntok - 1);
-      const int fh = tlast - a.W;
-      if (fh >= 0) blocks = fh / kBN + 1;
+      const int fh = tlast - a.W;  // far keys [A, fh]
+      if (fh >= a.A) blocks = fh / kBN - a.A / kBN + 1;
     }
     sv.n_items[T_] = blocks;
     mine += blocks;
@@ -432,8 +451,9 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
 }
 
 // ---------------------------------------------------------------------------
-// Far part of the full branch for gathered rows.  One workgroup per work
-// item (tile, chunk); grid = upper bound, idle workgroups exit at once.
+// Far part of the full branch for gathered rows: keys [A, i-W] (the full set
+// minus the window and its anchors).  One workgroup per work item (tile,
+// chunk); grid = upper bound, idle workgroups exit at once.
 // A tile with a single chunk merges with the window result in place; the
 // chunks of longer tiles write normalised partials for merge_kernel.
 // ---------------------------------------------------------------------------
@@ -453,8 +473,9 @@ SWI_DEV void far_item(const PrefillArgs& a, char* buf0, char* buf1, int item) {
   const int cnt = far_count(a, b, g_gate);
   const int ntok = min(a.tpt_far, cnt - t_ * a.tpt_far);
   const int far_hi = far_pos(a, b, g_gate, t_ * a.tpt_far + ntok - 1) - a.W;
-  const int c0 = ch * cb * kBN;
-  const int c1 = min(far_hi + 1, (ch + 1) * cb * kBN);  // keys [c0, c1)
+  const int fb = (a.A / kBN) * kBN;  // block holding the first far key A
+  const int c0 = fb + ch * cb * kBN;
+  const int c1 = min(far_hi + 1, fb + (ch + 1) * cb * kBN);  // keys [c0, c1)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane & 31, g = lane >> 5;
@@ -470,7 +491,7 @@ SWI_DEV void far_item(const PrefillArgs& a, char* buf0, char* buf1, int item) {
     valid[t] = slot < ntok;
     tok[t] = valid[t] ? far_pos(a, b, g_gate, t_ * a.tpt_far + slot) : 0;
     h[t] = u * a.hpu + hh;
-    lo[t] = c0;
+    lo[t] = max(c0, a.A);
     hi[t] = valid[t] ? min(tok[t] - a.W, c1 - 1) : -1;
     c.load_q(t, valid[t] ? Qp + ((int64_t(b) * a.N + tok[t]) * a.Hq + h[t]) * D : nullptr, g);
   }
@@ -531,8 +552,9 @@ SWI_DEV int resolve(int* queue, const TileQueue& tq, int& x, int p) {
 }
 
 // Window tile lin: tpt_band consecutive tokens x the HK heads of one KV head.
+// Its blocks: na anchor blocks [0, 64 na), then nb window blocks from kb0.
 struct BandTile {
-  int b, kvh, q0, kb0, nb;
+  int b, kvh, q0, kb0, nb, na;
   SWI_DEV void set(const PrefillArgs& a, int lin) {
     const int tile = lin % a.band_tiles, bk = lin / a.band_tiles;
     b = bk / a.Hkv;
@@ -541,7 +563,10 @@ struct BandTile {
     const int qlast = min(a.N - 1, q0 + a.tpt_band - 1);
     kb0 = (max(0, q0 - a.W + 1) / kBN) * kBN;
     nb = (qlast - kb0) / kBN + 1;
+    na = (min(a.A, max(0, qlast - a.W + 1)) + kBN - 1) / kBN;
   }
+  SWI_DEV int total() const { return na + nb; }
+  SWI_DEV int kb(int n) const { return n < na ? n * kBN : kb0 + (n - na) * kBN; }
 };
 
 template <typename T, int D>
@@ -576,7 +601,7 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
   c.init();
   c.load_q(0, qrow(t), g);
   Dma::issue(buf0, static_cast<const T*>(a.K) + kv_off(t), static_cast<const T*>(a.V) + kv_off(t), rs,
-             t.kb0, a.N, tid);
+             t.kb(0), a.N, tid);
   int s = 0;  // blocks streamed so far: block s sits in buffer s % 2
   int next_raw = 0;  // thread 0: raw position of the pending claim on queue qx
   if (tid == 0) next_raw = claim(a.queue, qx);
@@ -585,27 +610,33 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
     const int tok = t.q0 + slot;
     const bool valid = slot < a.tpt_band && tok < a.N;
     const int lo = valid ? max(0, tok - a.W + 1) : 0, hi = valid ? tok : -1;
-    TileBounds<1> tb;
+    const int ahi = valid ? min(a.A, lo) - 1 : -1;  // anchors [0, ahi]
+    TileBounds<1> tb, tba;
     {
       const bool v1[1] = {valid};
       const int l1[1] = {lo}, h1[1] = {hi};
       tb.init(v1, l1, h1);
+      if (t.na > 0) {
+        const int l0[1] = {0}, h0[1] = {ahi};
+        tba.init(v1, l0, h0);
+      }
     }
     const T* Kb = static_cast<const T*>(a.K) + kv_off(t);
     const T* Vb = static_cast<const T*>(a.V) + kv_off(t);
     // the next id is published at step pub and read one barrier later
-    const int pub = t.nb >= 2 ? t.nb - 2 : 0;
-    const int rd = t.nb >= 2 ? pub + 1 : 0;
+    const int nbt = t.total();
+    const int pub = nbt >= 2 ? nbt - 2 : 0;
+    const int rd = nbt >= 2 ? pub + 1 : 0;
     int nlin = -1;
     BandTile nt;
     nt.set(a, 0);
-    for (int n = 0; n < t.nb; ++n, ++s) {
+    for (int n = 0; n < nbt; ++n, ++s) {
       char* cur = (s & 1) ? buf1 : buf0;
       char* nxt = (s & 1) ? buf0 : buf1;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (n == pub && tid == 0) s_next = resolve(a.queue, tq, qx, next_raw);
-      if (t.nb < 2) __syncthreads();
+      if (nbt < 2) __syncthreads();
       if (n == rd) {
         nlin = __builtin_amdgcn_readfirstlane(s_next);
         if (nlin >= 0) nt.set(a, nlin);
@@ -613,16 +644,17 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
         // tile publishes it
         if (tid == 0 && nlin >= 0) next_raw = claim(a.queue, qx);
       }
-      if (n + 1 < t.nb)
-        Dma::issue(nxt, Kb, Vb, rs, t.kb0 + (n + 1) * kBN, a.N, tid);
+      if (n + 1 < nbt)
+        Dma::issue(nxt, Kb, Vb, rs, t.kb(n + 1), a.N, tid);
       else if (nlin >= 0)
         Dma::issue(nxt, static_cast<const T*>(a.K) + kv_off(nt), static_cast<const T*>(a.V) + kv_off(nt),
-                   rs, nt.kb0, a.N, tid);
-      const int kb = t.kb0 + n * kBN;
-      if (!tb.needed(kb)) continue;
+                   rs, nt.kb(0), a.N, tid);
+      const int kb = t.kb(n);
+      const bool anc = n < t.na;  // wave-uniform
+      if (!(anc ? tba.needed(kb) : tb.needed(kb))) continue;
       // last block of the tile: the next tile's queries follow its scores
-      const bool pre = n + 1 == t.nb && nlin >= 0;
-      c.block_hook(cur, kb, tb.masked(kb), lo, hi, a.sl2, q, g, [&]() {
+      const bool pre = n + 1 == nbt && nlin >= 0;
+      c.block_hook(cur, kb, anc || tb.masked(kb), anc ? 0 : lo, anc ? ahi : hi, a.sl2, q, g, [&]() {
         if (pre) c.c.load_q(qrow(nt), g);
       });
       q_pref = q_pref || pre;
@@ -722,7 +754,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PrefillArgs a) {
     // (the 8 threads of a row take every branch together)
     if (slot >= ntok) continue;
     const int tok = far_pos(a, b, g_gate, t * a.tpt_far + slot);
-    if (tok < a.W) continue;
+    if (tok - a.W < a.A) continue;  // no far keys: O_FULL = O_SWA
     const int h = u * a.hpu + hh;
     const float ls = a.lse_s[(int64_t(b) * a.Hq + h) * a.N + tok];
     float M = ls;
@@ -911,6 +943,7 @@ hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const vo
   a.Hkv = sh.Hkv;
   a.G = sh.G;
   a.W = sh.W;
+  a.A = sh.A;
   a.HK = p.HK;
   a.HG = p.HG;
   a.hpu = p.hpu;

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("swiattn_route", "swiattn_prefill", "swiattn_decode", "swiattn_prefill_workspace_size",
               "swiattn_decode_workspace_size", "swiattn_strerror", "swiattn_prefill_ex", "swiattn_decode_ex",
-              "swiattn_regularizer", "swiattn_decode_step"):
+              "swiattn_regularizer", "swiattn_decode_step", "swiattn_prefill_anchored",
+              "swiattn_decode_anchored"):
         assert n in names
 
 
@@ -157,3 +158,40 @@ def test_decode_step_rejects_invalid_arguments(lib, kw, code):
                                  a["Hkv"], a["G"], a["d"], a["W"], a["scale"], a["dt"], a["ws"], a["ws_bytes"],
                                  a["stream"])
     assert rc == code
+
+
+def _prefill_anchored(lib, anchors, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, gate=FAKE, idx=FAKE, cnt=FAKE, O=FAKE, diff=None,
+             B=1, N=100, Hq=4, Hkv=2, G=1, d=128, W=16, scale=0.088, dt=BF16, flags=0,
+             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.swiattn_prefill_anchored(a["Q"], a["K"], a["V"], a["gate"], a["idx"], a["cnt"], a["O"],
+                                        a["diff"], a["B"], a["N"], a["Hq"], a["Hkv"], a["G"], a["d"],
+                                        a["W"], anchors, a["scale"], a["dt"], a["flags"], a["ws"],
+                                        a["ws_bytes"], a["stream"], None)
+
+
+def _decode_anchored(lib, anchors, **kw):
+    a = dict(q=FAKE, Kc=FAKE, Vc=FAKE, lens=FAKE, gate=FAKE, o=FAKE, B=4, Lmax=100, Hq=4, Hkv=2, G=1,
+             d=128, W=16, scale=0.088, dt=BF16, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.swiattn_decode_anchored(a["q"], a["Kc"], a["Vc"], a["lens"], a["gate"], a["o"], a["B"],
+                                       a["Lmax"], a["Hq"], a["Hkv"], a["G"], a["d"], a["W"], anchors,
+                                       a["scale"], a["dt"], a["ws"], a["ws_bytes"], a["stream"], None)
+
+
+@pytest.mark.parametrize("anchors,kw,code", [
+    (-1, {}, INVALID), (-256, {}, INVALID),
+    (256, dict(N=0), INVALID), (256, dict(d=96), UNSUPPORTED), (256, dict(Q=None), INVALID),
+    (256, dict(ws=None), WORKSPACE), (256, dict(flags=1, diff=None), INVALID),
+])
+def test_prefill_anchored_rejects_invalid_arguments(lib, anchors, kw, code):
+    assert _prefill_anchored(lib, anchors, **kw) == code
+
+
+@pytest.mark.parametrize("anchors,kw,code", [
+    (-1, {}, INVALID), (256, dict(Lmax=0), INVALID), (256, dict(d=32), UNSUPPORTED),
+    (256, dict(lens=None), INVALID), (256, dict(ws_bytes=8), WORKSPACE),
+])
+def test_decode_anchored_rejects_invalid_arguments(lib, anchors, kw, code):
+    assert _decode_anchored(lib, anchors, **kw) == code
