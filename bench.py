@@ -61,6 +61,10 @@ def parse():
                     help="timed serving decode steps (route + append + decode; after the timed steps; 0 = skip)")
     ap.add_argument("--both-steps", type=int, default=3,
                     help="timed runs of the both-branch prefill (after the timed steps; 0 = skip)")
+    ap.add_argument("--anchor-steps", type=int, default=3,
+                    help="timed runs of the anchored prefill and decode (after the timed steps; 0 = skip)")
+    ap.add_argument("--anchors", type=int, default=256,
+                    help="global anchor keys of the window branch in the anchored runs")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB before the steps "
                          "(a known-size reference for hardware byte counters)")
@@ -68,13 +72,14 @@ def parse():
 
 
 # ------------------------------------------------------------------ accounting
-def prefill_pairs(gate, W, Hq, G):
+def prefill_pairs(gate, W, Hq, G, A=0):
     """Attended (query head, key) pairs: full rows see i+1 keys, window rows
-    min(i+1, W).  Returns (useful total, window part, far part)."""
+    min(i+1, W) plus min(A, i-W+1) anchors when i-W+1 > 0.  Returns (useful
+    total, window part, far part)."""
     B, N, _ = gate.shape
     i = np.arange(N, dtype=np.int64)
-    band = np.minimum(i + 1, W)
-    far = np.maximum(i + 1 - W, 0)
+    band = np.minimum(i + 1, W) + np.minimum(A, np.maximum(i - W + 1, 0))
+    far = i + 1 - band
     tot_b = tot_f = 0
     for h in range(Hq):
         g = gate[:, :, h * G // Hq].astype(bool)
@@ -83,9 +88,10 @@ def prefill_pairs(gate, W, Hq, G):
     return tot_b + tot_f, tot_b, tot_f
 
 
-def decode_bytes(gate, cache_len, W, Hq, Hkv, d, elem=2):
+def decode_bytes(gate, cache_len, W, Hq, Hkv, d, elem=2, A=0):
     """Algorithmic HBM bytes of one decode step: every attended key and value
-    row of a KV head is read once for its Hq/Hkv query heads, plus q and o."""
+    row of a KV head is read once for its Hq/Hkv query heads, plus q and o
+    (a window pair also reads its min(A, L-W) anchors)."""
     B, G = gate.shape
     HK = Hq // Hkv
     keys = 0
@@ -93,7 +99,7 @@ def decode_bytes(gate, cache_len, W, Hq, Hkv, d, elem=2):
         L = int(cache_len[b])
         for kv in range(Hkv):
             full = any(gate[b, (kv * HK + j) * G // Hq] for j in range(HK))
-            keys += L if full else min(L, W)
+            keys += L if full else min(L, W) + min(A, max(0, L - W))
     return keys * d * 2 * elem + B * Hq * d * 2 * elem, keys
 
 
@@ -255,6 +261,9 @@ def main():
             if args.both_steps > 0 else None)
     serve = (serve_run(swa, q_d, Kc, Vc, len_d, r, bias, W, args.serve_steps)
              if args.serve_steps > 0 else None)
+    anch = (anchors_run(swa, Q, K, V, gate, idx, cnt, W, args.anchors, q_d, Kc, Vc, len_d, gate_d,
+                        dec, args.anchor_steps)
+            if args.anchor_steps > 0 else None)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -288,6 +297,7 @@ def main():
                        "frac_of_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4)},
             "both_branch": both,
             "serving_step": serve,
+            "anchors": anch,
         },
         "kernel_ms": {k: round(v, 4) for k, v in t.items()},
         "roofline": dict(rooflines[dominant], kernel=dominant),
@@ -339,6 +349,60 @@ def serve_run(swa, q, Kc, Vc, cache_len, r, bias, W, steps):
             "ms": round(ms, 4), "tok_per_s": round(B / (ms * 1e-3), 1),
             "GB_per_s": round(byts / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def anchors_run(swa, Q, K, V, gate, idx, cnt, W, A, q_d, Kc, Vc, len_d, gate_d, dec, steps):
+    """Anchored prefill and decode on the same inputs and gates (outside the
+    timed steps): the window branch also sees the first A keys.  Stage times
+    from events recorded inside the library; useful work counts the anchors
+    (prefill) and the anchor rows read (decode)."""
+    import torch
+    B, N, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    dev = Q.device
+    G = gate.shape[2]
+    O = torch.empty_like(Q)
+    o = torch.empty_like(q_d)
+    ws_p = torch.empty(swa.prefill_workspace_size(B, N, Hq, Hkv, G, d, W), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(swa.decode_workspace_size(q_d.shape[0], Kc.shape[1], Hq, Hkv, gate_d.shape[1], d, W),
+                       dtype=torch.uint8, device=dev)
+
+    def run(ev=None):
+        swa.prefill(Q, K, V, gate, W, idx=idx, cnt=cnt, out=O, workspace=ws_p, anchors=A,
+                    events=ev[0:4] if ev is not None else None)
+        swa.decode(q_d, Kc, Vc, len_d, gate_d, W, out=o, workspace=ws_d, anchors=A,
+                   events=ev[4:7] if ev is not None else None)
+
+    run()
+    torch.cuda.synchronize()
+    sets = []
+    for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+        for e in ev:
+            e.record()
+        sets.append(ev)
+    torch.cuda.synchronize()
+    for ev in sets:
+        run(ev)
+    torch.cuda.synchronize()
+
+    def avg(i, j):
+        return float(np.mean([ev[i].elapsed_time(ev[j]) for ev in sets]))
+
+    pre_ms, attn_ms, dec_ms, split_ms = avg(0, 3), avg(1, 2), avg(4, 6), avg(4, 5)
+    useful = prefill_pairs(gate.cpu().numpy(), W, Hq, G, A)[0]
+    flop = 4.0 * d * useful
+    dbytes, keys = decode_bytes(dec["gate"], dec["cache_len"], W, Hq, Hkv, d, A=A)
+    return {"anchors": A,
+            "prefill": {"useful_tflop": round(flop / 1e12, 4), "ms": round(pre_ms, 4),
+                        "tflops": round(flop / (pre_ms * 1e-3) / 1e12, 2),
+                        "kernel_ms": {"far_schedule": round(avg(0, 1), 4), "attn": round(attn_ms, 4),
+                                      "merge": round(avg(2, 3), 4)},
+                        "attn_frac_of_bf16_peak": round(flop / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+            "decode": {"attended_kv_rows": keys, "bytes": dbytes, "ms": round(dec_ms, 4),
+                       "tok_per_s": round(q_d.shape[0] / (dec_ms * 1e-3), 1),
+                       "GB_per_s": round(dbytes / (dec_ms * 1e-3) / 1e9, 1),
+                       "splitk_frac_of_hbm_peak": round(dbytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
 def both_branch_run(swa, Q, K, V, gate, W, steps, H, r, bias):

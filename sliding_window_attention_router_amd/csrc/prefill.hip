@@ -553,6 +553,8 @@ SWI_DEV int resolve(int* queue, const TileQueue& tq, int& x, int p) {
 
 // Window tile lin: tpt_band consecutive tokens x the HK heads of one KV head.
 // Its blocks: na anchor blocks [0, 64 na), then nb window blocks from kb0.
+// kAnch = false compiles the anchor-free stream (na = 0 is a constant).
+template <bool kAnch>
 struct BandTile {
   int b, kvh, q0, kb0, nb, na;
   SWI_DEV void set(const PrefillArgs& a, int lin) {
@@ -563,13 +565,14 @@ struct BandTile {
     const int qlast = min(a.N - 1, q0 + a.tpt_band - 1);
     kb0 = (max(0, q0 - a.W + 1) / kBN) * kBN;
     nb = (qlast - kb0) / kBN + 1;
-    na = (min(a.A, max(0, qlast - a.W + 1)) + kBN - 1) / kBN;
+    na = kAnch ? (min(a.A, max(0, qlast - a.W + 1)) + kBN - 1) / kBN : 0;
   }
-  SWI_DEV int total() const { return na + nb; }
-  SWI_DEV int kb(int n) const { return n < na ? n * kBN : kb0 + (n - na) * kBN; }
+  SWI_DEV int anchors() const { return kAnch ? na : 0; }
+  SWI_DEV int total() const { return anchors() + nb; }
+  SWI_DEV int kb(int n) const { return n < anchors() ? n * kBN : kb0 + (n - anchors()) * kBN; }
 };
 
-template <typename T, int D>
+template <typename T, int D, bool kAnch>
 SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
   using Core = typename TileCfg<T, D>::Core;
   constexpr int NT = TileCfg<T, D>::kWaves * 64;
@@ -589,6 +592,7 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
   const int r = wave * kQR + q, slot = r / a.HK, hh = r - slot * a.HK;
   const T* Qp = static_cast<const T*>(a.Q);
   const int64_t rs = int64_t(a.Hkv) * D;
+  using BandTile = swi::BandTile<kAnch>;
   auto qrow = [&](const BandTile& t) -> const T* {
     const int tok = t.q0 + slot;
     const bool v = slot < a.tpt_band && tok < a.N;
@@ -616,7 +620,7 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
       const bool v1[1] = {valid};
       const int l1[1] = {lo}, h1[1] = {hi};
       tb.init(v1, l1, h1);
-      if (t.na > 0) {
+      if (t.anchors() > 0) {
         const int l0[1] = {0}, h0[1] = {ahi};
         tba.init(v1, l0, h0);
       }
@@ -650,7 +654,7 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
         Dma::issue(nxt, static_cast<const T*>(a.K) + kv_off(nt), static_cast<const T*>(a.V) + kv_off(nt),
                    rs, nt.kb(0), a.N, tid);
       const int kb = t.kb(n);
-      const bool anc = n < t.na;  // wave-uniform
+      const bool anc = n < t.anchors();  // wave-uniform
       if (!(anc ? tba.needed(kb) : tb.needed(kb))) continue;
       // last block of the tile: the next tile's queries follow its scores
       const bool pre = n + 1 == nbt && nlin >= 0;
@@ -697,7 +701,10 @@ __global__ __launch_bounds__((TileCfg<T, D>::kWaves * 64), (TileCfg<T, D>::kMinW
     return;
   }
   if constexpr (TileCfg<T, D>::kDma) {
-    band_worker<T, D>(a, buf0, buf1);
+    if (a.A > 0)
+      band_worker<T, D, true>(a, buf0, buf1);
+    else
+      band_worker<T, D, false>(a, buf0, buf1);
   } else {
     const int lin = xcd_slice(blockIdx.x - a.far_grid, a.band_tiles * a.B * a.Hkv);
     if (lin >= 0) band_tile<T, D>(a, buf0, buf1, lin);

@@ -45,3 +45,20 @@ def test_profiled_traffic_is_tied_to_the_kernel_sources(tmp_path):
     stale.write_text("kernel sources sha256: `" + "0" * 64 + "`\n\n" + table)
     assert bench.profiled_traffic(str(stale)) == {}
     assert bench.profiled_traffic(str(tmp_path / "missing.md")) == {}
+
+
+def test_anchored_accounting_closed_form():
+    """Window rows past the window add min(A, i-W+1) anchor pairs; full rows
+    are unchanged; decode window pairs read min(A, L-W) anchor rows more."""
+    N, W, Hq, A = 1000, 64, 4, 100
+    zeros = np.zeros((1, N, 1), np.uint8)
+    u0, b0, f0 = bench.prefill_pairs(zeros, W, Hq, 1)
+    uA, bA, fA = bench.prefill_pairs(zeros, W, Hq, 1, A)
+    # sum over i >= W of min(A, i-W+1) = A(A+1)/2 + (N-W-A)A
+    assert uA - u0 == Hq * (A * (A + 1) // 2 + (N - W - A) * A) and fA == 0
+    ones = np.ones((1, N, 1), np.uint8)
+    assert bench.prefill_pairs(ones, W, Hq, 1, A)[0] == Hq * N * (N + 1) // 2
+    lens = np.array([32768, 32768, 500, 1100])
+    gate = np.array([[1], [0], [0], [0]], np.uint8)
+    _, keys = bench.decode_bytes(gate, lens, 1024, 16, 4, 128, A=256)
+    assert keys == 4 * (32768 + (1024 + 256) + 500 + (1024 + 76))
