@@ -61,7 +61,7 @@ def parse():
                     help="timed serving decode steps (route + append + decode; after the timed steps; 0 = skip)")
     ap.add_argument("--both-steps", type=int, default=3,
                     help="timed runs of the both-branch prefill (after the timed steps; 0 = skip)")
-    ap.add_argument("--anchor-steps", type=int, default=3,
+    ap.add_argument("--anchor-steps", type=int, default=10,
                     help="timed runs of the anchored prefill and decode (after the timed steps; 0 = skip)")
     ap.add_argument("--anchors", type=int, default=256,
                     help="global anchor keys of the window branch in the anchored runs")

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   DecSeg cur;
   cur.from(a, win, j, s, e);
   Core c;
-  int lo_h = 0, hi = -1, ahi = -1, wmax_lo = 0;
+  int lo_h = 0, hi = -1, ahi = -1, wmax_lo = 0, wmin_ahi = -1;
   auto begin = [&]() {
     c.init();
     const int h = cur.kvh * a.HK + q;
@@ -188,6 +188,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     // a window head's anchors [0, ahi] end where its window starts; a full
     // head (lo_h = 0) has none
     ahi = valid ? min(a.A, lo_h) - 1 : -1;
+    // anchor blocks every head covers whole need no mask
+    wmin_ahi = wave_min_i(valid ? ahi : INT_MAX);
     // heads of one KV head may start at different keys (window heads next
     // to full ones): blocks before the latest start are masked
     wmax_lo = wave_max_i(valid ? lo_h : -1);
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     if (more) ld.load(nx.kbase<T, D>(a), nx.vbase<T, D>(a), rs, nx.kb(nn), nx.L, lane);
     const int kb = cur.kb(n);
     const bool anc = n < cur.na;  // wave-uniform
-    const bool masked = anc || kb < wmax_lo || kb + kBN > cur.L;
+    const bool masked = anc ? kb + kBN - 1 > wmin_ahi : (kb < wmax_lo || kb + kBN > cur.L);
     c.block(lds, kb, masked, anc ? 0 : lo_h, anc ? ahi : hi, a.sl2, q, g);
     if (!seg_end) {
       n = nn;

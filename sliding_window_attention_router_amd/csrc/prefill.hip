@@ -658,7 +658,8 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
       if (!(anc ? tba.needed(kb) : tb.needed(kb))) continue;
       // last block of the tile: the next tile's queries follow its scores
       const bool pre = n + 1 == nbt && nlin >= 0;
-      c.block_hook(cur, kb, anc || tb.masked(kb), anc ? 0 : lo, anc ? ahi : hi, a.sl2, q, g, [&]() {
+      const bool msk = anc ? tba.masked(kb) : tb.masked(kb);
+      c.block_hook(cur, kb, msk, anc ? 0 : lo, anc ? ahi : hi, a.sl2, q, g, [&]() {
         if (pre) c.c.load_q(qrow(nt), g);
       });
       q_pref = q_pref || pre;
