@@ -410,6 +410,61 @@ struct KVDma {
   }
 };
 
+// Register-staged loads into the DMA layout (used by decode, which keeps one
+// LDS buffer per wave): lane i of copy m loads the 16 bytes that the DMA
+// copy above would place at buf + m*1024 + 16i (the same source swizzle),
+// and stores them there, so the stores are linear 16-byte writes with no
+// transposition.  K and V are loaded and stored separately, so that the
+// next block's K loads can be issued before the current block's V is
+// stored.  kStream adds the non-temporal hint (rows read once).
+template <int D, int NT, bool kStream>
+struct KVRegDma {
+  using L = LdsDma<D>;
+  static constexpr int kCopies = L::kKBytes / 1024;
+  static constexpr int kPer = kCopies / (NT / 64);
+  static_assert(kCopies % (NT / 64) == 0, "copies per wave");
+  u32x4 kr[kPer], vr[kPer];
+
+  template <bool kIsK>
+  SWI_DEV static void load_part(u32x4 (&r)[kPer], const bf16_t* __restrict__ base, int64_t rs, int kb,
+                                int kend, int tid) {
+    const int wave = tid >> 6, lane = tid & 63;
+    const char* p0 = reinterpret_cast<const char*>(base + int64_t(kb) * rs);
+    const uint32_t rb = uint32_t(rs) * 2u;
+    const int last = kend - 1 - kb;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int m = wave * kPer + i;
+      const int byte = m * 1024 + lane * 16;
+      const int row = byte / L::kRowB, pc = (byte % L::kRowB) >> 4;
+      const int sw = kIsK ? L::k_swz(row) : L::v_swz(row);
+      r[i] = load16<kStream>(p0 + (int64_t(min(row, last)) * rb + ((pc ^ sw) << 4)));
+    }
+  }
+  SWI_DEV void load_k(const bf16_t* Kb, int64_t rs, int kb, int kend, int tid) {
+    load_part<true>(kr, Kb, rs, kb, kend, tid);
+  }
+  SWI_DEV void load_v(const bf16_t* Vb, int64_t rs, int kb, int kend, int tid) {
+    load_part<false>(vr, Vb, rs, kb, kend, tid);
+  }
+  SWI_DEV void load(const bf16_t* Kb, const bf16_t* Vb, int64_t rs, int kb, int kend, int tid) {
+    load_k(Kb, rs, kb, kend, tid);
+    load_v(Vb, rs, kb, kend, tid);
+  }
+  SWI_DEV void store_k(char* lds, int tid) const {
+    const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      *reinterpret_cast<u32x4*>(lds + (wave * kPer + i) * 1024 + lane * 16) = kr[i];
+  }
+  SWI_DEV void store_v(char* lds, int tid) const {
+    const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      *reinterpret_cast<u32x4*>(lds + L::kKBytes + (wave * kPer + i) * 1024 + lane * 16) = vr[i];
+  }
+};
+
 // LDS reads of the DMA layout are issued from inline assembly with explicit
 // waits.  The compiler cannot tell that the transposing reads touch only
 // the buffer that is not being filled, and would otherwise wait for the

@@ -34,7 +34,7 @@
 namespace swi {
 
 constexpr int kDecThreads = 64;  // one wave per workgroup
-constexpr int kDecGrid = 1024;   // four 35 KB workgroups per CU (LDS-bound)
+constexpr int kDecGrid = 1024;   // four single-wave workgroups per CU (bf16: 32 KB LDS each)
 #ifndef SWI_DEC_STREAM
 #define SWI_DEC_STREAM true
 #endif
@@ -133,10 +133,34 @@ struct DecSeg {
   }
 };
 
+// Per-dtype staging of the decode's K/V blocks.  bf16: the swizzled row
+// layout of the prefill's DMA path, filled from registers with linear
+// 16-byte stores (K and V separately, so the next block's K loads are in
+// flight while V is stored), read by the DMA-layout core (V^T through
+// transposing LDS reads).  float32: the padded layout with V^T staged by
+// the loader.
+template <typename T, int D>
+struct DecCfg;
+template <int D>
+struct DecCfg<bf16_t, D> {
+  using Core = CoreBF16Dma<D>;
+  using Loader = KVRegDma<D, kDecThreads, SWI_DEC_STREAM>;
+  static constexpr int kLds = LdsDma<D>::kBytes;
+  static constexpr bool kSplit = true;
+};
+template <int D>
+struct DecCfg<float, D> {
+  using Core = CoreF32<D>;
+  using Loader = KVLoader<float, D, kDecThreads, SWI_DEC_STREAM>;
+  static constexpr int kLds = Lds<float, D>::kBytes;
+  static constexpr bool kSplit = false;
+};
+
 template <typename T, int D>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
-  using Core = typename CoreSel<T, D>::type;
-  __shared__ __align__(16) char lds[Lds<T, D>::kBytes];
+  using Cfg = DecCfg<T, D>;
+  using Core = typename Cfg::Core;
+  __shared__ __align__(16) char lds[Cfg::kLds];
   const int lane = threadIdx.x, q = lane & 31, g = lane >> 5;
   const int npairs = a.B * a.Hkv;
   const int G = gridDim.x, w = blockIdx.x;
@@ -195,7 +219,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     wmax_lo = wave_max_i(valid ? lo_h : -1);
   };
   begin();
-  KVLoader<T, D, kDecThreads, SWI_DEC_STREAM> ld;
+  typename Cfg::Loader ld;
   ld.load(cur.kbase<T, D>(a), cur.vbase<T, D>(a), rs, cur.kb(cur.blk0), cur.L, lane);
   int n = cur.blk0;
   while (true) {
@@ -213,9 +237,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
       nn = nx.blk0;
     }
     __syncthreads();
-    ld.store(lds, lane);
-    __syncthreads();
-    if (more) ld.load(nx.kbase<T, D>(a), nx.vbase<T, D>(a), rs, nx.kb(nn), nx.L, lane);
+    if constexpr (Cfg::kSplit) {
+      // The loads are issued whether or not a next block exists (without
+      // one they re-read row 0 of this block: in bounds, 256 bytes), so the
+      // load sequence does not depend on `more` and the waits before the V
+      // stores count the new K loads instead of waiting for them.
+      const T* kbn = more ? nx.kbase<T, D>(a) : cur.kbase<T, D>(a);
+      const T* vbn = more ? nx.vbase<T, D>(a) : cur.vbase<T, D>(a);
+      const int lkb = more ? nx.kb(nn) : cur.kb(n);
+      const int lend = more ? nx.L : lkb + 1;
+      ld.store_k(lds, lane);
+      ld.load_k(kbn, rs, lkb, lend, lane);
+      ld.store_v(lds, lane);
+      ld.load_v(vbn, rs, lkb, lend, lane);
+      __syncthreads();
+    } else {
+      ld.store(lds, lane);
+      __syncthreads();
+      if (more) ld.load(nx.kbase<T, D>(a), nx.vbase<T, D>(a), rs, nx.kb(nn), nx.L, lane);
+    }
     const int kb = cur.kb(n);
     const bool anc = n < cur.na;  // wave-uniform
     const bool masked = anc ? kb + kBN - 1 > wmin_ahi : (kb < wmax_lo || kb + kBN > cur.L);
