@@ -14,6 +14,7 @@ from .swiattn_ref import (  # noqa: F401
     prefill,
     regularizer,
     route,
+    router_backward,
     softplus,
     swa_key_range,
 )

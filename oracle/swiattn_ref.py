@@ -43,6 +43,7 @@ __all__ = [
     "softplus",
     "regularizer",
     "decode_step",
+    "router_backward",
 ]
 
 NEAR_THRESHOLD = 1e-5
@@ -388,3 +389,48 @@ def regularizer(z, nll, diff, gamma_base=1e-3, eps=0.1, alpha=100.0):
     z = np.asarray(z, np.float64)
     gamma = gamma_base / (eps + np.asarray(nll, np.float64) + alpha * np.asarray(diff, np.float64))
     return gamma[..., None] * softplus(z)
+
+
+# ---------------------------------------------------------------------------
+# Router gradient through the straight-through gate  ([SwiAttn] section 2,
+# router and dual-branch paragraphs)
+# ---------------------------------------------------------------------------
+def router_backward(dO, O_full, O_swa, z, H, r):
+    """Gradient of the loss with respect to the router's logits, hidden
+    states, weight and bias, given the gradient dO of the layer output.
+
+    [SwiAttn] section 2: the hard gate is sigma = 1(soft > 0.5) + soft -
+    sg(soft) with soft = sigmoid(z), so its value is the 0/1 indicator and
+    its derivative is d soft / dz = soft * (1 - soft); the output is
+    O = sigma * O_FULL + (1 - sigma) * O_SWA, so dL/dsigma is the inner
+    product of dO with O_FULL - O_SWA over the heads the gate multiplies
+    and their channels.  With z = H.r + bias (route()):
+      dz[b,t,g]  = soft(1 - soft) * sum_{h in g} sum_c dO (O_FULL - O_SWA)
+      dH[b,t,k]  = sum_g dz[b,t,g] r[k,g]
+      dr[k,g]    = sum_{b,t} H[b,t,k] dz[b,t,g]
+      dbias[g]   = sum_{b,t} dz[b,t,g]
+    Only the router's path is covered: the gradients that reach Q, K, V
+    through O_FULL and O_SWA are not part of this function.
+
+    dO, O_full, O_swa [B,N,Hq,d]; z [B,N,G]; H [B,N,hidden]; r [hidden,G]
+    ->  dict dz [B,N,G], dH [B,N,hidden], dr [hidden,G], dbias [G]  (float64)
+    Reading: query head h belongs to gate group h // (Hq/G), as everywhere.
+    """
+    dO = np.asarray(dO, np.float64)
+    diff = np.asarray(O_full, np.float64) - np.asarray(O_swa, np.float64)
+    z = np.asarray(z, np.float64)
+    H = np.asarray(H, np.float64)
+    r = np.asarray(r, np.float64)
+    B, N, Hq, d = dO.shape
+    G = z.shape[2]
+    if Hq % G:
+        raise ValueError("Hq must be a multiple of G")
+    hg = Hq // G
+    per_head = (dO * diff).sum(axis=3)                          # [B,N,Hq]
+    s = per_head.reshape(B, N, G, hg).sum(axis=3)               # [B,N,G]
+    soft = 1.0 / (1.0 + np.exp(-z))
+    dz = s * soft * (1.0 - soft)
+    dH = dz @ r.T                                               # [B,N,hidden]
+    dr = np.einsum("btk,btg->kg", H, dz)
+    dbias = dz.sum(axis=(0, 1))
+    return {"dz": dz, "dH": dH, "dr": dr, "dbias": dbias}

@@ -408,6 +408,90 @@ def check_decode_step_ragged_and_full():
     np.testing.assert_allclose(st["o"][1:2], want, rtol=0, atol=0)
 
 
+def _router_grad_case(seed, B=2, N=5, Hq=4, d=3, G=2, hidden=6):
+    rng = np.random.default_rng(seed)
+    H = rng.standard_normal((B, N, hidden))
+    r = rng.standard_normal((hidden, G)) * 0.5
+    bias = rng.standard_normal(G) * 0.3
+    Of = rng.standard_normal((B, N, Hq, d))
+    Os = rng.standard_normal((B, N, Hq, d))
+    dO = rng.standard_normal((B, N, Hq, d))
+    return H, r, bias, Of, Os, dO
+
+
+def _soft_surrogate(H, r, bias, Of, Os, dO):
+    """Sum of dO times the output with the soft gate in place of the hard one
+    (the function whose gradient the straight-through estimator returns)."""
+    B, N, Hq, d = Of.shape
+    G = r.shape[1]
+    soft = 1.0 / (1.0 + np.exp(-(H @ r + bias)))                # [B,N,G]
+    sh = np.repeat(soft, Hq // G, axis=2)[..., None]            # heads in group order
+    return float((dO * (sh * Of + (1.0 - sh) * Os)).sum())
+
+
+def check_router_backward_finite_differences():
+    """Central differences (h = 1e-6) of the soft surrogate with respect to
+    every entry of H, r and bias match dH, dr and dbias."""
+    H, r, bias, Of, Os, dO = _router_grad_case(51)
+    z = H @ r + bias
+    g = ref.router_backward(dO, Of, Os, z, H, r)
+    eps = 1e-6
+    for name, arr, want in (("H", H, g["dH"]), ("r", r, g["dr"]), ("bias", bias, g["dbias"])):
+        num = np.zeros_like(arr)
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            a1, a2 = arr.copy(), arr.copy()
+            a1[i] += eps
+            a2[i] -= eps
+            args = {"H": H, "r": r, "bias": bias}
+            args[name] = a1
+            f1 = _soft_surrogate(args["H"], args["r"], args["bias"], Of, Os, dO)
+            args[name] = a2
+            f2 = _soft_surrogate(args["H"], args["r"], args["bias"], Of, Os, dO)
+            num[i] = (f1 - f2) / (2 * eps)
+        np.testing.assert_allclose(want, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def check_router_backward_against_autograd():
+    """torch float64 autograd of the soft surrogate gives the same dz, dH,
+    dr and dbias (a library routine, independent of the formula)."""
+    H, r, bias, Of, Os, dO = _router_grad_case(52, B=1, N=7, Hq=6, d=4, G=3, hidden=5)
+    Ht = torch.tensor(H, requires_grad=True)
+    rt = torch.tensor(r, requires_grad=True)
+    bt = torch.tensor(bias, requires_grad=True)
+    zt = Ht @ rt + bt
+    zt.retain_grad()
+    soft = torch.sigmoid(zt).repeat_interleave(2, dim=2)[..., None]
+    loss = (torch.tensor(dO) * (soft * torch.tensor(Of) + (1 - soft) * torch.tensor(Os))).sum()
+    loss.backward()
+    g = ref.router_backward(dO, Of, Os, (H @ r + bias), H, r)
+    np.testing.assert_allclose(g["dz"], zt.grad.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(g["dH"], Ht.grad.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(g["dr"], rt.grad.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(g["dbias"], bt.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def check_router_backward_special_cases():
+    """Identical branches give zero gradients; dO = O_FULL - O_SWA gives
+    dz = soft(1-soft) * (the group's squared branch distance) >= 0; at
+    z = 0 the factor is exactly 1/4; one hot r picks H's column."""
+    H, r, bias, Of, Os, dO = _router_grad_case(53, B=1, N=4, Hq=2, d=3, G=1, hidden=3)
+    z = H @ r + bias
+    zero = ref.router_backward(dO, Of, Of, z, H, r)
+    for k in ("dz", "dH", "dr", "dbias"):
+        assert np.all(zero[k] == 0.0), k
+    g = ref.router_backward(Of - Os, Of, Os, np.zeros_like(z), H, r)
+    dist = ((Of - Os) ** 2).sum(axis=(2, 3))[..., None]
+    np.testing.assert_allclose(g["dz"], 0.25 * dist, rtol=1e-14)
+    r1 = np.zeros((3, 1))
+    r1[1, 0] = 1.0
+    g1 = ref.router_backward(dO, Of, Os, z, H, r1)
+    np.testing.assert_allclose(g1["dH"][..., 1], g1["dz"][..., 0], rtol=0, atol=0)
+    assert np.all(g1["dH"][..., [0, 2]] == 0.0)
+    np.testing.assert_allclose(g1["dr"][:, 0], (H * g1["dz"]).sum(axis=(0, 1)), rtol=1e-14)
+
+
 ALL_PINS = [
     check_w4_key_ranges,
     check_w4_attention_weights,
@@ -429,4 +513,7 @@ ALL_PINS = [
     check_anchors_closed_form,
     check_anchors_against_sdpa_and_cover,
     check_anchored_decode_equals_last_prefill_row,
+    check_router_backward_finite_differences,
+    check_router_backward_against_autograd,
+    check_router_backward_special_cases,
 ]

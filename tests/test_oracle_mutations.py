@@ -148,3 +148,53 @@ def test_decode_step_mutants_caught(monkeypatch):
     for name, m in mutants.items():
         monkeypatch.setattr(ref, "decode_step", m)
         assert _run_all_pins() > 0, name
+
+
+def test_router_backward_mutants_caught(monkeypatch):
+    """Plausible mistakes in the router gradient, each caught by a pin."""
+    good = ref.router_backward
+
+    def make(kind):
+        def mutant(dO, O_full, O_swa, z, H, r):
+            dO = np.asarray(dO, np.float64)
+            diff = np.asarray(O_full, np.float64) - np.asarray(O_swa, np.float64)
+            if kind == "flipped_difference":
+                diff = -diff
+            z = np.asarray(z, np.float64)
+            B, N, Hq, d = dO.shape
+            G = z.shape[2]
+            per_head = (dO * diff).sum(axis=3)
+            if kind == "heads_interleaved":  # head h in group h % G
+                s = per_head.reshape(B, N, Hq // G, G).sum(axis=2)
+            else:
+                s = per_head.reshape(B, N, G, Hq // G).sum(axis=3)
+            soft = 1.0 / (1.0 + np.exp(-z))
+            if kind == "no_sigmoid_derivative":
+                dz = s
+            elif kind == "sigmoid_not_derivative":
+                dz = s * soft
+            else:
+                dz = s * soft * (1.0 - soft)
+            out = good(dO, O_full, O_swa, z, H, r)
+            out["dz"] = dz
+            out["dH"] = dz @ np.asarray(r, np.float64).T
+            out["dr"] = np.einsum("btk,btg->kg", np.asarray(H, np.float64), dz)
+            out["dbias"] = dz.mean(axis=(0, 1)) if kind == "bias_mean" else dz.sum(axis=(0, 1))
+            return out
+        return mutant
+
+    checks = [pins.check_router_backward_finite_differences, pins.check_router_backward_against_autograd,
+              pins.check_router_backward_special_cases]
+    for kind in ("flipped_difference", "heads_interleaved", "no_sigmoid_derivative",
+                 "sigmoid_not_derivative", "bias_mean"):
+        monkeypatch.setattr(ref, "router_backward", make(kind))
+        caught = 0
+        for c in checks:
+            try:
+                c()
+            except AssertionError:
+                caught += 1
+        assert caught > 0, kind
+    monkeypatch.setattr(ref, "router_backward", good)
+    for c in checks:
+        c()
