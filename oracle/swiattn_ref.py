@@ -428,8 +428,10 @@ def router_backward(dO, O_full, O_swa, z, H, r):
     hg = Hq // G
     per_head = (dO * diff).sum(axis=3)                          # [B,N,Hq]
     s = per_head.reshape(B, N, G, hg).sum(axis=3)               # [B,N,G]
-    soft = 1.0 / (1.0 + np.exp(-z))
-    dz = s * soft * (1.0 - soft)
+    # soft * (1 - soft) written as e^-|z| / (1 + e^-|z|)^2 (the same
+    # function): in the tails 1 - soft cancels to a few significant digits
+    u = np.exp(-np.abs(z))
+    dz = s * (u / ((1.0 + u) * (1.0 + u)))
     dH = dz @ r.T                                               # [B,N,hidden]
     dr = np.einsum("btk,btg->kg", H, dz)
     dbias = dz.sum(axis=(0, 1))
