@@ -282,6 +282,43 @@ int swiattn_decode_anchored(const void* q, const void* Kc, const void* Vc,
                             float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
                             swiattn_stream_t stream, const swiattn_events_t* events);
 
+/*
+ * swiattn_router_backward - gradient that reaches the router through the
+ * straight-through gate.
+ * (SwiAttn report, section 2: the hard gate is
+ * sigma = 1(soft > 0.5) + soft - sg(soft) with soft = sigmoid(R(H)), so its
+ * forward value is the 0/1 decision and its backward derivative the
+ * sigmoid's; the layer output is O = sigma * O_FULL + (1 - sigma) * O_SWA.)
+ *
+ *   dO            [B,N,Hq,d]  dtype  gradient of the loss w.r.t. O
+ *   O_full, O_swa [B,N,Hq,d]  dtype  the two branch outputs of the forward
+ *                                    (e.g. prefill with the gate all ones /
+ *                                    all zeros)
+ *   z             [B,N,G]     float  router logits (swiattn_route's z_out)
+ *   H             [B,N,hidden] dtype hidden states, r [hidden,G] dtype weight
+ *   dz            [B,N,G]     float  out: soft'(z) * sum over the heads of
+ *                                    group g and their channels of
+ *                                    dO * (O_full - O_swa)
+ *   dH            [B,N,hidden] dtype out: sum_g dz r[:,g]
+ *   dr            [hidden,G]  float  out: sum over tokens of H dz
+ *   dbias         [G]         float  out: sum over tokens of dz
+ *   ws, ws_bytes: device workspace of at least
+ *   swiattn_router_backward_workspace_size(B, N, hidden, G) bytes, clobbered.
+ * Query head h belongs to gate group h / (Hq/G).  Sums are float32 in a fixed
+ * order (bitwise reproducible); soft'(z) is evaluated as
+ * e^-|z| / (1 + e^-|z|)^2.  The gradients that reach Q, K, V through the
+ * two branch outputs are not computed.  Outputs must not overlap inputs.
+ * Errors: INVALID_ARG (sizes < 1, Hq % G, NULL pointers), UNSUPPORTED
+ * (d not 64/128, hidden not a multiple of 8, G > 64), WORKSPACE.
+ */
+size_t swiattn_router_backward_workspace_size(int B, int N, int hidden, int G);
+
+int swiattn_router_backward(const void* dO, const void* O_full, const void* O_swa, const float* z,
+                            const void* H, const void* r, float* dz, void* dH, float* dr,
+                            float* dbias, int B, int N, int Hq, int d, int hidden, int G,
+                            swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
+                            swiattn_stream_t stream);
+
 /* Static text for an error code. */
 const char* swiattn_strerror(int code);
 

@@ -15,4 +15,5 @@ from .binding import (  # noqa: F401
     prefill_workspace_size,
     regularizer,
     route,
+    router_backward,
 )

@@ -48,6 +48,8 @@ SYMBOLS = {
     "swiattn_decode_step": (_i32, [_vp] * 11 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp]),
     "swiattn_prefill_anchored": (_i32, [_vp] * 8 + [_i32] * 8 + [_f32, _i32, _u32, _vp, _sz, _vp, _vp]),
     "swiattn_decode_anchored": (_i32, [_vp] * 6 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp, _vp]),
+    "swiattn_router_backward_workspace_size": (_sz, [_i32] * 4),
+    "swiattn_router_backward": (_i32, [_vp] * 10 + [_i32] * 7 + [_vp, _sz, _vp]),
     "swiattn_strerror": (ctypes.c_char_p, [_i32]),
     "swiattn_version": (ctypes.c_char_p, []),
 }
@@ -189,6 +191,47 @@ def regularizer(z, nll, diff, *, gamma_base=1e-3, eps=0.1, alpha=100.0, out=None
                                    float(eps), float(alpha), _stream(dev))
     _check(rc, "swiattn_regularizer")
     return loss
+
+
+def router_backward(dO, O_full, O_swa, z, H, r, *, out=None, workspace=None):
+    """Router gradient through the straight-through gate.  dO, O_full, O_swa
+    [B,N,Hq,d]; z [B,N,G] float32 (router logits); H [B,N,hidden]; r
+    [hidden,G] (dO, O_*, H, r in one dtype).  Returns (dz [B,N,G] fp32,
+    dH [B,N,hidden] dtype, dr [hidden,G] fp32, dbias [G] fp32); `out` may
+    give those four tensors."""
+    L = lib()
+    _need(dO, "dO")
+    code = _dtype_code(dO)
+    B, N, Hq, d = dO.shape
+    dev = dO.device
+    _need(O_full, "O_full", shape=dO.shape, dtype=dO.dtype, device=dev)
+    _need(O_swa, "O_swa", shape=dO.shape, dtype=dO.dtype, device=dev)
+    _need(z, "z", dtype=torch.float32, device=dev)
+    if z.dim() != 3 or z.shape[:2] != (B, N):
+        raise ValueError("z must be [B,N,G]")
+    G = z.shape[2]
+    _need(H, "H", dtype=dO.dtype, device=dev)
+    if H.dim() != 3 or H.shape[:2] != (B, N):
+        raise ValueError("H must be [B,N,hidden]")
+    hidden = H.shape[2]
+    _need(r, "r", shape=(hidden, G), dtype=dO.dtype, device=dev)
+    if out is None:
+        out = (torch.empty((B, N, G), dtype=torch.float32, device=dev),
+               torch.empty((B, N, hidden), dtype=dO.dtype, device=dev),
+               torch.empty((hidden, G), dtype=torch.float32, device=dev),
+               torch.empty((G,), dtype=torch.float32, device=dev))
+    dz, dH, dr, dbias = out
+    _need(dz, "dz", shape=(B, N, G), dtype=torch.float32, device=dev)
+    _need(dH, "dH", shape=(B, N, hidden), dtype=dO.dtype, device=dev)
+    _need(dr, "dr", shape=(hidden, G), dtype=torch.float32, device=dev)
+    _need(dbias, "dbias", shape=(G,), dtype=torch.float32, device=dev)
+    nbytes = int(L.swiattn_router_backward_workspace_size(B, N, hidden, G))
+    ws = _workspace(nbytes, dev, workspace)
+    rc = L.swiattn_router_backward(_p(dO), _p(O_full), _p(O_swa), _p(z), _p(H), _p(r), _p(dz), _p(dH),
+                                   _p(dr), _p(dbias), B, N, Hq, d, hidden, G, code, _p(ws), ws.numel(),
+                                   _stream(dev))
+    _check(rc, "swiattn_router_backward")
+    return dz, dH, dr, dbias
 
 
 def prefill_workspace_size(B, N, Hq, Hkv, G, d, W, dtype=torch.bfloat16, both_branch=False):

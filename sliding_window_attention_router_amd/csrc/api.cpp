@@ -212,6 +212,31 @@ int swiattn_decode_step(const void* Hn, const void* r, const float* bias, const 
                                         gate, o, ws, reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t swiattn_router_backward_workspace_size(int B, int N, int hidden, int G) {
+  if (B < 1 || N < 1 || hidden < 1 || G < 1) return 0;
+  return swi::router_grad_workspace((int64_t)B * N, hidden, G);
+}
+
+int swiattn_router_backward(const void* dO, const void* O_full, const void* O_swa, const float* z,
+                            const void* H, const void* r, float* dz, void* dH, float* dr,
+                            float* dbias, int B, int N, int Hq, int d, int hidden, int G,
+                            swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
+                            swiattn_stream_t stream) {
+  if (B < 1 || N < 1 || Hq < 1 || hidden < 1 || G < 1 || !dtype_ok(dtype))
+    return SWIATTN_ERR_INVALID_ARG;
+  if (Hq % G != 0) return SWIATTN_ERR_INVALID_ARG;
+  if (!dO || !O_full || !O_swa || !z || !H || !r || !dz || !dH || !dr || !dbias)
+    return SWIATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return SWIATTN_ERR_UNSUPPORTED;
+  if (hidden % 8 != 0 || G > swi::router_grad_max_groups()) return SWIATTN_ERR_UNSUPPORTED;
+  if ((long long)B * N > INT_MAX / 2) return SWIATTN_ERR_UNSUPPORTED;
+  const size_t need = swi::router_grad_workspace((int64_t)B * N, hidden, G);
+  if (!ws || ws_bytes < need) return SWIATTN_ERR_WORKSPACE;
+  return hip_rc(swi::launch_router_grad(dO, O_full, O_swa, z, H, r, dz, dH, dr, dbias, B, N, Hq, d,
+                                        hidden, G, dtype == SWIATTN_F32, ws,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
 const char* swiattn_strerror(int code) {
   switch (code) {
     case SWIATTN_OK: return "ok";

@@ -18,6 +18,14 @@ hipError_t launch_regularizer(const float* z, const float* nll, const float* dif
                               int B, int N, int G, float gamma_base, float eps, float alpha,
                               hipStream_t s);
 
+// ---- router gradient through the straight-through gate -----------------
+size_t router_grad_workspace(int64_t ntok, int hidden, int G);
+int router_grad_max_groups();
+hipError_t launch_router_grad(const void* dO, const void* Of, const void* Os, const float* z,
+                              const void* H, const void* r, float* dz, void* dH, float* dr,
+                              float* dbias, int B, int N, int Hq, int d, int hidden, int G, bool f32,
+                              void* ws, hipStream_t s);
+
 // ---- prefill ------------------------------------------------------------
 struct PrefillShape {
   int B, N, Hq, Hkv, G, d, W;

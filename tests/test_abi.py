@@ -195,3 +195,30 @@ def test_prefill_anchored_rejects_invalid_arguments(lib, anchors, kw, code):
 ])
 def test_decode_anchored_rejects_invalid_arguments(lib, anchors, kw, code):
     assert _decode_anchored(lib, anchors, **kw) == code
+
+
+def _router_backward(lib, **kw):
+    a = dict(dO=FAKE, Of=FAKE, Os=FAKE, z=FAKE, H=FAKE, r=FAKE, dz=FAKE, dH=FAKE, dr=FAKE, db=FAKE,
+             B=1, N=100, Hq=16, d=128, hidden=2048, G=1, dt=BF16, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.swiattn_router_backward(a["dO"], a["Of"], a["Os"], a["z"], a["H"], a["r"], a["dz"], a["dH"],
+                                       a["dr"], a["db"], a["B"], a["N"], a["Hq"], a["d"], a["hidden"], a["G"],
+                                       a["dt"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(Hq=0), INVALID), (dict(hidden=0), INVALID),
+    (dict(G=0), INVALID), (dict(G=3), INVALID), (dict(dt=9), INVALID), (dict(dO=None), INVALID),
+    (dict(z=None), INVALID), (dict(db=None), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(hidden=100), UNSUPPORTED), (dict(Hq=128, G=128), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=64), WORKSPACE),
+])
+def test_router_backward_rejects_invalid_arguments(lib, kw, code):
+    assert _router_backward(lib, **kw) == code
+
+
+def test_router_backward_workspace_size(lib):
+    # one float per (split of 64 tokens, group, hidden unit + bias)
+    assert lib.swiattn_router_backward_workspace_size(1, 32768, 2048, 1) == 512 * 2049 * 4
+    assert lib.swiattn_router_backward_workspace_size(2, 33, 8, 2) == 2 * 2 * 9 * 4
+    assert lib.swiattn_router_backward_workspace_size(0, 10, 8, 1) == 0
