@@ -65,6 +65,8 @@ def parse():
                     help="timed runs of the anchored prefill and decode (after the timed steps; 0 = skip)")
     ap.add_argument("--anchors", type=int, default=256,
                     help="global anchor keys of the window branch in the anchored runs")
+    ap.add_argument("--rgrad-steps", type=int, default=10,
+                    help="timed runs of the router gradient (after the timed steps; 0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB before the steps "
                          "(a known-size reference for hardware byte counters)")
@@ -264,6 +266,8 @@ def main():
     anch = (anchors_run(swa, Q, K, V, gate, idx, cnt, W, args.anchors, q_d, Kc, Vc, len_d, gate_d,
                         dec, args.anchor_steps)
             if args.anchor_steps > 0 else None)
+    rgrad = (router_grad_run(swa, Q, K, V, W, H, r, bias, args.rgrad_steps)
+             if args.rgrad_steps > 0 else None)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -298,6 +302,7 @@ def main():
             "both_branch": both,
             "serving_step": serve,
             "anchors": anch,
+            "router_grad": rgrad,
         },
         "kernel_ms": {k: round(v, 4) for k, v in t.items()},
         "roofline": dict(rooflines[dominant], kernel=dominant),
@@ -403,6 +408,49 @@ def anchors_run(swa, Q, K, V, gate, idx, cnt, W, A, q_d, Kc, Vc, len_d, gate_d, 
                        "tok_per_s": round(q_d.shape[0] / (dec_ms * 1e-3), 1),
                        "GB_per_s": round(dbytes / (dec_ms * 1e-3) / 1e9, 1),
                        "splitk_frac_of_hbm_peak": round(dbytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+
+
+def router_grad_run(swa, Q, K, V, W, H, r, bias, steps):
+    """Router gradient through the straight-through gate on the prefill
+    layer (outside the timed steps): the two branch outputs come from the
+    prefill with the gate all ones and all zeros, dO ~ N(0,1) from a seeded
+    generator, z from the router.  Timed with events around the call (three
+    launches); algorithmic bytes: dO, O_FULL, O_SWA and H read once, dH
+    written once, plus z, dz and the split partials."""
+    import torch
+    B, N, Hq, d = Q.shape
+    dev = Q.device
+    hidden, G = r.shape
+    ones = torch.ones((B, N, G), dtype=torch.uint8, device=dev)
+    zeros = torch.zeros((B, N, G), dtype=torch.uint8, device=dev)
+    O_full, _ = swa.prefill(Q, K, V, ones, W)
+    O_swa, _ = swa.prefill(Q, K, V, zeros, W)
+    z = swa.route(H, r, bias, want_z=True)[3]
+    gen = torch.Generator(device=dev).manual_seed(29)
+    dO = torch.randn(Q.shape, generator=gen, device=dev).to(Q.dtype)
+    out = (torch.empty((B, N, G), dtype=torch.float32, device=dev), torch.empty_like(H),
+           torch.empty((hidden, G), dtype=torch.float32, device=dev),
+           torch.empty((G,), dtype=torch.float32, device=dev))
+    ws = torch.empty(int(swa.lib().swiattn_router_backward_workspace_size(B, N, hidden, G)),
+                     dtype=torch.uint8, device=dev)
+    swa.router_backward(dO, O_full, O_swa, z, H, r, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        swa.router_backward(dO, O_full, O_swa, z, H, r, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    el = Q.element_size()
+    splits = (B * N + 31) // 32
+    byts = (3 * B * N * Hq * d * el + 2 * B * N * hidden * el + 3 * 4 * B * N * G
+            + 2 * 4 * splits * G * (hidden + 1))
+    return {"B": B, "N": N, "Hq": Hq, "d": d, "hidden": hidden, "G": G, "bytes": byts,
+            "ms": round(ms, 4), "GB_per_s": round(byts / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def both_branch_run(swa, Q, K, V, gate, W, steps, H, r, bias):

@@ -31,7 +31,7 @@
 namespace swi {
 
 constexpr int kRgThreads = 256;   // four waves
-constexpr int kSplitTokens = 64;  // tokens per partial of the weight and bias sums
+constexpr int kSplitTokens = 32;  // tokens per partial of the weight and bias sums
 constexpr int kRedWaves = 16;     // waves that share one column block of the final sums
 constexpr int kRgMaxG = 64;       // gate groups supported (dz of a token lives in LDS)
 

@@ -218,7 +218,7 @@ def test_router_backward_rejects_invalid_arguments(lib, kw, code):
 
 
 def test_router_backward_workspace_size(lib):
-    # one float per (split of 64 tokens, group, hidden unit + bias)
-    assert lib.swiattn_router_backward_workspace_size(1, 32768, 2048, 1) == 512 * 2049 * 4
-    assert lib.swiattn_router_backward_workspace_size(2, 33, 8, 2) == 2 * 2 * 9 * 4
+    # one float per (split of 32 tokens, group, hidden unit + bias)
+    assert lib.swiattn_router_backward_workspace_size(1, 32768, 2048, 1) == 1024 * 2049 * 4
+    assert lib.swiattn_router_backward_workspace_size(2, 33, 8, 2) == 3 * 2 * 9 * 4
     assert lib.swiattn_router_backward_workspace_size(0, 10, 8, 1) == 0

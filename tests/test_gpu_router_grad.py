@@ -6,7 +6,7 @@ outputs ~ N(0,1), router logits z ~ N(0, 2^2) in float32, H ~ N(0,1),
 r ~ N(0, 1/hidden).  Tolerances follow from float32 summation: a sum of n
 products carries an error of at most about n * 2^-24 of the sum of their
 magnitudes (the kernels add at most 32 products per lane plus a 6-level
-wave tree for dz, and 64 tokens per split plus 512 split sums for dr), and
+wave tree for dz, and 32 tokens per split plus 1024 split sums for dr), and
 dH is rounded once to its storage type (2^-8 relative for bf16)."""
 import numpy as np
 import pytest
