@@ -910,7 +910,7 @@ static hipError_t run_prefill(const PrefillShape& sh, const PrefillPlan& p, Pref
                      s, a);
   SWI_TRY(hipGetLastError());
   SWI_TRY(mark(ev, 2, s));
-  hipLaunchKernelGGL((merge_kernel<T, D>), dim3(4 * cus), dim3(kMergeThreads), 0, s, a);
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3(8 * cus), dim3(kMergeThreads), 0, s, a);
   SWI_TRY(hipGetLastError());
   SWI_TRY(mark(ev, 3, s));
   if (sh.both_branch) {
