@@ -282,6 +282,17 @@ int swiattn_decode_anchored(const void* q, const void* Kc, const void* Vc,
                             float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
                             swiattn_stream_t stream, const swiattn_events_t* events);
 
+/* swiattn_decode_step_anchored - swiattn_decode_step whose decode has the
+ * global anchors above (the anchors stay in the linear cache like every
+ * key); anchors = 0 is swiattn_decode_step.  Same arguments, workspace and
+ * errors, plus INVALID_ARG for anchors < 0. */
+int swiattn_decode_step_anchored(const void* Hn, const void* r, const float* bias, const void* q,
+                                 const void* k, const void* v, void* Kc, void* Vc,
+                                 int32_t* cache_len, uint8_t* gate, void* o, int B, int Lmax,
+                                 int hidden, int Hq, int Hkv, int G, int d, int W, int anchors,
+                                 float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
+                                 swiattn_stream_t stream);
+
 /*
  * swiattn_router_backward - gradient that reaches the router through the
  * straight-through gate.

@@ -48,6 +48,7 @@ SYMBOLS = {
     "swiattn_decode_step": (_i32, [_vp] * 11 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp]),
     "swiattn_prefill_anchored": (_i32, [_vp] * 8 + [_i32] * 8 + [_f32, _i32, _u32, _vp, _sz, _vp, _vp]),
     "swiattn_decode_anchored": (_i32, [_vp] * 6 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp, _vp]),
+    "swiattn_decode_step_anchored": (_i32, [_vp] * 11 + [_i32] * 9 + [_f32, _i32, _vp, _sz, _vp]),
     "swiattn_router_backward_workspace_size": (_sz, [_i32] * 4),
     "swiattn_router_backward": (_i32, [_vp] * 10 + [_i32] * 7 + [_vp, _sz, _vp]),
     "swiattn_strerror": (ctypes.c_char_p, [_i32]),
@@ -351,11 +352,13 @@ def decode(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None, workspace=Non
 
 
 def decode_step(Hn, r, bias, q, k, v, Kc, Vc, cache_len, W, *, scale=None, gate=None, out=None,
-                workspace=None):
+                workspace=None, anchors=0):
     """One serving step: route the new tokens (Hn [B,hidden], r [hidden,G],
     bias [G] fp32), append k, v [B,Hkv,d] to the cache Kc/Vc [B,Lmax,Hkv,d]
     at position cache_len[b] (int32 [B], advanced in place), then decode q
-    [B,Hq,d] over the updated cache.  Returns (o [B,Hq,d], gate uint8 [B,G])."""
+    [B,Hq,d] over the updated cache.  Returns (o [B,Hq,d], gate uint8 [B,G]).
+    anchors: global anchor keys of the window branch
+    (swiattn_decode_step_anchored); 0 calls swiattn_decode_step."""
     L = lib()
     _need(q, "q")
     code = _dtype_code(q)
@@ -388,8 +391,13 @@ def decode_step(Hn, r, bias, q, k, v, Kc, Vc, cache_len, W, *, scale=None, gate=
     _need(out, "out", shape=q.shape, dtype=q.dtype, device=dev)
     nbytes = int(L.swiattn_decode_workspace_size(B, Lmax, Hq, Hkv, G, d, W, code))
     ws = _workspace(nbytes, dev, workspace)
-    rc = L.swiattn_decode_step(_p(Hn), _p(r), _p(bias), _p(q), _p(k), _p(v), _p(Kc), _p(Vc),
-                               _p(cache_len), _p(gate), _p(out), B, Lmax, hidden, Hq, Hkv, G, d, W,
-                               float(scale), code, _p(ws), ws.numel(), _stream(dev))
+    ptrs = (_p(Hn), _p(r), _p(bias), _p(q), _p(k), _p(v), _p(Kc), _p(Vc), _p(cache_len), _p(gate),
+            _p(out))
+    if anchors:
+        rc = L.swiattn_decode_step_anchored(*ptrs, B, Lmax, hidden, Hq, Hkv, G, d, W, int(anchors),
+                                            float(scale), code, _p(ws), ws.numel(), _stream(dev))
+    else:
+        rc = L.swiattn_decode_step(*ptrs, B, Lmax, hidden, Hq, Hkv, G, d, W, float(scale), code,
+                                   _p(ws), ws.numel(), _stream(dev))
     _check(rc, "swiattn_decode_step")
     return out, gate

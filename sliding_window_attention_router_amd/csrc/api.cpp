@@ -195,21 +195,34 @@ int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t*
                                  scale, dtype, ws, ws_bytes, stream, nullptr);
 }
 
-int swiattn_decode_step(const void* Hn, const void* r, const float* bias, const void* q,
-                        const void* k, const void* v, void* Kc, void* Vc, int32_t* cache_len,
-                        uint8_t* gate, void* o, int B, int Lmax, int hidden, int Hq, int Hkv, int G,
-                        int d, int W, float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
-                        swiattn_stream_t stream) {
+int swiattn_decode_step_anchored(const void* Hn, const void* r, const float* bias, const void* q,
+                                 const void* k, const void* v, void* Kc, void* Vc,
+                                 int32_t* cache_len, uint8_t* gate, void* o, int B, int Lmax,
+                                 int hidden, int Hq, int Hkv, int G, int d, int W, int anchors,
+                                 float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
+                                 swiattn_stream_t stream) {
   swi::DecodeShape sh;
   swi::DecodePlan p;
   const int rc = decode_shape(B, Lmax, Hq, Hkv, G, d, W, scale, dtype, &sh, &p);
   if (rc != SWIATTN_OK) return rc;
+  if (anchors < 0) return SWIATTN_ERR_INVALID_ARG;
+  sh.A = anchors < Lmax ? anchors : Lmax;
   if (hidden < 1) return SWIATTN_ERR_INVALID_ARG;
   if (!Hn || !r || !bias || !q || !k || !v || !Kc || !Vc || !cache_len || !gate || !o)
     return SWIATTN_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.bytes) return SWIATTN_ERR_WORKSPACE;
   return hip_rc(swi::launch_decode_step(sh, p, Hn, r, bias, hidden, q, k, v, Kc, Vc, cache_len,
                                         gate, o, ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int swiattn_decode_step(const void* Hn, const void* r, const float* bias, const void* q,
+                        const void* k, const void* v, void* Kc, void* Vc, int32_t* cache_len,
+                        uint8_t* gate, void* o, int B, int Lmax, int hidden, int Hq, int Hkv, int G,
+                        int d, int W, float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
+                        swiattn_stream_t stream) {
+  return swiattn_decode_step_anchored(Hn, r, bias, q, k, v, Kc, Vc, cache_len, gate, o, B, Lmax,
+                                      hidden, Hq, Hkv, G, d, W, 0, scale, dtype, ws, ws_bytes,
+                                      stream);
 }
 
 size_t swiattn_router_backward_workspace_size(int B, int N, int hidden, int G) {

@@ -222,3 +222,12 @@ def test_router_backward_workspace_size(lib):
     assert lib.swiattn_router_backward_workspace_size(1, 32768, 2048, 1) == 1024 * 2049 * 4
     assert lib.swiattn_router_backward_workspace_size(2, 33, 8, 2) == 3 * 2 * 9 * 4
     assert lib.swiattn_router_backward_workspace_size(0, 10, 8, 1) == 0
+
+
+def test_decode_step_anchored_rejects_negative_anchors(lib):
+    rc = lib.swiattn_decode_step_anchored(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          4, 100, 64, 4, 2, 1, 128, 16, -1, 0.088, BF16, FAKE, 1 << 40, None)
+    assert rc == INVALID
+    rc = lib.swiattn_decode_step_anchored(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          4, 100, 64, 4, 2, 1, 96, 16, 8, 0.088, BF16, FAKE, 1 << 40, None)
+    assert rc == UNSUPPORTED

@@ -218,3 +218,36 @@ def test_decode_64x32k_anchored():
     assert max(errs) <= TOL["bf16"]
     del d
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_step_anchored(dtype):
+    """Serving step with anchors: route the new tokens, append their K/V at
+    each sequence's length (empty, short, long and full caches), decode
+    with the first A keys in every window head's key set."""
+    B, Lmax, Hq, Hkv, G, d, W, A, hidden = 6, 700, 8, 2, 2, 128, 100, 256, 128
+    rng = np.random.default_rng(71)
+    rnd = (lambda *sh: synth.round_bf16(rng.standard_normal(sh, dtype=np.float32))) if dtype == "bf16" \
+        else (lambda *sh: rng.standard_normal(sh, dtype=np.float32))
+    Kc, Vc = rnd(B, Lmax, Hkv, d), rnd(B, Lmax, Hkv, d)
+    q, k, v = rnd(B, Hq, d), rnd(B, Hkv, d), rnd(B, Hkv, d)
+    Hn = rnd(B, hidden)
+    r = (rnd(hidden, G) / np.sqrt(hidden)).astype(np.float32)
+    if dtype == "bf16":
+        r = synth.round_bf16(r)
+    bias = np.array([-0.3, 0.2], np.float32)
+    L0 = np.array([0, 5, 300, 457, 699, 700], np.int32)
+    td = TORCH_DTYPE[dtype]
+    Kg, Vg, Lg = dev(Kc, td), dev(Vc, td), dev(L0)
+    o, gate = swa().decode_step(dev(Hn, td), dev(r, td), dev(bias), dev(q, td), dev(k, td), dev(v, td),
+                                Kg, Vg, Lg, W, anchors=A)
+    torch.cuda.synchronize()
+    ref = oracle.decode_step(Hn, r, bias, q, k, v, Kc, Vc, L0, W, anchors=A)
+    near = np.abs(ref["z"]) < 1e-5
+    g = gate.cpu().numpy()
+    assert np.array_equal(g[~near], ref["gate"][~near])
+    assert np.array_equal(Lg.cpu().numpy(), ref["cache_len"])
+    ok = ~near.any(axis=1)
+    err = max_abs(host(o)[ok], ref["o"][ok])
+    say(f"anchored decode step {dtype}: o max-abs {err:.3e}, gates {g.tolist()}")
+    assert err <= TOL[dtype]
