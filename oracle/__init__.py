@@ -12,6 +12,7 @@ from .swiattn_ref import (  # noqa: F401
     decode_step,
     full_key_range,
     prefill,
+    prefill_backward,
     regularizer,
     route,
     router_backward,

@@ -44,6 +44,7 @@ __all__ = [
     "regularizer",
     "decode_step",
     "router_backward",
+    "prefill_backward",
 ]
 
 NEAR_THRESHOLD = 1e-5
@@ -436,3 +437,64 @@ def router_backward(dO, O_full, O_swa, z, H, r):
     dr = np.einsum("btk,btg->kg", H, dz)
     dbias = dz.sum(axis=(0, 1))
     return {"dz": dz, "dH": dH, "dr": dr, "dbias": dbias}
+
+
+# ---------------------------------------------------------------------------
+# Attention backward of the hard-gated layer  ([SwiAttn] section 2: the
+# gated output O = sigma * O_FULL + (1 - sigma) * O_SWA with a 0/1 forward
+# gate, so each row's output is one softmax attention over its own key set)
+# ---------------------------------------------------------------------------
+def prefill_backward(Q, K, V, gate, W, dO, scale=None):
+    """Gradients of L = sum(dO * O) with respect to Q, K, V for the routed
+    prefill (hard gate: row i of a head in gate group g attends to [0, i]
+    if gate[b,i,g] else [max(0, i-W+1), i]).
+
+    With s_ij = scale * <q_i, k_j> over row i's key set S_i,
+    P_ij = exp(s_ij) / sum_{j' in S_i} exp(s_ij'), O_i = sum_j P_ij v_j:
+      dV_j = sum_i P_ij dO_i
+      dP_ij = <dO_i, v_j>,  dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')
+      dQ_i = scale * sum_j dS_ij k_j,   dK_j = scale * sum_i dS_ij q_i
+    where sum_j' P_ij' dP_ij' = <dO_i, O_i>.  K and V gradients add over the
+    query heads that share a KV head.  The gate's own gradient (through the
+    straight-through estimator) is router_backward's.
+
+    Q, dO [B,N,Hq,d]; K, V [B,N,Hkv,d]; gate [B,N,G]
+    ->  dict dQ [B,N,Hq,d], dK, dV [B,N,Hkv,d]  (float64)
+    Each (b, h) is evaluated with explicit [N, N] matrices: small N only.
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    dO = np.asarray(dO, np.float64)
+    gate = np.asarray(gate)
+    B, N, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    G = gate.shape[2]
+    hk, hg = _head_maps(Hq, Hkv, G)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    full_mask = j <= i
+    band_mask = full_mask & (j > i - W)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for b in range(B):
+        for h in range(Hq):
+            kv, g = h // hk, h // hg
+            sig = gate[b, :, g].astype(bool)[:, None]
+            mask = np.where(sig, full_mask, band_mask)
+            s = scale * (Q[b, :, h] @ K[b, :, kv].T)
+            s = np.where(mask, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            P = np.exp(s)
+            P /= P.sum(axis=1, keepdims=True)
+            O = P @ V[b, :, kv]
+            dP = dO[b, :, h] @ V[b, :, kv].T
+            Dr = (dO[b, :, h] * O).sum(axis=1, keepdims=True)
+            dS = P * (dP - Dr)
+            dQ[b, :, h] = scale * (dS @ K[b, :, kv])
+            dK[b, :, kv] += scale * (dS.T @ Q[b, :, h])
+            dV[b, :, kv] += P.T @ dO[b, :, h]
+    return {"dQ": dQ, "dK": dK, "dV": dV}

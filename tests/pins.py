@@ -492,6 +492,82 @@ def check_router_backward_special_cases():
     np.testing.assert_allclose(g1["dr"][:, 0], (H * g1["dz"]).sum(axis=(0, 1)), rtol=1e-14)
 
 
+def check_prefill_backward_finite_differences():
+    """Central differences (h = 1e-6) of L = sum(dO * O) through the forward
+    reference prefill() give dQ, dK, dV, for a mixed gate, GQA and two gate
+    groups (the forward is pinned on its own)."""
+    rng = np.random.default_rng(81)
+    B, N, Hq, Hkv, d, W = 1, 7, 4, 2, 3, 3
+    Q, K, V = (rng.standard_normal(s) for s in ((B, N, Hq, d), (B, N, Hkv, d), (B, N, Hkv, d)))
+    dO = rng.standard_normal((B, N, Hq, d))
+    gate = (rng.random((B, N, 2)) < 0.5).astype(np.uint8)
+    g = ref.prefill_backward(Q, K, V, gate, W, dO, scale=0.8)
+    eps = 1e-6
+
+    def loss(q, k, v):
+        return float((dO * ref.prefill(q, k, v, gate, W, scale=0.8)["O"]).sum())
+    for name, arr in (("dQ", Q), ("dK", K), ("dV", V)):
+        num = np.zeros_like(arr)
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            a1, a2 = arr.copy(), arr.copy()
+            a1[idx] += eps
+            a2[idx] -= eps
+            args1 = [Q, K, V]
+            args2 = [Q, K, V]
+            pos = {"dQ": 0, "dK": 1, "dV": 2}[name]
+            args1[pos], args2[pos] = a1, a2
+            num[idx] = (loss(*args1) - loss(*args2)) / (2 * eps)
+        np.testing.assert_allclose(g[name], num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def check_prefill_backward_against_autograd():
+    """torch float64 autograd through scaled_dot_product_attention with the
+    per-row masks of the gate (a library routine) gives dQ, dK, dV."""
+    rng = np.random.default_rng(82)
+    B, N, Hq, Hkv, d, W = 2, 40, 4, 2, 8, 9
+    Q, K, V = (rng.standard_normal(s) for s in ((B, N, Hq, d), (B, N, Hkv, d), (B, N, Hkv, d)))
+    dO = rng.standard_normal((B, N, Hq, d))
+    gate = (rng.random((B, N, 1)) < 0.3).astype(np.uint8)
+    g = ref.prefill_backward(Q, K, V, gate, W, dO)
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    qt = torch.tensor(Q, requires_grad=True)
+    kt = torch.tensor(K, requires_grad=True)
+    vt = torch.tensor(V, requires_grad=True)
+    outs = []
+    for b in range(B):
+        sig = gate[b, :, 0].astype(bool)[:, None]
+        mask = torch.from_numpy(np.where(sig, j <= i, (j <= i) & (j > i - W)))
+        q = qt[b].permute(1, 0, 2)
+        k = kt[b].permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+        v = vt[b].permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+        outs.append(torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask).permute(1, 0, 2))
+    loss = (torch.stack(outs) * torch.tensor(dO)).sum()
+    loss.backward()
+    np.testing.assert_allclose(g["dQ"], qt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dK"], kt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dV"], vt.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def check_prefill_backward_special_cases():
+    """W = 1 (each row sees only itself): dV = dO summed over the query heads
+    of the KV head, dQ = dK = 0 (a one-key softmax does not depend on the
+    score).  Gate all ones equals the W >= N result."""
+    rng = np.random.default_rng(83)
+    B, N, Hq, Hkv, d = 1, 9, 4, 2, 5
+    Q, K, V = (rng.standard_normal(s) for s in ((B, N, Hq, d), (B, N, Hkv, d), (B, N, Hkv, d)))
+    dO = rng.standard_normal((B, N, Hq, d))
+    g = ref.prefill_backward(Q, K, V, np.zeros((B, N, 1), np.uint8), 1, dO)
+    np.testing.assert_allclose(g["dV"], dO.reshape(B, N, Hkv, Hq // Hkv, d).sum(axis=3), rtol=1e-14, atol=1e-14)
+    assert np.all(np.abs(g["dQ"]) < 1e-14) and np.all(np.abs(g["dK"]) < 1e-14)
+    a = ref.prefill_backward(Q, K, V, np.ones((B, N, 1), np.uint8), 3, dO)
+    c = ref.prefill_backward(Q, K, V, np.zeros((B, N, 1), np.uint8), N, dO)
+    for k in ("dQ", "dK", "dV"):
+        np.testing.assert_allclose(a[k], c[k], rtol=1e-13, atol=1e-13)
+
+
 ALL_PINS = [
     check_w4_key_ranges,
     check_w4_attention_weights,
@@ -516,4 +592,7 @@ ALL_PINS = [
     check_router_backward_finite_differences,
     check_router_backward_against_autograd,
     check_router_backward_special_cases,
+    check_prefill_backward_finite_differences,
+    check_prefill_backward_against_autograd,
+    check_prefill_backward_special_cases,
 ]

@@ -198,3 +198,56 @@ def test_router_backward_mutants_caught(monkeypatch):
     monkeypatch.setattr(ref, "router_backward", good)
     for c in checks:
         c()
+
+
+def test_prefill_backward_mutants_caught(monkeypatch):
+    """Plausible mistakes in the attention backward, each caught by a pin."""
+    good = ref.prefill_backward
+
+    def make(kind):
+        def mutant(Q, K, V, gate, W, dO, scale=None):
+            Q = np.asarray(Q, np.float64)
+            K = np.asarray(K, np.float64)
+            V = np.asarray(V, np.float64)
+            dO = np.asarray(dO, np.float64)
+            B, N, Hq, d = Q.shape
+            Hkv, G = K.shape[2], np.asarray(gate).shape[2]
+            if scale is None:
+                scale = 1.0 / np.sqrt(d)
+            i = np.arange(N)[:, None]
+            j = np.arange(N)[None, :]
+            dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+            for b in range(B):
+                for h in range(Hq):
+                    kv, g = h // (Hq // Hkv), h // (Hq // G)
+                    sig = np.asarray(gate)[b, :, g].astype(bool)[:, None]
+                    mask = np.where(sig, j <= i, (j <= i) & (j > i - W))
+                    s = np.where(mask, scale * (Q[b, :, h] @ K[b, :, kv].T), -np.inf)
+                    P = np.exp(s - s.max(axis=1, keepdims=True))
+                    P /= P.sum(axis=1, keepdims=True)
+                    dP = dO[b, :, h] @ V[b, :, kv].T
+                    Dr = (dO[b, :, h] * (P @ V[b, :, kv])).sum(axis=1, keepdims=True)
+                    dS = P * dP if kind == "no_row_term" else P * (dP - Dr)
+                    sq = 1.0 if kind == "dq_unscaled" else scale
+                    dQ[b, :, h] = sq * (dS @ K[b, :, kv])
+                    if kind == "kv_overwritten":
+                        dK[b, :, kv] = scale * (dS.T @ Q[b, :, h])
+                        dV[b, :, kv] = P.T @ dO[b, :, h]
+                    else:
+                        dK[b, :, kv] += scale * (dS.T @ Q[b, :, h])
+                        dV[b, :, kv] += (P.T if kind != "dv_untransposed" else P) @ dO[b, :, h]
+            return {"dQ": dQ, "dK": dK, "dV": dV}
+        return mutant
+
+    checks = [pins.check_prefill_backward_finite_differences, pins.check_prefill_backward_against_autograd,
+              pins.check_prefill_backward_special_cases]
+    for kind in ("no_row_term", "dq_unscaled", "kv_overwritten", "dv_untransposed"):
+        monkeypatch.setattr(ref, "prefill_backward", make(kind))
+        caught = 0
+        for c in checks:
+            try:
+                c()
+            except AssertionError:
+                caught += 1
+        assert caught > 0, kind
+    monkeypatch.setattr(ref, "prefill_backward", good)
