@@ -330,6 +330,38 @@ int swiattn_router_backward(const void* dO, const void* O_full, const void* O_sw
                             swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
                             swiattn_stream_t stream);
 
+/*
+ * swiattn_prefill_backward - gradients of L = sum(dO * O) with respect to
+ * Q, K, V for the hard-gated prefill.
+ * (SwiAttn report, section 2: with a 0/1 forward gate, row i of a head in
+ * gate group g is softmax attention over [0, i] (gate 1) or
+ * [max(0, i-W+1), i] (gate 0); weimeta glossary "详细解释" for the window.)
+ *
+ *   Q, dO [B,N,Hq,d], K, V [B,N,Hkv,d], O [B,N,Hq,d]  dtype  the forward's
+ *                    inputs, its output (swiattn_prefill) and the output's
+ *                    gradient
+ *   gate [B,N,G] uint8, idx [B,G,N] / cnt [B,G] int32  the forward's gate
+ *                    and its compaction (swiattn_route)
+ *   dQ [B,N,Hq,d], dK, dV [B,N,Hkv,d]  dtype  out (K, V gradients summed
+ *                    over the query heads of each KV head)
+ *   W, scale as swiattn_prefill.  ws, ws_bytes: at least
+ *   swiattn_prefill_backward_workspace_size(B, N, Hq) bytes (each row's
+ *   log-sum-exp and <dO, O>), clobbered.
+ * Only the attention path: the gate's gradient is swiattn_router_backward's.
+ * float32 arithmetic in a fixed order (bitwise reproducible); a plain
+ * vector-ALU implementation, one wave per (row, query head) for dQ and per
+ * (key, KV head) for dK and dV.  Outputs must not overlap inputs.
+ * Errors: as swiattn_prefill (INVALID_ARG, UNSUPPORTED, WORKSPACE).
+ */
+size_t swiattn_prefill_backward_workspace_size(int B, int N, int Hq);
+
+int swiattn_prefill_backward(const void* Q, const void* K, const void* V, const void* O,
+                             const void* dO, const uint8_t* gate, const int32_t* idx,
+                             const int32_t* cnt, void* dQ, void* dK, void* dV, int B, int N,
+                             int Hq, int Hkv, int G, int d, int W, float scale,
+                             swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
+                             swiattn_stream_t stream);
+
 /* Static text for an error code. */
 const char* swiattn_strerror(int code);
 

@@ -45,6 +45,7 @@ __all__ = [
     "decode_step",
     "router_backward",
     "prefill_backward",
+    "prefill_backward_rows",
 ]
 
 NEAR_THRESHOLD = 1e-5
@@ -444,6 +445,41 @@ def router_backward(dO, O_full, O_swa, z, H, r):
 # gated output O = sigma * O_FULL + (1 - sigma) * O_SWA with a 0/1 forward
 # gate, so each row's output is one softmax attention over its own key set)
 # ---------------------------------------------------------------------------
+def prefill_backward_rows(Q, K, V, gate, W, dO, rows, scale=None):
+    """dQ of prefill_backward for the given token positions only (row i's
+    dQ depends on row i alone): dQ [B,R,Hq,d] float64.  The same steps
+    per row, over row i's own key set."""
+    Q = np.asarray(Q)
+    K = np.asarray(K)
+    V = np.asarray(V)
+    dO = np.asarray(dO)
+    gate = np.asarray(gate)
+    B, N, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    G = gate.shape[2]
+    hk, hg = _head_maps(Hq, Hkv, G)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rows = np.asarray(rows, np.int64)
+    dQ = np.zeros((B, rows.size, Hq, d))
+    for b in range(B):
+        for h in range(Hq):
+            kv, g = h // hk, h // hg
+            for r, i in enumerate(rows):
+                lo, hi = full_key_range(int(i)) if gate[b, i, g] else swa_key_range(int(i), W)
+                k = np.asarray(K[b, lo:hi + 1, kv], np.float64)
+                v = np.asarray(V[b, lo:hi + 1, kv], np.float64)
+                q = np.asarray(Q[b, i, h], np.float64)
+                go = np.asarray(dO[b, i, h], np.float64)
+                s = scale * (k @ q)
+                p = np.exp(s - s.max())
+                p /= p.sum()
+                dp = v @ go
+                ds = p * (dp - go @ (p @ v))
+                dQ[b, r, h] = scale * (ds @ k)
+    return dQ
+
+
 def prefill_backward(Q, K, V, gate, W, dO, scale=None):
     """Gradients of L = sum(dO * O) with respect to Q, K, V for the routed
     prefill (hard gate: row i of a head in gate group g attends to [0, i]

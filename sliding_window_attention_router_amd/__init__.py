@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     decode_workspace_size,
     lib,
     prefill,
+    prefill_backward,
     prefill_workspace_size,
     regularizer,
     route,

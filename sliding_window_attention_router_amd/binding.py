@@ -50,6 +50,8 @@ SYMBOLS = {
     "swiattn_decode_anchored": (_i32, [_vp] * 6 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp, _vp]),
     "swiattn_decode_step_anchored": (_i32, [_vp] * 11 + [_i32] * 9 + [_f32, _i32, _vp, _sz, _vp]),
     "swiattn_router_backward_workspace_size": (_sz, [_i32] * 4),
+    "swiattn_prefill_backward_workspace_size": (_sz, [_i32] * 3),
+    "swiattn_prefill_backward": (_i32, [_vp] * 11 + [_i32] * 7 + [_f32, _i32, _vp, _sz, _vp]),
     "swiattn_router_backward": (_i32, [_vp] * 10 + [_i32] * 7 + [_vp, _sz, _vp]),
     "swiattn_strerror": (ctypes.c_char_p, [_i32]),
     "swiattn_version": (ctypes.c_char_p, []),
@@ -192,6 +194,49 @@ def regularizer(z, nll, diff, *, gamma_base=1e-3, eps=0.1, alpha=100.0, out=None
                                    float(eps), float(alpha), _stream(dev))
     _check(rc, "swiattn_regularizer")
     return loss
+
+
+def prefill_backward(Q, K, V, O, dO, gate, W, *, idx=None, cnt=None, scale=None, out=None,
+                     workspace=None):
+    """Attention backward of the hard-gated prefill: gradients of
+    sum(dO * O) w.r.t. Q, K, V.  Q, O, dO [B,N,Hq,d]; K, V [B,N,Hkv,d];
+    gate [B,N,G] (idx, cnt from route(); computed here if not given).
+    Returns (dQ, dK, dV)."""
+    L = lib()
+    _need(Q, "Q")
+    code = _dtype_code(Q)
+    B, N, Hq, d = Q.shape
+    dev = Q.device
+    _need(K, "K", dtype=Q.dtype, device=dev)
+    if K.dim() != 4 or K.shape[0] != B or K.shape[1] != N or K.shape[3] != d:
+        raise ValueError("K must be [B,N,Hkv,d]")
+    Hkv = K.shape[2]
+    _need(V, "V", shape=K.shape, dtype=Q.dtype, device=dev)
+    _need(O, "O", shape=Q.shape, dtype=Q.dtype, device=dev)
+    _need(dO, "dO", shape=Q.shape, dtype=Q.dtype, device=dev)
+    _need(gate, "gate", dtype=torch.uint8, device=dev)
+    if gate.dim() != 3 or gate.shape[:2] != (B, N):
+        raise ValueError("gate must be [B,N,G]")
+    G = gate.shape[2]
+    if idx is None or cnt is None:
+        _, idx, cnt, _ = route(None, gate=gate)
+    _need(idx, "idx", shape=(B, G, N), dtype=torch.int32, device=dev)
+    _need(cnt, "cnt", shape=(B, G), dtype=torch.int32, device=dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+    dQ, dK, dV = out
+    _need(dQ, "dQ", shape=Q.shape, dtype=Q.dtype, device=dev)
+    _need(dK, "dK", shape=K.shape, dtype=Q.dtype, device=dev)
+    _need(dV, "dV", shape=K.shape, dtype=Q.dtype, device=dev)
+    nbytes = int(L.swiattn_prefill_backward_workspace_size(B, N, Hq))
+    ws = _workspace(nbytes, dev, workspace)
+    rc = L.swiattn_prefill_backward(_p(Q), _p(K), _p(V), _p(O), _p(dO), _p(gate), _p(idx), _p(cnt),
+                                    _p(dQ), _p(dK), _p(dV), B, N, Hq, Hkv, G, d, W, float(scale), code,
+                                    _p(ws), ws.numel(), _stream(dev))
+    _check(rc, "swiattn_prefill_backward")
+    return dQ, dK, dV
 
 
 def router_backward(dO, O_full, O_swa, z, H, r, *, out=None, workspace=None):

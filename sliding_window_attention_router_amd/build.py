@@ -17,7 +17,8 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libswiattn.so")
-SOURCES = ["api.cpp", "route.hip", "prefill.hip", "decode.hip", "regularizer.hip", "router_grad.hip"]
+SOURCES = ["api.cpp", "route.hip", "prefill.hip", "decode.hip", "regularizer.hip", "router_grad.hip",
+           "backward.hip"]
 ARCH = "gfx950"
 
 

@@ -225,6 +225,31 @@ int swiattn_decode_step(const void* Hn, const void* r, const float* bias, const 
                                       stream);
 }
 
+size_t swiattn_prefill_backward_workspace_size(int B, int N, int Hq) {
+  if (B < 1 || N < 1 || Hq < 1) return 0;
+  if ((long long)B * N > INT_MAX / 2 || (long long)B * Hq > INT_MAX / 2) return 0;
+  return swi::backward_workspace(B, N, Hq);
+}
+
+int swiattn_prefill_backward(const void* Q, const void* K, const void* V, const void* O,
+                             const void* dO, const uint8_t* gate, const int32_t* idx,
+                             const int32_t* cnt, void* dQ, void* dK, void* dV, int B, int N,
+                             int Hq, int Hkv, int G, int d, int W, float scale,
+                             swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
+                             swiattn_stream_t stream) {
+  if (B < 1 || N < 1 || !dtype_ok(dtype)) return SWIATTN_ERR_INVALID_ARG;
+  const int rc = check_heads(Hq, Hkv, G, d, W, scale);
+  if (rc != SWIATTN_OK) return rc;
+  if ((long long)B * N > INT_MAX / 2 || (long long)B * Hq > INT_MAX / 2)
+    return SWIATTN_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !O || !dO || !gate || !idx || !cnt || !dQ || !dK || !dV)
+    return SWIATTN_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < swi::backward_workspace(B, N, Hq)) return SWIATTN_ERR_WORKSPACE;
+  return hip_rc(swi::launch_backward(Q, K, V, O, dO, gate, idx, cnt, dQ, dK, dV, B, N, Hq, Hkv, G,
+                                     d, W, scale, dtype == SWIATTN_F32, ws,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t swiattn_router_backward_workspace_size(int B, int N, int hidden, int G) {
   if (B < 1 || N < 1 || hidden < 1 || G < 1) return 0;
   return swi::router_grad_workspace((int64_t)B * N, hidden, G);

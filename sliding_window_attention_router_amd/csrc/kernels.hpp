@@ -26,6 +26,14 @@ hipError_t launch_router_grad(const void* dO, const void* Of, const void* Os, co
                               float* dbias, int B, int N, int Hq, int d, int hidden, int G, bool f32,
                               void* ws, hipStream_t s);
 
+// ---- attention backward of the hard-gated prefill -----------------------
+size_t backward_workspace(int B, int N, int Hq);
+hipError_t launch_backward(const void* Q, const void* K, const void* V, const void* O,
+                           const void* dO, const uint8_t* gate, const int32_t* idx,
+                           const int32_t* cnt, void* dQ, void* dK, void* dV, int B, int N, int Hq,
+                           int Hkv, int G, int d, int W, float scale, bool f32, void* ws,
+                           hipStream_t s);
+
 // ---- prefill ------------------------------------------------------------
 struct PrefillShape {
   int B, N, Hq, Hkv, G, d, W;

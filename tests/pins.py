@@ -568,6 +568,19 @@ def check_prefill_backward_special_cases():
         np.testing.assert_allclose(a[k], c[k], rtol=1e-13, atol=1e-13)
 
 
+def check_prefill_backward_rows_matches_full():
+    """The per-row dQ evaluation equals the rows of the full backward."""
+    rng = np.random.default_rng(84)
+    B, N, Hq, Hkv, d, W = 2, 30, 4, 2, 6, 7
+    Q, K, V = (rng.standard_normal(s) for s in ((B, N, Hq, d), (B, N, Hkv, d), (B, N, Hkv, d)))
+    dO = rng.standard_normal((B, N, Hq, d))
+    gate = (rng.random((B, N, 2)) < 0.4).astype(np.uint8)
+    full = ref.prefill_backward(Q, K, V, gate, W, dO)["dQ"]
+    rows = np.array([0, 1, 6, 7, 8, 29])
+    np.testing.assert_allclose(ref.prefill_backward_rows(Q, K, V, gate, W, dO, rows), full[:, rows],
+                               rtol=1e-12, atol=1e-13)
+
+
 ALL_PINS = [
     check_w4_key_ranges,
     check_w4_attention_weights,
@@ -595,4 +608,5 @@ ALL_PINS = [
     check_prefill_backward_finite_differences,
     check_prefill_backward_against_autograd,
     check_prefill_backward_special_cases,
+    check_prefill_backward_rows_matches_full,
 ]

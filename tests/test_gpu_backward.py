@@ -1,0 +1,111 @@
+"""GPU parity of the attention backward of the hard-gated prefill
+(swiattn_prefill_backward) against the float64 CPU reference.
+
+Q, K, V and dO are seeded and synthetic (the same stored values on both
+sides); O is the library's forward output, as in a forward -> backward
+pipeline (the reference forms its own).  Tolerance: max-abs error at most
+2^-6 of the largest reference magnitude of that gradient for bf16 (outputs
+rounded to bf16, O rounded to bf16 in the forward) and 1e-4 of it for
+float32."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sliding_window_attention_router_amd import synth
+from tests.gpu_util import TORCH_DTYPE, dev, ensure_built, host, max_abs, say
+
+pytestmark = pytest.mark.gpu
+
+REL = {"bf16": 2.0 ** -6, "f32": 1e-4}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_built()
+    yield
+    torch.cuda.empty_cache()
+
+
+def swa():
+    import sliding_window_attention_router_amd as m
+
+    return m
+
+
+def _inputs(seed, B, N, Hq, Hkv, d, dtype):
+    rng = np.random.default_rng(seed)
+    mk = (lambda s: synth.round_bf16(rng.standard_normal(s, dtype=np.float32))) if dtype == "bf16" \
+        else (lambda s: rng.standard_normal(s, dtype=np.float32))
+    return mk((B, N, Hq, d)), mk((B, N, Hkv, d)), mk((B, N, Hkv, d)), mk((B, N, Hq, d))
+
+
+CASES = [
+    # B, N,   Hq, Hkv, G, d,  W,   p,   dtype
+    (1, 300, 4, 2, 1, 128, 64, 0.3, "bf16"),     # GQA 2:1, ragged
+    (2, 200, 4, 4, 2, 64, 50, 0.4, "bf16"),      # MHA, two gate groups, d=64
+    (1, 257, 8, 2, 4, 128, 100, 0.5, "bf16"),    # gate groups inside a KV group
+    (1, 150, 4, 2, 1, 128, 400, 0.5, "bf16"),    # W > N
+    (1, 120, 4, 1, 1, 64, 1, 0.0, "bf16"),       # W = 1: dQ = dK = 0
+    (1, 200, 4, 2, 2, 64, 30, 1.0, "bf16"),      # gate all ones
+    (1, 220, 4, 2, 1, 128, 40, 0.3, "f32"),      # float32
+]
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,G,d,W,p,dtype", CASES)
+def test_prefill_backward(B, N, Hq, Hkv, G, d, W, p, dtype):
+    say(f"backward B={B} N={N} Hq={Hq} Hkv={Hkv} G={G} d={d} W={W} p={p} {dtype}")
+    Q, K, V, dO = _inputs(N * 5 + d, B, N, Hq, Hkv, d, dtype)
+    gate = (np.random.default_rng(N + W).random((B, N, G)) < p).astype(np.uint8)
+    td = TORCH_DTYPE[dtype]
+    Qg, Kg, Vg, dOg, gg = dev(Q, td), dev(K, td), dev(V, td), dev(dO, td), dev(gate)
+    O, _ = swa().prefill(Qg, Kg, Vg, gg, W)
+    dQ, dK, dV = swa().prefill_backward(Qg, Kg, Vg, O, dOg, gg, W)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_backward(Q, K, V, gate, W, dO)
+    for name, got in (("dQ", dQ), ("dK", dK), ("dV", dV)):
+        r = ref[name]
+        err = max_abs(host(got), r)
+        bound = REL[dtype] * max(float(np.abs(r).max()), 1e-30)
+        say(f"  {name} max-abs {err:.3e} (bound {bound:.3e})")
+        assert err <= bound or (np.abs(r).max() < 1e-12 and err < 1e-6)
+
+
+def test_prefill_backward_32k_layer():
+    """N=32768, GQA 16/4, d=128, W=1024, gate Bernoulli(0.13): two runs
+    bitwise equal; per KV head the dK rows sum to 0 and the dV rows sum to
+    the dO rows of its query heads (softmax rows sum to one); sampled dQ
+    rows against the reference."""
+    say("backward N=32768 GQA 16/4 W=1024 gate Bernoulli(0.13)")
+    W = 1024
+    w = synth.long_prefill(seed=3)
+    bf = torch.bfloat16
+    rng = np.random.default_rng(91)
+    dO = synth.round_bf16(rng.standard_normal(w.Q.shape, dtype=np.float32))
+    Qg, Kg, Vg, dOg, gg = dev(w.Q, bf), dev(w.K, bf), dev(w.V, bf), dev(dO, bf), dev(w.gate)
+    O, _ = swa().prefill(Qg, Kg, Vg, gg, W)
+    g1 = swa().prefill_backward(Qg, Kg, Vg, O, dOg, gg, W)
+    g2 = swa().prefill_backward(Qg, Kg, Vg, O, dOg, gg, W)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b), "two runs differ"
+    dQ, dK, dV = (host(t) for t in g1)
+    assert np.all(np.isfinite(dQ)) and np.all(np.isfinite(dK)) and np.all(np.isfinite(dV))
+    Hq, Hkv = w.Q.shape[2], w.K.shape[2]
+    sum_dO = dO.astype(np.float64).reshape(1, -1, Hkv, Hq // Hkv, 128).sum(axis=(1, 3))  # [1,Hkv,d]
+    scale_v = np.abs(dO).astype(np.float64).reshape(1, -1, Hkv, Hq // Hkv, 128).sum(axis=(1, 3))
+    ev = np.abs(dV.sum(axis=1) - sum_dO)
+    say(f"  sum dV - sum dO: worst {np.max(ev / scale_v):.3e} of sum |dO|")
+    assert np.all(ev <= 2.0 ** -6 * scale_v)
+    sk = np.abs(dK.sum(axis=1))
+    mk = np.abs(dK).sum(axis=1)
+    say(f"  |sum dK|: worst {np.max(sk / mk):.3e} of sum |dK|")
+    assert np.all(sk <= 2.0 ** -5 * mk)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(W - 4, W + 4), np.arange(32760, 32768),
+                                     rng.choice(np.flatnonzero(w.gate[0, :, 0]), 24, replace=False),
+                                     rng.choice(np.flatnonzero(w.gate[0, :, 0] == 0), 24, replace=False)]))
+    ref = oracle.prefill_backward_rows(w.Q, w.K, w.V, w.gate, W, dO, rows)
+    err = max_abs(dQ[:, rows], ref)
+    bound = REL["bf16"] * float(np.abs(ref).max())
+    say(f"  {rows.size} sampled dQ rows x 16 heads: max-abs {err:.3e} (bound {bound:.3e})")
+    assert err <= bound
