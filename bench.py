@@ -40,6 +40,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (256 CUs x 2.4 GHz x 256 FLOP/clk)
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # rocprofv3 counter summary of this benchmark (FETCH_SIZE / WRITE_SIZE per
@@ -67,6 +68,8 @@ def parse():
                     help="global anchor keys of the window branch in the anchored runs")
     ap.add_argument("--rgrad-steps", type=int, default=10,
                     help="timed runs of the router gradient (after the timed steps; 0 = skip)")
+    ap.add_argument("--bwd-steps", type=int, default=2,
+                    help="timed runs of the attention backward (after the timed steps; 0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB before the steps "
                          "(a known-size reference for hardware byte counters)")
@@ -268,6 +271,8 @@ def main():
             if args.anchor_steps > 0 else None)
     rgrad = (router_grad_run(swa, Q, K, V, W, H, r, bias, args.rgrad_steps)
              if args.rgrad_steps > 0 else None)
+    bwd = (backward_run(swa, Q, K, V, O, gate, idx, cnt, W, useful, args.bwd_steps)
+           if args.bwd_steps > 0 else None)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -303,6 +308,7 @@ def main():
             "serving_step": serve,
             "anchors": anch,
             "router_grad": rgrad,
+            "attention_backward": bwd,
         },
         "kernel_ms": {k: round(v, 4) for k, v in t.items()},
         "roofline": dict(rooflines[dominant], kernel=dominant),
@@ -408,6 +414,40 @@ def anchors_run(swa, Q, K, V, gate, idx, cnt, W, A, q_d, Kc, Vc, len_d, gate_d, 
                        "tok_per_s": round(q_d.shape[0] / (dec_ms * 1e-3), 1),
                        "GB_per_s": round(dbytes / (dec_ms * 1e-3) / 1e9, 1),
                        "splitk_frac_of_hbm_peak": round(dbytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+
+
+def backward_run(swa, Q, K, V, O, gate, idx, cnt, W, pairs, steps):
+    """Attention backward of the routed prefill (outside the timed steps) on
+    the timed step's inputs, gate and output, with dO ~ N(0,1) from a seeded
+    generator.  Useful work: 10*d FLOP per attended (query head, key) pair
+    (scores, dP, dV, dQ, dK); the kernels are vector-ALU float32, so the
+    roofline is the fp32 vector peak."""
+    import torch
+    d = Q.shape[3]
+    dev = Q.device
+    gen = torch.Generator(device=dev).manual_seed(31)
+    dO = torch.randn(Q.shape, generator=gen, device=dev).to(Q.dtype)
+    out = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+    B, N, Hq = Q.shape[:3]
+    ws = torch.empty(int(swa.lib().swiattn_prefill_backward_workspace_size(B, N, Hq)), dtype=torch.uint8,
+                     device=dev)
+    swa.prefill_backward(Q, K, V, O, dO, gate, W, idx=idx, cnt=cnt, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        swa.prefill_backward(Q, K, V, O, dO, gate, W, idx=idx, cnt=cnt, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    flop = 10.0 * d * pairs
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"useful_tflop": round(flop / 1e12, 4), "ms": round(ms, 3), "tflops": round(tf, 2),
+            "bound": "alu", "peak_fp32_vector_tflops": FP32_PEAK_TFLOPS,
+            "frac_of_fp32_vector_peak": round(tf / FP32_PEAK_TFLOPS, 4),
+            "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
 
 
 def router_grad_run(swa, Q, K, V, W, H, r, bias, steps):

@@ -231,3 +231,23 @@ def test_decode_step_anchored_rejects_negative_anchors(lib):
     rc = lib.swiattn_decode_step_anchored(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                           4, 100, 64, 4, 2, 1, 96, 16, 8, 0.088, BF16, FAKE, 1 << 40, None)
     assert rc == UNSUPPORTED
+
+
+def test_prefill_backward_rejects_invalid_arguments(lib):
+    def call(**kw):
+        a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, gate=FAKE, idx=FAKE, cnt=FAKE, dQ=FAKE, dK=FAKE,
+                 dV=FAKE, B=1, N=100, Hq=4, Hkv=2, G=1, d=128, W=16, scale=0.088, dt=BF16, ws=FAKE,
+                 ws_bytes=1 << 40, stream=None)
+        a.update(kw)
+        return lib.swiattn_prefill_backward(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["gate"], a["idx"],
+                                            a["cnt"], a["dQ"], a["dK"], a["dV"], a["B"], a["N"], a["Hq"],
+                                            a["Hkv"], a["G"], a["d"], a["W"], a["scale"], a["dt"], a["ws"],
+                                            a["ws_bytes"], a["stream"])
+    for kw, code in ((dict(B=0), INVALID), (dict(N=0), INVALID), (dict(W=0), INVALID),
+                     (dict(Hq=6, Hkv=4), INVALID), (dict(scale=0.0), INVALID), (dict(O=None), INVALID),
+                     (dict(dO=None), INVALID), (dict(idx=None), INVALID), (dict(dV=None), INVALID),
+                     (dict(d=96), UNSUPPORTED), (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE)):
+        assert call(**kw) == code, kw
+    # two floats (log-sum-exp, <dO, O>) per (sequence, query head, token)
+    assert lib.swiattn_prefill_backward_workspace_size(2, 100, 4) == 2 * 2 * 4 * 100 * 4
+    assert lib.swiattn_prefill_backward_workspace_size(0, 100, 4) == 0
