@@ -13,7 +13,7 @@
 //   bwd_row_kernel  one wave per (token, query head): pass 1 forms LSE_i over
 //                   S_i, pass 2 accumulates dQ_i; LSE_i and D_i go to the
 //                   workspace for the column pass
-//   bwd_col_kernel  one wave per (token j, KV head): walks the rows that see
+//   bwd_col_kernel  one wave per (key j, KV head), keys fastest: walks the rows that see
 //                   key j (the window rows j .. j+W-1 of every gate, then the
 //                   gate=1 rows past the window from the compacted list) for
 //                   each query head of the KV head and accumulates dK_j, dV_j
@@ -167,9 +167,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_col_kernel(BwdArgs a) {
   const T* Vp = static_cast<const T*>(a.V);
   const T* dOp = static_cast<const T*>(a.dO);
   for (int64_t c = int64_t(blockIdx.x) * (kBwdThreads / kWave) + (threadIdx.x >> 6); c < ncols; c += nw) {
-    const int kvh = int(c % a.Hkv);
-    const int64_t bj = c / a.Hkv;  // b * N + j
-    const int j = int(bj % a.N), b = int(bj / a.N);
+    // token fastest: the waves of a workgroup (and the workgroups an XCD
+    // runs) take neighbouring keys of one KV head, whose rows overlap
+    const int j = int(c % a.N);
+    const int64_t bk = c / a.N;  // b * Hkv + kvh
+    const int kvh = int(bk % a.Hkv), b = int(bk / a.Hkv);
+    const int64_t bj = int64_t(b) * a.N + j;
     const int64_t koff = (bj * a.Hkv + kvh) * D + lane * CPL;
     float k[CPL], v[CPL], dk[CPL], dv[CPL];
     load_ch<T, CPL>(Kp + koff, k);
