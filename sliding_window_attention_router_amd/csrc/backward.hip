@@ -10,16 +10,18 @@
 //   dV_j = sum_i P_ij dO_i   (K, V gradients summed over the query heads of
 //   a KV head).
 //
-//   bwd_row_kernel  one wave per (token, query head): pass 1 forms LSE_i over
-//                   S_i, pass 2 accumulates dQ_i; LSE_i and D_i go to the
-//                   workspace for the column pass
-//   bwd_col_kernel  one wave per (key j, KV head), keys fastest: walks the rows that see
-//                   key j (the window rows j .. j+W-1 of every gate, then the
-//                   gate=1 rows past the window from the compacted list) for
-//                   each query head of the KV head and accumulates dK_j, dV_j
-// A lane holds d/64 channels; every dot product is a lane product followed
-// by the wave's DPP sum, four keys (or rows) at a time.  This is a plain
-// VALU implementation (no matrix cores); every sum has a fixed order.
+//   bwd_row_kernel  one 16-lane group per (token, query head): pass 1 forms
+//                   LSE_i over S_i, pass 2 accumulates dQ_i; LSE_i and D_i
+//                   go to the workspace for the column pass
+//   bwd_col_kernel  one 16-lane group per (key j, KV head), keys fastest:
+//                   walks the rows that see key j (the window rows j ..
+//                   j+W-1 of every gate, then the gate=1 rows past the
+//                   window from the compacted list) for each query head of
+//                   the KV head and accumulates dK_j, dV_j
+// A wave holds four groups of 16 lanes (one row or key each, d/16 channels
+// per lane); a dot product is a lane product plus the 16-lane DPP row sum,
+// four keys (or rows) at a time.  This is a plain vector-ALU implementation
+// (no matrix cores); every sum has a fixed order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -44,6 +46,9 @@ struct BwdArgs {
   float scale;
 };
 
+constexpr int kGL = 16;               // lanes per group (one row or key each)
+constexpr int kGroups = kWave / kGL;  // groups per wave
+
 template <typename T, int CPL>
 SWI_DEV void load_ch(const T* p, float (&x)[CPL]) {
 #pragma unroll
@@ -58,11 +63,25 @@ SWI_DEV float lane_dot(const float (&a)[CPL], const float (&b)[CPL]) {
   return s;
 }
 
-// Row pass: wave w -> (b, i, h).
+// Sum over the 16 lanes of a DPP row (quads, half-rows, rows); each step
+// adds two equal-shaped partial sums, so all 16 lanes end with the same bits.
+SWI_DEV float row16_sum(float v) {
+  int x = __float_as_int(v);
+  const auto add = [](int p, int q) { return __float_as_int(__int_as_float(p) + __int_as_float(q)); };
+  x = add(x, dpp_src<0xB1>(x, 0));   // quad_perm [1,0,3,2]
+  x = add(x, dpp_src<0x4E>(x, 0));   // quad_perm [2,3,0,1]
+  x = add(x, dpp_src<0x141>(x, 0));  // row_half_mirror
+  x = add(x, dpp_src<0x140>(x, 0));  // row_mirror
+  return __int_as_float(x);
+}
+
+// Row pass: group grp of wave w -> item r = 4w + grp of the (b, i, h) order
+// (heads fastest: the groups of a wave are the heads of one token).  The
+// wave walks the union of its groups' key ranges; each group masks its own.
 template <typename T, int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_row_kernel(BwdArgs a) {
-  constexpr int CPL = D / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int CPL = D / kGL;
+  const int lane = threadIdx.x & (kWave - 1), grp = lane / kGL, gl = lane % kGL;
   const int64_t nrows = int64_t(a.B) * a.N * a.Hq;
   const int64_t nw = int64_t(gridDim.x) * (kBwdThreads / kWave);
   const T* Qp = static_cast<const T*>(a.Q);
@@ -70,53 +89,64 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_row_kernel(BwdArgs a) {
   const T* Vp = static_cast<const T*>(a.V);
   const T* Op = static_cast<const T*>(a.O);
   const T* dOp = static_cast<const T*>(a.dO);
-  for (int64_t r = int64_t(blockIdx.x) * (kBwdThreads / kWave) + (threadIdx.x >> 6); r < nrows; r += nw) {
-    const int h = int(r % a.Hq);
-    const int64_t bi = r / a.Hq;  // b * N + i
+  for (int64_t w = int64_t(blockIdx.x) * (kBwdThreads / kWave) + (threadIdx.x >> 6); w * kGroups < nrows;
+       w += nw) {
+    const int64_t r = w * kGroups + grp;
+    const bool act = r < nrows;
+    const int64_t rr = act ? r : nrows - 1;
+    const int h = int(rr % a.Hq);
+    const int64_t bi = rr / a.Hq;  // b * N + i
     const int i = int(bi % a.N), b = int(bi / a.N);
     const int kvh = h / a.HK, g = h / a.HG;
     const bool full = a.gate[bi * a.G + g] != 0;
     const int lo = full ? 0 : max(0, i - a.W + 1);
-    const int64_t qoff = (bi * a.Hq + h) * D + lane * CPL;
+    const int64_t qoff = (bi * a.Hq + h) * D + gl * CPL;
     const int64_t krow = int64_t(a.Hkv) * D;  // elements between key rows
-    const T* kb = Kp + (int64_t(b) * a.N * a.Hkv + kvh) * D + lane * CPL;
-    const T* vb = Vp + (int64_t(b) * a.N * a.Hkv + kvh) * D + lane * CPL;
+    const T* kb = Kp + (int64_t(b) * a.N * a.Hkv + kvh) * D + gl * CPL;
+    const T* vb = Vp + (int64_t(b) * a.N * a.Hkv + kvh) * D + gl * CPL;
     float q[CPL], go[CPL], o[CPL];
     load_ch<T, CPL>(Qp + qoff, q);
     load_ch<T, CPL>(dOp + qoff, go);
     load_ch<T, CPL>(Op + qoff, o);
+    const int jlo = wave_min_i(act ? lo : INT_MAX), jhi = wave_max_i(act ? i : -1);
     // pass 1: log-sum-exp over the key set (log2 units)
     float m = kNegInf, l = 0.f;
-    for (int j0 = lo; j0 <= i; j0 += kBwdGroup) {
+    for (int j0 = jlo; j0 <= jhi; j0 += kBwdGroup) {
       float s[kBwdGroup];
 #pragma unroll
       for (int u = 0; u < kBwdGroup; ++u) {
-        const int j = min(j0 + u, i);
+        const int j = min(j0 + u, jhi);
         float k[CPL];
         load_ch<T, CPL>(kb + int64_t(j) * krow, k);
         s[u] = lane_dot<CPL>(q, k);
       }
 #pragma unroll
-      for (int u = 0; u < kBwdGroup; ++u) s[u] = j0 + u <= i ? wave_sum(s[u]) * a.sl2 : kNegInf;
+      for (int u = 0; u < kBwdGroup; ++u) {
+        const int j = j0 + u;
+        const bool in = act && j <= jhi && j >= lo && j <= i;
+        s[u] = in ? row16_sum(s[u]) * a.sl2 : kNegInf;
+      }
       float mb = m;
 #pragma unroll
       for (int u = 0; u < kBwdGroup; ++u) mb = fmaxf(mb, s[u]);
-      l *= exp2f(m - mb);
+      if (mb != kNegInf) {
+        l *= exp2f(m - mb);
 #pragma unroll
-      for (int u = 0; u < kBwdGroup; ++u) l += exp2f(s[u] - mb);
-      m = mb;
+        for (int u = 0; u < kBwdGroup; ++u) l += exp2f(s[u] - mb);
+        m = mb;
+      }
     }
     const float lse = m + log2f(l);
-    const float Dv = wave_sum(lane_dot<CPL>(go, o));
+    const float Dv = row16_sum(lane_dot<CPL>(go, o));
     // pass 2: dQ
     float dq[CPL];
 #pragma unroll
     for (int e = 0; e < CPL; ++e) dq[e] = 0.f;
-    for (int j0 = lo; j0 <= i; j0 += kBwdGroup) {
+    for (int j0 = jlo; j0 <= jhi; j0 += kBwdGroup) {
       float s[kBwdGroup], dp[kBwdGroup], k[kBwdGroup][CPL];
 #pragma unroll
       for (int u = 0; u < kBwdGroup; ++u) {
-        const int j = min(j0 + u, i);
+        const int j = min(j0 + u, jhi);
         float v[CPL];
         load_ch<T, CPL>(kb + int64_t(j) * krow, k[u]);
         load_ch<T, CPL>(vb + int64_t(j) * krow, v);
@@ -125,19 +155,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_row_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < kBwdGroup; ++u) {
-        const float p = j0 + u <= i ? exp2f(wave_sum(s[u]) * a.sl2 - lse) : 0.f;
-        const float ds = p * (wave_sum(dp[u]) - Dv);
+        const int j = j0 + u;
+        const bool in = act && j <= jhi && j >= lo && j <= i;
+        const float sv = row16_sum(s[u]), dv = row16_sum(dp[u]);
+        const float p = in ? exp2f(sv * a.sl2 - lse) : 0.f;
+        const float ds = p * (dv - Dv);
 #pragma unroll
         for (int e = 0; e < CPL; ++e) dq[e] = fmaf(ds, k[u][e], dq[e]);
       }
     }
-    T* dqp = static_cast<T*>(a.dQ) + qoff;
+    if (act) {
+      T* dqp = static_cast<T*>(a.dQ) + qoff;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) Elem<T>::store(dqp + e, dq[e] * a.scale);
-    if (lane == 0) {
-      const int64_t sidx = (int64_t(b) * a.Hq + h) * a.N + i;
-      a.lse2[sidx] = lse;
-      a.Drow[sidx] = Dv;
+      for (int e = 0; e < CPL; ++e) Elem<T>::store(dqp + e, dq[e] * a.scale);
+      if (gl == 0) {
+        const int64_t sidx = (int64_t(b) * a.Hq + h) * a.N + i;
+        a.lse2[sidx] = lse;
+        a.Drow[sidx] = Dv;
+      }
     }
   }
 }
@@ -155,25 +190,31 @@ SWI_DEV int lower_bound_idx(const int32_t* list, int n, int x) {
   return lo;
 }
 
-// Column pass: wave w -> (b, j, kvh).
+// Column pass: group grp of wave w -> item c = 4w + grp of the (b, kvh, j)
+// order (keys fastest: the groups of a wave are four neighbouring keys of
+// one KV head, and neighbouring waves share their rows in cache).  For each
+// query head of the KV head the wave walks the union of its groups' window
+// rows (a row sees key j if i >= j and (i <= j+W-1 or its gate is 1)), then
+// the gate=1 rows past that union from the compacted list.
 template <typename T, int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_col_kernel(BwdArgs a) {
-  constexpr int CPL = D / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int CPL = D / kGL;
+  const int lane = threadIdx.x & (kWave - 1), grp = lane / kGL, gl = lane % kGL;
   const int64_t ncols = int64_t(a.B) * a.N * a.Hkv;
   const int64_t nw = int64_t(gridDim.x) * (kBwdThreads / kWave);
   const T* Qp = static_cast<const T*>(a.Q);
   const T* Kp = static_cast<const T*>(a.K);
   const T* Vp = static_cast<const T*>(a.V);
   const T* dOp = static_cast<const T*>(a.dO);
-  for (int64_t c = int64_t(blockIdx.x) * (kBwdThreads / kWave) + (threadIdx.x >> 6); c < ncols; c += nw) {
-    // token fastest: the waves of a workgroup (and the workgroups an XCD
-    // runs) take neighbouring keys of one KV head, whose rows overlap
-    const int j = int(c % a.N);
-    const int64_t bk = c / a.N;  // b * Hkv + kvh
+  for (int64_t w = int64_t(blockIdx.x) * (kBwdThreads / kWave) + (threadIdx.x >> 6); w * kGroups < ncols;
+       w += nw) {
+    const int64_t c = w * kGroups + grp;
+    const bool act = c < ncols;
+    const int64_t cc = act ? c : ncols - 1;
+    const int j = int(cc % a.N);
+    const int64_t bk = cc / a.N;  // b * Hkv + kvh
     const int kvh = int(bk % a.Hkv), b = int(bk / a.Hkv);
-    const int64_t bj = int64_t(b) * a.N + j;
-    const int64_t koff = (bj * a.Hkv + kvh) * D + lane * CPL;
+    const int64_t koff = ((int64_t(b) * a.N + j) * a.Hkv + kvh) * D + gl * CPL;
     float k[CPL], v[CPL], dk[CPL], dv[CPL];
     load_ch<T, CPL>(Kp + koff, k);
     load_ch<T, CPL>(Vp + koff, v);
@@ -181,24 +222,20 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_col_kernel(BwdArgs a) {
     for (int e = 0; e < CPL; ++e) dk[e] = dv[e] = 0.f;
     const int64_t qrow = int64_t(a.Hq) * D;  // elements between query rows
     const int wend = int(min<int64_t>(int64_t(a.N) - 1, int64_t(j) + a.W - 1));  // last window row
+    const int ilo = wave_min_i(act ? j : INT_MAX), ihi = wave_max_i(act ? wend : -1);
     for (int hh = 0; hh < a.HK; ++hh) {
       const int h = kvh * a.HK + hh, g = h / a.HG;
-      const T* qb = Qp + (int64_t(b) * a.N * a.Hq + h) * D + lane * CPL;
-      const T* db = dOp + (int64_t(b) * a.N * a.Hq + h) * D + lane * CPL;
+      const T* qb = Qp + (int64_t(b) * a.N * a.Hq + h) * D + gl * CPL;
+      const T* db = dOp + (int64_t(b) * a.N * a.Hq + h) * D + gl * CPL;
       const float* lrow = a.lse2 + (int64_t(b) * a.Hq + h) * a.N;
       const float* drow = a.Drow + (int64_t(b) * a.Hq + h) * a.N;
+      const uint8_t* grow = a.gate + int64_t(b) * a.N * a.G + g;
       const int32_t* list = a.idx + (int64_t(b) * a.G + g) * a.N;
       const int n = a.cnt[b * a.G + g];
-      // rows: window rows j .. wend (any gate), then gate=1 rows > wend
-      const int f0 = lower_bound_idx(list, n, wend + 1);
-      const int nwin = wend - j + 1, total = nwin + (n - f0);
-      for (int t0 = 0; t0 < total; t0 += kBwdGroup) {
-        int row[kBwdGroup];
+      const auto visit = [&](const int (&row)[kBwdGroup], const bool (&sees)[kBwdGroup]) {
         float s[kBwdGroup], dp[kBwdGroup], qv[kBwdGroup][CPL], gv[kBwdGroup][CPL];
 #pragma unroll
         for (int u = 0; u < kBwdGroup; ++u) {
-          const int t = min(t0 + u, total - 1);
-          row[u] = t < nwin ? j + t : list[f0 + (t - nwin)];
           load_ch<T, CPL>(qb + int64_t(row[u]) * qrow, qv[u]);
           load_ch<T, CPL>(db + int64_t(row[u]) * qrow, gv[u]);
           s[u] = lane_dot<CPL>(qv[u], k);
@@ -206,23 +243,52 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_col_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < kBwdGroup; ++u) {
-          const bool live = t0 + u < total;
-          const float p = live ? exp2f(wave_sum(s[u]) * a.sl2 - lrow[row[u]]) : 0.f;
-          const float ds = p * (wave_sum(dp[u]) - drow[row[u]]);
+          const float sv = row16_sum(s[u]), dpv = row16_sum(dp[u]);
+          const float p = sees[u] ? exp2f(sv * a.sl2 - lrow[row[u]]) : 0.f;
+          const float ds = p * (dpv - drow[row[u]]);
 #pragma unroll
           for (int e = 0; e < CPL; ++e) {
             dv[e] = fmaf(p, gv[u][e], dv[e]);
             dk[e] = fmaf(ds, qv[u][e], dk[e]);
           }
         }
+      };
+      // the union of the groups' window rows
+      for (int i0 = ilo; i0 <= ihi; i0 += kBwdGroup) {
+        int row[kBwdGroup];
+        bool sees[kBwdGroup];
+#pragma unroll
+        for (int u = 0; u < kBwdGroup; ++u) {
+          const int i = i0 + u;
+          row[u] = min(i, ihi);
+          sees[u] = act && i <= ihi && i >= j && (i <= wend || grow[int64_t(row[u]) * a.G] != 0);
+        }
+        visit(row, sees);
+      }
+      // gate=1 rows past the union
+      const int f0 = lower_bound_idx(list, n, ihi + 1);
+      const int cnt_g = act ? n - f0 : 0;
+      const int tmax = wave_max_i(cnt_g);
+      for (int t0 = 0; t0 < tmax; t0 += kBwdGroup) {
+        int row[kBwdGroup];
+        bool sees[kBwdGroup];
+#pragma unroll
+        for (int u = 0; u < kBwdGroup; ++u) {
+          const int t = t0 + u;
+          sees[u] = t < cnt_g;
+          row[u] = cnt_g > 0 ? list[f0 + min(t, cnt_g - 1)] : j;
+        }
+        visit(row, sees);
       }
     }
-    T* dkp = static_cast<T*>(a.dK) + koff;
-    T* dvp = static_cast<T*>(a.dV) + koff;
+    if (act) {
+      T* dkp = static_cast<T*>(a.dK) + koff;
+      T* dvp = static_cast<T*>(a.dV) + koff;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      Elem<T>::store(dkp + e, dk[e] * a.scale);
-      Elem<T>::store(dvp + e, dv[e]);
+      for (int e = 0; e < CPL; ++e) {
+        Elem<T>::store(dkp + e, dk[e] * a.scale);
+        Elem<T>::store(dvp + e, dv[e]);
+      }
     }
   }
 }
@@ -233,8 +299,8 @@ template <typename T, int D>
 static hipError_t run_backward(BwdArgs& a, hipStream_t s) {
   const int64_t rows = int64_t(a.B) * a.N * a.Hq;
   const int64_t cols = int64_t(a.B) * a.N * a.Hkv;
-  const int wpb = kBwdThreads / kWave;
-  const int64_t g1 = (rows + wpb - 1) / wpb, g2 = (cols + wpb - 1) / wpb;
+  const int per_wg = (kBwdThreads / kWave) * kGroups;  // items per workgroup
+  const int64_t g1 = (rows + per_wg - 1) / per_wg, g2 = (cols + per_wg - 1) / per_wg;
   hipLaunchKernelGGL((bwd_row_kernel<T, D>), dim3(unsigned(g1 < 65536 ? g1 : 65536)), dim3(kBwdThreads), 0,
                      s, a);
   hipError_t e = hipGetLastError();
