@@ -10,9 +10,10 @@
 //   dV_j = sum_i P_ij dO_i   (K, V gradients summed over the query heads of
 //   a KV head).
 //
-//   bwd_row_kernel  one 16-lane group per (token, query head): pass 1 forms
-//                   LSE_i over S_i, pass 2 accumulates dQ_i; LSE_i and D_i
-//                   go to the workspace for the column pass
+//   bwd_row_kernel  one 16-lane group per (token, query head): one online
+//                   pass over S_i accumulates dQ_i and LSE_i (running
+//                   maximum, rescaled sums); LSE_i and D_i go to the
+//                   workspace for the column pass
 //   bwd_col_kernel  one 16-lane group per (key j, KV head), keys fastest:
 //                   walks the rows that see key j (the window rows j ..
 //                   j+W-1 of every gate, then the gate=1 rows past the
@@ -109,37 +110,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_row_kernel(BwdArgs a) {
     load_ch<T, CPL>(dOp + qoff, go);
     load_ch<T, CPL>(Op + qoff, o);
     const int jlo = wave_min_i(act ? lo : INT_MAX), jhi = wave_max_i(act ? i : -1);
-    // pass 1: log-sum-exp over the key set (log2 units)
-    float m = kNegInf, l = 0.f;
-    for (int j0 = jlo; j0 <= jhi; j0 += kBwdGroup) {
-      float s[kBwdGroup];
-#pragma unroll
-      for (int u = 0; u < kBwdGroup; ++u) {
-        const int j = min(j0 + u, jhi);
-        float k[CPL];
-        load_ch<T, CPL>(kb + int64_t(j) * krow, k);
-        s[u] = lane_dot<CPL>(q, k);
-      }
-#pragma unroll
-      for (int u = 0; u < kBwdGroup; ++u) {
-        const int j = j0 + u;
-        const bool in = act && j <= jhi && j >= lo && j <= i;
-        s[u] = in ? row16_sum(s[u]) * a.sl2 : kNegInf;
-      }
-      float mb = m;
-#pragma unroll
-      for (int u = 0; u < kBwdGroup; ++u) mb = fmaxf(mb, s[u]);
-      if (mb != kNegInf) {
-        l *= exp2f(m - mb);
-#pragma unroll
-        for (int u = 0; u < kBwdGroup; ++u) l += exp2f(s[u] - mb);
-        m = mb;
-      }
-    }
-    const float lse = m + log2f(l);
+    // one online pass: with m the running maximum of the scores (log2
+    // units), l = sum 2^(s - m) and dq = sum 2^(s - m) (dP - D) k; when m
+    // rises both are rescaled.  D = <dO, O> is known before the pass, so
+    // dQ = dq / l and LSE = m + log2(l) at the end.
     const float Dv = row16_sum(lane_dot<CPL>(go, o));
-    // pass 2: dQ
-    float dq[CPL];
+    float m = kNegInf, l = 0.f, dq[CPL];
 #pragma unroll
     for (int e = 0; e < CPL; ++e) dq[e] = 0.f;
     for (int j0 = jlo; j0 <= jhi; j0 += kBwdGroup) {
@@ -153,17 +129,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_row_kernel(BwdArgs a) {
         s[u] = lane_dot<CPL>(q, k[u]);
         dp[u] = lane_dot<CPL>(go, v);
       }
+      float mb = m;
 #pragma unroll
       for (int u = 0; u < kBwdGroup; ++u) {
         const int j = j0 + u;
         const bool in = act && j <= jhi && j >= lo && j <= i;
-        const float sv = row16_sum(s[u]), dv = row16_sum(dp[u]);
-        const float p = in ? exp2f(sv * a.sl2 - lse) : 0.f;
-        const float ds = p * (dv - Dv);
+        s[u] = in ? row16_sum(s[u]) * a.sl2 : kNegInf;
+        dp[u] = row16_sum(dp[u]);
+        mb = fmaxf(mb, s[u]);
+      }
+      if (mb == kNegInf) continue;  // no key of this group in the step (group-uniform)
+      const float sc = exp2f(m - mb);  // 0 while m is -inf
+      l *= sc;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) dq[e] *= sc;
+#pragma unroll
+      for (int u = 0; u < kBwdGroup; ++u) {
+        const float p = exp2f(s[u] - mb);
+        l += p;
+        const float ds = p * (dp[u] - Dv);
 #pragma unroll
         for (int e = 0; e < CPL; ++e) dq[e] = fmaf(ds, k[u][e], dq[e]);
       }
+      m = mb;
     }
+    const float lse = m + log2f(l);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) dq[e] *= inv;
     if (act) {
       T* dqp = static_cast<T*>(a.dQ) + qoff;
 #pragma unroll
