@@ -13,7 +13,9 @@
 //   bwd_row_kernel  one 16-lane group per (token, query head): one online
 //                   pass over S_i accumulates dQ_i and LSE_i (running
 //                   maximum, rescaled sums); LSE_i and D_i go to the
-//                   workspace for the column pass
+//                   workspace for the column pass.  Two launches: the
+//                   gate=0 rows in token order, the gate=1 rows gathered
+//                   (neighbouring routed tokens share their keys)
 //   bwd_col_kernel  one 16-lane group per (key j, KV head), keys fastest:
 //                   walks the rows that see key j (the window rows j ..
 //                   j+W-1 of every gate, then the gate=1 rows past the
@@ -76,10 +78,15 @@ SWI_DEV float row16_sum(float v) {
   return __int_as_float(x);
 }
 
-// Row pass: group grp of wave w -> item r = 4w + grp of the (b, i, h) order
-// (heads fastest: the groups of a wave are the heads of one token).  The
-// wave walks the union of its groups' key ranges; each group masks its own.
-template <typename T, int D>
+// Row pass, in two launches.  kFar = false: group grp of wave w -> item
+// r = 4w + grp of the (b, i, h) order (heads fastest: the groups of a wave
+// are the heads of one token); rows whose gate is 1 are left to the other
+// launch.  kFar = true: item r of the (b, h, t) order with t fastest is the
+// t-th gate=1 token of head h's gate group (from the compacted list), so
+// the groups of a workgroup are 16 neighbouring routed tokens of one head,
+// which walk the same keys [0, i] together.  The wave walks the union of its
+// groups' key ranges; each group masks its own.
+template <typename T, int D, bool kFar>
 __global__ __launch_bounds__(kBwdThreads) void bwd_row_kernel(BwdArgs a) {
   constexpr int CPL = D / kGL;
   const int lane = threadIdx.x & (kWave - 1), grp = lane / kGL, gl = lane % kGL;
@@ -93,13 +100,29 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_row_kernel(BwdArgs a) {
   for (int64_t w = int64_t(blockIdx.x) * (kBwdThreads / kWave) + (threadIdx.x >> 6); w * kGroups < nrows;
        w += nw) {
     const int64_t r = w * kGroups + grp;
-    const bool act = r < nrows;
+    bool act = r < nrows;
     const int64_t rr = act ? r : nrows - 1;
-    const int h = int(rr % a.Hq);
-    const int64_t bi = rr / a.Hq;  // b * N + i
-    const int i = int(bi % a.N), b = int(bi / a.N);
+    int h, i, b;
+    if constexpr (kFar) {
+      const int t = int(rr % a.N);
+      const int64_t bh = rr / a.N;  // b * Hq + h
+      h = int(bh % a.Hq);
+      b = int(bh / a.Hq);
+      const int gg = h / a.HG;
+      const int n = a.cnt[b * a.G + gg];
+      act = act && t < n;
+      i = a.idx[(int64_t(b) * a.G + gg) * a.N + (t < n ? t : 0)];
+      if (!act) i = 0;
+    } else {
+      h = int(rr % a.Hq);
+      const int64_t bi0 = rr / a.Hq;  // b * N + i
+      i = int(bi0 % a.N);
+      b = int(bi0 / a.N);
+    }
+    const int64_t bi = int64_t(b) * a.N + i;
     const int kvh = h / a.HK, g = h / a.HG;
     const bool full = a.gate[bi * a.G + g] != 0;
+    if constexpr (!kFar) act = act && !full;  // gate=1 rows: the other launch
     const int lo = full ? 0 : max(0, i - a.W + 1);
     const int64_t qoff = (bi * a.Hq + h) * D + gl * CPL;
     const int64_t krow = int64_t(a.Hkv) * D;  // elements between key rows
@@ -294,10 +317,13 @@ static hipError_t run_backward(BwdArgs& a, hipStream_t s) {
   const int64_t cols = int64_t(a.B) * a.N * a.Hkv;
   const int per_wg = (kBwdThreads / kWave) * kGroups;  // items per workgroup
   const int64_t g1 = (rows + per_wg - 1) / per_wg, g2 = (cols + per_wg - 1) / per_wg;
-  hipLaunchKernelGGL((bwd_row_kernel<T, D>), dim3(unsigned(g1 < 65536 ? g1 : 65536)), dim3(kBwdThreads), 0,
-                     s, a);
+  hipLaunchKernelGGL((bwd_row_kernel<T, D, false>), dim3(unsigned(g1 < 65536 ? g1 : 65536)),
+                     dim3(kBwdThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_row_kernel<T, D, true>), dim3(unsigned(g1 < 65536 ? g1 : 65536)),
+                     dim3(kBwdThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_col_kernel<T, D>), dim3(unsigned(g2 < 65536 ? g2 : 65536)), dim3(kBwdThreads), 0,
                      s, a);
   return hipGetLastError();
