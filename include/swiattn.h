@@ -348,9 +348,9 @@ int swiattn_router_backward(const void* dO, const void* O_full, const void* O_sw
  *   swiattn_prefill_backward_workspace_size(B, N, Hq) bytes (each row's
  *   log-sum-exp and <dO, O>), clobbered.
  * Only the attention path: the gate's gradient is swiattn_router_backward's.
- * float32 arithmetic in a fixed order (bitwise reproducible); a plain
- * vector-ALU implementation, one wave per (row, query head) for dQ and per
- * (key, KV head) for dK and dV.  Outputs must not overlap inputs.
+ * float32 arithmetic in a fixed order (bitwise reproducible); vector-ALU
+ * kernels, 16 lanes per (row, query head) for dQ and per (key, KV head)
+ * for dK and dV.  Outputs must not overlap inputs.
  * Errors: as swiattn_prefill (INVALID_ARG, UNSUPPORTED, WORKSPACE).
  */
 size_t swiattn_prefill_backward_workspace_size(int B, int N, int Hq);
