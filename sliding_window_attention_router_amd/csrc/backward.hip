@@ -16,17 +16,23 @@
 //                   workspace for the column pass.  Two launches: the
 //                   gate=0 rows in token order, the gate=1 rows gathered
 //                   (neighbouring routed tokens share their keys)
-//   bwd_col_kernel  one 16-lane group per (key j, KV head), keys fastest:
-//                   walks the rows that see key j (the window rows j ..
-//                   j+W-1 of every gate, then the gate=1 rows past the
+//   bwd_kv_mfma_kernel  (bfloat16) dK, dV on the matrix cores: a
+//                   workgroup per 128 keys of a KV head walks 32-row tiles
+//                   of the rows that see them (window rows of every gate,
+//                   then gathered gate=1 rows) for each query head
+//   bwd_col_kernel  (float32) one 16-lane group per (key j, KV head), keys
+//                   fastest: walks the rows that see key j (the window rows
+//                   j .. j+W-1 of every gate, then the gate=1 rows past the
 //                   window from the compacted list) for each query head of
 //                   the KV head and accumulates dK_j, dV_j
-// A wave holds four groups of 16 lanes (one row or key each, d/16 channels
-// per lane); a dot product is a lane product plus the 16-lane DPP row sum,
-// four keys (or rows) at a time.  This is a plain vector-ALU implementation
-// (no matrix cores); every sum has a fixed order.
+// In the vector-ALU kernels a wave holds four groups of 16 lanes (one row
+// or key each, d/16 channels per lane); a dot product is a lane product
+// plus the 16-lane DPP row sum, four keys (or rows) at a time.  Every sum
+// has a fixed order (bitwise reproducible).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -309,6 +315,227 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_col_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV on the matrix cores (bfloat16).  A workgroup owns kKvKeys keys of
+// one KV head, 32 per wave; each wave keeps its keys' K and V rows in
+// registers as MFMA B operands.  For every query head of the KV head the
+// workgroup walks tiles of 32 query rows: first the window rows
+// [k0, min(N, k0 + kKvKeys - 1 + W)) (any gate; masked per pair), then the
+// gate=1 rows past them, gathered from the compacted list.  The four waves
+// share each tile: Q and dO rows are staged once in LDS (double-buffered,
+// one barrier per tile) with each row's LSE, D and visible key range.
+//   S  = Q K^T,  dP = dO V^T         (32 rows x 32 keys, k = channels)
+//   P  = 2^(S sl2 - LSE) on visible pairs,  dS = P (dP - D)
+//   dV^T += dO^T P,  dK^T += Q^T dS  (channels x 32 keys, k = rows)
+// The 32x32 accumulator of S gives lane l the key l % 32 and rows
+// 8(i/4) + 4(l/32) + i%4; those are exactly the contraction slots a B
+// operand of the second products holds (rows permuted the same way on the
+// A side), so P and dS feed the next MFMAs from registers, and the
+// transposed A operands (dO^T, Q^T) come from ds_read_b64_tr_b16: within 16
+// lanes, source lane 4r + k points at row r, channels c0 + 4k .. c0 + 4k + 3,
+// and lane i receives channel c0 + i of rows 0..3.
+// LDS rows are XOR-swizzled by 16-byte chunk so that both the plain 16-byte
+// reads (16 lanes, 16 consecutive rows, one chunk) and the transposing
+// reads (32 lanes, 4 rows x 4 chunks) hit distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int kKvKeys = 128;  // keys per workgroup (4 waves x 32)
+constexpr int kRT = 32;       // query rows per tile
+
+template <int D>
+struct KvTile {
+  static constexpr int kRowB = 2 * D;
+  static constexpr int kMat = kRT * kRowB;           // one staged matrix (Q or dO)
+  static constexpr int kInfo = 2 * kMat;             // lse2, D, first key, last key: [4][kRT]
+  static constexpr int kBytes = kInfo + 4 * kRT * 4;
+  static constexpr int kCPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int kPer = kRT * kCPR / kBwdThreads;  // chunks per thread and matrix
+  static_assert(kPer >= 1 && kRT * kCPR % kBwdThreads == 0, "tile staging");
+  SWI_DEV static constexpr int swz(int row) {
+    return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  }
+  SWI_DEV static constexpr int pos(int row, int chunk) { return row * kRowB + ((chunk ^ swz(row)) << 4); }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+SWI_DEV s16x4 lds_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(BwdArgs a) {
+  using L = KvTile<D>;
+  constexpr int KS = D / 16;  // k-steps of the channel contractions
+  constexpr int MD = D / 32;  // 32-channel tiles of dK^T, dV^T
+  __shared__ __attribute__((aligned(16))) char lds[2][L::kBytes];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int rl = lane & 31, hf = lane >> 5;
+  const int nbk = a.B * a.Hkv;
+  const int kblk = blockIdx.x / nbk, bk = blockIdx.x % nbk;  // heaviest key blocks first
+  const int b = bk / a.Hkv, kvh = bk % a.Hkv;
+  const int k0 = kblk * kKvKeys;
+  const int j = k0 + wave * 32 + rl;  // this lane's key
+  const int jc = min(j, a.N - 1);
+  const bf16_t* Qp = static_cast<const bf16_t*>(a.Q);
+  const bf16_t* dOp = static_cast<const bf16_t*>(a.dO);
+  bf16x8 kreg[KS], vreg[KS];
+  {
+    const int64_t off = ((int64_t(b) * a.N + jc) * a.Hkv + kvh) * D + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kreg[ks] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16_t*>(a.K) + off + 16 * ks);
+      vreg[ks] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16_t*>(a.V) + off + 16 * ks);
+    }
+  }
+  f32x16 dk[MD], dv[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) dk[md] = dv[md] = f32x16{};
+  const int wend = int(min<int64_t>(a.N, int64_t(k0) + kKvKeys - 1 + a.W));  // window rows end here
+  const int nwt = (wend - k0 + kRT - 1) / kRT;
+  const int64_t qrs = int64_t(a.Hq) * D;  // elements between query rows
+  // transposing-read lane roles: row r of a 4-row group, channel quad kq,
+  // 16-channel half c16 of a 32-channel tile
+  const int tr_r = (lane >> 2) & 3, tr_kq = lane & 3, tr_c16 = (lane >> 4) & 1;
+  for (int hh = 0; hh < a.HK; ++hh) {
+    const int h = kvh * a.HK + hh, g = h / a.HG;
+    const int32_t* list = a.idx + (int64_t(b) * a.G + g) * a.N;
+    const int n = a.cnt[b * a.G + g];
+    const int f0 = lower_bound_idx(list, n, wend);
+    const int nt = nwt + (n - f0 + kRT - 1) / kRT;
+    const bf16_t* qh = Qp + int64_t(b) * a.N * qrs + int64_t(h) * D;
+    const bf16_t* dh = dOp + int64_t(b) * a.N * qrs + int64_t(h) * D;
+    const float* lrow = a.lse2 + (int64_t(b) * a.Hq + h) * a.N;
+    const float* drow = a.Drow + (int64_t(b) * a.Hq + h) * a.N;
+    const uint8_t* grow = a.gate + int64_t(b) * a.N * a.G + g;
+    // query row of tile t, slot m (-1: padding)
+    const auto row_of = [&](int t, int m) -> int {
+      if (t < nwt) {
+        const int r = k0 + t * kRT + m;
+        return r < wend ? r : -1;
+      }
+      const int p = f0 + (t - nwt) * kRT + m;
+      return p < n ? list[p] : -1;
+    };
+    u32x4 sq[L::kPer], sd[L::kPer];
+    float s_l = 0.f, s_d = 0.f;
+    int s_lo = 0, s_hi = -1;
+    const auto load_tile = [&](int t) {
+#pragma unroll
+      for (int p = 0; p < L::kPer; ++p) {
+        const int u = tid + p * kBwdThreads, m = u / L::kCPR, c = u % L::kCPR;
+        const int r = row_of(t, m);
+        if (r >= 0) {
+          sq[p] = *reinterpret_cast<const u32x4*>(qh + int64_t(r) * qrs + 8 * c);
+          sd[p] = *reinterpret_cast<const u32x4*>(dh + int64_t(r) * qrs + 8 * c);
+        } else {
+          sq[p] = sd[p] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      if (tid < kRT) {
+        const int r = row_of(t, tid);
+        if (r >= 0) {
+          s_l = lrow[r];
+          s_d = drow[r];
+          s_hi = r;
+          s_lo = grow[int64_t(r) * a.G] != 0 ? 0 : r - a.W + 1;
+        } else {
+          s_l = __builtin_huge_valf();
+          s_d = 0.f;
+          s_lo = 0;
+          s_hi = -1;
+        }
+      }
+    };
+    const auto store_tile = [&](char* buf) {
+#pragma unroll
+      for (int p = 0; p < L::kPer; ++p) {
+        const int u = tid + p * kBwdThreads, m = u / L::kCPR, c = u % L::kCPR;
+        *reinterpret_cast<u32x4*>(buf + L::pos(m, c)) = sq[p];
+        *reinterpret_cast<u32x4*>(buf + L::kMat + L::pos(m, c)) = sd[p];
+      }
+      if (tid < kRT) {
+        float* info = reinterpret_cast<float*>(buf + L::kInfo);
+        info[tid] = s_l;
+        info[kRT + tid] = s_d;
+        reinterpret_cast<int*>(info)[2 * kRT + tid] = s_lo;
+        reinterpret_cast<int*>(info)[3 * kRT + tid] = s_hi;
+      }
+    };
+    load_tile(0);
+    store_tile(lds[0]);
+    __syncthreads();
+    for (int t = 0; t < nt; ++t) {
+      const bool more = t + 1 < nt;
+      if (more) load_tile(t + 1);
+      const char* qt = lds[t & 1];
+      const char* dt = qt + L::kMat;
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + L::pos(rl, 2 * ks + hf));
+        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dt + L::pos(rl, 2 * ks + hf));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[ks], dp, 0, 0, 0);
+      }
+      // P and dS for rows 8q + 4hf + e (slot 4q + e)
+      const float* info = reinterpret_cast<const float*>(qt + L::kInfo);
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m0 = 8 * q + 4 * hf;
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(info + m0);
+        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(info + kRT + m0);
+        typedef int i32x4 __attribute__((ext_vector_type(4)));
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(info + 2 * kRT + m0);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(info + 3 * kRT + m0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q + e;
+          const bool vis = j >= lo[e] && j <= hi[e];
+          const float p = vis ? fast_exp2(s[i] * a.sl2 - lv[e]) : 0.f;
+          pb[i >> 3][i & 7] = bf16_t(p);
+          sb[i >> 3][i & 7] = bf16_t(p * (dp[i] - dv4[e]));
+        }
+      }
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const int c = 4 * md + 2 * tr_c16 + (tr_kq >> 1), cb = (tr_kq & 1) * 8;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int r0 = 16 * st + 4 * hf + tr_r, r1 = r0 + 8;
+          const s16x4 d0 = lds_tr16(dt + L::pos(r0, c) + cb), d1 = lds_tr16(dt + L::pos(r1, c) + cb);
+          const s16x4 q0 = lds_tr16(qt + L::pos(r0, c) + cb), q1 = lds_tr16(qt + L::pos(r1, c) + cb);
+          const bf16x8 ad = __builtin_bit_cast(bf16x8, __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7));
+          const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
+          dv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, pb[st], dv[md], 0, 0, 0);
+          dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[st], dk[md], 0, 0, 0);
+        }
+      }
+      if (more) store_tile(lds[(t + 1) & 1]);
+      __syncthreads();
+    }
+  }
+  if (j < a.N) {
+    const int64_t off = ((int64_t(b) * a.N + j) * a.Hkv + kvh) * D;
+    bf16_t* dkp = static_cast<bf16_t*>(a.dK) + off;
+    bf16_t* dvp = static_cast<bf16_t*>(a.dV) + off;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ch = 32 * md + 8 * q + 4 * hf;
+        bf16x4 vk, vv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vk[e] = bf16_t(dk[md][4 * q + e] * a.scale);
+          vv[e] = bf16_t(dv[md][4 * q + e]);
+        }
+        *reinterpret_cast<bf16x4*>(dkp + ch) = vk;
+        *reinterpret_cast<bf16x4*>(dvp + ch) = vv;
+      }
+  }
+}
+
 size_t backward_workspace(int B, int N, int Hq) { return size_t(2) * B * Hq * N * sizeof(float); }
 
 template <typename T, int D>
@@ -324,8 +551,14 @@ static hipError_t run_backward(BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_row_kernel<T, D, true>), dim3(unsigned(g1 < 65536 ? g1 : 65536)),
                      dim3(kBwdThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_col_kernel<T, D>), dim3(unsigned(g2 < 65536 ? g2 : 65536)), dim3(kBwdThreads), 0,
-                     s, a);
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    const int64_t nkb = (int64_t(a.N) + kKvKeys - 1) / kKvKeys;
+    hipLaunchKernelGGL((bwd_kv_mfma_kernel<D>), dim3(unsigned(nkb * a.B * a.Hkv)), dim3(kBwdThreads), 0, s,
+                       a);
+  } else {
+    hipLaunchKernelGGL((bwd_col_kernel<T, D>), dim3(unsigned(g2 < 65536 ? g2 : 65536)), dim3(kBwdThreads), 0,
+                       s, a);
+  }
   return hipGetLastError();
 }
 
