@@ -536,6 +536,207 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// dQ on the matrix cores (bfloat16), with each row's LSE and D for the dK/dV
+// kernel.  A workgroup owns kQRows query rows of one head, 32 per wave;
+// each wave keeps its rows' Q and dO as MFMA B operands in registers, so
+// the 32x32 accumulators put one query per lane column (lanes l and l^32
+// share query l % 32).  Blocks of kQKeys keys of the KV head are staged in
+// LDS (double-buffered, one barrier per block) and shared by the waves:
+//   S^T = K Q^T,  dP^T = V dO^T            (keys x queries, k = channels)
+//   one online pass: m = running maximum of S sl2 (raised only when a
+//   block exceeds it; dq and the sum rescaled then), p = 2^(S sl2 - m),
+//   dS^T = p (dP^T - D)
+//   dQ^T += K^T dS^T                        (channels x queries, k = keys)
+// and at the end dQ = scale dq / l, LSE = m + log2(l), D = <dO, O> (formed
+// from the same registers before the pass).  K is read both ways (plain
+// rows for the scores, ds_read_b64_tr_b16 for K^T), with the swizzle of
+// KvTile.  kFar = false: rows in token order, only gate=0 rows written
+// (their keys are the window); kFar = true: the gate=1 rows of the head's
+// gate group, gathered from the compacted list (keys [0, i]), heaviest
+// tiles first.
+// ---------------------------------------------------------------------------
+constexpr int kQRows = 128;  // query rows per workgroup (4 waves x 32)
+constexpr int kQKeys = 64;   // keys per LDS block
+
+template <int D, bool kFar>
+__global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_kernel(BwdArgs a) {
+  using L = KvTile<D>;
+  constexpr int KS = D / 16;
+  constexpr int MD = D / 32;
+  constexpr int kMat = kQKeys * L::kRowB;             // one staged K or V block
+  constexpr int kPer = kQKeys * L::kCPR / kBwdThreads;  // chunks per thread and matrix
+  static_assert(kQKeys * L::kCPR % kBwdThreads == 0, "block staging");
+  __shared__ __attribute__((aligned(16))) char lds[2][2 * kMat];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int rl = lane & 31, hf = lane >> 5;
+  const int nbh = a.B * a.Hq;
+  const int ntile = (a.N + kQRows - 1) / kQRows;
+  const int bh = blockIdx.x % nbh;
+  const int b = bh / a.Hq, h = bh % a.Hq, kvh = h / a.HK, g = h / a.HG;
+  const int32_t* list = a.idx + (int64_t(b) * a.G + g) * a.N;
+  int tile = blockIdx.x / nbh;
+  int n = 0;
+  if constexpr (kFar) {
+    n = a.cnt[b * a.G + g];
+    tile = ntile - 1 - tile;  // the last gathered tiles hold the longest rows: first
+    if (tile * kQRows >= n) return;  // workgroup-uniform, before any barrier
+  }
+  // this lane's query row and its visible keys [lo, hi]; act: row written here
+  const int slot = tile * kQRows + wave * 32 + rl;
+  int row, lo, hi;
+  bool act;
+  if constexpr (kFar) {
+    act = slot < n;
+    row = list[act ? slot : n - 1];
+    lo = 0;
+    hi = act ? row : -1;
+  } else {
+    row = min(slot, a.N - 1);
+    act = slot < a.N && a.gate[(int64_t(b) * a.N + row) * a.G + g] == 0;
+    lo = act ? row - a.W + 1 : 1;
+    hi = act ? row : 0;
+  }
+  // key blocks of the workgroup: the union of its rows' ranges
+  int wlo, whi;
+  if constexpr (kFar) {
+    wlo = 0;
+    whi = list[min(n, tile * kQRows + kQRows) - 1];
+  } else {
+    wlo = max(0, tile * kQRows - a.W + 1);
+    whi = min(a.N, tile * kQRows + kQRows) - 1;
+  }
+  const int kb0 = wlo / kQKeys, kb1 = whi / kQKeys;
+  const int vlo = wave_min_i(act ? lo : INT_MAX), vhi = wave_max_i(act ? hi : -1);  // this wave's keys
+  const int64_t qrs = int64_t(a.Hq) * D;
+  const int64_t qoff = (int64_t(b) * a.N + row) * qrs + int64_t(h) * D + 8 * hf;
+  bf16x8 qreg[KS], oreg[KS];
+  float Dv = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qreg[ks] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16_t*>(a.Q) + qoff + 16 * ks);
+    oreg[ks] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16_t*>(a.dO) + qoff + 16 * ks);
+    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(static_cast<const bf16_t*>(a.O) + qoff + 16 * ks);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Dv = fmaf(float(oreg[ks][e]), float(ov[e]), Dv);
+  }
+  Dv += __shfl_xor(Dv, 32);
+  const int64_t krs = int64_t(a.Hkv) * D;
+  const bf16_t* kh = static_cast<const bf16_t*>(a.K) + int64_t(b) * a.N * krs + int64_t(kvh) * D;
+  const bf16_t* vh = static_cast<const bf16_t*>(a.V) + int64_t(b) * a.N * krs + int64_t(kvh) * D;
+  u32x4 sk[kPer], sv[kPer];
+  const auto load_block = [&](int kb) {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int u = tid + p * kBwdThreads, r = u / L::kCPR, c = u % L::kCPR;
+      const int key = min(kb * kQKeys + r, a.N - 1);  // past the end: masked
+      sk[p] = *reinterpret_cast<const u32x4*>(kh + int64_t(key) * krs + 8 * c);
+      sv[p] = *reinterpret_cast<const u32x4*>(vh + int64_t(key) * krs + 8 * c);
+    }
+  };
+  const auto store_block = [&](char* buf) {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int u = tid + p * kBwdThreads, r = u / L::kCPR, c = u % L::kCPR;
+      *reinterpret_cast<u32x4*>(buf + L::pos(r, c)) = sk[p];
+      *reinterpret_cast<u32x4*>(buf + kMat + L::pos(r, c)) = sv[p];
+    }
+  };
+  f32x16 dq[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) dq[md] = f32x16{};
+  float m = kNegInf, l = 0.f;
+  const int tr_r = (lane >> 2) & 3, tr_kq = lane & 3, tr_c16 = (lane >> 4) & 1;
+  load_block(kb0);
+  store_block(lds[0]);
+  __syncthreads();
+  for (int kb = kb0; kb <= kb1; ++kb) {
+    const bool more = kb < kb1;
+    if (more) load_block(kb + 1);
+    const char* kt = lds[(kb - kb0) & 1];
+    const char* vt = kt + kMat;
+    const int key0 = kb * kQKeys;
+    if (key0 + kQKeys - 1 >= vlo && key0 <= vhi) {  // wave-uniform: any of this wave's pairs here
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        s[mt] = dp[mt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kt + L::pos(32 * mt + rl, 2 * ks + hf));
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt + L::pos(32 * mt + rl, 2 * ks + hf));
+          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], s[mt], 0, 0, 0);
+          dp[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, oreg[ks], dp[mt], 0, 0, 0);
+        }
+      }
+      // element i of slice mt: key key0 + 32 mt + 8 (i/4) + 4 hf + i%4
+      float bmax = kNegInf;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + 32 * mt + 8 * (i >> 2) + 4 * hf + (i & 3);
+          const float x = (key >= lo && key <= hi) ? s[mt][i] * a.sl2 : kNegInf;
+          s[mt][i] = x;
+          bmax = fmaxf(bmax, x);
+        }
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      const bool raise = bmax > m;
+      if (__any(raise)) {
+        const float alpha = raise ? fast_exp2(m - bmax) : 1.f;  // 0 while m is -inf
+        l *= alpha;
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) dq[md][i] *= alpha;
+        if (raise) m = bmax;
+      }
+      bf16x8 sb[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float x = s[mt][i];
+          const float p = x == kNegInf ? 0.f : fast_exp2(x - m);
+          l += p;
+          sb[2 * mt + (i >> 3)][i & 7] = bf16_t(p * (dp[mt][i] - Dv));
+        }
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const int c = 4 * md + 2 * tr_c16 + (tr_kq >> 1), cb = (tr_kq & 1) * 8;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const int r0 = 16 * st + 4 * hf + tr_r, r1 = r0 + 8;
+          const s16x4 k0 = lds_tr16(kt + L::pos(r0, c) + cb), k1 = lds_tr16(kt + L::pos(r1, c) + cb);
+          const bf16x8 ak = __builtin_bit_cast(bf16x8, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
+          dq[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sb[st], dq[md], 0, 0, 0);
+        }
+      }
+    }
+    if (more) store_block(lds[(kb + 1 - kb0) & 1]);
+    __syncthreads();
+  }
+  const float lt = l + __shfl_xor(l, 32);
+  if (act) {
+    const float inv = a.scale / lt;
+    bf16_t* dqp = static_cast<bf16_t*>(a.dQ) + (int64_t(b) * a.N + row) * qrs + int64_t(h) * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = bf16_t(dq[md][4 * q + e] * inv);
+        *reinterpret_cast<bf16x4*>(dqp + 32 * md + 8 * q + 4 * hf) = v;
+      }
+    if (hf == 0) {
+      const int64_t sidx = (int64_t(b) * a.Hq + h) * a.N + row;
+      a.lse2[sidx] = m + log2f(lt);
+      a.Drow[sidx] = Dv;
+    }
+  }
+}
+
 size_t backward_workspace(int B, int N, int Hq) { return size_t(2) * B * Hq * N * sizeof(float); }
 
 template <typename T, int D>
@@ -544,18 +745,23 @@ static hipError_t run_backward(BwdArgs& a, hipStream_t s) {
   const int64_t cols = int64_t(a.B) * a.N * a.Hkv;
   const int per_wg = (kBwdThreads / kWave) * kGroups;  // items per workgroup
   const int64_t g1 = (rows + per_wg - 1) / per_wg, g2 = (cols + per_wg - 1) / per_wg;
-  hipLaunchKernelGGL((bwd_row_kernel<T, D, false>), dim3(unsigned(g1 < 65536 ? g1 : 65536)),
-                     dim3(kBwdThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_row_kernel<T, D, true>), dim3(unsigned(g1 < 65536 ? g1 : 65536)),
-                     dim3(kBwdThreads), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e;
   if constexpr (std::is_same<T, bf16_t>::value) {
+    const int64_t nq = (int64_t(a.N) + kQRows - 1) / kQRows * a.B * a.Hq;
+    hipLaunchKernelGGL((bwd_q_mfma_kernel<D, false>), dim3(unsigned(nq)), dim3(kBwdThreads), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_q_mfma_kernel<D, true>), dim3(unsigned(nq)), dim3(kBwdThreads), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nkb = (int64_t(a.N) + kKvKeys - 1) / kKvKeys;
     hipLaunchKernelGGL((bwd_kv_mfma_kernel<D>), dim3(unsigned(nkb * a.B * a.Hkv)), dim3(kBwdThreads), 0, s,
                        a);
   } else {
+    hipLaunchKernelGGL((bwd_row_kernel<T, D, false>), dim3(unsigned(g1 < 65536 ? g1 : 65536)),
+                       dim3(kBwdThreads), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_row_kernel<T, D, true>), dim3(unsigned(g1 < 65536 ? g1 : 65536)),
+                       dim3(kBwdThreads), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_col_kernel<T, D>), dim3(unsigned(g2 < 65536 ? g2 : 65536)), dim3(kBwdThreads), 0,
                        s, a);
   }

@@ -63,12 +63,24 @@ def test_prefill_backward(B, N, Hq, Hkv, G, d, W, p, dtype):
     dQ, dK, dV = swa().prefill_backward(Qg, Kg, Vg, O, dOg, gg, W)
     torch.cuda.synchronize()
     ref = oracle.prefill_backward(Q, K, V, gate, W, dO)
+    # Where the exact gradient is zero (W = 1: each row attends to itself
+    # alone, P = 1 and dP - D = <dO, v_i> - <dO, O_i> = 0), the computed one
+    # is the float32 rounding of that difference: two d-term dot products,
+    # each off by at most d 2^-24 sum |dO v|, times scale |q| (or |k|) and
+    # summed over the query heads of a KV head for dK.
+    HK = Hq // Hkv
+    Vq = np.repeat(np.asarray(V, np.float64), HK, axis=2)
+    dov = float((np.abs(np.asarray(dO, np.float64)) * np.abs(Vq)).sum(axis=3).max())
+    qk = max(float(np.abs(Q).max()), float(np.abs(K).max()))
+    zero_bound = 2 * d * 2.0 ** -24 * dov * d ** -0.5 * qk * HK
     for name, got in (("dQ", dQ), ("dK", dK), ("dV", dV)):
         r = ref[name]
         err = max_abs(host(got), r)
         bound = REL[dtype] * max(float(np.abs(r).max()), 1e-30)
+        if np.abs(r).max() < 1e-12:
+            bound = zero_bound
         say(f"  {name} max-abs {err:.3e} (bound {bound:.3e})")
-        assert err <= bound or (np.abs(r).max() < 1e-12 and err < 1e-6)
+        assert err <= bound
 
 
 def test_prefill_backward_32k_layer():
