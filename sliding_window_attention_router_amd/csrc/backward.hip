@@ -368,6 +368,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(BwdArgs a) {
   constexpr int KS = D / 16;  // k-steps of the channel contractions
   constexpr int MD = D / 32;  // 32-channel tiles of dK^T, dV^T
   __shared__ __attribute__((aligned(16))) char lds[2][L::kBytes];
+  __shared__ int rowbuf[2][kRT];  // query row of each slot of the next tiles (-1: padding)
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int rl = lane & 31, hf = lane >> 5;
   const int nbk = a.B * a.Hkv;
@@ -407,66 +408,85 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(BwdArgs a) {
     const float* lrow = a.lse2 + (int64_t(b) * a.Hq + h) * a.N;
     const float* drow = a.Drow + (int64_t(b) * a.Hq + h) * a.N;
     const uint8_t* grow = a.gate + int64_t(b) * a.N * a.G + g;
-    // query row of tile t, slot m (-1: padding)
-    const auto row_of = [&](int t, int m) -> int {
-      if (t < nwt) {
-        const int r = k0 + t * kRT + m;
-        return r < wend ? r : -1;
-      }
-      const int p = f0 + (t - nwt) * kRT + m;
-      return p < n ? list[p] : -1;
+    // Row indices run one tile ahead of the row loads: the gathered rows of
+    // tile t + 2 are looked up in the list while tile t is computed and kept
+    // in LDS (rowbuf), so the loads of a tile never wait on a list lookup.
+    // Every load is unconditional (clamped to a valid row) and consumed in
+    // the iteration that issues it; padding slots are zeroed when the tile
+    // is written to LDS.
+    // (branch-free: the list is read for window tiles too, at a clamped
+    // index, so the looked-up value is never merged with another one while
+    // its load is in flight)
+    int fw = 0, fl = 0;
+    bool fok = false, fwin = true;
+    const auto fetch_row = [&](int t) {  // slot tid % kRT of tile t
+      const int m = tid % kRT;
+      const int q = f0 + (t - nwt) * kRT + m;
+      fl = list[min(max(q, 0), max(n - 1, 0))];
+      fw = k0 + t * kRT + m;
+      fwin = t < nwt;
+      fok = fwin ? fw < wend : q < n;
+    };
+    const auto put_row = [&](int* rb) {
+      if (tid < kRT) rb[tid] = fok ? (fwin ? fw : fl) : -1;
     };
     u32x4 sq[L::kPer], sd[L::kPer];
+    bool sok[L::kPer + 1];
     float s_l = 0.f, s_d = 0.f;
-    int s_lo = 0, s_hi = -1;
-    const auto load_tile = [&](int t) {
+    int s_row = 0;
+    uint8_t s_g = 0;
+    const auto load_tile = [&](const int* rb) {
 #pragma unroll
       for (int p = 0; p < L::kPer; ++p) {
         const int u = tid + p * kBwdThreads, m = u / L::kCPR, c = u % L::kCPR;
-        const int r = row_of(t, m);
-        if (r >= 0) {
-          sq[p] = *reinterpret_cast<const u32x4*>(qh + int64_t(r) * qrs + 8 * c);
-          sd[p] = *reinterpret_cast<const u32x4*>(dh + int64_t(r) * qrs + 8 * c);
-        } else {
-          sq[p] = sd[p] = u32x4{0u, 0u, 0u, 0u};
-        }
+        const int r = rb[m];
+        sok[p] = r >= 0;
+        const int rc = r >= 0 ? r : 0;
+        sq[p] = *reinterpret_cast<const u32x4*>(qh + int64_t(rc) * qrs + 8 * c);
+        sd[p] = *reinterpret_cast<const u32x4*>(dh + int64_t(rc) * qrs + 8 * c);
       }
-      if (tid < kRT) {
-        const int r = row_of(t, tid);
-        if (r >= 0) {
-          s_l = lrow[r];
-          s_d = drow[r];
-          s_hi = r;
-          s_lo = grow[int64_t(r) * a.G] != 0 ? 0 : r - a.W + 1;
-        } else {
-          s_l = __builtin_huge_valf();
-          s_d = 0.f;
-          s_lo = 0;
-          s_hi = -1;
-        }
-      }
+      const int r = rb[tid % kRT];
+      sok[L::kPer] = r >= 0;
+      s_row = r >= 0 ? r : 0;
+      s_l = lrow[s_row];
+      s_d = drow[s_row];
+      s_g = grow[int64_t(s_row) * a.G];
     };
     const auto store_tile = [&](char* buf) {
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int p = 0; p < L::kPer; ++p) {
         const int u = tid + p * kBwdThreads, m = u / L::kCPR, c = u % L::kCPR;
-        *reinterpret_cast<u32x4*>(buf + L::pos(m, c)) = sq[p];
-        *reinterpret_cast<u32x4*>(buf + L::kMat + L::pos(m, c)) = sd[p];
+        *reinterpret_cast<u32x4*>(buf + L::pos(m, c)) = sok[p] ? sq[p] : z;
+        *reinterpret_cast<u32x4*>(buf + L::kMat + L::pos(m, c)) = sok[p] ? sd[p] : z;
       }
       if (tid < kRT) {
+        const bool ok = sok[L::kPer];
         float* info = reinterpret_cast<float*>(buf + L::kInfo);
-        info[tid] = s_l;
-        info[kRT + tid] = s_d;
-        reinterpret_cast<int*>(info)[2 * kRT + tid] = s_lo;
-        reinterpret_cast<int*>(info)[3 * kRT + tid] = s_hi;
+        info[tid] = ok ? s_l : __builtin_huge_valf();
+        info[kRT + tid] = ok ? s_d : 0.f;
+        reinterpret_cast<int*>(info)[2 * kRT + tid] = ok ? (s_g != 0 ? 0 : s_row - a.W + 1) : 0;
+        reinterpret_cast<int*>(info)[3 * kRT + tid] = ok ? s_row : -1;
       }
     };
-    load_tile(0);
+    // rows of tiles 0 and 1, then tile 0 itself
+    fetch_row(0);
+    put_row(rowbuf[0]);
+    if (nt > 1) {
+      fetch_row(1);
+      put_row(rowbuf[1]);
+    }
+    __syncthreads();
+    load_tile(rowbuf[0]);
     store_tile(lds[0]);
     __syncthreads();
+    // iteration t: tile t is in LDS buffer t % 2 and the rows of tile t + 1
+    // in rowbuf[(t + 1) % 2]; the rows of tile t + 2 are looked up and tile
+    // t + 1 is loaded while tile t is computed; one barrier per tile
     for (int t = 0; t < nt; ++t) {
       const bool more = t + 1 < nt;
-      if (more) load_tile(t + 1);
+      if (t + 2 < nt) fetch_row(t + 2);
+      if (more) load_tile(rowbuf[(t + 1) & 1]);
       const char* qt = lds[t & 1];
       const char* dt = qt + L::kMat;
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -512,6 +532,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(BwdArgs a) {
         }
       }
       if (more) store_tile(lds[(t + 1) & 1]);
+      if (t + 2 < nt) put_row(rowbuf[t & 1]);
       __syncthreads();
     }
   }
