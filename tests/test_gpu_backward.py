@@ -49,6 +49,10 @@ CASES = [
     (1, 120, 4, 1, 1, 64, 1, 0.0, "bf16"),       # W = 1: dQ = dK = 0
     (1, 200, 4, 2, 2, 64, 30, 1.0, "bf16"),      # gate all ones
     (1, 220, 4, 2, 1, 128, 40, 0.3, "f32"),      # float32
+    # several gathered tiles per head for dQ (about 460 routed rows) and many
+    # window and gathered tiles per key block for dK, dV; ragged N
+    (1, 1531, 8, 2, 2, 128, 200, 0.3, "bf16"),
+    (2, 777, 4, 4, 1, 64, 97, 0.5, "bf16"),
 ]
 
 
