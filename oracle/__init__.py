@@ -13,6 +13,7 @@ from .swiattn_ref import (  # noqa: F401
     full_key_range,
     prefill,
     prefill_backward,
+    prefill_backward_keys,
     prefill_backward_rows,
     regularizer,
     route,

@@ -46,6 +46,7 @@ __all__ = [
     "router_backward",
     "prefill_backward",
     "prefill_backward_rows",
+    "prefill_backward_keys",
 ]
 
 NEAR_THRESHOLD = 1e-5
@@ -478,6 +479,72 @@ def prefill_backward_rows(Q, K, V, gate, W, dO, rows, scale=None):
                 ds = p * (dp - go @ (p @ v))
                 dQ[b, r, h] = scale * (ds @ k)
     return dQ
+
+
+def prefill_backward_keys(Q, K, V, gate, W, dO, keys, kv_heads=None, scale=None):
+    """dK, dV of prefill_backward for the given key positions only:
+    dK_j = scale * sum_i dS_ij q_i and dV_j = sum_i P_ij dO_i over the rows i
+    that see key j (i >= j, and i - j < W or gate 1), summed over the query
+    heads of the KV head.  P_ij and D_i = <dO_i, O_i> need row i's whole key
+    set; those row quantities are formed for blocks of rows with one masked
+    matrix product each (a library matmul; each row masked to its own key
+    set) and reused across keys.
+
+    -> dict dK, dV [B,R,len(kv_heads),d] float64 (kv_heads: the KV heads to
+    evaluate, all by default)."""
+    Q = np.asarray(Q)
+    K = np.asarray(K)
+    V = np.asarray(V)
+    dO = np.asarray(dO)
+    gate = np.asarray(gate)
+    B, N, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    G = gate.shape[2]
+    hk, hg = _head_maps(Hq, Hkv, G)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    keys = np.asarray(keys, np.int64)
+    kv_heads = list(range(Hkv)) if kv_heads is None else list(kv_heads)
+    dK = np.zeros((B, keys.size, len(kv_heads), d))
+    dV = np.zeros((B, keys.size, len(kv_heads), d))
+    for b in range(B):
+        for c, kv in enumerate(kv_heads):
+            Kf = np.asarray(K[b, :, kv], np.float64)
+            Vf = np.asarray(V[b, :, kv], np.float64)
+            for h in range(kv * hk, (kv + 1) * hk):
+                g = h // hg
+                Qh = np.asarray(Q[b, :, h], np.float64)
+                dOh = np.asarray(dO[b, :, h], np.float64)
+                # the rows that see each key
+                sees = []
+                for j in keys:
+                    i = np.arange(int(j), N)
+                    sees.append(i[(i - j < W) | (gate[b, i, g] != 0)])
+                need = np.unique(np.concatenate(sees))
+                # log-normaliser and D of every needed row, over its own key set
+                lse = np.zeros(N)
+                Drow = np.zeros(N)
+                for i0 in range(0, need.size, 256):
+                    rows = need[i0:i0 + 256]
+                    lo = np.array([(full_key_range(int(i)) if gate[b, i, g] else swa_key_range(int(i), W))[0]
+                                   for i in rows])
+                    a, e = int(lo.min()), int(rows.max()) + 1
+                    S = scale * (Qh[rows] @ Kf[a:e].T)
+                    cols = np.arange(a, e)
+                    S[(cols[None, :] < lo[:, None]) | (cols[None, :] > rows[:, None])] = -np.inf
+                    mx = S.max(axis=1, keepdims=True)
+                    Pn = np.exp(S - mx)
+                    tot = Pn.sum(axis=1, keepdims=True)
+                    lse[rows] = (mx + np.log(tot))[:, 0]
+                    O = (Pn / tot) @ Vf[a:e]
+                    Drow[rows] = (dOh[rows] * O).sum(axis=1)
+                for r, j in enumerate(keys):
+                    i = sees[r]
+                    p = np.exp(scale * (Qh[i] @ Kf[j]) - lse[i])
+                    ds = p * (dOh[i] @ Vf[j] - Drow[i])
+                    dK[b, r, c] += scale * (ds @ Qh[i])
+                    dV[b, r, c] += p @ dOh[i]
+    return {"dK": dK, "dV": dV}
 
 
 def prefill_backward(Q, K, V, gate, W, dO, scale=None):

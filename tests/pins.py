@@ -581,6 +581,23 @@ def check_prefill_backward_rows_matches_full():
                                rtol=1e-12, atol=1e-13)
 
 
+def check_prefill_backward_keys_matches_full():
+    """The per-key dK, dV evaluation equals the rows of the full backward
+    (keys at both ends and at the window edge; one KV head alone too)."""
+    rng = np.random.default_rng(85)
+    B, N, Hq, Hkv, d, W = 2, 40, 4, 2, 6, 7
+    Q, K, V = (rng.standard_normal(s) for s in ((B, N, Hq, d), (B, N, Hkv, d), (B, N, Hkv, d)))
+    dO = rng.standard_normal((B, N, Hq, d))
+    gate = (rng.random((B, N, 2)) < 0.4).astype(np.uint8)
+    full = ref.prefill_backward(Q, K, V, gate, W, dO)
+    keys = np.array([0, 1, 6, 7, 20, 33, 39])
+    got = ref.prefill_backward_keys(Q, K, V, gate, W, dO, keys)
+    for k in ("dK", "dV"):
+        np.testing.assert_allclose(got[k], full[k][:, keys], rtol=1e-12, atol=1e-13)
+    one = ref.prefill_backward_keys(Q, K, V, gate, W, dO, keys, kv_heads=[1])
+    np.testing.assert_allclose(one["dK"][:, :, 0], full["dK"][:, keys, 1], rtol=1e-12, atol=1e-13)
+
+
 ALL_PINS = [
     check_w4_key_ranges,
     check_w4_attention_weights,
@@ -609,4 +626,5 @@ ALL_PINS = [
     check_prefill_backward_against_autograd,
     check_prefill_backward_special_cases,
     check_prefill_backward_rows_matches_full,
+    check_prefill_backward_keys_matches_full,
 ]
