@@ -91,7 +91,7 @@ def test_prefill_backward_32k_layer():
     """N=32768, GQA 16/4, d=128, W=1024, gate Bernoulli(0.13): two runs
     bitwise equal; per KV head the dK rows sum to 0 and the dV rows sum to
     the dO rows of its query heads (softmax rows sum to one); sampled dQ
-    rows against the reference."""
+    rows and sampled dK, dV keys against the reference."""
     say("backward N=32768 GQA 16/4 W=1024 gate Bernoulli(0.13)")
     W = 1024
     w = synth.long_prefill(seed=3)
@@ -125,3 +125,14 @@ def test_prefill_backward_32k_layer():
     bound = REL["bf16"] * float(np.abs(ref).max())
     say(f"  {rows.size} sampled dQ rows x 16 heads: max-abs {err:.3e} (bound {bound:.3e})")
     assert err <= bound
+    # sampled keys of KV head 1: the first key block (every gate=1 row of
+    # the sequence sees key 70), the middle, the window edge and the end
+    N = w.Q.shape[1]
+    keys = np.array([70, N // 2, N - 1500, N - W - 40, N - W + 5, N - 1])
+    refk = oracle.prefill_backward_keys(w.Q, w.K, w.V, w.gate, W, dO, keys, kv_heads=[1])
+    for name, got in (("dK", dK), ("dV", dV)):
+        r = refk[name][:, :, 0]
+        err = max_abs(got[:, keys, 1], r)
+        bound = REL["bf16"] * float(np.abs(r).max())
+        say(f"  {keys.size} sampled {name} keys of KV head 1: max-abs {err:.3e} (bound {bound:.3e})")
+        assert err <= bound
