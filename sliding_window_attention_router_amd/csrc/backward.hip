@@ -10,25 +10,31 @@
 //   dV_j = sum_i P_ij dO_i   (K, V gradients summed over the query heads of
 //   a KV head).
 //
+// bfloat16, on the matrix cores (three launches):
+//   bwd_q_mfma_kernel   a workgroup per 128 query rows of a head: one online
+//                       pass over 64-key blocks gives dQ, LSE and D (the
+//                       latter two go to the workspace); launched for the
+//                       gate=0 rows in token order and for the gate=1 rows
+//                       gathered from the compacted list
+//   bwd_kv_mfma_kernel  a workgroup per 128 keys of a KV head walks 32-row
+//                       tiles of the rows that see them (window rows of every
+//                       gate, then gathered gate=1 rows) for each query head
+//                       and accumulates dK, dV
+// float32, on the vector ALU (three launches):
 //   bwd_row_kernel  one 16-lane group per (token, query head): one online
-//                   pass over S_i accumulates dQ_i and LSE_i (running
-//                   maximum, rescaled sums); LSE_i and D_i go to the
-//                   workspace for the column pass.  Two launches: the
-//                   gate=0 rows in token order, the gate=1 rows gathered
-//                   (neighbouring routed tokens share their keys)
-//   bwd_kv_mfma_kernel  (bfloat16) dK, dV on the matrix cores: a
-//                   workgroup per 128 keys of a KV head walks 32-row tiles
-//                   of the rows that see them (window rows of every gate,
-//                   then gathered gate=1 rows) for each query head
-//   bwd_col_kernel  (float32) one 16-lane group per (key j, KV head), keys
-//                   fastest: walks the rows that see key j (the window rows
-//                   j .. j+W-1 of every gate, then the gate=1 rows past the
+//                   pass over S_i gives dQ_i, LSE_i and D_i; launched for
+//                   the gate=0 rows in token order and for the gate=1 rows
+//                   gathered (neighbouring routed tokens share their keys)
+//   bwd_col_kernel  one 16-lane group per (key j, KV head), keys fastest:
+//                   walks the rows that see key j (the window rows j ..
+//                   j+W-1 of every gate, then the gate=1 rows past the
 //                   window from the compacted list) for each query head of
 //                   the KV head and accumulates dK_j, dV_j
 // In the vector-ALU kernels a wave holds four groups of 16 lanes (one row
 // or key each, d/16 channels per lane); a dot product is a lane product
-// plus the 16-lane DPP row sum, four keys (or rows) at a time.  Every sum
-// has a fixed order (bitwise reproducible).
+// plus the 16-lane DPP row sum, four keys (or rows) at a time.  In every
+// kernel each sum has a fixed order and no atomics are used, so two runs
+// give the same bits.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
