@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_col_kernel(BwdArgs a) {
 // reads (32 lanes, 4 rows x 4 chunks) hit distinct banks.
 // ---------------------------------------------------------------------------
 constexpr int kKvKeys = 128;  // keys per workgroup (4 waves x 32)
-constexpr int kRT = 32;       // query rows per tile
+constexpr int kRT = 64;       // query rows per tile (a multiple of 32)
 
 template <int D>
 struct KvTile {
@@ -495,39 +495,47 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(BwdArgs a) {
       if (more) load_tile(rowbuf[(t + 1) & 1]);
       const char* qt = lds[t & 1];
       const char* dt = qt + L::kMat;
-      f32x16 s = f32x16{}, dp = f32x16{};
+      constexpr int RH = kRT / 32;  // 32-row halves of the tile
+      f32x16 s[RH], dp[RH];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + L::pos(rl, 2 * ks + hf));
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dt + L::pos(rl, 2 * ks + hf));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[ks], dp, 0, 0, 0);
-      }
-      // P and dS for rows 8q + 4hf + e (slot 4q + e)
-      const float* info = reinterpret_cast<const float*>(qt + L::kInfo);
-      bf16x8 pb[2], sb[2];
+      for (int rh = 0; rh < RH; ++rh) {
+        s[rh] = dp[rh] = f32x16{};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m0 = 8 * q + 4 * hf;
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(info + m0);
-        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(info + kRT + m0);
-        typedef int i32x4 __attribute__((ext_vector_type(4)));
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(info + 2 * kRT + m0);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(info + 3 * kRT + m0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * q + e;
-          const bool vis = j >= lo[e] && j <= hi[e];
-          const float p = vis ? fast_exp2(s[i] * a.sl2 - lv[e]) : 0.f;
-          pb[i >> 3][i & 7] = bf16_t(p);
-          sb[i >> 3][i & 7] = bf16_t(p * (dp[i] - dv4[e]));
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + L::pos(32 * rh + rl, 2 * ks + hf));
+          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dt + L::pos(32 * rh + rl, 2 * ks + hf));
+          s[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s[rh], 0, 0, 0);
+          dp[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[ks], dp[rh], 0, 0, 0);
         }
       }
+      // P and dS for rows 32rh + 8q + 4hf + e (slot 4q + e of half rh); the
+      // 16-row k-step st = 2rh + (slot / 8) of the second products
+      const float* info = reinterpret_cast<const float*>(qt + L::kInfo);
+      bf16x8 pb[2 * RH], sb[2 * RH];
+#pragma unroll
+      for (int rh = 0; rh < RH; ++rh)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m0 = 32 * rh + 8 * q + 4 * hf;
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(info + m0);
+          const f32x4 dv4 = *reinterpret_cast<const f32x4*>(info + kRT + m0);
+          typedef int i32x4 __attribute__((ext_vector_type(4)));
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(info + 2 * kRT + m0);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(info + 3 * kRT + m0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q + e;
+            const bool vis = j >= lo[e] && j <= hi[e];
+            const float p = vis ? fast_exp2(s[rh][i] * a.sl2 - lv[e]) : 0.f;
+            pb[2 * rh + (i >> 3)][i & 7] = bf16_t(p);
+            sb[2 * rh + (i >> 3)][i & 7] = bf16_t(p * (dp[rh][i] - dv4[e]));
+          }
+        }
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
         const int c = 4 * md + 2 * tr_c16 + (tr_kq >> 1), cb = (tr_kq & 1) * 8;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
+        for (int st = 0; st < 2 * RH; ++st) {
           const int r0 = 16 * st + 4 * hf + tr_r, r1 = r0 + 8;
           const s16x4 d0 = lds_tr16(dt + L::pos(r0, c) + cb), d1 = lds_tr16(dt + L::pos(r1, c) + cb);
           const s16x4 q0 = lds_tr16(qt + L::pos(r0, c) + cb), q1 = lds_tr16(qt + L::pos(r1, c) + cb);
