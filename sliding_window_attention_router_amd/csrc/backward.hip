@@ -16,7 +16,7 @@
 //                       latter two go to the workspace); launched for the
 //                       gate=0 rows in token order and for the gate=1 rows
 //                       gathered from the compacted list
-//   bwd_kv_mfma_kernel  a workgroup per 128 keys of a KV head walks 32-row
+//   bwd_kv_mfma_kernel  a workgroup per 128 keys of a KV head walks 64-row
 //                       tiles of the rows that see them (window rows of every
 //                       gate, then gathered gate=1 rows) for each query head
 //                       and accumulates dK, dV
@@ -325,12 +325,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_col_kernel(BwdArgs a) {
 // dK, dV on the matrix cores (bfloat16).  A workgroup owns kKvKeys keys of
 // one KV head, 32 per wave; each wave keeps its keys' K and V rows in
 // registers as MFMA B operands.  For every query head of the KV head the
-// workgroup walks tiles of 32 query rows: first the window rows
+// workgroup walks tiles of kRT query rows: first the window rows
 // [k0, min(N, k0 + kKvKeys - 1 + W)) (any gate; masked per pair), then the
 // gate=1 rows past them, gathered from the compacted list.  The four waves
 // share each tile: Q and dO rows are staged once in LDS (double-buffered,
 // one barrier per tile) with each row's LSE, D and visible key range.
-//   S  = Q K^T,  dP = dO V^T         (32 rows x 32 keys, k = channels)
+//   S  = Q K^T,  dP = dO V^T         (per 32-row half: 32 rows x 32 keys,
+//                                      k = channels)
 //   P  = 2^(S sl2 - LSE) on visible pairs,  dS = P (dP - D)
 //   dV^T += dO^T P,  dK^T += Q^T dS  (channels x 32 keys, k = rows)
 // The 32x32 accumulator of S gives lane l the key l % 32 and rows
