@@ -157,7 +157,10 @@ int swiattn_prefill(const void* Q, const void* K, const void* V, const uint8_t* 
 /*
  * swiattn_decode_workspace_size - bytes of device workspace for
  * swiattn_decode (upper bound over every gate and cache length).
- * Returns 0 if the arguments are invalid.
+ * G is the number of gate groups of the call; it does not change the size
+ * but is validated with the other head arguments (Hq % G, group nesting),
+ * so a size query succeeds exactly when the matching decode call's shapes
+ * are accepted.  Returns 0 if the arguments are invalid.
  */
 size_t swiattn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int G, int d, int W,
                                      swiattn_dtype_t dtype);
@@ -348,9 +351,17 @@ int swiattn_router_backward(const void* dO, const void* O_full, const void* O_sw
  *   swiattn_prefill_backward_workspace_size(B, N, Hq) bytes (each row's
  *   log-sum-exp and <dO, O>), clobbered.
  * Only the attention path: the gate's gradient is swiattn_router_backward's.
- * float32 arithmetic in a fixed order (bitwise reproducible); vector-ALU
- * kernels, 16 lanes per (row, query head) for dQ and per (key, KV head)
- * for dK and dV.  Outputs must not overlap inputs.
+ * Arithmetic, in a fixed order (bitwise reproducible):
+ *   bf16:    every product on the matrix cores (bf16 operands, float32
+ *            accumulation).  Scores, softmax and D = <dO, O> are float32;
+ *            the probabilities P and dS = P (dP - D) are rounded to bf16
+ *            where they become operands of the dV, dQ and dK products.
+ *            One launch for dQ of the gate=0 rows, one for the gathered
+ *            gate=1 rows (both also write LSE and D to the workspace), one
+ *            for dK and dV per 128 keys of a KV head.
+ *   float32: float32 throughout on the vector ALUs, 16 lanes per (row,
+ *            query head) for dQ and per (key, KV head) for dK and dV.
+ * Outputs must not overlap inputs.
  * Errors: as swiattn_prefill (INVALID_ARG, UNSUPPORTED, WORKSPACE).
  */
 size_t swiattn_prefill_backward_workspace_size(int B, int N, int Hq);

@@ -454,8 +454,9 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
 // Far part of the full branch for gathered rows: keys [A, i-W] (the full set
 // minus the window and its anchors).  One workgroup per work item (tile,
 // chunk); grid = upper bound, idle workgroups exit at once.
-// A tile with a single chunk merges with the window result in place; the
-// chunks of longer tiles write normalised partials for merge_kernel.
+// Every item, also the only chunk of a tile, writes its normalised partial
+// output and log-sum-exp; merge_kernel combines them with the window
+// result.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 SWI_DEV void far_item(const PrefillArgs& a, char* buf0, char* buf1, int item) {

@@ -45,6 +45,34 @@ def sample_rows(gate, seed, n_routed=96, n_window=96):
     return np.array(sorted(r for r in rows if 0 <= r < N))
 
 
+def stratified_rows(gate, seed, n_each=1024, max_edges=512, tokens_per_far_tile=32):
+    """Stratified sample of one gate group's rows:
+      - every row i < W + 128 (rows whose window is still filling, the first
+        rows that have far keys, and the tiles around the window edge);
+      - both sides of every run boundary of the gate (of max_edges random
+        ones when there are more);
+      - the first and last row of every far tile: compacted gate=1 positions
+        k with k % tokens_per_far_tile in {0, tokens_per_far_tile - 1};
+      - n_each random gate=1 rows and n_each random gate=0 rows;
+      - the last 64 rows."""
+    N = gate.shape[1]
+    g = gate[0, :, 0]
+    rng = np.random.default_rng(seed)
+    rows = set(range(0, min(N, W + 128))) | set(range(max(0, N - 64), N))
+    edges = np.flatnonzero(np.diff(g.astype(np.int8)) != 0)
+    if edges.size > max_edges:
+        edges = rng.choice(edges, max_edges, replace=False)
+    rows |= set(edges.tolist()) | set((edges + 1).tolist())
+    routed = np.flatnonzero(g)
+    plain = np.flatnonzero(g == 0)
+    k = np.arange(routed.size)
+    rows |= set(routed[(k % tokens_per_far_tile == 0) | (k % tokens_per_far_tile == tokens_per_far_tile - 1)].tolist())
+    for pool in (routed, plain):
+        if pool.size:
+            rows |= set(rng.choice(pool, min(n_each, pool.size), replace=False).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
 def f64(*arrays):
     return [np.asarray(a, np.float64) for a in arrays]
 
@@ -61,7 +89,7 @@ def test_long_prefill_32k(mode):
     assert torch.equal(O, O2), "two runs differ"
     Oh = host(O)
     assert np.all(np.abs(Oh) <= np.abs(w.V).max() + 1e-2)  # softmax averages never leave the V range
-    rows = sample_rows(w.gate, 30)
+    rows = stratified_rows(w.gate, 30)
     Qd, Kd, Vd = f64(w.Q, w.K, w.V)
     ref = oracle.prefill(Qd, Kd, Vd, w.gate, W, rows=rows)["O"]
     err = max_abs(Oh[:, rows], ref)
@@ -124,7 +152,7 @@ def test_structured_both_branch_32k(p):
     O, diff = swa().prefill(Q, K, V, G, W, both_branch=True)
     Oh, _ = swa().prefill(Q, K, V, G, W)
     torch.cuda.synchronize()
-    rows = sample_rows(w.gate, 32, 48, 48)
+    rows = stratified_rows(w.gate, 32, tokens_per_far_tile=128)
     Qd, Kd, Vd = f64(w.Q, w.K, w.V)
     ref = oracle.prefill(Qd, Kd, Vd, w.gate, W, both_branch=True, rows=rows)
     err = max_abs(host(O)[:, rows], ref["O"])
