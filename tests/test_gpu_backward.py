@@ -96,15 +96,15 @@ def zero_gradient_bounds(Q, K, V, dO, scale):
                      e = 0 .. 7), then the two halves are added;
       dP (products)  the matrix core adds 16 exact bf16 products per k-step
                      into a float32 accumulator, d/16 k-steps.
-    First-order rounding analysis: each rounded addition errs by at most
-    u = 2^-24 of its result, so |fl(D) - D| <= u (sum of |partial sums| of the
-    chain, both halves, plus |D|), and a k-step errs by at most u (|new
-    accumulator| + sum of |its 16 products|), which covers any internal
-    order of the 16-term sum with one rounding.  Their sum bounds
-    |dP - D|; dS is rounded to bf16 (factor 1 + 2^-8), dQ_i = scale dS_i k_i
-    and dK_i = scale sum_h dS_ih q_ih (one term per head), each rounded to
-    the output type (1 + 2^-8).  A factor 2 covers second-order terms and
-    an extra rounding inside the matrix core."""
+    First-order rounding analysis (terms of order u^2 are dropped): each
+    rounded addition errs by at most u = 2^-24 of its result, so
+    |fl(D) - D| <= u (sum of |partial sums| of the chain, both halves, plus
+    |D|), and a k-step errs by at most u (|new accumulator| + sum of |its 16
+    products|): one rounding of the step's 16-term sum of exact products and
+    one of its addition to the accumulator.  Their sum bounds |dP - D|; dS
+    is rounded to bf16 (factor 1 + 2^-8), dQ_i = scale dS_i k_i and
+    dK_i = scale sum_h dS_ih q_ih (one term per head), each rounded to the
+    output type (1 + 2^-8)."""
     Q, K, V, dO = (np.asarray(x, np.float64) for x in (Q, K, V, dO))
     B, N, Hq, d = Q.shape
     HK = Hq // K.shape[2]
@@ -118,7 +118,7 @@ def zero_gradient_bounds(Q, K, V, dO, scale):
     steps = t.reshape(B, N, Hq, d // 16, 16)
     acc = np.cumsum(steps.sum(axis=4), axis=3)
     sP = np.abs(acc).sum(axis=3) + np.abs(t).sum(axis=3)
-    ds = 2.0 * u * (sD + sP) * (1 + 2.0 ** -8)  # [B,N,Hq]
+    ds = u * (sD + sP) * (1 + 2.0 ** -8)  # [B,N,Hq]
     out = 1 + 2.0 ** -8
     dQ = scale * ds[..., None] * np.abs(np.repeat(K, HK, axis=2)) * out
     dK = (scale * ds[..., None] * np.abs(Q)).reshape(B, N, K.shape[2], HK, d).sum(axis=3) * out
