@@ -56,7 +56,9 @@ enum {
   SWIATTN_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad scale      */
   SWIATTN_ERR_UNSUPPORTED = -2, /* d not 64/128, group sizes not nested   */
   SWIATTN_ERR_WORKSPACE = -3,   /* workspace null or smaller than needed  */
-  SWIATTN_ERR_HIP = -4          /* a HIP launch or runtime call failed    */
+  SWIATTN_ERR_HIP = -4,         /* a HIP launch or runtime call failed    */
+  SWIATTN_ERR_TOO_LARGE = -5    /* sizes exceed the fixed scratch of
+                                   swiattn_decode_noalloc                 */
 };
 
 /* Both-branch mode for swiattn_prefill: compute both branches for every
@@ -187,6 +189,35 @@ int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t*
                    const uint8_t* gate, void* o, int B, int Lmax, int Hq, int Hkv, int G,
                    int d, int W, float scale, swiattn_dtype_t dtype, void* ws,
                    size_t ws_bytes, swiattn_stream_t stream);
+
+/*
+ * swiattn_decode_noalloc - swiattn_decode without a workspace argument and
+ * without any device allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).
+ *
+ *   Arguments, outputs, arithmetic and errors are those of swiattn_decode;
+ *   the split-K workspace lives instead in a fixed scratch array that the
+ *   library holds in device memory, one copy per GPU, for the life of the
+ *   process: swiattn_decode_noalloc_scratch_bytes() bytes (16 MiB).  Sizes
+ *   whose decode workspace (swiattn_decode_workspace_size) exceeds it are
+ *   rejected with SWIATTN_ERR_TOO_LARGE before anything is enqueued.  At
+ *   Hq/Hkv = 4 and d = 128 the partials take 4 MiB whatever the cache
+ *   length, and up to 1.5 million (sequence, KV head) pairs fit.
+ *   Every call on one GPU uses that GPU's scratch: calls that overlap in
+ *   time on one GPU (other streams, other threads) race and must be
+ *   serialised by the caller.  Nothing in the scratch needs to start at
+ *   zero; a call overwrites what it reads.  The scratch's device address
+ *   is looked up on the first call on each device (hipGetSymbolAddress
+ *   with that device current); the call allocates nothing.
+ */
+int swiattn_decode_noalloc(const void* q, const void* Kc, const void* Vc, const int32_t* cache_len,
+                           const uint8_t* gate, void* o, int B, int Lmax, int Hq, int Hkv, int G,
+                           int d, int W, float scale, swiattn_dtype_t dtype,
+                           swiattn_stream_t stream);
+
+/* Bytes of the fixed scratch used by swiattn_decode_noalloc. */
+size_t swiattn_decode_noalloc_scratch_bytes(void);
 
 /*
  * swiattn_decode_step - one serving step: route the new tokens, append

@@ -8,6 +8,7 @@ the library has not been built.
 from .binding import (  # noqa: F401
     SwiAttnError,
     decode,
+    decode_noalloc,
     decode_step,
     decode_workspace_size,
     lib,

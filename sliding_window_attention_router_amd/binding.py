@@ -23,6 +23,7 @@ __all__ = [
     "prefill",
     "decode",
     "decode_step",
+    "decode_noalloc",
     "prefill_workspace_size",
     "decode_workspace_size",
     "strerror",
@@ -53,6 +54,8 @@ SYMBOLS = {
     "swiattn_prefill_backward_workspace_size": (_sz, [_i32] * 3),
     "swiattn_prefill_backward": (_i32, [_vp] * 11 + [_i32] * 7 + [_f32, _i32, _vp, _sz, _vp]),
     "swiattn_router_backward": (_i32, [_vp] * 10 + [_i32] * 7 + [_vp, _sz, _vp]),
+    "swiattn_decode_noalloc": (_i32, [_vp] * 6 + [_i32] * 7 + [_f32, _i32, _vp]),
+    "swiattn_decode_noalloc_scratch_bytes": (_sz, []),
     "swiattn_strerror": (ctypes.c_char_p, [_i32]),
     "swiattn_version": (ctypes.c_char_p, []),
 }
@@ -393,6 +396,37 @@ def decode(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None, workspace=Non
         rc = L.swiattn_decode_ex(*ptrs, B, Lmax, Hq, Hkv, G, d, W, float(scale), code, _p(ws),
                                  ws.numel(), _stream(dev), _events(events))
     _check(rc, "swiattn_decode")
+    return out
+
+
+def decode_noalloc(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None):
+    """Routed decode through swiattn_decode_noalloc: the same arguments and
+    result as decode(), with the split-K workspace in the library's fixed
+    per-GPU scratch (no workspace tensor).  Calls that overlap on one GPU
+    race on that scratch."""
+    L = lib()
+    _need(q, "q")
+    code = _dtype_code(q)
+    B, Hq, d = q.shape
+    dev = q.device
+    _need(Kc, "Kc", dtype=q.dtype, device=dev)
+    if Kc.dim() != 4 or Kc.shape[0] != B or Kc.shape[3] != d:
+        raise ValueError("Kc must be [B,Lmax,Hkv,d]")
+    Lmax, Hkv = Kc.shape[1], Kc.shape[2]
+    _need(Vc, "Vc", shape=Kc.shape, dtype=q.dtype, device=dev)
+    _need(cache_len, "cache_len", shape=(B,), dtype=torch.int32, device=dev)
+    _need(gate, "gate", dtype=torch.uint8, device=dev)
+    if gate.dim() != 2 or gate.shape[0] != B:
+        raise ValueError("gate must be [B,G]")
+    G = gate.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", shape=q.shape, dtype=q.dtype, device=dev)
+    rc = L.swiattn_decode_noalloc(_p(q), _p(Kc), _p(Vc), _p(cache_len), _p(gate), _p(out), B, Lmax, Hq,
+                                  Hkv, G, d, W, float(scale), code, _stream(dev))
+    _check(rc, "swiattn_decode_noalloc")
     return out
 
 

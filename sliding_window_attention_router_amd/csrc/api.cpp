@@ -195,6 +195,26 @@ int swiattn_decode(const void* q, const void* Kc, const void* Vc, const int32_t*
                                  scale, dtype, ws, ws_bytes, stream, nullptr);
 }
 
+int swiattn_decode_noalloc(const void* q, const void* Kc, const void* Vc,
+                           const int32_t* cache_len, const uint8_t* gate, void* o, int B, int Lmax,
+                           int Hq, int Hkv, int G, int d, int W, float scale,
+                           swiattn_dtype_t dtype, swiattn_stream_t stream) {
+  swi::DecodeShape sh;
+  swi::DecodePlan p;
+  const int rc = decode_shape(B, Lmax, Hq, Hkv, G, d, W, scale, dtype, &sh, &p);
+  if (rc != SWIATTN_OK) return rc;
+  if (!q || !Kc || !Vc || !cache_len || !gate || !o) return SWIATTN_ERR_INVALID_ARG;
+  // the decode plan must fit the fixed scratch (checked before any HIP call)
+  if (p.bytes > swi::decode_scratch_bytes()) return SWIATTN_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  const int src = hip_rc(swi::decode_scratch(&ws));
+  if (src != SWIATTN_OK) return src;
+  return hip_rc(swi::launch_decode(sh, p, q, Kc, Vc, cache_len, gate, o, ws,
+                                   reinterpret_cast<hipStream_t>(stream), nullptr));
+}
+
+size_t swiattn_decode_noalloc_scratch_bytes(void) { return swi::decode_scratch_bytes(); }
+
 int swiattn_decode_step_anchored(const void* Hn, const void* r, const float* bias, const void* q,
                                  const void* k, const void* v, void* Kc, void* Vc,
                                  int32_t* cache_len, uint8_t* gate, void* o, int B, int Lmax,
@@ -282,6 +302,8 @@ const char* swiattn_strerror(int code) {
     case SWIATTN_ERR_UNSUPPORTED: return "unsupported shape or head dimension";
     case SWIATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case SWIATTN_ERR_HIP: return "HIP runtime or launch error";
+    case SWIATTN_ERR_TOO_LARGE:
+      return "sizes exceed the fixed scratch of the allocation-free entry point";
     default: return "unknown error code";
   }
 }

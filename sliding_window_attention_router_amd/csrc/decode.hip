@@ -27,6 +27,7 @@
 // anchor blocks [0, 64 na) (masked to each head's anchors) before its main
 // range; the masks keep the two key sets of a head disjoint.
 #include <climits>
+#include <mutex>
 
 #include "attn_core.hpp"
 #include "kernels.hpp"
@@ -422,6 +423,41 @@ hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void*
   }
   if (sh.d == 64) return run_decode<bf16_t, 64>(sh, p, a, s, ev);
   return run_decode<bf16_t, 128>(sh, p, a, s, ev);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed scratch of the allocation-free decode entry point: the decode
+// workspace (pair table, partial outputs and log-sum-exps of the split-K
+// pieces) placed in one file-scope device array instead of caller memory.
+// Each GPU that loads the library holds its own copy of the array until the
+// process ends.  Host code never passes the array's name to a kernel (on
+// the host that name is only a stand-in, not a device address): the device
+// address is looked up once per device with hipGetSymbolAddress, with that
+// device current, and that pointer is used from then on.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

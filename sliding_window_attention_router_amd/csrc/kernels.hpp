@@ -83,6 +83,10 @@ hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void*
                          const void* Kc, const void* Vc, const int32_t* cache_len,
                          const uint8_t* gate, void* o, void* ws, hipStream_t s,
                          void* const* ev);
+// Device address (on the current device) and size of the fixed scratch that
+// the allocation-free decode uses as its workspace.
+hipError_t decode_scratch(void** ptr);
+size_t decode_scratch_bytes();
 // route of the new tokens (N = 1), append of their K/V rows, decode
 hipError_t launch_decode_step(const DecodeShape& sh, const DecodePlan& p, const void* Hn,
                               const void* r, const float* bias, int hidden, const void* q,

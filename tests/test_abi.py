@@ -10,7 +10,7 @@ import pytest
 from sliding_window_attention_router_amd import binding
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "swiattn.h")
-OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, -1, -2, -3, -4
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP, TOO_LARGE = 0, -1, -2, -3, -4, -5
 BF16, F32 = 0, 1
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
 
@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_strerror_and_version(lib):
     assert binding.strerror(OK) == "ok"
-    for c in (INVALID, UNSUPPORTED, WORKSPACE, HIP):
+    for c in (INVALID, UNSUPPORTED, WORKSPACE, HIP, TOO_LARGE):
         assert binding.strerror(c) not in ("ok", "unknown error code")
     assert binding.strerror(-99) == "unknown error code"
     assert lib.swiattn_version().decode().count(".") == 2
@@ -251,3 +251,25 @@ def test_prefill_backward_rejects_invalid_arguments(lib):
     # two floats (log-sum-exp, <dO, O>) per (sequence, query head, token)
     assert lib.swiattn_prefill_backward_workspace_size(2, 100, 4) == 2 * 2 * 4 * 100 * 4
     assert lib.swiattn_prefill_backward_workspace_size(0, 100, 4) == 0
+
+
+def test_decode_noalloc_validates_before_touching_the_device(lib):
+    """The allocation-free decode checks its arguments and that the decode
+    plan fits its fixed scratch before any HIP call."""
+    scratch = lib.swiattn_decode_noalloc_scratch_bytes()
+    assert scratch == 16 << 20
+
+    def call(**kw):
+        a = dict(B=64, Lmax=32768, Hq=16, Hkv=4, G=1, d=128, W=1024, scale=0.088, dt=BF16, q=FAKE)
+        a.update(kw)
+        return lib.swiattn_decode_noalloc(a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["Lmax"], a["Hq"],
+                                          a["Hkv"], a["G"], a["d"], a["W"], a["scale"], a["dt"], None)
+
+    assert call(q=None) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(scale=-1.0) == INVALID
+    # 32 query heads per KV head at d=128: 32 MiB of split-K partials
+    assert lib.swiattn_decode_workspace_size(64, 32768, 32, 1, 1, 128, 1024, BF16) > scratch
+    assert call(Hq=32, Hkv=1) == TOO_LARGE
+    # the bench's decode shape fits
+    assert lib.swiattn_decode_workspace_size(64, 32768, 16, 4, 1, 128, 1024, BF16) <= scratch
