@@ -36,6 +36,7 @@ __all__ = [
     "compact",
     "swa_key_range",
     "anchor_key_range",
+    "offset_window_key_range",
     "full_key_range",
     "attend_rows",
     "prefill",
@@ -134,6 +135,25 @@ def anchor_key_range(i, W, A):
     return 0, min(A, lo) - 1
 
 
+def offset_window_key_range(i, W, offset):
+    """Window branch key set of query position i in a layer whose window is
+    offset by `offset` >= 0 positions: the W keys at distances offset ..
+    offset+W-1 behind the query, i.e. the plain window of the query `offset`
+    positions earlier -> inclusive [max(0, i-offset-W+1), i-offset]; empty
+    (hi < lo) when i < offset.
+
+    [Glossary] section "两个核心工程参数（W 和步长 S）详解": the stride S is
+    the offset between the windows of different layers (no offset, or half a
+    window between neighbouring layers; offsets 0, W/4, W/2, 3W/4 in turn
+    reach past W); pitfall 2, fix (2): the windows of layers 0, 1, 2 are
+    [0, W], [W/2, 3W/2], [W, 2W].
+    Reading: those intervals are distances behind the query, W keys each
+    (the glossary's window holds W keys); the query itself is in the set
+    only for offset 0; a row with no key in its window has window output 0
+    (an empty attention sum)."""
+    return swa_key_range(i - offset, W)
+
+
 def full_key_range(i):
     """Full branch key set of query position i: every key up to and including
     i -> inclusive [0, i].
@@ -152,11 +172,12 @@ def attend_rows(q, K, V, lo, hi, scale, lo2=None, hi2=None):
     (and, if given, a second interval disjoint from it: one key set, their
     union).
 
-    q [R,d], K [L,d], V [L,dv], lo/hi int [R] (lo <= hi)  ->
+    q [R,d], K [L,d], V [L,dv], lo/hi int [R]  ->
       O   float64 [R,dv]  sum_j p_j v_j / sum_j p_j,  p_j = exp(s_j - max s)
       lse float64 [R]     log sum_j exp(s_j)
-    with s_j = scale * <q, k_j> for lo <= j <= hi (or lo2 <= j <= hi2; a row
-    with hi2 < lo2 has no second interval).
+    with s_j = scale * <q, k_j> for lo <= j <= hi (or lo2 <= j <= hi2; an
+    interval with hi < lo is empty).  A row whose key set is empty attends
+    to nothing: O = 0, lse = -inf.
     """
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -172,14 +193,27 @@ def attend_rows(q, K, V, lo, hi, scale, lo2=None, hi2=None):
     lse = np.empty(R, dtype=np.float64)
     if R == 0:
         return O, lse
-    # rows are independent: evaluate them in batches that bound memory
-    order = np.argsort(hi, kind="stable")
-    n = max(1, (1 << 24) // (int(hi.max()) + 1))  # score elements per batch
+    # a row whose key set is empty attends to nothing: output 0, lse -inf
+    live = hi >= lo
+    if two:
+        live |= hi2 >= lo2
+    O[~live] = 0.0
+    lse[~live] = -np.inf
+    # rows are independent: evaluate the live ones in batches that bound memory
+    top = np.maximum(hi, hi2) if two else hi
+    order = np.flatnonzero(live)[np.argsort(top[live], kind="stable")]
+    R = order.size
+    if R == 0:
+        return O, lse
+    n = max(1, (1 << 24) // (int(top[live].max()) + 1))  # score elements per batch
     start = 0
     while start < R:
         sel = order[start : start + n]
-        kmax = int(hi[sel].max()) + 1
-        kmin = int(lo[sel].min())
+        live1 = hi[sel] >= lo[sel]
+        kmin, kmax = np.iinfo(np.int64).max, 0
+        if live1.any():
+            kmin = int(lo[sel][live1].min())
+            kmax = int(hi[sel][live1].max()) + 1
         if two:
             live2 = hi2[sel] >= lo2[sel]
             if live2.any():
@@ -210,7 +244,7 @@ def _head_maps(Hq, Hkv, G):
 # ---------------------------------------------------------------------------
 # Prefill: both branches on shared Q/K/V, gated combination
 # ---------------------------------------------------------------------------
-def prefill(Q, K, V, gate, W, scale=None, both_branch=False, rows=None, anchors=0):
+def prefill(Q, K, V, gate, W, scale=None, both_branch=False, rows=None, anchors=0, offset=0):
     """Dual-branch attention forward over a prefix.
 
     [SwiAttn] section 2, dual-branch paragraph: both branches use the same Q,
@@ -226,6 +260,9 @@ def prefill(Q, K, V, gate, W, scale=None, both_branch=False, rows=None, anchors=
     rows: optional sorted token positions to evaluate (default all N)
     anchors: A >= 0 global anchor keys added to the window branch
              (anchor_key_range); 0 is plain SWA
+    offset:  o >= 0 window offset of the layer (offset_window_key_range):
+             the window branch of query i takes the window and anchors of
+             query i - o; 0 is plain SWA
     ->  dict
       O     float64 [B,R,Hq,d]
       lse   float64 [B,R,Hq]      natural-log normaliser of the chosen branch
@@ -250,8 +287,10 @@ def prefill(Q, K, V, gate, W, scale=None, both_branch=False, rows=None, anchors=
     if both_branch:
         Of = np.empty((B, R, Hq, dv))
         Os = np.empty((B, R, Hq, dv))
-    sw = np.array([swa_key_range(int(i), W) for i in rows], dtype=np.int64).reshape(R, 2)
-    an = np.array([anchor_key_range(int(i), W, anchors) for i in rows], dtype=np.int64).reshape(R, 2)
+    sw = np.array([offset_window_key_range(int(i), W, offset) for i in rows],
+                  dtype=np.int64).reshape(R, 2)
+    an = np.array([anchor_key_range(int(i) - offset, W, anchors) for i in rows],
+                  dtype=np.int64).reshape(R, 2)
     fu = np.array([full_key_range(int(i)) for i in rows], dtype=np.int64).reshape(R, 2)
     none = np.array([0, -1], dtype=np.int64)  # no second interval
     for b in range(B):
@@ -283,7 +322,7 @@ def prefill(Q, K, V, gate, W, scale=None, both_branch=False, rows=None, anchors=
 # ---------------------------------------------------------------------------
 # Decode: one new query per sequence against the shared KV cache
 # ---------------------------------------------------------------------------
-def decode(q, Kc, Vc, cache_len, gate, W, scale=None, anchors=0):
+def decode(q, Kc, Vc, cache_len, gate, W, scale=None, anchors=0, offset=0):
     """One decode step per sequence, both branches reading one KV cache.
 
     [SwiAttn] section 2: in decode the two branches share the KV cache.
@@ -296,6 +335,9 @@ def decode(q, Kc, Vc, cache_len, gate, W, scale=None, anchors=0):
     gate [B,G]  ->  dict  o float64 [B,Hq,d], lse float64 [B,Hq]
     anchors: A >= 0 global anchor keys of the window branch (anchor_key_range
     at position L-1); the anchors stay in the linear cache like every key.
+    offset: o >= 0 window offset of the layer (offset_window_key_range): a
+    window head takes the window and anchors of position L-1-o (none when
+    L-1 < o: output 0).
     """
     q = np.asarray(q)
     gate = np.asarray(gate)
@@ -314,7 +356,8 @@ def decode(q, Kc, Vc, cache_len, gate, W, scale=None, anchors=0):
             if gate[b, g]:
                 (lo, hi), (lo2, hi2) = full_key_range(i), (0, -1)
             else:
-                (lo, hi), (lo2, hi2) = swa_key_range(i, W), anchor_key_range(i, W, anchors)
+                (lo, hi) = offset_window_key_range(i, W, offset)
+                (lo2, hi2) = anchor_key_range(i - offset, W, anchors)
             ob, lb = attend_rows(q[b, h][None, :], np.asarray(Kc[b, : i + 1, kv]),
                                  np.asarray(Vc[b, : i + 1, kv]), [lo], [hi], scale, [lo2], [hi2])
             o[b, h], lse[b, h] = ob[0], lb[0]

@@ -153,10 +153,12 @@ def check_decode_equals_last_prefill_row():
         np.testing.assert_allclose(dec[b], pre, rtol=0, atol=1e-13)
 
 
-def brute_force(Q, K, V, gate, W, scale, A=0):
+def brute_force(Q, K, V, gate, W, scale, A=0, o=0):
     """Independent pure-Python evaluation: explicit loops, math.exp.  The
-    window branch's keys are chosen by a membership test: causal, and either
-    among the W newest or among the first A of the sequence."""
+    window branch's keys are chosen by a membership test at position
+    p = i - o (o = the layer's window offset): j <= p, and either among the
+    W newest up to p or among the first A of the sequence.  A row with no
+    key gets output 0."""
     B, N, Hq, d = Q.shape
     Hkv, G = K.shape[2], gate.shape[2]
     Of = np.zeros(Q.shape)
@@ -166,8 +168,12 @@ def brute_force(Q, K, V, gate, W, scale, A=0):
             kv = h * Hkv // Hq
             for i in range(N):
                 for which, out in (("full", Of), ("swa", Os)):
+                    p = i if which == "full" else i - o
                     keys = [j for j in range(N)
-                            if j <= i and (which == "full" or i - j < W or j < A)]
+                            if j <= p and (which == "full" or p - j < W or j < A)]
+                    if not keys:
+                        out[b, i, h, :] = 0.0
+                        continue
                     s = [scale * sum(Q[b, i, h, c] * K[b, j, kv, c] for c in range(d)) for j in keys]
                     mx = max(s)
                     w = [math.exp(x - mx) for x in s]
@@ -267,6 +273,127 @@ def check_anchored_decode_equals_last_prefill_row():
     # a window sequence past W + A differs from its anchor-free decode
     plain = ref.decode(q, K, V, lens, gate, W)["o"]
     assert not np.allclose(dec[0], plain[0])
+
+
+def load_offset_table():
+    layers, offsets = [], None
+    with open(os.path.join(GOLDEN, "window_offsets.txt"), encoding="utf-8") as f:
+        for line in f:
+            parts = line.split("#", 1)[0].split()
+            if not parts:
+                continue
+            if parts[0] == "layers":
+                layers.append((int(parts[1]), float(parts[2]), float(parts[3])))
+            elif parts[0] == "offsets":
+                offsets = [float(x) for x in parts[1:]]
+    return layers, offsets
+
+
+def _distances(i, W, o, N):
+    lo, hi = ref.offset_window_key_range(i, W, o)
+    return sorted(i - j for j in range(N) if lo <= j <= hi)
+
+
+def check_offset_layer_windows_match_page():
+    """The page's layer windows [0, W], [W/2, 3W/2], [W, 2W] are distance
+    ranges behind the query: the key set of a layer with offset o = lower * W
+    is the W distances lower*W .. upper*W - 1 (a window holds W keys, so the
+    printed upper end is where the next window starts).  The offsets 0, W/4,
+    W/2, 3W/4 together reach every distance below 7W/4."""
+    layers, offsets = load_offset_table()
+    W, N = 16, 200
+    i = N - 1
+    for _, lo, hi in layers:
+        o = int(lo * W)
+        assert _distances(i, W, o, N) == list(range(int(lo * W), int(hi * W)))
+    reach = set()
+    for f in offsets:
+        reach |= set(_distances(i, W, int(f * W), N))
+    assert reach == set(range(int((offsets[-1] + 1) * W)))
+
+
+def check_offset_brute_force():
+    """Offset windows (with and without anchors) against the membership-test
+    brute force, both branches and the distance; offsets inside the window,
+    equal to it, beyond it and beyond the sequence (every window empty)."""
+    B, N, Hq, Hkv, d, W = 1, 13, 4, 2, 3, 4
+    Q, K, V = _rand_qkv(36, B, N, Hq, Hkv, d)
+    gate = (np.random.default_rng(37).random((B, N, 2)) < 0.5).astype(np.uint8)
+    for o, A in ((1, 0), (2, 0), (4, 0), (6, 0), (20, 0), (3, 2), (5, 3)):
+        O_bf, diff_bf = brute_force(Q, K, V, gate, W, 0.9, A=A, o=o)
+        out = ref.prefill(Q, K, V, gate, W, scale=0.9, both_branch=True, anchors=A, offset=o)
+        np.testing.assert_allclose(out["O"], O_bf, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(out["diff"], diff_bf, rtol=1e-12, atol=1e-14)
+        hard = ref.prefill(Q, K, V, gate, W, scale=0.9, anchors=A, offset=o)["O"]
+        np.testing.assert_allclose(hard, O_bf, rtol=0, atol=1e-12)
+
+
+def check_offset_against_sdpa():
+    """Gate all zeros with offset o equals torch's float64 attention under
+    the mask i-o-W < j <= i-o on rows i >= o; rows i < o are exactly 0;
+    offset 0 is the plain window; with W + o >= N every row i >= o sees the
+    prefix [0, i-o]; gate all ones does not depend on the offset."""
+    B, N, Hq, Hkv, d, W = 1, 90, 4, 2, 8, 16
+    Q, K, V = _rand_qkv(38, B, N, Hq, Hkv, d)
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    zeros = np.zeros((B, N, 1), np.uint8)
+    for o, Wl in ((5, W), (16, W), (23, W), (0, W), (40, 60)):
+        out = ref.prefill(Q, K, V, zeros, W=Wl, offset=o)["O"]
+        mask = (j <= i - o) & (j > i - o - Wl)
+        live = np.arange(N) >= o
+        np.testing.assert_allclose(out[:, live], _torch_sdpa(Q, K, V, mask)[:, live], rtol=0, atol=1e-12)
+        assert np.all(out[:, ~live] == 0.0)
+        if Wl + o >= N:
+            np.testing.assert_allclose(out[:, live], _torch_sdpa(Q, K, V, j <= i - o)[:, live], rtol=0,
+                                       atol=1e-12)
+    plain = ref.prefill(Q, K, V, zeros, W=W)["O"]
+    np.testing.assert_allclose(ref.prefill(Q, K, V, zeros, W=W, offset=0)["O"], plain, rtol=0, atol=0)
+    ones = np.ones((B, N, 1), np.uint8)
+    full = _torch_sdpa(Q, K, V, j <= i)
+    for o in (0, 7, 30):
+        np.testing.assert_allclose(ref.prefill(Q, K, V, ones, W=W, offset=o)["O"], full, rtol=0, atol=1e-12)
+
+
+def check_offset_closed_forms():
+    """W = 1, offset 2: row i returns v_{i-2} exactly and rows 0, 1 return 0;
+    q = 0 with V = identity gives weight 1/W on the W keys at distances
+    o .. o+W-1 (the window of the page's table shifted back by o)."""
+    N = 9
+    Q, K, V = _rand_qkv(39, 1, N, 2, 1, 4)
+    out = ref.prefill(Q, K, V, np.zeros((1, N, 1), np.uint8), W=1, offset=2)["O"][0]
+    for h in range(2):
+        assert np.all(out[:2, h] == 0.0)
+        assert np.array_equal(out[2:, h], V[0, :-2, 0])
+    table = load_w4_table()
+    Nt, o = 7 + 3, 3
+    Qz = np.zeros((1, Nt, 1, Nt))
+    Kz = np.random.default_rng(40).standard_normal((1, Nt, 1, Nt))
+    Vi = np.eye(Nt)[None, :, None, :]
+    got = ref.prefill(Qz, Kz, Vi, np.zeros((1, Nt, 1), np.uint8), W=4, offset=o)["O"][0, :, 0, :]
+    assert np.all(got[:o] == 0.0)
+    expect = table / table.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(got[o:, :7], expect, rtol=0, atol=1e-15)
+    assert np.all(got[o:, 7:] == 0.0)
+
+
+def check_offset_decode_equals_last_prefill_row():
+    """Decode with a window offset at cache length L reproduces the offset
+    prefill row L-1, also for L <= o (output 0) and with anchors."""
+    B, Lmax, Hq, Hkv, d, W = 4, 60, 4, 2, 8, 12
+    Q, K, V = _rand_qkv(41, B, Lmax, Hq, Hkv, d)
+    lens = np.array([60, 16, 5, 30])
+    gate = np.array([[0], [0], [0], [1]], np.uint8)
+    q = np.stack([Q[b, lens[b] - 1] for b in range(B)])
+    for o, A in ((6, 0), (6, 4), (20, 0)):
+        dec = ref.decode(q, K, V, lens, gate, W, anchors=A, offset=o)["o"]
+        for b in range(B):
+            L = lens[b]
+            g = np.broadcast_to(gate[b], (1, L, 1)).astype(np.uint8)
+            pre = ref.prefill(Q[b:b + 1, :L], K[b:b + 1, :L], V[b:b + 1, :L], g, W, anchors=A,
+                              offset=o)["O"][0, L - 1]
+            np.testing.assert_allclose(dec[b], pre, rtol=0, atol=1e-13)
+        assert np.all(dec[2] == 0.0) == (lens[2] <= o)
 
 
 def check_convex_hull():
@@ -619,6 +746,11 @@ ALL_PINS = [
     check_anchors_closed_form,
     check_anchors_against_sdpa_and_cover,
     check_anchored_decode_equals_last_prefill_row,
+    check_offset_layer_windows_match_page,
+    check_offset_brute_force,
+    check_offset_against_sdpa,
+    check_offset_closed_forms,
+    check_offset_decode_equals_last_prefill_row,
     check_router_backward_finite_differences,
     check_router_backward_against_autograd,
     check_router_backward_special_cases,

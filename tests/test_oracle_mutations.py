@@ -50,6 +50,16 @@ MUTANTS = {
                       lambda i, W, A: (max(0, i - W + 1 - A), max(0, i - W + 1) - 1)),
     # anchors ignored altogether
     "anchors_ignored": ("anchor_key_range", lambda i, W, A: (0, -1)),
+    # window offset ignored (every layer a plain window)
+    "offset_ignored": ("offset_window_key_range", lambda i, W, o: ref.swa_key_range(i, W)),
+    # window moved forward instead of back (sees keys past the query)
+    "offset_forward": ("offset_window_key_range", lambda i, W, o: ref.swa_key_range(i + o, W)),
+    # one position too far back
+    "offset_one_too_far": ("offset_window_key_range", lambda i, W, o: ref.swa_key_range(i - o - 1, W)),
+    # the shifted window's start with the keys up to the query kept
+    "offset_runs_to_query": ("offset_window_key_range", lambda i, W, o: (max(0, i - o - W + 1), i)),
+    # the shift applied as a window of W + o keys ending at the query
+    "offset_widens_window": ("offset_window_key_range", lambda i, W, o: ref.swa_key_range(i, W + o)),
 }
 
 
