@@ -316,6 +316,42 @@ int swiattn_decode_anchored(const void* q, const void* Kc, const void* Vc,
                             float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
                             swiattn_stream_t stream, const swiattn_events_t* events);
 
+/*
+ * swiattn_prefill_offset / swiattn_decode_offset - the anchored calls with a
+ * window offset, for stacked layers whose windows are staggered.
+ * (weimeta glossary "滑窗注意力 Sliding Window Attention 是什么？", section
+ * "两个核心工程参数（W 和步长 S）详解": the stride S offsets the windows of
+ * different layers, e.g. 0, W/4, W/2, 3W/4 in turn, so that together they
+ * reach past W; section "SWA 落地的四个常见坑", pitfall 2, fix (2): the
+ * windows of layers 0, 1, 2 are [0, W], [W/2, 3W/2], [W, 2W].)
+ *
+ *   offset  o >= 0: the window branch of query i takes the window and the
+ *           anchors of query i - o: keys [max(0, i-o-W+1), i-o] (the W keys
+ *           at distances o .. o+W-1 behind the query; the query itself only
+ *           for o = 0) and [0, min(A, i-o-W+1) - 1].  A row i < o has no
+ *           window key: its window-branch output is 0.  The full branch is
+ *           unchanged ([0, i]).  o = 0 is swiattn_prefill_anchored /
+ *           swiattn_decode_anchored; o >= N (prefill) or o >= Lmax (decode)
+ *           is treated as N or Lmax.
+ *   Decode: a window head of a sequence with L = cache_len takes the window
+ *   of position L-1-o (output 0 when L <= o).
+ *   Every other argument, the workspace (same size queries), the outputs
+ *   and the events are those of the anchored calls.
+ * Errors: as the anchored calls, plus INVALID_ARG for offset < 0 and
+ * UNSUPPORTED for offset > 0 in both-branch mode.
+ */
+int swiattn_prefill_offset(const void* Q, const void* K, const void* V, const uint8_t* gate,
+                           const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B, int N,
+                           int Hq, int Hkv, int G, int d, int W, int anchors, int offset, float scale,
+                           swiattn_dtype_t dtype, unsigned flags, void* ws, size_t ws_bytes,
+                           swiattn_stream_t stream, const swiattn_events_t* events);
+
+int swiattn_decode_offset(const void* q, const void* Kc, const void* Vc, const int32_t* cache_len,
+                          const uint8_t* gate, void* o, int B, int Lmax, int Hq, int Hkv, int G,
+                          int d, int W, int anchors, int offset, float scale, swiattn_dtype_t dtype,
+                          void* ws, size_t ws_bytes, swiattn_stream_t stream,
+                          const swiattn_events_t* events);
+
 /* swiattn_decode_step_anchored - swiattn_decode_step whose decode has the
  * global anchors above (the anchors stay in the linear cache like every
  * key); anchors = 0 is swiattn_decode_step.  Same arguments, workspace and

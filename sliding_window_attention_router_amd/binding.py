@@ -50,6 +50,8 @@ SYMBOLS = {
     "swiattn_prefill_anchored": (_i32, [_vp] * 8 + [_i32] * 8 + [_f32, _i32, _u32, _vp, _sz, _vp, _vp]),
     "swiattn_decode_anchored": (_i32, [_vp] * 6 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp, _vp]),
     "swiattn_decode_step_anchored": (_i32, [_vp] * 11 + [_i32] * 9 + [_f32, _i32, _vp, _sz, _vp]),
+    "swiattn_prefill_offset": (_i32, [_vp] * 8 + [_i32] * 9 + [_f32, _i32, _u32, _vp, _sz, _vp, _vp]),
+    "swiattn_decode_offset": (_i32, [_vp] * 6 + [_i32] * 9 + [_f32, _i32, _vp, _sz, _vp, _vp]),
     "swiattn_router_backward_workspace_size": (_sz, [_i32] * 4),
     "swiattn_prefill_backward_workspace_size": (_sz, [_i32] * 3),
     "swiattn_prefill_backward": (_i32, [_vp] * 11 + [_i32] * 7 + [_f32, _i32, _vp, _sz, _vp]),
@@ -302,10 +304,11 @@ def _workspace(nbytes, device, workspace):
 
 
 def prefill(Q, K, V, gate, W, *, idx=None, cnt=None, scale=None, both_branch=False,
-            out=None, diff=None, workspace=None, events=None, anchors=0):
+            out=None, diff=None, workspace=None, events=None, anchors=0, offset=0):
     """Dual-branch prefill.  Q [B,N,Hq,d], K/V [B,N,Hkv,d], gate [B,N,G] uint8.
     anchors: global anchor keys of the window branch (swiattn_prefill_anchored);
-    0 calls swiattn_prefill_ex.
+    offset: window offset of the layer (swiattn_prefill_offset); both 0 calls
+    swiattn_prefill_ex.
 
     In hard-gate mode the compacted positions (idx, cnt) from route() are
     used, or computed here by the library's compaction if not given.
@@ -348,7 +351,11 @@ def prefill(Q, K, V, gate, W, *, idx=None, cnt=None, scale=None, both_branch=Fal
     ws = _workspace(nbytes, dev, workspace)
     ptrs = (_p(Q), _p(K), _p(V), _p(gate), _p(idx if not both_branch else None),
             _p(cnt if not both_branch else None), _p(out), _p(diff))
-    if anchors:
+    if offset:
+        rc = L.swiattn_prefill_offset(*ptrs, B, N, Hq, Hkv, G, d, W, int(anchors), int(offset),
+                                      float(scale), code, flags, _p(ws), ws.numel(), _stream(dev),
+                                      _events(events))
+    elif anchors:
         rc = L.swiattn_prefill_anchored(*ptrs, B, N, Hq, Hkv, G, d, W, int(anchors), float(scale),
                                         code, flags, _p(ws), ws.numel(), _stream(dev),
                                         _events(events))
@@ -360,11 +367,12 @@ def prefill(Q, K, V, gate, W, *, idx=None, cnt=None, scale=None, both_branch=Fal
 
 
 def decode(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None, workspace=None, events=None,
-           anchors=0):
+           anchors=0, offset=0):
     """Routed decode.  q [B,Hq,d], Kc/Vc [B,Lmax,Hkv,d], cache_len int32 [B],
     gate uint8 [B,G].  Returns o [B,Hq,d].  events: as for prefill, recorded
     at the stage boundaries documented for swiattn_decode_ex.  anchors: global
-    anchor keys of the window branch (swiattn_decode_anchored); 0 calls
+    anchor keys of the window branch (swiattn_decode_anchored); offset: window
+    offset of the layer (swiattn_decode_offset); both 0 calls
     swiattn_decode_ex."""
     L = lib()
     _need(q, "q")
@@ -389,7 +397,11 @@ def decode(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None, workspace=Non
     nbytes = int(L.swiattn_decode_workspace_size(B, Lmax, Hq, Hkv, G, d, W, code))
     ws = _workspace(nbytes, dev, workspace)
     ptrs = (_p(q), _p(Kc), _p(Vc), _p(cache_len), _p(gate), _p(out))
-    if anchors:
+    if offset:
+        rc = L.swiattn_decode_offset(*ptrs, B, Lmax, Hq, Hkv, G, d, W, int(anchors), int(offset),
+                                     float(scale), code, _p(ws), ws.numel(), _stream(dev),
+                                     _events(events))
+    elif anchors:
         rc = L.swiattn_decode_anchored(*ptrs, B, Lmax, Hq, Hkv, G, d, W, int(anchors), float(scale),
                                        code, _p(ws), ws.numel(), _stream(dev), _events(events))
     else:

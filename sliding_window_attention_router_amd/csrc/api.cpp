@@ -42,8 +42,9 @@ int prefill_shape(int B, int N, int Hq, int Hkv, int G, int d, int W, float scal
   sh->Hkv = Hkv;
   sh->G = G;
   sh->d = d;
-  sh->W = W;
+  sh->W = W < N ? W : N;  // a window of N or more keys sees every earlier key
   sh->A = 0;
+  sh->off = 0;
   sh->scale = scale;
   sh->f32 = dt == SWIATTN_F32;
   sh->both_branch = (flags & SWIATTN_FLAG_BOTH_BRANCH) != 0;
@@ -63,8 +64,9 @@ int decode_shape(int B, int Lmax, int Hq, int Hkv, int G, int d, int W, float sc
   sh->Hkv = Hkv;
   sh->G = G;
   sh->d = d;
-  sh->W = W;
+  sh->W = W < Lmax ? W : Lmax;
   sh->A = 0;
+  sh->off = 0;
   sh->scale = scale;
   sh->f32 = dt == SWIATTN_F32;
   if (!swi::plan_decode(*sh, plan)) return SWIATTN_ERR_UNSUPPORTED;
@@ -116,24 +118,35 @@ size_t swiattn_prefill_workspace_size(int B, int N, int Hq, int Hkv, int G, int 
   return p.bytes;
 }
 
-int swiattn_prefill_anchored(const void* Q, const void* K, const void* V, const uint8_t* gate,
-                             const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B,
-                             int N, int Hq, int Hkv, int G, int d, int W, int anchors,
-                             float scale, swiattn_dtype_t dtype, unsigned flags, void* ws,
-                             size_t ws_bytes, swiattn_stream_t stream,
-                             const swiattn_events_t* events) {
+int swiattn_prefill_offset(const void* Q, const void* K, const void* V, const uint8_t* gate,
+                           const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B, int N,
+                           int Hq, int Hkv, int G, int d, int W, int anchors, int offset, float scale,
+                           swiattn_dtype_t dtype, unsigned flags, void* ws, size_t ws_bytes,
+                           swiattn_stream_t stream, const swiattn_events_t* events) {
   swi::PrefillShape sh;
   swi::PrefillPlan p;
   const int rc = prefill_shape(B, N, Hq, Hkv, G, d, W, scale, dtype, flags, &sh, &p);
   if (rc != SWIATTN_OK) return rc;
-  if (anchors < 0) return SWIATTN_ERR_INVALID_ARG;
+  if (anchors < 0 || offset < 0) return SWIATTN_ERR_INVALID_ARG;
+  if (offset > 0 && sh.both_branch) return SWIATTN_ERR_UNSUPPORTED;
   sh.A = anchors < N ? anchors : N;
+  sh.off = offset < N ? offset : N;
   if (!Q || !K || !V || !gate || !O) return SWIATTN_ERR_INVALID_ARG;
   if (sh.both_branch ? !diff : (!idx || !cnt)) return SWIATTN_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.bytes) return SWIATTN_ERR_WORKSPACE;
   return hip_rc(swi::launch_prefill(sh, p, Q, K, V, gate, idx, cnt, O, diff, ws,
                                     reinterpret_cast<hipStream_t>(stream),
                                     events ? events->ev : nullptr));
+}
+
+int swiattn_prefill_anchored(const void* Q, const void* K, const void* V, const uint8_t* gate,
+                             const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B,
+                             int N, int Hq, int Hkv, int G, int d, int W, int anchors,
+                             float scale, swiattn_dtype_t dtype, unsigned flags, void* ws,
+                             size_t ws_bytes, swiattn_stream_t stream,
+                             const swiattn_events_t* events) {
+  return swiattn_prefill_offset(Q, K, V, gate, idx, cnt, O, diff, B, N, Hq, Hkv, G, d, W, anchors, 0,
+                                scale, dtype, flags, ws, ws_bytes, stream, events);
 }
 
 int swiattn_prefill_ex(const void* Q, const void* K, const void* V, const uint8_t* gate,
@@ -161,22 +174,32 @@ size_t swiattn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int G, in
   return p.bytes;
 }
 
-int swiattn_decode_anchored(const void* q, const void* Kc, const void* Vc,
-                            const int32_t* cache_len, const uint8_t* gate, void* o, int B,
-                            int Lmax, int Hq, int Hkv, int G, int d, int W, int anchors,
-                            float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
-                            swiattn_stream_t stream, const swiattn_events_t* events) {
+int swiattn_decode_offset(const void* q, const void* Kc, const void* Vc, const int32_t* cache_len,
+                          const uint8_t* gate, void* o, int B, int Lmax, int Hq, int Hkv, int G,
+                          int d, int W, int anchors, int offset, float scale, swiattn_dtype_t dtype,
+                          void* ws, size_t ws_bytes, swiattn_stream_t stream,
+                          const swiattn_events_t* events) {
   swi::DecodeShape sh;
   swi::DecodePlan p;
   const int rc = decode_shape(B, Lmax, Hq, Hkv, G, d, W, scale, dtype, &sh, &p);
   if (rc != SWIATTN_OK) return rc;
-  if (anchors < 0) return SWIATTN_ERR_INVALID_ARG;
+  if (anchors < 0 || offset < 0) return SWIATTN_ERR_INVALID_ARG;
   sh.A = anchors < Lmax ? anchors : Lmax;
+  sh.off = offset < Lmax ? offset : Lmax;
   if (!q || !Kc || !Vc || !cache_len || !gate || !o) return SWIATTN_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.bytes) return SWIATTN_ERR_WORKSPACE;
   return hip_rc(swi::launch_decode(sh, p, q, Kc, Vc, cache_len, gate, o, ws,
                                    reinterpret_cast<hipStream_t>(stream),
                                    events ? events->ev : nullptr));
+}
+
+int swiattn_decode_anchored(const void* q, const void* Kc, const void* Vc,
+                            const int32_t* cache_len, const uint8_t* gate, void* o, int B,
+                            int Lmax, int Hq, int Hkv, int G, int d, int W, int anchors,
+                            float scale, swiattn_dtype_t dtype, void* ws, size_t ws_bytes,
+                            swiattn_stream_t stream, const swiattn_events_t* events) {
+  return swiattn_decode_offset(q, Kc, Vc, cache_len, gate, o, B, Lmax, Hq, Hkv, G, d, W, anchors, 0,
+                               scale, dtype, ws, ws_bytes, stream, events);
 }
 
 int swiattn_decode_ex(const void* q, const void* Kc, const void* Vc, const int32_t* cache_len,

@@ -51,22 +51,33 @@ struct DecodeArgs {
   float* part_o;    // [2*grid][HK][D] pieces of cut pairs, slot 2w (first piece of share w) or 2w+1
   float* part_lse;  // [2*grid][HK]
   int B, Lmax, Hq, Hkv, G, W, HK, HG;
-  int A;  // global anchor keys of the window branch (0 = none)
+  int A;    // global anchor keys of the window branch (0 = none)
+  int off;  // window offset of the layer: a window head takes the window of position L-1-off
   float sl2;
 };
 
 SWI_DEV int clamp_len(int L, int Lmax) { return L < 1 ? 1 : (L > Lmax ? Lmax : L); }
 
-// first key of head h's range in sequence b
-SWI_DEV int head_lo(const DecodeArgs& a, int b, int h, int L) {
-  const bool full = a.gate[b * a.G + h / a.HG] != 0;
-  return full ? 0 : max(0, L - a.W);
+// Keys [lo, hi] of head h in sequence b: [0, L-1] for a full head; for a
+// window head the window of position p = L-1-off, [max(0, p-W+1), p]
+// (empty, hi < lo, when p < 0).
+SWI_DEV void head_range(const DecodeArgs& a, int b, int h, int L, int& lo, int& hi) {
+  if (a.gate[b * a.G + h / a.HG] != 0) {
+    lo = 0;
+    hi = L - 1;
+    return;
+  }
+  const int p = L - 1 - a.off;
+  lo = max(0, p - a.W + 1);
+  hi = p;
 }
 
-// Keys [lo, L) read for pair bk = (sequence, KV head): the union of the
-// ranges of its query heads; na anchor blocks precede them when a head of
+// Keys [lo, hi] read for pair bk = (sequence, KV head): the union of the
+// ranges of its query heads (at least one block: a pair whose window heads
+// all have an empty window visits one fully masked block, so that its
+// output is still written); na anchor blocks precede them when a head of
 // the pair is a window head.  Returns the number of 64-key blocks.
-SWI_DEV int pair_blocks(const DecodeArgs& a, int bk, int& L, int& lo, int& na) {
+SWI_DEV int pair_blocks(const DecodeArgs& a, int bk, int& L, int& lo, int& hi, int& na) {
   const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
   L = clamp_len(a.cache_len[b], a.Lmax);
   const int g0 = kvh * a.HK / a.HG, g1 = (kvh * a.HK + a.HK - 1) / a.HG;
@@ -76,9 +87,12 @@ SWI_DEV int pair_blocks(const DecodeArgs& a, int bk, int& L, int& lo, int& na) {
     full = full || f;
     win = win || !f;
   }
-  lo = full ? 0 : max(0, L - a.W);
-  na = win ? (min(a.A, max(0, L - a.W)) + kBN - 1) / kBN : 0;
-  return na + (L - lo + kBN - 1) / kBN;
+  const int p = L - 1 - a.off;
+  const int wlo = max(0, p - a.W + 1);
+  lo = full ? 0 : wlo;
+  hi = full ? L - 1 : max(p, wlo);
+  na = win ? (min(a.A, wlo) + kBN - 1) / kBN : 0;
+  return na + (hi - lo) / kBN + 1;
 }
 
 // First block of share w: floor(w*T/G).
@@ -93,15 +107,16 @@ SWI_DEV int lane_of(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
 // 64 consecutive pairs, one per lane, with the inclusive prefix sum of their
 // block counts (absolute: carry holds the blocks of all earlier pairs).
 struct PairWindow {
-  int base, L, lo, na, incl;
+  int base, L, lo, hi, na, incl;
   SWI_DEV void fill(const DecodeArgs& a, int base_, int carry, int lane, int npairs) {
     base = base_;
     const int bk = base + lane;
     int n = 0;
     L = 1;
     lo = 0;
+    hi = 0;
     na = 0;
-    if (bk < npairs) n = pair_blocks(a, bk, L, lo, na);
+    if (bk < npairs) n = pair_blocks(a, bk, L, lo, hi, na);
     incl = wave_incl_scan_i(n) + carry;
   }
 };
@@ -116,9 +131,10 @@ struct DecSeg {
     kvh = bk - b * a.Hkv;
     L = lane_of(win.L, j);
     lo = lane_of(win.lo, j);
+    const int hi = lane_of(win.hi, j);
     na = lane_of(win.na, j);
     const int incl = lane_of(win.incl, j);
-    nb = na + (L - lo + kBN - 1) / kBN;
+    nb = na + (hi - lo) / kBN + 1;
     first = incl - nb;
     blk0 = max(s, first) - first;
     blk1 = min(e, incl) - first;
@@ -173,8 +189,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int bk = base + k * kWave + lane;
-      int L, lo, na;
-      n[k] = bk < npairs ? pair_blocks(a, bk, L, lo, na) : 0;
+      int L, lo, hi, na;
+      n[k] = bk < npairs ? pair_blocks(a, bk, L, lo, hi, na) : 0;
     }
     tsum += n[0] + n[1] + n[2] + n[3];
   }
@@ -202,22 +218,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   DecSeg cur;
   cur.from(a, win, j, s, e);
   Core c;
-  int lo_h = 0, hi = -1, ahi = -1, wmax_lo = 0, wmin_ahi = -1;
+  int lo_h = 0, hi_h = -1, ahi = -1, wmax_lo = 0, wmin_hi = -1, wmin_ahi = -1;
   auto begin = [&]() {
     c.init();
     const int h = cur.kvh * a.HK + q;
     const T* qp = static_cast<const T*>(a.q) + (int64_t(cur.b) * a.Hq + h) * D;
     c.load_q(valid ? qp : nullptr, g);
-    lo_h = valid ? head_lo(a, cur.b, h, cur.L) : 0;
-    hi = valid ? cur.L - 1 : -1;
+    lo_h = 0;
+    hi_h = -1;
+    if (valid) head_range(a, cur.b, h, cur.L, lo_h, hi_h);
     // a window head's anchors [0, ahi] end where its window starts; a full
     // head (lo_h = 0) has none
     ahi = valid ? min(a.A, lo_h) - 1 : -1;
     // anchor blocks every head covers whole need no mask
     wmin_ahi = wave_min_i(valid ? ahi : INT_MAX);
-    // heads of one KV head may start at different keys (window heads next
-    // to full ones): blocks before the latest start are masked
+    // heads of one KV head may start and end at different keys (window
+    // heads next to full ones): blocks before the latest start or past the
+    // earliest end are masked
     wmax_lo = wave_max_i(valid ? lo_h : -1);
+    wmin_hi = wave_min_i(valid ? hi_h : INT_MAX);
   };
   begin();
   typename Cfg::Loader ld;
@@ -259,8 +278,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     }
     const int kb = cur.kb(n);
     const bool anc = n < cur.na;  // wave-uniform
-    const bool masked = anc ? kb + kBN - 1 > wmin_ahi : (kb < wmax_lo || kb + kBN > cur.L);
-    c.block(lds, kb, masked, anc ? 0 : lo_h, anc ? ahi : hi, a.sl2, q, g);
+    const bool masked = anc ? kb + kBN - 1 > wmin_ahi : (kb < wmax_lo || kb + kBN - 1 > wmin_hi);
+    c.block(lds, kb, masked, anc ? 0 : lo_h, anc ? ahi : hi_h, a.sl2, q, g);
     if (!seg_end) {
       n = nn;
       continue;
@@ -414,6 +433,7 @@ hipError_t launch_decode(const DecodeShape& sh, const DecodePlan& p, const void*
   a.G = sh.G;
   a.W = sh.W;
   a.A = sh.A;
+  a.off = sh.off;
   a.HK = p.HK;
   a.HG = p.HG;
   a.sl2 = sh.scale * kLog2e;

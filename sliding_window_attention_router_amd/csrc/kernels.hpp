@@ -36,8 +36,9 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
 
 // ---- prefill ------------------------------------------------------------
 struct PrefillShape {
-  int B, N, Hq, Hkv, G, d, W;
-  int A;  // global anchor keys of the window branch (0 = none)
+  int B, N, Hq, Hkv, G, d, W;  // W clamped to N (a longer window sees the same keys)
+  int A;    // global anchor keys of the window branch (0 = none)
+  int off;  // window offset of the layer (0 = none), clamped to N
   float scale;
   bool f32;
   bool both_branch;
@@ -68,8 +69,9 @@ hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const vo
 
 // ---- decode -------------------------------------------------------------
 struct DecodeShape {
-  int B, Lmax, Hq, Hkv, G, d, W;
-  int A;  // global anchor keys of the window branch (0 = none)
+  int B, Lmax, Hq, Hkv, G, d, W;  // W clamped to Lmax
+  int A;    // global anchor keys of the window branch (0 = none)
+  int off;  // window offset of the layer (0 = none), clamped to Lmax
   float scale;
   bool f32;
 };

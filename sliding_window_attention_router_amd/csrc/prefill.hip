@@ -64,7 +64,9 @@ struct PrefillArgs {
   float* diff;      // [B,N]
   int* queue;       // [8] window-tile queue positions (zeroed by the schedule kernel)
   int B, N, Hq, Hkv, G, W;
-  int A;  // global anchor keys of the window branch (0 = none)
+  int A;    // global anchor keys of the window branch (0 = none)
+  int off;  // window offset of the layer: the window of query i is that of query i - off
+  int Wf;   // W + off: gate=1 rows take keys [i-off-W+1, i] in the window pass, the far part below
   int HK, HG, hpu, units, tpt_band, tpt_far, band_tiles, far_tiles, max_items;
   int far_grid;  // workgroups of attn_kernel reserved for far items (multiple of 8)
   int band_grid; // workgroups of attn_kernel that work off the window-tile queues
@@ -252,6 +254,52 @@ struct TileLds {
   static constexpr int kBuf1 = kDma ? LdsDma<D>::kBytes : 16;
 };
 
+// Key ranges of one row in the window pass: the window [lo, hi] and the
+// anchors [0, ahi].  With a window offset o the window is that of query
+// i - o, [max(0, i-o-W+1), i-o] (empty for i < o); a gate=1 row then also
+// takes the keys (i-o, i] here, so that its window-pass range [lo, i] and
+// its far part [A, lo-1] again cover [0, i] (with the anchors [0, A)).
+SWI_DEV void window_row(const PrefillArgs& a, int b, int tok, int h, bool valid, int& lo, int& hi,
+                        int& ahi) {
+  if (!valid) {
+    lo = 0;
+    hi = -1;
+    ahi = -1;
+    return;
+  }
+  const int p = tok - a.off;
+  lo = max(0, p - a.W + 1);
+  hi = p;
+  if (a.off > 0 && a.gate[(int64_t(b) * a.N + tok) * a.G + h / a.HG] != 0) hi = tok;
+  ahi = min(a.A, lo) - 1;  // anchors end where the window starts
+}
+
+// Whether a window tile (tokens q0..qlast of KV head kvh) holds a gate=1 row:
+// with a window offset its block range then reaches the diagonal.  At most
+// 128 (token, gate group) pairs, one ballot per 64; the result is
+// wave-uniform.
+SWI_DEV bool tile_has_full_row(const PrefillArgs& a, int b, int kvh, int q0, int qlast) {
+  const int g0 = kvh * a.HK / a.HG, g1 = (kvh * a.HK + a.HK - 1) / a.HG;
+  const int ng = g1 - g0 + 1, n = (qlast - q0 + 1) * ng;
+  bool any = false;
+  for (int k = threadIdx.x & 63; k < n; k += 64) {
+    const int t = q0 + k / ng, g = g0 + k % ng;
+    any = any || a.gate[(int64_t(b) * a.N + t) * a.G + g] != 0;
+  }
+  return __any(any);
+}
+
+// Block range of a window tile: the first block holding a window key of
+// its first token, through the block holding the last key any row takes
+// (at least one block: a tile whose rows all have an empty window visits
+// block 0 fully masked).
+SWI_DEV void window_blocks(const PrefillArgs& a, int b, int kvh, int q0, int qlast, int& kb0, int& nb) {
+  kb0 = (max(0, q0 - a.off - a.W + 1) / kBN) * kBN;
+  int last = qlast - a.off;
+  if (a.off > 0 && tile_has_full_row(a, b, kvh, q0, qlast)) last = qlast;
+  nb = last >= kb0 ? (last - kb0) / kBN + 1 : 1;
+}
+
 // ---------------------------------------------------------------------------
 // Window branch over every row.  Rows of a tile are tpt_band consecutive
 // tokens x the HK query heads of one KV head (128 rows).
@@ -280,10 +328,8 @@ SWI_DEV void band_tile(const PrefillArgs& a, char* buf0, char* buf1, int lin) {
     tok[t] = q0 + slot;
     valid[t] = slot < a.tpt_band && tok[t] < a.N;
     h[t] = kvh * a.HK + hh;
-    lo[t] = valid[t] ? max(0, tok[t] - a.W + 1) : 0;
-    hi[t] = valid[t] ? tok[t] : -1;
+    window_row(a, b, tok[t], h[t], valid[t], lo[t], hi[t], ahi[t]);
     alo[t] = 0;
-    ahi[t] = valid[t] ? min(a.A, lo[t]) - 1 : -1;  // anchors end where the window starts
     c.load_q(t, valid[t] ? Qp + ((int64_t(b) * a.N + tok[t]) * a.Hq + h[t]) * D : nullptr, g);
   }
   TileBounds<TPW> tb;
@@ -293,16 +339,16 @@ SWI_DEV void band_tile(const PrefillArgs& a, char* buf0, char* buf1, int lin) {
   const T* Vb = static_cast<const T*>(a.V) + (int64_t(b) * a.N * a.Hkv + kvh) * D;
   const int64_t rs = int64_t(a.Hkv) * D;
   // anchor blocks first (the last row of the tile has the most anchors)
-  const int na = (min(a.A, max(0, qlast - a.W + 1)) + kBN - 1) / kBN;
+  const int na = (min(a.A, max(0, qlast - a.off - a.W + 1)) + kBN - 1) / kBN;
   if (na > 0) {
     TileBounds<TPW> tba;
     tba.init(valid, alo, ahi);
     block_loop<Core, T, D, NT>(c, buf0, buf1, Kb, Vb, rs, 0, na, a.N, tba, alo, ahi, a.sl2, tid, q, g);
     __syncthreads();  // every wave is done with the staging buffers
   }
-  const int kb0 = (max(0, q0 - a.W + 1) / kBN) * kBN;
-  block_loop<Core, T, D, NT>(c, buf0, buf1, Kb, Vb, rs, kb0, (qlast - kb0) / kBN + 1, a.N, tb, lo, hi,
-                             a.sl2, tid, q, g);
+  int kb0, nb;
+  window_blocks(a, b, kvh, q0, qlast, kb0, nb);
+  block_loop<Core, T, D, NT>(c, buf0, buf1, Kb, Vb, rs, kb0, nb, a.N, tb, lo, hi, a.sl2, tid, q, g);
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     float lse2;
@@ -378,7 +424,7 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
     int blocks = 0;
     if (ntok > 0) {
       const int tlast = far_pos(a, b, g, t * a.tpt_far + ntok - 1);
-      const int fh = tlast - a.W;  // far keys [A, fh]
+      const int fh = tlast - a.Wf;  // far keys [A, fh]
       if (fh >= a.A) blocks = fh / kBN - a.A / kBN + 1;
     }
     sv.n_items[T_] = blocks;
@@ -451,8 +497,8 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
 }
 
 // ---------------------------------------------------------------------------
-// Far part of the full branch for gathered rows: keys [A, i-W] (the full set
-// minus the window and its anchors).  One workgroup per work item (tile,
+// Far part of the full branch for gathered rows: keys [A, i-W-off] (the full
+// set minus the window pass's keys and the anchors).  One workgroup per work item (tile,
 // chunk); grid = upper bound, idle workgroups exit at once.
 // Every item, also the only chunk of a tile, writes its normalised partial
 // output and log-sum-exp; merge_kernel combines them with the window
@@ -473,7 +519,7 @@ SWI_DEV void far_item(const PrefillArgs& a, char* buf0, char* buf1, int item) {
   const int kvh = (u * a.hpu) / a.HK;
   const int cnt = far_count(a, b, g_gate);
   const int ntok = min(a.tpt_far, cnt - t_ * a.tpt_far);
-  const int far_hi = far_pos(a, b, g_gate, t_ * a.tpt_far + ntok - 1) - a.W;
+  const int far_hi = far_pos(a, b, g_gate, t_ * a.tpt_far + ntok - 1) - a.Wf;
   const int fb = (a.A / kBN) * kBN;  // block holding the first far key A
   const int c0 = fb + ch * cb * kBN;
   const int c1 = min(far_hi + 1, fb + (ch + 1) * cb * kBN);  // keys [c0, c1)
@@ -493,7 +539,7 @@ SWI_DEV void far_item(const PrefillArgs& a, char* buf0, char* buf1, int item) {
     tok[t] = valid[t] ? far_pos(a, b, g_gate, t_ * a.tpt_far + slot) : 0;
     h[t] = u * a.hpu + hh;
     lo[t] = max(c0, a.A);
-    hi[t] = valid[t] ? min(tok[t] - a.W, c1 - 1) : -1;
+    hi[t] = valid[t] ? min(tok[t] - a.Wf, c1 - 1) : -1;
     c.load_q(t, valid[t] ? Qp + ((int64_t(b) * a.N + tok[t]) * a.Hq + h[t]) * D : nullptr, g);
   }
   TileBounds<TPW> tb;
@@ -564,9 +610,8 @@ struct BandTile {
     kvh = bk - b * a.Hkv;
     q0 = tile * a.tpt_band;
     const int qlast = min(a.N - 1, q0 + a.tpt_band - 1);
-    kb0 = (max(0, q0 - a.W + 1) / kBN) * kBN;
-    nb = (qlast - kb0) / kBN + 1;
-    na = kAnch ? (min(a.A, max(0, qlast - a.W + 1)) + kBN - 1) / kBN : 0;
+    window_blocks(a, b, kvh, q0, qlast, kb0, nb);
+    na = kAnch ? (min(a.A, max(0, qlast - a.off - a.W + 1)) + kBN - 1) / kBN : 0;
   }
   SWI_DEV int anchors() const { return kAnch ? na : 0; }
   SWI_DEV int total() const { return anchors() + nb; }
@@ -614,8 +659,8 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
   while (true) {
     const int tok = t.q0 + slot;
     const bool valid = slot < a.tpt_band && tok < a.N;
-    const int lo = valid ? max(0, tok - a.W + 1) : 0, hi = valid ? tok : -1;
-    const int ahi = valid ? min(a.A, lo) - 1 : -1;  // anchors [0, ahi]
+    int lo, hi, ahi;  // window [lo, hi], anchors [0, ahi]
+    window_row(a, t.b, tok, t.kvh * a.HK + hh, valid, lo, hi, ahi);
     TileBounds<1> tb, tba;
     {
       const bool v1[1] = {valid};
@@ -763,7 +808,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PrefillArgs a) {
     // (the 8 threads of a row take every branch together)
     if (slot >= ntok) continue;
     const int tok = far_pos(a, b, g_gate, t * a.tpt_far + slot);
-    if (tok - a.W < a.A) continue;  // no far keys: O_FULL = O_SWA
+    if (tok - a.Wf < a.A) continue;  // no far keys: the window pass already holds O_FULL
     const int h = u * a.hpu + hh;
     const float ls = a.lse_s[(int64_t(b) * a.Hq + h) * a.N + tok];
     float M = ls;
@@ -953,6 +998,8 @@ hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const vo
   a.G = sh.G;
   a.W = sh.W;
   a.A = sh.A;
+  a.off = sh.off;
+  a.Wf = sh.W + sh.off;
   a.HK = p.HK;
   a.HG = p.HG;
   a.hpu = p.hpu;

@@ -273,3 +273,18 @@ def test_decode_noalloc_validates_before_touching_the_device(lib):
     assert call(Hq=32, Hkv=1) == TOO_LARGE
     # the bench's decode shape fits
     assert lib.swiattn_decode_workspace_size(64, 32768, 16, 4, 1, 128, 1024, BF16) <= scratch
+
+
+def test_offset_entry_points_validate(lib):
+    """Window offsets: negative offsets are rejected, both-branch mode with
+    an offset is unsupported (checked before any HIP call)."""
+    args = (FAKE,) * 8
+    rc = lib.swiattn_prefill_offset(*args, 1, 100, 4, 2, 1, 128, 16, 0, -1, 0.088, BF16, 0, FAKE, 1 << 40,
+                                    None, None)
+    assert rc == INVALID
+    rc = lib.swiattn_prefill_offset(*args, 1, 100, 4, 2, 1, 128, 16, 0, 8, 0.088, BF16, 1, FAKE, 1 << 40,
+                                    None, None)
+    assert rc == UNSUPPORTED
+    rc = lib.swiattn_decode_offset(*(FAKE,) * 6, 2, 100, 4, 2, 1, 128, 16, 0, -3, 0.088, BF16, FAKE,
+                                   1 << 40, None, None)
+    assert rc == INVALID
