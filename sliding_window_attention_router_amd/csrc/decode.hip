@@ -104,6 +104,50 @@ SWI_DEV int share_of(int x, int T, int G) {
 
 SWI_DEV int lane_of(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
 
+// float32 staging of one 64-key block (one wave, padded layout of the
+// float32 core): 16-key quarters through registers, the next quarter's loads
+// in flight while the current one is stored (a whole block in registers
+// would take 256 VGPRs).
+template <int D, bool kStream>
+struct DecF32Stage {
+  using L = Lds<float, D>;
+  static constexpr int CPR = D / 4;                 // 16-byte pieces per row
+  static constexpr int QK = 16;                     // keys per quarter
+  static constexpr int PER = QK * CPR / kWave;      // pieces per lane and matrix
+  static_assert(QK * CPR % kWave == 0, "quarter layout");
+  u32x4 kr[2][PER], vr[2][PER];
+  SWI_DEV void load(int st, const float* Kb, const float* Vb, int64_t rs, int k0, int kend, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int u = lane + kWave * j, key = u / CPR, c = u - key * CPR;
+      const int kk = clamp_row(k0 + key, kend);
+      kr[st][j] = load16<kStream>(Kb + kk * rs + c * 4);
+      vr[st][j] = load16<kStream>(Vb + kk * rs + c * 4);
+    }
+  }
+  SWI_DEV void store(int st, char* lds, int q0, int lane) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int u = lane + kWave * j, key = q0 + u / CPR, c = u % CPR;
+      uint32_t* kp = reinterpret_cast<uint32_t*>(lds + key * L::kKStride) + c * 4;
+      uint32_t* vp = reinterpret_cast<uint32_t*>(lds + L::kKBytes + key * L::kVStride) + c * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kp[e] = kr[st][j][e];
+        vp[e] = vr[st][j][e];
+      }
+    }
+  }
+  SWI_DEV void block(char* lds, const float* Kb, const float* Vb, int64_t rs, int kb, int kend, int lane) {
+    load(0, Kb, Vb, rs, kb, kend, lane);
+#pragma unroll
+    for (int qq = 0; qq < kBN / QK; ++qq) {
+      if (qq + 1 < kBN / QK) load((qq + 1) & 1, Kb, Vb, rs, kb + (qq + 1) * QK, kend, lane);
+      store(qq & 1, lds, qq * QK, lane);
+    }
+  }
+};
+
 // 64 consecutive pairs, one per lane, with the inclusive prefix sum of their
 // block counts (absolute: carry holds the blocks of all earlier pairs).
 struct PairWindow {
@@ -154,8 +198,8 @@ struct DecSeg {
 // layout of the prefill's DMA path, filled from registers with linear
 // 16-byte stores (K and V separately, so the next block's K loads are in
 // flight while V is stored), read by the DMA-layout core (V^T through
-// transposing LDS reads).  float32: the padded layout with V^T staged by
-// the loader.
+// transposing LDS reads).  float32: the padded layout of the float32 core,
+// staged in 16-key quarters (DecF32Stage).
 template <typename T, int D>
 struct DecCfg;
 template <int D>
@@ -168,7 +212,7 @@ struct DecCfg<bf16_t, D> {
 template <int D>
 struct DecCfg<float, D> {
   using Core = CoreF32<D>;
-  using Loader = KVLoader<float, D, kDecThreads, SWI_DEC_STREAM>;
+  using Loader = DecF32Stage<D, SWI_DEC_STREAM>;
   static constexpr int kLds = Lds<float, D>::kBytes;
   static constexpr bool kSplit = false;
 };
@@ -240,7 +284,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   };
   begin();
   typename Cfg::Loader ld;
-  ld.load(cur.kbase<T, D>(a), cur.vbase<T, D>(a), rs, cur.kb(cur.blk0), cur.L, lane);
+  if constexpr (Cfg::kSplit) ld.load(cur.kbase<T, D>(a), cur.vbase<T, D>(a), rs, cur.kb(cur.blk0), cur.L, lane);
   int n = cur.blk0;
   while (true) {
     // the block after this one, possibly the first block of the next pair
@@ -272,9 +316,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
       ld.load_v(vbn, rs, lkb, lend, lane);
       __syncthreads();
     } else {
-      ld.store(lds, lane);
+      ld.block(lds, cur.kbase<T, D>(a), cur.vbase<T, D>(a), rs, cur.kb(n), cur.L, lane);
       __syncthreads();
-      if (more) ld.load(nx.kbase<T, D>(a), nx.vbase<T, D>(a), rs, nx.kb(nn), nx.L, lane);
     }
     const int kb = cur.kb(n);
     const bool anc = n < cur.na;  // wave-uniform
