@@ -240,8 +240,12 @@ size_t swiattn_decode_noalloc_scratch_bytes(void);
  *                                 swiattn_route with N = 1)
  *   o      [B,Hq,d]        dtype  out: as swiattn_decode after the append
  *   ws, ws_bytes: as swiattn_decode (swiattn_decode_workspace_size).
- * Runs the router, the append and the decode on `stream`, in that order,
- * with no host synchronisation.
+ * Runs the router and the append (one launch) and then the decode on
+ * `stream`, with no host synchronisation.  A sequence whose cache is full
+ * must not be stepped: its append is skipped, cache_len stays Lmax and its
+ * output is the decode of the new query over the unchanged cache, which
+ * does not hold the new token's key (the library cannot report this on the
+ * host, since the lengths live on the device; callers check L < Lmax).
  * Errors: as swiattn_decode, plus INVALID_ARG for hidden < 1 or a NULL
  * router or k/v pointer.
  */

@@ -524,25 +524,51 @@ hipError_t decode_scratch(void** ptr) {
 }
 
 // ---------------------------------------------------------------------------
-// Serving step: the new token's key and value rows go to position
-// L = cache_len[b] of its sequence's cache and the length becomes L + 1
-// (SwiAttn report, section 2: both branches read one cache, so every token
-// is appended whatever its gate).  A length below 0 is taken as 0; a full
-// cache (L >= Lmax) is left as it is.  One workgroup per sequence copies the
-// Hkv*d-element rows in 16-byte pieces, then one thread stores the length
-// (every thread has read it before the barrier).
+// Serving step: route the new token of each sequence, append its key and
+// value rows at position L = cache_len[b] and advance the length to L + 1,
+// in one launch (SwiAttn report, section 2: a router per token; both
+// branches read one cache, so every token is appended whatever its gate),
+// then the decode.  One workgroup per sequence: wave w computes the logits of
+// gate groups w, w + 4, ... with the router's lane order and reduction tree
+// (the same logits as swiattn_route), the threads copy the Hkv*d-element
+// rows in 16-byte pieces, and one thread stores the new length after a
+// barrier (every thread has read the old one before it).  A length below 0
+// is taken as 0; a full cache (L >= Lmax) is left as it is.
 // ---------------------------------------------------------------------------
-constexpr int kAppendThreads = 256;
+constexpr int kStepThreads = 256;
 
-__global__ __launch_bounds__(kAppendThreads) void append_kernel(const uint4* k, const uint4* v, uint4* Kc,
-                                                                uint4* Vc, int32_t* cache_len, int Lmax,
-                                                                int row16) {
+template <typename T>
+__global__ __launch_bounds__(kStepThreads) void step_prep_kernel(
+    const T* __restrict__ Hn, const T* __restrict__ r, const float* __restrict__ bias,
+    uint8_t* __restrict__ gate, int hidden, int G, const uint4* __restrict__ k,
+    const uint4* __restrict__ v, uint4* __restrict__ Kc, uint4* __restrict__ Vc,
+    int32_t* __restrict__ cache_len, int Lmax, int row16) {
+  constexpr int VEC = 16 / Elem<T>::kBytes;  // elements per 16-byte load
   const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int L = max(cache_len[b], 0);
+  const T* row = Hn + int64_t(b) * hidden;
+  for (int g = wave; g < G; g += kStepThreads / 64) {
+    float acc = 0.f;
+    if (hidden % VEC == 0) {
+      for (int vv = lane; vv < hidden / VEC; vv += 64) {
+        u32x4 hv = *reinterpret_cast<const u32x4*>(row + int64_t(vv) * VEC);
+        const T* hp = reinterpret_cast<const T*>(&hv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          acc = fmaf(Elem<T>::load(hp + e), Elem<T>::load(r + int64_t(vv * VEC + e) * G + g), acc);
+      }
+    } else {
+      for (int kk = lane; kk < hidden; kk += 64)
+        acc = fmaf(Elem<T>::load(row + kk), Elem<T>::load(r + int64_t(kk) * G + g), acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) gate[int64_t(b) * G + g] = acc + bias[g] > 0.f ? 1 : 0;
+  }
   if (L < Lmax) {
     const int64_t dst = (int64_t(b) * Lmax + L) * row16;
     const int64_t src = int64_t(b) * row16;
-    for (int i = threadIdx.x; i < row16; i += kAppendThreads) {
+    for (int i = threadIdx.x; i < row16; i += kStepThreads) {
       Kc[dst + i] = k[src + i];
       Vc[dst + i] = v[src + i];
     }
@@ -555,13 +581,21 @@ hipError_t launch_decode_step(const DecodeShape& sh, const DecodePlan& p, const 
                               const void* r, const float* bias, int hidden, const void* q,
                               const void* k, const void* v, void* Kc, void* Vc, int32_t* cache_len,
                               uint8_t* gate, void* o, void* ws, hipStream_t s) {
-  hipError_t e = launch_route(Hn, r, bias, gate, nullptr, sh.B, 1, hidden, sh.G, sh.f32, s);
-  if (e != hipSuccess) return e;
   const int row16 = sh.Hkv * sh.d * (sh.f32 ? 4 : 2) / 16;
-  hipLaunchKernelGGL(append_kernel, dim3(sh.B), dim3(kAppendThreads), 0, s,
-                     static_cast<const uint4*>(k), static_cast<const uint4*>(v), static_cast<uint4*>(Kc),
-                     static_cast<uint4*>(Vc), cache_len, sh.Lmax, row16);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  auto k4 = static_cast<const uint4*>(k);
+  auto v4 = static_cast<const uint4*>(v);
+  auto K4 = static_cast<uint4*>(Kc);
+  auto V4 = static_cast<uint4*>(Vc);
+  if (sh.f32)
+    hipLaunchKernelGGL(step_prep_kernel<float>, dim3(sh.B), dim3(kStepThreads), 0, s,
+                       static_cast<const float*>(Hn), static_cast<const float*>(r), bias, gate, hidden,
+                       sh.G, k4, v4, K4, V4, cache_len, sh.Lmax, row16);
+  else
+    hipLaunchKernelGGL(step_prep_kernel<bf16_t>, dim3(sh.B), dim3(kStepThreads), 0, s,
+                       static_cast<const bf16_t*>(Hn), static_cast<const bf16_t*>(r), bias, gate, hidden,
+                       sh.G, k4, v4, K4, V4, cache_len, sh.Lmax, row16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   return launch_decode(sh, p, q, Kc, Vc, cache_len, gate, o, ws, s, nullptr);
 }
 

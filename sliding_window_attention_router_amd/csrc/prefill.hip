@@ -399,36 +399,75 @@ SWI_DEV int block_excl_scan(int v, int* sh, int& total) {
   return res;
 }
 
+// Per-unit chunk tables (first tile of chunk c, first item of chunk c, and
+// the unit's first item) are built in LDS when they fit, and written out once
+// at the end (the attention and merge kernels read them from global memory);
+// reading them from global memory inside the serial loops over chunks cost a
+// memory round trip per chunk.
+constexpr int kSchedLds = 4096;  // ints per LDS table
+constexpr int kSchedUnits = 1024;  // (batch, unit) entries of the LDS unit tables
+
 __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs a) {
   __shared__ long long red[kSchedThreads / 64];
+  __shared__ int scan_sh[33];
+  __shared__ int n_sh[kSchedLds], first_sh[kSchedLds], offset_sh[kSchedLds];
+  __shared__ int ubase_sh[kSchedUnits], mbase_sh[kSchedUnits + 1], ucnt_sh[kSchedUnits];
   SchedView sv(a);
   const int tid = threadIdx.x;
   const int nT = a.B * a.units * a.far_tiles;
   const int nbu = a.B * a.units;
   const int TT = a.far_tiles;
-  // active tiles of a unit: ceil(cnt / tpt_far)
-  auto active = [&](int bu) {
-    const int b = bu / a.units, u = bu - b * a.units;
-    const int c = far_count(a, b, (u * a.hpu) / a.HG);
-    return (c + a.tpt_far - 1) / a.tpt_far;
-  };
-  // pass 1: 64-key blocks of far work per tile (non-decreasing along the
-  // active tiles of a unit, since gathered positions ascend)
-  long long mine = 0;
-  for (int T_ = tid; T_ < nT; T_ += kSchedThreads) {
-    const int bu = T_ / TT, t = T_ - bu * TT;
-    const int b = bu / a.units, u = bu - b * a.units;
-    const int g = (u * a.hpu) / a.HG;
-    const int c = far_count(a, b, g);
-    const int ntok = min(a.tpt_far, c - t * a.tpt_far);
-    int blocks = 0;
-    if (ntok > 0) {
-      const int tlast = far_pos(a, b, g, t * a.tpt_far + ntok - 1);
-      const int fh = tlast - a.Wf;  // far keys [A, fh]
-      if (fh >= a.A) blocks = fh / kBN - a.A / kBN + 1;
+  const int ntab = nbu * a.cmax;
+  // every table in LDS when all fit, else every table in global memory
+  const bool in_lds = ntab <= kSchedLds && nT <= kSchedLds && nbu <= kSchedUnits;
+  int* n_items = in_lds ? n_sh : sv.n_items;
+  int* first = in_lds ? first_sh : sv.first;
+  int* offset = in_lds ? offset_sh : sv.offset;
+  int* unit_base = in_lds ? ubase_sh : sv.unit_base;
+  int* merge_base = in_lds ? mbase_sh : sv.merge_base;
+  // gathered rows of each (batch, unit): loaded once into LDS when they fit
+  const bool ucnt_lds = nbu <= kSchedUnits;
+  if (ucnt_lds)
+    for (int bu = tid; bu < nbu; bu += kSchedThreads) {
+      const int b = bu / a.units, u = bu - b * a.units;
+      ucnt_sh[bu] = far_count(a, b, (u * a.hpu) / a.HG);
     }
-    sv.n_items[T_] = blocks;
-    mine += blocks;
+  __syncthreads();
+  auto unit_count = [&](int bu) {
+    if (ucnt_lds) return ucnt_sh[bu];
+    const int b = bu / a.units, u = bu - b * a.units;
+    return far_count(a, b, (u * a.hpu) / a.HG);
+  };
+  // active tiles of a unit: ceil(count / tpt_far)
+  auto active = [&](int bu) { return (unit_count(bu) + a.tpt_far - 1) / a.tpt_far; };
+  // pass 1: 64-key blocks of far work per tile (non-decreasing along the
+  // active tiles of a unit, since gathered positions ascend).  Every thread
+  // issues the position loads of all its tiles before it uses any of them.
+  long long mine = 0;
+  constexpr int kLoads = 4;
+  for (int T0 = 0; T0 < nT; T0 += kLoads * kSchedThreads) {
+    int tlast[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int T_ = T0 + j * kSchedThreads + tid;
+      tlast[j] = -1;
+      if (T_ < nT) {
+        const int bu = T_ / TT, t = T_ - bu * TT;
+        const int b = bu / a.units, u = bu - b * a.units;
+        const int ntok = min(a.tpt_far, unit_count(bu) - t * a.tpt_far);
+        if (ntok > 0) tlast[j] = far_pos(a, b, (u * a.hpu) / a.HG, t * a.tpt_far + ntok - 1);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int T_ = T0 + j * kSchedThreads + tid;
+      if (T_ >= nT) continue;
+      int blocks = 0;
+      const int fh = tlast[j] - a.Wf;  // far keys [A, fh]
+      if (tlast[j] >= 0 && fh >= a.A) blocks = fh / kBN - a.A / kBN + 1;
+      n_items[T_] = blocks;
+      mine += blocks;
+    }
   }
   for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
   if ((tid & 63) == 0) red[tid >> 6] = mine;
@@ -437,62 +476,121 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
   for (int w = 0; w < kSchedThreads / 64; ++w) total_blocks += red[w];
   const int cb = int(max<long long>(kMinChunkBlocks, (total_blocks + a.target_items - 1) / a.target_items));
   // pass 2: chunks per tile
-  for (int T_ = tid; T_ < nT; T_ += kSchedThreads) sv.n_items[T_] = (sv.n_items[T_] + cb - 1) / cb;
+  for (int T_ = tid; T_ < nT; T_ += kSchedThreads) n_items[T_] = (n_items[T_] + cb - 1) / cb;
   __syncthreads();
   // pass 3: first tile holding chunk c (n_items steps up at tile t for the
   // chunks in [n(t-1), n(t)))
   for (int T_ = tid; T_ < nT; T_ += kSchedThreads) {
     const int bu = T_ / TT, t = T_ - bu * TT;
-    const int n = sv.n_items[T_];
-    const int nprev = t > 0 ? sv.n_items[T_ - 1] : 0;
-    for (int c = nprev; c < n; ++c) sv.first[bu * a.cmax + c] = t;
+    const int n = n_items[T_];
+    const int nprev = t > 0 ? n_items[T_ - 1] : 0;
+    for (int c = nprev; c < n; ++c) first[bu * a.cmax + c] = t;
   }
   __syncthreads();
-  // pass 4: per unit, offsets of its chunks (chunk c holds the active tiles
-  // from first[c] on), and the unit's item count
+  // pass 4: offset of chunk c inside its unit = sum over the unit's earlier
+  // chunks c' of (active tiles - first[c']) (chunk c' holds the active tiles
+  // from first[c'] on): one exclusive prefix sum over the flat (unit, chunk)
+  // table, less its value at the unit's first entry
+  {
+    int carry = 0;
+    for (int x0 = 0; x0 < ntab; x0 += kSchedThreads) {
+      const int x = x0 + tid;
+      int val = 0;
+      if (x < ntab) {
+        const int bu = x / a.cmax, c = x - bu * a.cmax;
+        const int nt = active(bu);
+        const int maxn = nt > 0 ? n_items[bu * TT + nt - 1] : 0;
+        val = c < maxn ? nt - first[x] : 0;
+      }
+      int tot;
+      const int ex = block_excl_scan(val, scan_sh, tot);
+      if (x < ntab) offset[x] = carry + ex;
+      carry += tot;
+    }
+  }
+  __syncthreads();
   for (int bu = tid; bu < nbu; bu += kSchedThreads) {
     const int nt = active(bu);
-    const int maxn = nt > 0 ? sv.n_items[bu * TT + nt - 1] : 0;
-    int run = 0;
-    for (int c = 0; c < maxn; ++c) {
-      sv.offset[bu * a.cmax + c] = run;
-      run += nt - sv.first[bu * a.cmax + c];
+    const int maxn = nt > 0 ? n_items[bu * TT + nt - 1] : 0;
+    // items of the unit: the offset of its last chunk (relative to the
+    // unit's first entry) plus that chunk's tile count
+    int items = 0;
+    if (maxn > 0) {
+      const int lastc = bu * a.cmax + maxn - 1;
+      items = offset[lastc] - offset[bu * a.cmax] + (nt - first[lastc]);
     }
-    sv.unit_base[bu] = run;  // item count for now
+    unit_base[bu] = items;  // item count for now
     // tiles with chunks: the unit's active tiles from first[0] on
-    sv.merge_base[bu] = maxn > 0 ? nt - sv.first[bu * a.cmax] : 0;  // count for now
+    merge_base[bu] = maxn > 0 ? nt - first[bu * a.cmax] : 0;  // count for now
   }
   __syncthreads();
   if (tid < 8) a.queue[tid] = 0;
   if (tid == 0) {
     int s = 0;
     for (int bu = 0; bu < nbu; ++bu) {
-      const int n = sv.unit_base[bu];
-      sv.unit_base[bu] = s;
+      const int n = unit_base[bu];
+      unit_base[bu] = s;
       s += n;
     }
     a.sched[0] = s;
     a.sched[1] = cb;
     int m = 0;
     for (int bu = 0; bu < nbu; ++bu) {
-      const int n = sv.merge_base[bu];
-      sv.merge_base[bu] = m;
+      const int n = merge_base[bu];
+      merge_base[bu] = m;
       m += n;
     }
-    sv.merge_base[nbu] = m;
+    merge_base[nbu] = m;
   }
   __syncthreads();
-  // pass 5: item list
+  // pass 5: item list (offsets relative to the unit), and the merge list
   for (int T_ = tid; T_ < nT; T_ += kSchedThreads) {
     const int bu = T_ / TT, t = T_ - bu * TT;
-    const int n = sv.n_items[T_];
+    const int n = n_items[T_];
+    const int ub = unit_base[bu], base = offset[bu * a.cmax];
     for (int c = 0; c < n; ++c) {
-      const int it = sv.item_of(bu, t, c, a.cmax);
+      const int x = bu * a.cmax + c;
+      const int it = ub + (offset[x] - base) + (t - first[x]);
       sv.item_tile[it] = T_;
       sv.item_chunk[it] = c;
     }
     // the merge list: tiles with chunks, unit by unit
-    if (n > 0) sv.merge_tile[sv.merge_base[bu] + t - sv.first[bu * a.cmax]] = T_;
+    if (n > 0) sv.merge_tile[merge_base[bu] + t - first[bu * a.cmax]] = T_;
+  }
+  // the tables for the attention and merge kernels (item_of), with offsets
+  // relative to the unit
+  if (in_lds) {
+    for (int x = tid; x < ntab; x += kSchedThreads) {
+      const int bu = x / a.cmax;
+      sv.first[x] = first_sh[x];
+      sv.offset[x] = offset_sh[x] - offset_sh[bu * a.cmax];
+    }
+    for (int T_ = tid; T_ < nT; T_ += kSchedThreads) sv.n_items[T_] = n_sh[T_];
+    for (int bu = tid; bu <= nbu; bu += kSchedThreads) {
+      if (bu < nbu) sv.unit_base[bu] = ubase_sh[bu];
+      sv.merge_base[bu] = mbase_sh[bu];
+    }
+  } else {
+    __syncthreads();
+    int keep[4];
+    // relative offsets in place: read every unit base first (at most
+    // 4 * kSchedThreads entries per thread pass), then subtract
+    for (int x0 = 0; x0 < ntab; x0 += 4 * kSchedThreads) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int x = x0 + j * kSchedThreads + tid;
+        keep[j] = x < ntab ? sv.offset[(x / a.cmax) * a.cmax] : 0;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int x = x0 + j * kSchedThreads + tid;
+        if (x < ntab && x % a.cmax != 0) sv.offset[x] -= keep[j];
+      }
+      __syncthreads();
+    }
+    // unit starts last (every other entry of the unit has read them)
+    for (int bu = tid; bu < nbu; bu += kSchedThreads) sv.offset[bu * a.cmax] = 0;
   }
 }
 

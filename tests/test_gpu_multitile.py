@@ -99,3 +99,25 @@ def test_every_row_multitile_both_branch():
     assert err <= TOL["bf16"]
     assert np.all(derr <= tol)
     assert np.all(dg[:, :W] == 0.0)
+
+
+def test_many_units_schedule_tables_in_global_memory():
+    """B=32 sequences x 32 KV heads (MHA) at N=2048: 1024 (sequence, unit)
+    pairs x 5 chunk slots exceed the far schedule's LDS tables, so the
+    schedule builds them in global memory.  Sampled rows of every sequence
+    against the oracle."""
+    B, N, H, d, W, p = 32, 2048, 32, 64, 64, 0.1
+    say(f"schedule in global memory: B={B} N={N} MHA {H} heads d={d} W={W} p={p}")
+    w = synth.long_prefill(seed=46, B=B, N=N, Hq=H, Hkv=H, d=d, W=W, p=p)
+    bf = torch.bfloat16
+    O, _ = swa().prefill(dev(w.Q, bf), dev(w.K, bf), dev(w.V, bf), dev(w.gate), W)
+    torch.cuda.synchronize()
+    Oh = host(O)
+    rows = np.unique(np.concatenate([np.arange(0, 80), np.arange(N - 40, N),
+                                     np.random.default_rng(47).integers(0, N, 120)]))
+    err = 0.0
+    for b in range(B):
+        ref = oracle.prefill(w.Q[b:b + 1], w.K[b:b + 1], w.V[b:b + 1], w.gate[b:b + 1], W, rows=rows)["O"]
+        err = max(err, max_abs(Oh[b:b + 1, rows], ref))
+    say(f"  {rows.size} rows x {B} sequences x {H} heads: max-abs {err:.3e}")
+    assert err <= TOL["bf16"]
