@@ -321,6 +321,36 @@ int swiattn_decode_anchored(const void* q, const void* Kc, const void* Vc,
                             swiattn_stream_t stream, const swiattn_events_t* events);
 
 /*
+ * swiattn_prefill_branches - both-branch prefill that also returns the two
+ * branch outputs of every token, for training.
+ * (SwiAttn report, section 2: the layer output is
+ * O = sigma * O_FULL + (1 - sigma) * O_SWA, and the straight-through gate
+ * passes the gradient <dO, O_FULL - O_SWA> to the router, so a training step
+ * needs both branch outputs of every token; swiattn_router_backward takes
+ * them.)
+ *
+ *   Q, K, V, gate, W, anchors, scale, dtype: as swiattn_prefill_anchored in
+ *                both-branch mode (idx, cnt are not used)
+ *   O      [B,N,Hq,d]  dtype  out: gate ? O_FULL : O_SWA
+ *   diff   [B,N]       float  out: as swiattn_prefill's both-branch distance
+ *   O_full [B,N,Hq,d]  dtype  out: the full-branch output of every token
+ *   O_swa  [B,N,Hq,d]  dtype  out: the window-branch output of every token
+ *   ws, ws_bytes: at least swiattn_prefill_workspace_size(...,
+ *   SWIATTN_FLAG_BOTH_BRANCH) bytes, clobbered; events as swiattn_prefill_ex
+ *   in both-branch mode (may be NULL).
+ * One pass: the window tiles write O_SWA (and O_FULL of rows whose window
+ * and anchors hold every key [0, i]), the merge writes O_FULL of the other
+ * rows.  O, O_FULL and O_SWA hold the same values as the gated output where
+ * the gate picks them.  Outputs must not overlap each other or the inputs.
+ * Errors: as swiattn_prefill, plus INVALID_ARG for a NULL output.
+ */
+int swiattn_prefill_branches(const void* Q, const void* K, const void* V, const uint8_t* gate,
+                             void* O, float* diff, void* O_full, void* O_swa, int B, int N, int Hq,
+                             int Hkv, int G, int d, int W, int anchors, float scale,
+                             swiattn_dtype_t dtype, void* ws, size_t ws_bytes, swiattn_stream_t stream,
+                             const swiattn_events_t* events);
+
+/*
  * swiattn_prefill_offset / swiattn_decode_offset - the anchored calls with a
  * window offset, for stacked layers whose windows are staggered.
  * (weimeta glossary "滑窗注意力 Sliding Window Attention 是什么？", section

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     lib,
     prefill,
     prefill_backward,
+    prefill_branches,
     prefill_workspace_size,
     regularizer,
     route,

@@ -21,6 +21,7 @@ __all__ = [
     "route",
     "regularizer",
     "prefill",
+    "prefill_branches",
     "decode",
     "decode_step",
     "decode_noalloc",
@@ -50,6 +51,7 @@ SYMBOLS = {
     "swiattn_prefill_anchored": (_i32, [_vp] * 8 + [_i32] * 8 + [_f32, _i32, _u32, _vp, _sz, _vp, _vp]),
     "swiattn_decode_anchored": (_i32, [_vp] * 6 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp, _vp]),
     "swiattn_decode_step_anchored": (_i32, [_vp] * 11 + [_i32] * 9 + [_f32, _i32, _vp, _sz, _vp]),
+    "swiattn_prefill_branches": (_i32, [_vp] * 8 + [_i32] * 8 + [_f32, _i32, _vp, _sz, _vp, _vp]),
     "swiattn_prefill_offset": (_i32, [_vp] * 8 + [_i32] * 9 + [_f32, _i32, _u32, _vp, _sz, _vp, _vp]),
     "swiattn_decode_offset": (_i32, [_vp] * 6 + [_i32] * 9 + [_f32, _i32, _vp, _sz, _vp, _vp]),
     "swiattn_router_backward_workspace_size": (_sz, [_i32] * 4),
@@ -364,6 +366,42 @@ def prefill(Q, K, V, gate, W, *, idx=None, cnt=None, scale=None, both_branch=Fal
                                   _p(ws), ws.numel(), _stream(dev), _events(events))
     _check(rc, "swiattn_prefill")
     return out, diff
+
+
+def prefill_branches(Q, K, V, gate, W, *, scale=None, anchors=0, out=None, workspace=None, events=None):
+    """Both-branch prefill that also returns the branch outputs
+    (swiattn_prefill_branches).  Returns (O, diff, O_full, O_swa); out, if
+    given, is that tuple of preallocated tensors."""
+    L = lib()
+    _need(Q, "Q")
+    code = _dtype_code(Q)
+    B, N, Hq, d = Q.shape
+    dev = Q.device
+    _need(K, "K", dtype=Q.dtype, device=dev)
+    if K.dim() != 4 or K.shape[0] != B or K.shape[1] != N or K.shape[3] != d:
+        raise ValueError("K must be [B,N,Hkv,d]")
+    Hkv = K.shape[2]
+    _need(V, "V", shape=K.shape, dtype=Q.dtype, device=dev)
+    _need(gate, "gate", dtype=torch.uint8, device=dev)
+    if gate.dim() != 3 or gate.shape[:2] != (B, N):
+        raise ValueError("gate must be [B,N,G]")
+    G = gate.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = (torch.empty_like(Q), torch.empty((B, N), dtype=torch.float32, device=dev), torch.empty_like(Q),
+               torch.empty_like(Q))
+    O, diff, Of, Os = out
+    for t, name in ((O, "O"), (Of, "O_full"), (Os, "O_swa")):
+        _need(t, name, shape=Q.shape, dtype=Q.dtype, device=dev)
+    _need(diff, "diff", shape=(B, N), dtype=torch.float32, device=dev)
+    nbytes = int(L.swiattn_prefill_workspace_size(B, N, Hq, Hkv, G, d, W, code, FLAG_BOTH_BRANCH))
+    ws = _workspace(nbytes, dev, workspace)
+    rc = L.swiattn_prefill_branches(_p(Q), _p(K), _p(V), _p(gate), _p(O), _p(diff), _p(Of), _p(Os), B, N, Hq,
+                                    Hkv, G, d, W, int(anchors), float(scale), code, _p(ws), ws.numel(),
+                                    _stream(dev), _events(events))
+    _check(rc, "swiattn_prefill_branches")
+    return O, diff, Of, Os
 
 
 def decode(q, Kc, Vc, cache_len, gate, W, *, scale=None, out=None, workspace=None, events=None,

@@ -139,6 +139,24 @@ int swiattn_prefill_offset(const void* Q, const void* K, const void* V, const ui
                                     events ? events->ev : nullptr));
 }
 
+int swiattn_prefill_branches(const void* Q, const void* K, const void* V, const uint8_t* gate,
+                             void* O, float* diff, void* O_full, void* O_swa, int B, int N, int Hq,
+                             int Hkv, int G, int d, int W, int anchors, float scale,
+                             swiattn_dtype_t dtype, void* ws, size_t ws_bytes, swiattn_stream_t stream,
+                             const swiattn_events_t* events) {
+  swi::PrefillShape sh;
+  swi::PrefillPlan p;
+  const int rc = prefill_shape(B, N, Hq, Hkv, G, d, W, scale, dtype, SWIATTN_FLAG_BOTH_BRANCH, &sh, &p);
+  if (rc != SWIATTN_OK) return rc;
+  if (anchors < 0) return SWIATTN_ERR_INVALID_ARG;
+  sh.A = anchors < N ? anchors : N;
+  if (!Q || !K || !V || !gate || !O || !diff || !O_full || !O_swa) return SWIATTN_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < p.bytes) return SWIATTN_ERR_WORKSPACE;
+  return hip_rc(swi::launch_prefill(sh, p, Q, K, V, gate, nullptr, nullptr, O, diff, ws,
+                                    reinterpret_cast<hipStream_t>(stream),
+                                    events ? events->ev : nullptr, O_full, O_swa));
+}
+
 int swiattn_prefill_anchored(const void* Q, const void* K, const void* V, const uint8_t* gate,
                              const int32_t* idx, const int32_t* cnt, void* O, float* diff, int B,
                              int N, int Hq, int Hkv, int G, int d, int W, int anchors,

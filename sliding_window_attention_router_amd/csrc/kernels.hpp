@@ -61,11 +61,12 @@ struct PrefillPlan {
 };
 
 bool plan_prefill(const PrefillShape& sh, PrefillPlan* p);
-// ev: optional array of 6 hipEvent_t recorded at stage boundaries (may be null)
+// ev: optional array of 6 hipEvent_t recorded at stage boundaries (may be null);
+// O_full, O_swa: optional branch outputs of both-branch mode (may be null)
 hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const void* Q,
                           const void* K, const void* V, const uint8_t* gate, const int32_t* idx,
                           const int32_t* cnt, void* O, float* diff, void* ws, hipStream_t s,
-                          void* const* ev);
+                          void* const* ev, void* O_full = nullptr, void* O_swa = nullptr);
 
 // ---- decode -------------------------------------------------------------
 struct DecodeShape {

@@ -62,6 +62,8 @@ struct PrefillArgs {
   float* part_lse;  // [max_items][kRows]
   float* diffp;     // [B,Hq,N] per-head squared distance (both-branch mode)
   float* diff;      // [B,N]
+  void* O_full;     // [B,N,Hq,D] both-branch mode, optional: O_FULL of every row
+  void* O_swa;      // [B,N,Hq,D] both-branch mode, optional: O_SWA of every row
   int* queue;       // [8] window-tile queue positions (zeroed by the schedule kernel)
   int B, N, Hq, Hkv, G, W;
   int A;    // global anchor keys of the window branch (0 = none)
@@ -254,6 +256,19 @@ struct TileLds {
   static constexpr int kBuf1 = kDma ? LdsDma<D>::kBytes : 16;
 };
 
+// Window-pass results of one row that also go to the optional branch
+// outputs of both-branch mode: O_SWA of every row, and O_FULL of the rows
+// whose window and anchors already hold every key [0, i] (no far part; the
+// merge writes O_FULL of the other rows).
+template <typename T, int MD>
+SWI_DEV void store_branches(const PrefillArgs& a, int b, int tok, int h, const f32x16 (&acc)[MD],
+                            float inv, int g) {
+  constexpr int D = MD * 32;
+  const int64_t row = ((int64_t(b) * a.N + tok) * a.Hq + h) * D;
+  if (a.O_swa) store_row<MD>(static_cast<T*>(a.O_swa) + row, acc, inv, g);
+  if (a.O_full && tok - a.Wf < a.A) store_row<MD>(static_cast<T*>(a.O_full) + row, acc, inv, g);
+}
+
 // Key ranges of one row in the window pass: the window [lo, hi] and the
 // anchors [0, ahi].  With a window offset o the window is that of query
 // i - o, [max(0, i-o-W+1), i-o] (empty for i < o); a gate=1 row then also
@@ -356,6 +371,7 @@ SWI_DEV void band_tile(const PrefillArgs& a, char* buf0, char* buf1, int lin) {
     if (valid[t]) {
       T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok[t]) * a.Hq + h[t]) * D;
       store_row<Core::MD>(orow, c.acc_of(t), inv, g);
+      store_branches<T, Core::MD>(a, b, tok[t], h[t], c.acc_of(t), inv, g);
       if (g == 0) a.lse_s[(int64_t(b) * a.Hq + h[t]) * a.N + tok[t]] = lse2;
       if (g == 0 && a.diffp) a.diffp[(int64_t(b) * a.Hq + h[t]) * a.N + tok[t]] = 0.f;
     }
@@ -815,6 +831,7 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
       const int h = t.kvh * a.HK + hh;
       T* orow = static_cast<T*>(a.O) + ((int64_t(t.b) * a.N + tok) * a.Hq + h) * D;
       store_row<Core::MD>(orow, c.acc_of(0), inv, g);
+      store_branches<T, Core::MD>(a, t.b, tok, h, c.acc_of(0), inv, g);
       if (g == 0) a.lse_s[(int64_t(t.b) * a.Hq + h) * a.N + tok] = lse2;
       if (g == 0 && a.diffp) a.diffp[(int64_t(t.b) * a.Hq + h) * a.N + tok] = 0.f;
     }
@@ -883,7 +900,7 @@ SWI_DEV float sq_distance(const float (&x)[n], const float (&y)[n]) {
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 256;
 constexpr int kMergeTPR = 8;  // threads per row
-template <typename T, int D>
+template <typename T, int D, bool kBoth>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PrefillArgs a) {
   constexpr int kRowsWG = kMergeThreads / kMergeTPR;  // rows per work unit
   constexpr int kParts = kRows / kRowsWG;
@@ -942,7 +959,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PrefillArgs a) {
 #pragma unroll
     for (int e = 0; e < CPT; ++e) o[e] *= inv;
     bool write = true;
-    if (a.diffp) {
+    if constexpr (kBoth) {
       // squared distance to the window output, summed over the row's 8
       // threads (lanes 8k .. 8k+7 of the wave) in a fixed order
       float dd = sq_distance<CPT>(o, os);
@@ -956,6 +973,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i4 = 0; i4 < CPT / 4; ++i4)
         store4(orow + i4 * 4, f32x4{o[i4 * 4], o[i4 * 4 + 1], o[i4 * 4 + 2], o[i4 * 4 + 3]});
+    }
+    if (kBoth && a.O_full) {
+      T* frow = static_cast<T*>(a.O_full) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D + c0;
+#pragma unroll
+      for (int i4 = 0; i4 < CPT / 4; ++i4)
+        store4(frow + i4 * 4, f32x4{o[i4 * 4], o[i4 * 4 + 1], o[i4 * 4 + 2], o[i4 * 4 + 3]});
     }
   }
 }
@@ -1054,7 +1077,10 @@ static hipError_t run_prefill(const PrefillShape& sh, const PrefillPlan& p, Pref
                      s, a);
   SWI_TRY(hipGetLastError());
   SWI_TRY(mark(ev, 2, s));
-  hipLaunchKernelGGL((merge_kernel<T, D>), dim3(8 * cus), dim3(kMergeThreads), 0, s, a);
+  if (sh.both_branch)
+    hipLaunchKernelGGL((merge_kernel<T, D, true>), dim3(8 * cus), dim3(kMergeThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((merge_kernel<T, D, false>), dim3(8 * cus), dim3(kMergeThreads), 0, s, a);
   SWI_TRY(hipGetLastError());
   SWI_TRY(mark(ev, 3, s));
   if (sh.both_branch) {
@@ -1070,7 +1096,7 @@ static hipError_t run_prefill(const PrefillShape& sh, const PrefillPlan& p, Pref
 hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const void* Q,
                           const void* K, const void* V, const uint8_t* gate, const int32_t* idx,
                           const int32_t* cnt, void* O, float* diff, void* ws, hipStream_t s,
-                          void* const* ev) {
+                          void* const* ev, void* O_full, void* O_swa) {
   char* w = static_cast<char*>(ws);
   PrefillArgs a;
   a.Q = Q;
@@ -1089,6 +1115,8 @@ hipError_t launch_prefill(const PrefillShape& sh, const PrefillPlan& p, const vo
   a.all_rows = sh.both_branch ? 1 : 0;
   a.target_items = p.target_items;
   a.diff = diff;
+  a.O_full = sh.both_branch ? O_full : nullptr;
+  a.O_swa = sh.both_branch ? O_swa : nullptr;
   a.B = sh.B;
   a.N = sh.N;
   a.Hq = sh.Hq;
