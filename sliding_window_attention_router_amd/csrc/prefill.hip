@@ -768,7 +768,6 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
              t.kb(0), a.N, tid);
   int s = 0;  // blocks streamed so far: block s sits in buffer s % 2
   int next_raw = 0;  // thread 0: raw position of the pending claim on queue qx
-  if (tid == 0) next_raw = claim(a.queue, qx);
   bool q_pref = false;
   while (true) {
     const int tok = t.q0 + slot;
@@ -787,10 +786,15 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
     }
     const T* Kb = static_cast<const T*>(a.K) + kv_off(t);
     const T* Vb = static_cast<const T*>(a.V) + kv_off(t);
-    // the next id is published at step pub and read one barrier later
+    // the next tile is claimed at step cl, its id resolved and published at
+    // step pub and read one barrier later (the claim is issued only a few
+    // blocks before the tile ends: claimed a whole tile ahead, the first
+    // workers to start took two tiles each when there are barely more tiles
+    // than workers, and the workers that started later found no tile)
     const int nbt = t.total();
     const int pub = nbt >= 2 ? nbt - 2 : 0;
     const int rd = nbt >= 2 ? pub + 1 : 0;
+    const int cl = pub >= 2 ? pub - 2 : 0;
     int nlin = -1;
     BandTile nt;
     nt.set(a, 0);
@@ -799,14 +803,12 @@ SWI_DEV void band_worker(const PrefillArgs& a, char* buf0, char* buf1) {
       char* nxt = (s & 1) ? buf0 : buf1;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      if (n == cl && tid == 0) next_raw = claim(a.queue, qx);
       if (n == pub && tid == 0) s_next = resolve(a.queue, tq, qx, next_raw);
       if (nbt < 2) __syncthreads();
       if (n == rd) {
         nlin = __builtin_amdgcn_readfirstlane(s_next);
         if (nlin >= 0) nt.set(a, nlin);
-        // claim the tile after that one now; it is resolved when the next
-        // tile publishes it
-        if (tid == 0 && nlin >= 0) next_raw = claim(a.queue, qx);
       }
       if (n + 1 < nbt)
         Dma::issue(nxt, Kb, Vb, rs, t.kb(n + 1), a.N, tid);
