@@ -322,30 +322,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_col_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV on the matrix cores (bfloat16).  A workgroup owns kKvKeys keys of
-// one KV head, 32 per wave; each wave keeps its keys' K and V rows in
-// registers as MFMA B operands.  For every query head of the KV head the
-// workgroup walks tiles of kRT query rows: first the window rows
-// [k0, min(N, k0 + kKvKeys - 1 + W)) (any gate; masked per pair), then the
-// gate=1 rows past them, gathered from the compacted list.  The four waves
-// share each tile: Q and dO rows are staged once in LDS (double-buffered,
-// one barrier per tile) with each row's LSE, D and visible key range.
-//   S  = Q K^T,  dP = dO V^T         (per 32-row half: 32 rows x 32 keys,
-//                                      k = channels)
-//   P  = 2^(S sl2 - LSE) on visible pairs,  dS = P (dP - D)
-//   dV^T += dO^T P,  dK^T += Q^T dS  (channels x 32 keys, k = rows)
-// The 32x32 accumulator of S gives lane l the key l % 32 and rows
-// 8(i/4) + 4(l/32) + i%4; those are exactly the contraction slots a B
-// operand of the second products holds (rows permuted the same way on the
-// A side), so P and dS feed the next MFMAs from registers, and the
-// transposed A operands (dO^T, Q^T) come from ds_read_b64_tr_b16: within 16
-// lanes, source lane 4r + k points at row r, channels c0 + 4k .. c0 + 4k + 3,
-// and lane i receives channel c0 + i of rows 0..3.
-// LDS rows are XOR-swizzled by 16-byte chunk so that both the plain 16-byte
-// reads (16 lanes, 16 consecutive rows, one chunk) and the transposing
+// Staged K/V blocks of the dQ kernel and Q/dO row tiles (kRT rows).  LDS rows
+// are XOR-swizzled by 16-byte chunk (KvTile) so that the dQ kernel's plain
+// 16-byte reads (16 lanes, 16 consecutive rows, one chunk) and transposing
 // reads (32 lanes, 4 rows x 4 chunks) hit distinct banks.
 // ---------------------------------------------------------------------------
-constexpr int kKvKeys = 128;  // keys per workgroup (4 waves x 32)
 constexpr int kRT = 64;       // query rows per tile (a multiple of 32)
 
 template <int D>
@@ -369,41 +350,112 @@ SWI_DEV s16x4 lds_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV on the matrix cores (bfloat16), with v_mfma_f32_16x16x32_bf16.  A
+// workgroup owns kKvKeys keys of one KV head, 16 per wave; each wave keeps
+// its keys' K and V rows as MFMA B operands (lane l: key l % 16, channels
+// 8 (l / 16) .. + 7 of each 32-channel step).  For every query head of the
+// KV head the workgroup walks tiles of kRT query rows: first the window rows
+// [k0, min(N, k0 + kKvKeys - 1 + W)) (any gate; masked per pair), then the
+// gate=1 rows past them, gathered from the compacted list.  The four waves
+// share each tile: its Q and dO rows are copied straight from global memory
+// into LDS (global_load_lds_dwordx4, double-buffered, one barrier per tile;
+// the lane -> source mapping applies the swizzle), with each row's LSE, D
+// and visible key range beside them.
+//   S  = Q K^T,  dP = dO V^T         (16-row tiles x 16 keys, k = channels)
+//   P  = 2^(S sl2 - LSE) on visible pairs,  dS = P (dP - D)
+//   dV^T += dO^T P,  dK^T += Q^T dS  (16-channel tiles x 16 keys, k = rows)
+// The 16x16 accumulator of S gives lane l the key l % 16 and rows
+// 4 (l / 16) + i of its 16-row tile; two tiles fill the eight contraction
+// slots a B operand of the second products holds (slot 8g + i: row
+// 32 st + 4g + i; slot 8g + 4 + i: row 32 st + 16 + 4g + i), so P and dS go
+// from registers to the next MFMAs, and the transposed A operands (dO^T,
+// Q^T) come from two ds_read_b64_tr_b16 each with the same row order
+// (within 16 lanes, source lane 4r + k points at row r, channels
+// c0 + 4k .. c0 + 4k + 3, and lane i receives channel c0 + i of rows
+// 0..3).  With 221 VGPRs a wave (d = 128; no AGPRs, no scratch) two
+// workgroups share a CU: two waves per SIMD, so one wave's exponentials and
+// conversions can overlap the other's products.
+// Layout of the row tiles (Kv16Tile), from LDS bank-conflict counts measured
+// on gfx950 (64 banks of 4 bytes; ds_read_b128 serves the 16 lanes of a
+// half-wave whose lane bits 2..4 have the same parity together, 8-byte reads
+// serve a half-wave at a time): chunk c (16 bytes) of row r goes to plane
+// c % 4, at r * (D / 2) bytes plus 16 * ((c / 4) ^ x(r, c)) inside the plane,
+// with x = ((r / 4) % 2) + 2 (c % 2) for d = 128 and x = c % 2 for d = 64.
+// Planes start at multiples of 256 bytes, so only the row and the slot pick
+// the banks.  A plain operand read (lane: row 16 rt + l % 16, chunk
+// 4 ks + l / 16) then finds the four lanes of a b128 group with equal l % 4
+// on four different slots, and a half-wave's transposing reads (8 rows x two
+// adjacent chunks x two 8-byte halves) on 32 different bank pairs.  (Whole
+// rows with an XOR swizzle, or planes whose slot ignores either the row or
+// the chunk parity, left one of the two reads with a two-way conflict.)
+// ---------------------------------------------------------------------------
+constexpr int kKvKeys = 64;  // keys per workgroup (4 waves x 16)
+
 template <int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(BwdArgs a) {
-  using L = KvTile<D>;
-  constexpr int KS = D / 16;  // k-steps of the channel contractions
-  constexpr int MD = D / 32;  // 32-channel tiles of dK^T, dV^T
+struct Kv16Tile {
+  static constexpr int kRowB = 2 * D;
+  static constexpr int kMat = kRT * kRowB;           // one staged matrix (Q or dO)
+  static constexpr int kInfo = 2 * kMat;             // lse2, D, first key, last key: [4][kRT]
+  static constexpr int kBytes = kInfo + 4 * kRT * 4;
+  static constexpr int kCopies = kMat / 1024;        // 1 KB direct copies per matrix
+  static constexpr int kPerWave = kCopies / (kBwdThreads / kWave);
+  static_assert(kPerWave >= 1 && kCopies % (kBwdThreads / kWave) == 0, "tile copies");
+  static constexpr int kPlaneRowB = kRowB / 4;       // bytes of a row in one plane
+  static constexpr int kPlaneB = kRT * kPlaneRowB;   // bytes of one plane
+  SWI_DEV static constexpr int x(int row, int chunk) {
+    return D == 128 ? (((row >> 2) & 1) | ((chunk & 1) << 1)) : (chunk & 1);
+  }
+  SWI_DEV static constexpr int pos(int row, int chunk) {
+    return (chunk & 3) * kPlaneB + row * kPlaneRowB + (((chunk >> 2) ^ x(row, chunk)) << 4);
+  }
+  // row and chunk held at byte offset o of a staged matrix (inverse of pos)
+  SWI_DEV static constexpr int row_at(int o) { return (o % kPlaneB) / kPlaneRowB; }
+  SWI_DEV static constexpr int chunk_at(int o) {
+    const int plane = o / kPlaneB, r = row_at(o), slot = (o % kPlaneRowB) >> 4;
+    return 4 * (slot ^ x(r, plane)) + plane;
+  }
+};
+
+#define SWI_BWD_GLOBAL(p) ((__attribute__((address_space(1))) void*)(p))
+#define SWI_BWD_LOCAL(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma_kernel(BwdArgs a) {
+  using L = Kv16Tile<D>;
+  constexpr int KS = D / 32;  // 32-channel steps of the score products
+  constexpr int CT = D / 16;  // 16-channel tiles of dK^T, dV^T
+  constexpr int RT = kRT / 16;  // 16-row tiles of a row tile
+  static_assert(kRT == 64, "two 32-row steps per row tile");
   __shared__ __attribute__((aligned(16))) char lds[2][L::kBytes];
   __shared__ int rowbuf[2][kRT];  // query row of each slot of the next tiles (-1: padding)
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int rl = lane & 31, hf = lane >> 5;
+  const int kl = lane & 15, grp = lane >> 4;
   const int nbk = a.B * a.Hkv;
   const int kblk = blockIdx.x / nbk, bk = blockIdx.x % nbk;  // heaviest key blocks first
   const int b = bk / a.Hkv, kvh = bk % a.Hkv;
   const int k0 = kblk * kKvKeys;
-  const int j = k0 + wave * 32 + rl;  // this lane's key
+  const int j = k0 + wave * 16 + kl;  // this lane's key
   const int jc = min(j, a.N - 1);
   const bf16_t* Qp = static_cast<const bf16_t*>(a.Q);
   const bf16_t* dOp = static_cast<const bf16_t*>(a.dO);
   bf16x8 kreg[KS], vreg[KS];
   {
-    const int64_t off = ((int64_t(b) * a.N + jc) * a.Hkv + kvh) * D + 8 * hf;
+    const int64_t off = ((int64_t(b) * a.N + jc) * a.Hkv + kvh) * D + 8 * grp;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kreg[ks] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16_t*>(a.K) + off + 16 * ks);
-      vreg[ks] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16_t*>(a.V) + off + 16 * ks);
+      kreg[ks] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16_t*>(a.K) + off + 32 * ks);
+      vreg[ks] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16_t*>(a.V) + off + 32 * ks);
     }
   }
-  f32x16 dk[MD], dv[MD];
+  f32x4 dk[CT], dv[CT];
 #pragma unroll
-  for (int md = 0; md < MD; ++md) dk[md] = dv[md] = f32x16{};
+  for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = f32x4{};
   const int wend = int(min<int64_t>(a.N, int64_t(k0) + kKvKeys - 1 + a.W));  // window rows end here
   const int nwt = (wend - k0 + kRT - 1) / kRT;
   const int64_t qrs = int64_t(a.Hq) * D;  // elements between query rows
-  // transposing-read lane roles: row r of a 4-row group, channel quad kq,
-  // 16-channel half c16 of a 32-channel tile
-  const int tr_r = (lane >> 2) & 3, tr_kq = lane & 3, tr_c16 = (lane >> 4) & 1;
+  // transposing-read lane roles: row r of a 4-row group, channel quad kq
+  const int tr_r = (lane >> 2) & 3, tr_kq = lane & 3;
   for (int hh = 0; hh < a.HK; ++hh) {
     const int h = kvh * a.HK + hh, g = h / a.HG;
     const int32_t* list = a.idx + (int64_t(b) * a.G + g) * a.N;
@@ -415,15 +467,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(BwdArgs a) {
     const float* lrow = a.lse2 + (int64_t(b) * a.Hq + h) * a.N;
     const float* drow = a.Drow + (int64_t(b) * a.Hq + h) * a.N;
     const uint8_t* grow = a.gate + int64_t(b) * a.N * a.G + g;
-    // Row indices run one tile ahead of the row loads: the gathered rows of
-    // tile t + 2 are looked up in the list while tile t is computed and kept
-    // in LDS (rowbuf), so the loads of a tile never wait on a list lookup.
-    // Every load is unconditional (clamped to a valid row) and consumed in
-    // the iteration that issues it; padding slots are zeroed when the tile
-    // is written to LDS.
-    // (branch-free: the list is read for window tiles too, at a clamped
-    // index, so the looked-up value is never merged with another one while
-    // its load is in flight)
+    // Row indices run one tile ahead of the copies: the rows of tile t + 2
+    // are looked up while tile t is computed and kept in LDS (rowbuf).  The
+    // list is read for window tiles too, at a clamped index (branch-free).
     int fw = 0, fl = 0;
     bool fok = false, fwin = true;
     const auto fetch_row = [&](int t) {  // slot tid % kRT of tile t
@@ -437,43 +483,45 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(BwdArgs a) {
     const auto put_row = [&](int* rb) {
       if (tid < kRT) rb[tid] = fok ? (fwin ? fw : fl) : -1;
     };
-    u32x4 sq[L::kPer], sd[L::kPer];
-    bool sok[L::kPer + 1];
-    float s_l = 0.f, s_d = 0.f;
-    int s_row = 0;
-    uint8_t s_g = 0;
-    const auto load_tile = [&](const int* rb) {
-#pragma unroll
-      for (int p = 0; p < L::kPer; ++p) {
-        const int u = tid + p * kBwdThreads, m = u / L::kCPR, c = u % L::kCPR;
-        const int r = rb[m];
-        sok[p] = r >= 0;
-        const int rc = r >= 0 ? r : 0;
-        sq[p] = *reinterpret_cast<const u32x4*>(qh + int64_t(rc) * qrs + 8 * c);
-        sd[p] = *reinterpret_cast<const u32x4*>(dh + int64_t(rc) * qrs + 8 * c);
-      }
-      const int r = rb[tid % kRT];
-      sok[L::kPer] = r >= 0;
-      s_row = r >= 0 ? r : 0;
-      s_l = lrow[s_row];
-      s_d = drow[s_row];
-      s_g = grow[int64_t(s_row) * a.G];
-    };
-    const auto store_tile = [&](char* buf) {
-      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int p = 0; p < L::kPer; ++p) {
-        const int u = tid + p * kBwdThreads, m = u / L::kCPR, c = u % L::kCPR;
-        *reinterpret_cast<u32x4*>(buf + L::pos(m, c)) = sok[p] ? sq[p] : z;
-        *reinterpret_cast<u32x4*>(buf + L::kMat + L::pos(m, c)) = sok[p] ? sd[p] : z;
-      }
+    // each row's LSE, D and visible keys (wave 0, one row per lane); the
+    // loads are issued before a tile's copies so that waiting for them
+    // leaves the copies in flight
+    float i_l = 0.f, i_d = 0.f;
+    int i_row = 0, i_ok = 0;
+    uint8_t i_g = 0;
+    const auto load_info = [&](const int* rb) {
       if (tid < kRT) {
-        const bool ok = sok[L::kPer];
+        const int r = rb[tid];
+        i_ok = r >= 0;
+        i_row = r >= 0 ? r : k0;
+        i_l = lrow[i_row];
+        i_d = drow[i_row];
+        i_g = grow[int64_t(i_row) * a.G];
+      }
+    };
+    const auto store_info = [&](char* buf) {
+      if (tid < kRT) {
         float* info = reinterpret_cast<float*>(buf + L::kInfo);
-        info[tid] = ok ? s_l : __builtin_huge_valf();
-        info[kRT + tid] = ok ? s_d : 0.f;
-        reinterpret_cast<int*>(info)[2 * kRT + tid] = ok ? (s_g != 0 ? 0 : s_row - a.W + 1) : 0;
-        reinterpret_cast<int*>(info)[3 * kRT + tid] = ok ? s_row : -1;
+        info[tid] = i_ok ? i_l : __builtin_huge_valf();
+        info[kRT + tid] = i_ok ? i_d : 0.f;
+        reinterpret_cast<int*>(info)[2 * kRT + tid] = i_ok ? (i_g != 0 ? 0 : i_row - a.W + 1) : 0;
+        reinterpret_cast<int*>(info)[3 * kRT + tid] = i_ok ? i_row : -1;
+      }
+    };
+    // the copies of one tile: copy m covers LDS bytes [1024 m, 1024 m + 1024)
+    // of each matrix; lane i writes 16 bytes at 16 i, which hold chunk
+    // chunk_at(...) of row row_at(...) (padding slots read a valid row; their
+    // pairs are masked by the info)
+    const auto issue_tile = [&](char* buf, const int* rb) {
+#pragma unroll
+      for (int i = 0; i < L::kPerWave; ++i) {
+        const int m = wave * L::kPerWave + i;
+        const int byte = m * 1024 + lane * 16;
+        const int row = rb[L::row_at(byte)];
+        const int64_t src = int64_t(row >= 0 ? row : k0) * qrs + 8 * L::chunk_at(byte);
+        __builtin_amdgcn_global_load_lds(SWI_BWD_GLOBAL(qh + src), SWI_BWD_LOCAL(buf + m * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(SWI_BWD_GLOBAL(dh + src), SWI_BWD_LOCAL(buf + L::kMat + m * 1024), 16,
+                                         0, 0);
       }
     };
     // rows of tiles 0 and 1, then tile 0 itself
@@ -484,91 +532,92 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(BwdArgs a) {
       put_row(rowbuf[1]);
     }
     __syncthreads();
-    load_tile(rowbuf[0]);
-    store_tile(lds[0]);
-    __syncthreads();
-    // iteration t: tile t is in LDS buffer t % 2 and the rows of tile t + 1
-    // in rowbuf[(t + 1) % 2]; the rows of tile t + 2 are looked up and tile
-    // t + 1 is loaded while tile t is computed; one barrier per tile
+    load_info(rowbuf[0]);
+    issue_tile(lds[0], rowbuf[0]);
+    store_info(lds[0]);
+    // iteration t: tile t lands in LDS buffer t % 2 (the wait + barrier at
+    // the top make every wave's copies and the info visible, and make sure
+    // every wave is done with tile t - 1, whose buffer the next copies
+    // overwrite); tile t + 1 is copied and the rows of tile t + 2 looked up
+    // while tile t is computed
     for (int t = 0; t < nt; ++t) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
       const bool more = t + 1 < nt;
+      if (more) {
+        load_info(rowbuf[(t + 1) & 1]);
+        issue_tile(lds[(t + 1) & 1], rowbuf[(t + 1) & 1]);
+      }
       if (t + 2 < nt) fetch_row(t + 2);
-      if (more) load_tile(rowbuf[(t + 1) & 1]);
       const char* qt = lds[t & 1];
       const char* dt = qt + L::kMat;
-      constexpr int RH = kRT / 32;  // 32-row halves of the tile
-      f32x16 s[RH], dp[RH];
+      f32x4 s[RT], dp[RT];
 #pragma unroll
-      for (int rh = 0; rh < RH; ++rh) {
-        s[rh] = dp[rh] = f32x16{};
+      for (int rt = 0; rt < RT; ++rt) {
+        s[rt] = dp[rt] = f32x4{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + L::pos(32 * rh + rl, 2 * ks + hf));
-          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dt + L::pos(32 * rh + rl, 2 * ks + hf));
-          s[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s[rh], 0, 0, 0);
-          dp[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[ks], dp[rh], 0, 0, 0);
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + L::pos(16 * rt + kl, 4 * ks + grp));
+          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dt + L::pos(16 * rt + kl, 4 * ks + grp));
+          s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kreg[ks], s[rt], 0, 0, 0);
+          dp[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, vreg[ks], dp[rt], 0, 0, 0);
         }
       }
-      // P and dS for rows 32rh + 8q + 4hf + e (slot 4q + e of half rh); the
-      // 16-row k-step st = 2rh + (slot / 8) of the second products
+      // P and dS of rows 16 rt + 4 grp + i; slot (rt % 2) * 4 + i of the
+      // 32-row step rt / 2 of the second products
       const float* info = reinterpret_cast<const float*>(qt + L::kInfo);
-      bf16x8 pb[2 * RH], sb[2 * RH];
+      typedef int i32x4 __attribute__((ext_vector_type(4)));
+      bf16x8 pb[RT / 2], sb[RT / 2];
 #pragma unroll
-      for (int rh = 0; rh < RH; ++rh)
+      for (int rt = 0; rt < RT; ++rt) {
+        const int m0 = 16 * rt + 4 * grp;
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(info + m0);
+        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(info + kRT + m0);
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(info + 2 * kRT + m0);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(info + 3 * kRT + m0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m0 = 32 * rh + 8 * q + 4 * hf;
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(info + m0);
-          const f32x4 dv4 = *reinterpret_cast<const f32x4*>(info + kRT + m0);
-          typedef int i32x4 __attribute__((ext_vector_type(4)));
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(info + 2 * kRT + m0);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(info + 3 * kRT + m0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * q + e;
-            const bool vis = j >= lo[e] && j <= hi[e];
-            const float p = vis ? fast_exp2(s[rh][i] * a.sl2 - lv[e]) : 0.f;
-            pb[2 * rh + (i >> 3)][i & 7] = bf16_t(p);
-            sb[2 * rh + (i >> 3)][i & 7] = bf16_t(p * (dp[rh][i] - dv4[e]));
-          }
+        for (int i = 0; i < 4; ++i) {
+          const bool vis = j >= lo[i] && j <= hi[i];
+          const float p = vis ? fast_exp2(s[rt][i] * a.sl2 - lv[i]) : 0.f;
+          pb[rt >> 1][(rt & 1) * 4 + i] = bf16_t(p);
+          sb[rt >> 1][(rt & 1) * 4 + i] = bf16_t(p * (dp[rt][i] - dv4[i]));
         }
+      }
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        const int c = 4 * md + 2 * tr_c16 + (tr_kq >> 1), cb = (tr_kq & 1) * 8;
+      for (int ct = 0; ct < CT; ++ct) {
+        const int c = 2 * ct + (tr_kq >> 1), cb = (tr_kq & 1) * 8;
 #pragma unroll
-        for (int st = 0; st < 2 * RH; ++st) {
-          const int r0 = 16 * st + 4 * hf + tr_r, r1 = r0 + 8;
+        for (int st = 0; st < RT / 2; ++st) {
+          const int r0 = 32 * st + 4 * grp + tr_r, r1 = r0 + 16;
           const s16x4 d0 = lds_tr16(dt + L::pos(r0, c) + cb), d1 = lds_tr16(dt + L::pos(r1, c) + cb);
           const s16x4 q0 = lds_tr16(qt + L::pos(r0, c) + cb), q1 = lds_tr16(qt + L::pos(r1, c) + cb);
           const bf16x8 ad = __builtin_bit_cast(bf16x8, __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7));
           const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
-          dv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, pb[st], dv[md], 0, 0, 0);
-          dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[st], dk[md], 0, 0, 0);
+          dv[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, pb[st], dv[ct], 0, 0, 0);
+          dk[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, sb[st], dk[ct], 0, 0, 0);
         }
       }
-      if (more) store_tile(lds[(t + 1) & 1]);
+      if (more) store_info(lds[(t + 1) & 1]);
       if (t + 2 < nt) put_row(rowbuf[t & 1]);
-      __syncthreads();
     }
+    __syncthreads();  // every wave is done with the last tile before the next head's copies
   }
   if (j < a.N) {
     const int64_t off = ((int64_t(b) * a.N + j) * a.Hkv + kvh) * D;
     bf16_t* dkp = static_cast<bf16_t*>(a.dK) + off;
     bf16_t* dvp = static_cast<bf16_t*>(a.dV) + off;
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
+    for (int ct = 0; ct < CT; ++ct) {
+      const int ch = 16 * ct + 4 * grp;
+      bf16x4 vk, vv;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int ch = 32 * md + 8 * q + 4 * hf;
-        bf16x4 vk, vv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vk[e] = bf16_t(dk[md][4 * q + e] * a.scale);
-          vv[e] = bf16_t(dv[md][4 * q + e]);
-        }
-        *reinterpret_cast<bf16x4*>(dkp + ch) = vk;
-        *reinterpret_cast<bf16x4*>(dvp + ch) = vv;
+      for (int i = 0; i < 4; ++i) {
+        vk[i] = bf16_t(dk[ct][i] * a.scale);
+        vv[i] = bf16_t(dv[ct][i]);
       }
+      *reinterpret_cast<bf16x4*>(dkp + ch) = vk;
+      *reinterpret_cast<bf16x4*>(dvp + ch) = vv;
+    }
   }
 }
 
