@@ -626,13 +626,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma_kernel(BwdArgs a) 
 // kernel.  A workgroup owns kQRows query rows of one head, 32 per wave;
 // each wave keeps its rows' Q and dO as MFMA B operands in registers, so
 // the 32x32 accumulators put one query per lane column (lanes l and l^32
-// share query l % 32).  Blocks of kQKeys keys of the KV head are staged in
-// LDS (double-buffered, one barrier per block) and shared by the waves:
-//   S^T = K Q^T,  dP^T = V dO^T            (keys x queries, k = channels)
+// share query l % 32).  Blocks of kQKeys keys of the KV head are copied
+// straight into LDS (global_load_lds_dwordx4, double-buffered, one barrier
+// per block) and shared by the waves; each block is taken in two 32-key
+// steps, each of them complete:
+//   S^T = K Q^T,  dP^T = V dO^T            (32 keys x queries, k = channels)
 //   one online pass: m = running maximum of S sl2 (raised only when a
-//   block exceeds it; dq and the sum rescaled then), p = 2^(S sl2 - m),
+//   step exceeds it; dq and the sum rescaled then), p = 2^(S sl2 - m),
 //   dS^T = p (dP^T - D)
 //   dQ^T += K^T dS^T                        (channels x queries, k = keys)
+// so only one step's scores are held (251-252 VGPRs at d = 128, no AGPRs:
+// two waves per SIMD), and a step with none of the wave's pairs is skipped.
 // and at the end dQ = scale dq / l, LSE = m + log2(l), D = <dO, O> (formed
 // from the same registers before the pass).  K is read both ways (plain
 // rows for the scores, ds_read_b64_tr_b16 for K^T), with the swizzle of
@@ -645,13 +649,13 @@ constexpr int kQRows = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kQKeys = 64;   // keys per LDS block
 
 template <int D, bool kFar>
-__global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma_kernel(BwdArgs a) {
   using L = KvTile<D>;
   constexpr int KS = D / 16;
   constexpr int MD = D / 32;
-  constexpr int kMat = kQKeys * L::kRowB;             // one staged K or V block
-  constexpr int kPer = kQKeys * L::kCPR / kBwdThreads;  // chunks per thread and matrix
-  static_assert(kQKeys * L::kCPR % kBwdThreads == 0, "block staging");
+  constexpr int kMat = kQKeys * L::kRowB;  // one staged K or V block
+  constexpr int kPerWave = kMat / 1024 / (kBwdThreads / kWave);  // 1 KB direct copies per wave and matrix
+  static_assert(kPerWave >= 1 && kMat / 1024 % (kBwdThreads / kWave) == 0, "block copies");
   __shared__ __attribute__((aligned(16))) char lds[2][2 * kMat];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int rl = lane & 31, hf = lane >> 5;
@@ -709,22 +713,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_kernel(BwdArgs a) {
   const int64_t krs = int64_t(a.Hkv) * D;
   const bf16_t* kh = static_cast<const bf16_t*>(a.K) + int64_t(b) * a.N * krs + int64_t(kvh) * D;
   const bf16_t* vh = static_cast<const bf16_t*>(a.V) + int64_t(b) * a.N * krs + int64_t(kvh) * D;
-  u32x4 sk[kPer], sv[kPer];
-  const auto load_block = [&](int kb) {
+  // the copies of one key block: copy m covers LDS bytes [1024 m, 1024 m +
+  // 1024) of each matrix; lane i writes the 16 bytes at 16 i, which hold
+  // chunk slot ^ swz(r) of row r (keys past the end read the last key; their
+  // pairs are masked)
+  const auto issue_block = [&](char* buf, int kb) {
 #pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-      const int u = tid + p * kBwdThreads, r = u / L::kCPR, c = u % L::kCPR;
-      const int key = min(kb * kQKeys + r, a.N - 1);  // past the end: masked
-      sk[p] = *reinterpret_cast<const u32x4*>(kh + int64_t(key) * krs + 8 * c);
-      sv[p] = *reinterpret_cast<const u32x4*>(vh + int64_t(key) * krs + 8 * c);
-    }
-  };
-  const auto store_block = [&](char* buf) {
-#pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-      const int u = tid + p * kBwdThreads, r = u / L::kCPR, c = u % L::kCPR;
-      *reinterpret_cast<u32x4*>(buf + L::pos(r, c)) = sk[p];
-      *reinterpret_cast<u32x4*>(buf + kMat + L::pos(r, c)) = sv[p];
+    for (int i = 0; i < kPerWave; ++i) {
+      const int m = wave * kPerWave + i;
+      const int byte = m * 1024 + lane * 16;
+      const int r = byte / L::kRowB, c = ((byte % L::kRowB) >> 4) ^ L::swz(r);
+      const int64_t src = int64_t(min(kb * kQKeys + r, a.N - 1)) * krs + 8 * c;
+      __builtin_amdgcn_global_load_lds(SWI_BWD_GLOBAL(kh + src), SWI_BWD_LOCAL(buf + m * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(SWI_BWD_GLOBAL(vh + src), SWI_BWD_LOCAL(buf + kMat + m * 1024), 16, 0, 0);
     }
   };
   f32x16 dq[MD];
@@ -732,40 +733,40 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_kernel(BwdArgs a) {
   for (int md = 0; md < MD; ++md) dq[md] = f32x16{};
   float m = kNegInf, l = 0.f;
   const int tr_r = (lane >> 2) & 3, tr_kq = lane & 3, tr_c16 = (lane >> 4) & 1;
-  load_block(kb0);
-  store_block(lds[0]);
-  __syncthreads();
+  issue_block(lds[0], kb0);
+  // iteration kb: block kb lands in buffer (kb - kb0) % 2 (the wait + barrier
+  // at the top make every wave's copies visible and make sure every wave is
+  // done with block kb - 1, whose buffer the next copies overwrite)
   for (int kb = kb0; kb <= kb1; ++kb) {
-    const bool more = kb < kb1;
-    if (more) load_block(kb + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kb < kb1) issue_block(lds[(kb + 1 - kb0) & 1], kb + 1);
     const char* kt = lds[(kb - kb0) & 1];
     const char* vt = kt + kMat;
-    const int key0 = kb * kQKeys;
-    if (key0 + kQKeys - 1 >= vlo && key0 <= vhi) {  // wave-uniform: any of this wave's pairs here
-      f32x16 s[2], dp[2];
+    // the block in two halves of 32 keys, each a full step (scores, softmax
+    // update, dS, dQ products): half the score registers of a 64-key step
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        s[mt] = dp[mt] = f32x16{};
+    for (int mt = 0; mt < 2; ++mt) {
+      const int key0 = kb * kQKeys + 32 * mt;
+      if (key0 + 31 < vlo || key0 > vhi) continue;  // wave-uniform: none of this wave's pairs here
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kt + L::pos(32 * mt + rl, 2 * ks + hf));
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt + L::pos(32 * mt + rl, 2 * ks + hf));
-          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], s[mt], 0, 0, 0);
-          dp[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, oreg[ks], dp[mt], 0, 0, 0);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kt + L::pos(32 * mt + rl, 2 * ks + hf));
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt + L::pos(32 * mt + rl, 2 * ks + hf));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, oreg[ks], dp, 0, 0, 0);
       }
-      // element i of slice mt: key key0 + 32 mt + 8 (i/4) + 4 hf + i%4
+      // element i: key key0 + 8 (i/4) + 4 hf + i%4
       float bmax = kNegInf;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + 32 * mt + 8 * (i >> 2) + 4 * hf + (i & 3);
-          const float x = (key >= lo && key <= hi) ? s[mt][i] * a.sl2 : kNegInf;
-          s[mt][i] = x;
-          bmax = fmaxf(bmax, x);
-        }
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      for (int i = 0; i < 16; ++i) {
+        const int key = key0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+        const float x = (key >= lo && key <= hi) ? s[i] * a.sl2 : kNegInf;
+        s[i] = x;
+        bmax = fmaxf(bmax, x);
+      }
+      bmax = fmaxf(bmax, xor32(bmax));
       const bool raise = bmax > m;
       if (__any(raise)) {
         const float alpha = raise ? fast_exp2(m - bmax) : 1.f;  // 0 while m is -inf
@@ -776,32 +777,29 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_kernel(BwdArgs a) {
           for (int i = 0; i < 16; ++i) dq[md][i] *= alpha;
         if (raise) m = bmax;
       }
-      bf16x8 sb[4];
+      // dS^T of k-steps st = 2 mt + j (slot e: key 16 st + 8 (e/4) + 4 hf + e%4)
+      bf16x8 sb[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = s[mt][i];
-          const float p = x == kNegInf ? 0.f : fast_exp2(x - m);
-          l += p;
-          sb[2 * mt + (i >> 3)][i & 7] = bf16_t(p * (dp[mt][i] - Dv));
-        }
+      for (int i = 0; i < 16; ++i) {
+        const float x = s[i];
+        const float p = x == kNegInf ? 0.f : fast_exp2(x - m);
+        l += p;
+        sb[i >> 3][i & 7] = bf16_t(p * (dp[i] - Dv));
+      }
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
         const int c = 4 * md + 2 * tr_c16 + (tr_kq >> 1), cb = (tr_kq & 1) * 8;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int r0 = 16 * st + 4 * hf + tr_r, r1 = r0 + 8;
+        for (int j = 0; j < 2; ++j) {
+          const int r0 = 16 * (2 * mt + j) + 4 * hf + tr_r, r1 = r0 + 8;
           const s16x4 k0 = lds_tr16(kt + L::pos(r0, c) + cb), k1 = lds_tr16(kt + L::pos(r1, c) + cb);
           const bf16x8 ak = __builtin_bit_cast(bf16x8, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
-          dq[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sb[st], dq[md], 0, 0, 0);
+          dq[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sb[j], dq[md], 0, 0, 0);
         }
       }
     }
-    if (more) store_block(lds[(kb + 1 - kb0) & 1]);
-    __syncthreads();
   }
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = l + xor32(l);
   if (act) {
     const float inv = a.scale / lt;
     bf16_t* dqp = static_cast<bf16_t*>(a.dQ) + (int64_t(b) * a.N + row) * qrs + int64_t(h) * D;
