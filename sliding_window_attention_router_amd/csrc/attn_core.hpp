@@ -746,18 +746,46 @@ SWI_DEV constexpr int acc_channel(int md, int i, int g) {
   return md * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
 }
 
-// Store this lane's half of an output row (channels acc_channel(...)).
+// Store this lane's half of an output row: the two lanes of a row swap
+// 4-channel groups first (v_permlane32_swap), so that lane g holds channels
+// 16g .. 16g + 15 of each 32-channel tile and writes them as two 16-byte
+// stores.
 template <int MD>
 SWI_DEV void store_row(bf16_t* orow, const f32x16 (&acc)[MD], float inv, int g) {
+  typedef uint32_t u32x4_ __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int md = 0; md < MD; ++md)
+  for (int md = 0; md < MD; ++md) {
+    uint32_t pk[4][2];
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       bf16x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = bf16_t(acc[md][i4 * 4 + e] * inv);
-      *reinterpret_cast<bf16x4*>(orow + md * 32 + i4 * 8 + g * 4) = v;
+      const auto w = __builtin_bit_cast(u32x2, v);
+      pk[i4][0] = w[0];
+      pk[i4][1] = w[1];
     }
+    // lane group 0 sends groups 2, 3; lane group 1 sends groups 0, 1
+    uint32_t rv[2][2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t out = g ? pk[k][h] : pk[k + 2][h];
+        const auto r = __builtin_amdgcn_permlane32_swap(out, out, false, false);
+        rv[k][h] = g ? r[0] : r[1];
+      }
+    u32x4_ s0, s1;
+    if (g == 0) {
+      s0 = u32x4_{pk[0][0], pk[0][1], rv[0][0], rv[0][1]};
+      s1 = u32x4_{pk[1][0], pk[1][1], rv[1][0], rv[1][1]};
+    } else {
+      s0 = u32x4_{rv[0][0], rv[0][1], pk[2][0], pk[2][1]};
+      s1 = u32x4_{rv[1][0], rv[1][1], pk[3][0], pk[3][1]};
+    }
+    *reinterpret_cast<u32x4_*>(orow + md * 32 + 16 * g) = s0;
+    *reinterpret_cast<u32x4_*>(orow + md * 32 + 16 * g + 8) = s1;
+  }
 }
 template <int MD>
 SWI_DEV void store_row(float* orow, const f32x16 (&acc)[MD], float inv, int g) {

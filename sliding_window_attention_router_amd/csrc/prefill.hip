@@ -36,6 +36,7 @@
 // of the same section uses this distance).
 #include <atomic>
 #include <climits>
+#include <type_traits>
 
 #include "attn_core.hpp"
 #include "kernels.hpp"
@@ -87,32 +88,39 @@ SWI_DEV int far_pos(const PrefillArgs& a, int b, int g, int k) {
   return a.all_rows ? k : a.idx[(int64_t(b) * a.G + g) * a.N + k];
 }
 
-// Far-part schedule inside a.sched (int32):
-//   [0] total items  [1] 64-key blocks per chunk
-//   n_items[nT]            chunks of each tile (global tile index T)
-//   unit_base[nbu]         first item of each (batch, unit)
-//   first[nbu][cmax]       first tile of the unit that has a chunk c
-//   offset[nbu][cmax]      first item of chunk c inside the unit
-//   item_tile[max], item_chunk[max]
-// Items of a unit are ordered by (chunk, tile): consecutive items read the
-// same key range of the same KV head.
+// Far-part schedule inside a.sched (int32).  Per (batch, unit) bu the
+// gathered rows are cut into nt(bu) active tiles of tpt_far rows; the active
+// tiles of all units are laid end to end (active tile x, abase[bu] = first
+// one of unit bu).  Tile (bu, t) is cut into chunks of cb 64-key blocks,
+// and the items (tile, chunk) are ordered by (unit, chunk, tile), so that
+// consecutive items read the same key range of the same KV head: chunk c
+// of unit bu holds the tiles from first[bu][c] (the first tile with more
+// than c chunks) on, and its items start at off[bu][c], so the item of
+// chunk c of tile t is off[bu][c] + t - first[bu][c].
+//   [0] items  [1] cb  [2] active tiles  [3] unused
+//   item_tile[max_items]   global tile index bu * far_tiles + t of each item
+//   item_chunk[max_items]  its chunk
+//   meta[nT][4]            per active tile: bu, t, chunks, gathered rows
+//   first[nbu][cmax], off[nbu][cmax]
+//   abase[nbu + 1], ucnt[nbu], maxc[nbu]  (schedule kernel's own tables when
+//                          they do not fit its LDS)
 struct SchedView {
-  int32_t *n_items, *unit_base, *first, *offset, *item_tile, *item_chunk, *merge_base, *merge_tile;
+  int32_t *item_tile, *item_chunk, *meta, *first, *off, *abase, *ucnt, *maxc;
   SWI_DEV SchedView(const PrefillArgs& a) {
     const int nT = a.B * a.units * a.far_tiles;
     const int nbu = a.B * a.units;
-    n_items = a.sched + 2;
-    unit_base = n_items + nT;
-    first = unit_base + nbu;
-    offset = first + nbu * a.cmax;
-    item_tile = offset + nbu * a.cmax;
+    item_tile = a.sched + 4;
     item_chunk = item_tile + a.max_items;
-    merge_base = item_chunk + a.max_items;  // per unit; merge_base[nbu]: total
-    merge_tile = merge_base + nbu + 1;
+    meta = item_chunk + a.max_items;
+    first = meta + 4 * nT;
+    off = first + nbu * a.cmax;
+    abase = off + nbu * a.cmax;
+    ucnt = abase + nbu + 1;
+    maxc = ucnt + nbu;
   }
   // item holding chunk c of tile t of unit bu
   SWI_DEV int item_of(int bu, int t, int c, int cmax) const {
-    return unit_base[bu] + offset[bu * cmax + c] + (t - first[bu * cmax + c]);
+    return off[bu * cmax + c] + (t - first[bu * cmax + c]);
   }
 };
 
@@ -415,198 +423,172 @@ SWI_DEV int block_excl_scan(int v, int* sh, int& total) {
   return res;
 }
 
-// Per-unit chunk tables (first tile of chunk c, first item of chunk c, and
-// the unit's first item) are built in LDS when they fit, and written out once
-// at the end (the attention and merge kernels read them from global memory);
-// reading them from global memory inside the serial loops over chunks cost a
-// memory round trip per chunk.
-constexpr int kSchedLds = 4096;  // ints per LDS table
-constexpr int kSchedUnits = 1024;  // (batch, unit) entries of the LDS unit tables
+// The schedule kernel keeps its tables in LDS when they fit (the per-unit
+// ones up to kSchedUnits units, the (unit, chunk) ones up to kSchedLds
+// entries) and in the workspace otherwise.  Work is spread over the active
+// tiles only; each pass issues the position loads of all its tiles before
+// using them.
+constexpr int kSchedLds = 4096;    // ints per (unit, chunk) table in LDS
+constexpr int kSchedUnits = 1024;  // (batch, unit) entries of the per-unit tables in LDS
+constexpr int kSchedPer = 4;       // active tiles a thread takes per round
 
 __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs a) {
-  __shared__ long long red[kSchedThreads / 64];
   __shared__ int scan_sh[33];
-  __shared__ int n_sh[kSchedLds], first_sh[kSchedLds], offset_sh[kSchedLds];
-  __shared__ int ubase_sh[kSchedUnits], mbase_sh[kSchedUnits + 1], ucnt_sh[kSchedUnits];
+  __shared__ long long red[kSchedThreads / 64];
+  __shared__ int cb_sh;
+  __shared__ int first_sh[kSchedLds], off_sh[kSchedLds];
+  __shared__ int abase_sh[kSchedUnits + 1], ucnt_sh[kSchedUnits], maxc_sh[kSchedUnits];
   SchedView sv(a);
   const int tid = threadIdx.x;
-  const int nT = a.B * a.units * a.far_tiles;
-  const int nbu = a.B * a.units;
-  const int TT = a.far_tiles;
-  const int ntab = nbu * a.cmax;
-  // every table in LDS when all fit, else every table in global memory
-  const bool in_lds = ntab <= kSchedLds && nT <= kSchedLds && nbu <= kSchedUnits;
-  int* n_items = in_lds ? n_sh : sv.n_items;
-  int* first = in_lds ? first_sh : sv.first;
-  int* offset = in_lds ? offset_sh : sv.offset;
-  int* unit_base = in_lds ? ubase_sh : sv.unit_base;
-  int* merge_base = in_lds ? mbase_sh : sv.merge_base;
-  // gathered rows of each (batch, unit): loaded once into LDS when they fit
-  const bool ucnt_lds = nbu <= kSchedUnits;
-  if (ucnt_lds)
-    for (int bu = tid; bu < nbu; bu += kSchedThreads) {
+  const int nbu = a.B * a.units, TT = a.far_tiles, cmax = a.cmax;
+  const int ntab = nbu * cmax;
+  const bool u_lds = nbu <= kSchedUnits;
+  const bool t_lds = ntab <= kSchedLds;
+  int* abase = u_lds ? abase_sh : sv.abase;
+  int* ucnt = u_lds ? ucnt_sh : sv.ucnt;
+  int* maxc = u_lds ? maxc_sh : sv.maxc;
+  int* first = t_lds ? first_sh : sv.first;
+  int* off = t_lds ? off_sh : sv.off;
+  if (tid < 8) a.queue[tid] = 0;
+  // gathered rows and active tiles of each unit, and their prefix
+  int NA = 0;
+  for (int x0 = 0; x0 < nbu; x0 += kSchedThreads) {
+    const int bu = x0 + tid;
+    int nt = 0;
+    if (bu < nbu) {
       const int b = bu / a.units, u = bu - b * a.units;
-      ucnt_sh[bu] = far_count(a, b, (u * a.hpu) / a.HG);
+      const int c = far_count(a, b, (u * a.hpu) / a.HG);
+      ucnt[bu] = c;
+      maxc[bu] = 0;
+      nt = (c + a.tpt_far - 1) / a.tpt_far;
     }
+    int tot;
+    const int ex = block_excl_scan(nt, scan_sh, tot);
+    if (bu < nbu) abase[bu] = NA + ex;
+    NA += tot;
+  }
+  if (tid == 0) abase[nbu] = NA;
   __syncthreads();
-  auto unit_count = [&](int bu) {
-    if (ucnt_lds) return ucnt_sh[bu];
-    const int b = bu / a.units, u = bu - b * a.units;
-    return far_count(a, b, (u * a.hpu) / a.HG);
+  // unit of active tile x: the last unit whose first active tile is <= x
+  const auto unit_of = [&](int x) {
+    int lo = 0, hi = nbu - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (abase[mid] <= x) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
   };
-  // active tiles of a unit: ceil(count / tpt_far)
-  auto active = [&](int bu) { return (unit_count(bu) + a.tpt_far - 1) / a.tpt_far; };
-  // pass 1: 64-key blocks of far work per tile (non-decreasing along the
-  // active tiles of a unit, since gathered positions ascend).  Every thread
-  // issues the position loads of all its tiles before it uses any of them.
+  // position of the last gathered row of tile (bu, t) (a memory load)
+  const auto last_pos = [&](int bu, int t) {
+    const int b = bu / a.units, u = bu - b * a.units;
+    const int ntok = min(a.tpt_far, ucnt[bu] - t * a.tpt_far);
+    return far_pos(a, b, (u * a.hpu) / a.HG, t * a.tpt_far + ntok - 1);
+  };
+  // 64-key blocks of far keys [A, pos - W - off] (none when empty)
+  const auto blocks_of = [&](int pos) {
+    const int fh = pos - a.Wf;
+    return fh >= a.A ? fh / kBN - a.A / kBN + 1 : 0;
+  };
+  // pass 1: total blocks, then the chunk size
   long long mine = 0;
-  constexpr int kLoads = 4;
-  for (int T0 = 0; T0 < nT; T0 += kLoads * kSchedThreads) {
-    int tlast[kLoads];
+  for (int x0 = 0; x0 < NA; x0 += kSchedPer * kSchedThreads) {
+    int pos[kSchedPer];
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int T_ = T0 + j * kSchedThreads + tid;
-      tlast[j] = -1;
-      if (T_ < nT) {
-        const int bu = T_ / TT, t = T_ - bu * TT;
-        const int b = bu / a.units, u = bu - b * a.units;
-        const int ntok = min(a.tpt_far, unit_count(bu) - t * a.tpt_far);
-        if (ntok > 0) tlast[j] = far_pos(a, b, (u * a.hpu) / a.HG, t * a.tpt_far + ntok - 1);
+    for (int j = 0; j < kSchedPer; ++j) {
+      const int x = x0 + j * kSchedThreads + tid;
+      pos[j] = -1;
+      if (x < NA) {
+        const int bu = unit_of(x);
+        pos[j] = last_pos(bu, x - abase[bu]);
       }
     }
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int T_ = T0 + j * kSchedThreads + tid;
-      if (T_ >= nT) continue;
-      int blocks = 0;
-      const int fh = tlast[j] - a.Wf;  // far keys [A, fh]
-      if (tlast[j] >= 0 && fh >= a.A) blocks = fh / kBN - a.A / kBN + 1;
-      n_items[T_] = blocks;
-      mine += blocks;
-    }
+    for (int j = 0; j < kSchedPer; ++j) mine += pos[j] >= 0 ? blocks_of(pos[j]) : 0;
   }
   for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
   if ((tid & 63) == 0) red[tid >> 6] = mine;
   __syncthreads();
-  long long total_blocks = 0;
-  for (int w = 0; w < kSchedThreads / 64; ++w) total_blocks += red[w];
-  const int cb = int(max<long long>(kMinChunkBlocks, (total_blocks + a.target_items - 1) / a.target_items));
-  // pass 2: chunks per tile
-  for (int T_ = tid; T_ < nT; T_ += kSchedThreads) n_items[T_] = (n_items[T_] + cb - 1) / cb;
-  __syncthreads();
-  // pass 3: first tile holding chunk c (n_items steps up at tile t for the
-  // chunks in [n(t-1), n(t)))
-  for (int T_ = tid; T_ < nT; T_ += kSchedThreads) {
-    const int bu = T_ / TT, t = T_ - bu * TT;
-    const int n = n_items[T_];
-    const int nprev = t > 0 ? n_items[T_ - 1] : 0;
-    for (int c = nprev; c < n; ++c) first[bu * a.cmax + c] = t;
-  }
-  __syncthreads();
-  // pass 4: offset of chunk c inside its unit = sum over the unit's earlier
-  // chunks c' of (active tiles - first[c']) (chunk c' holds the active tiles
-  // from first[c'] on): one exclusive prefix sum over the flat (unit, chunk)
-  // table, less its value at the unit's first entry
-  {
-    int carry = 0;
-    for (int x0 = 0; x0 < ntab; x0 += kSchedThreads) {
-      const int x = x0 + tid;
-      int val = 0;
-      if (x < ntab) {
-        const int bu = x / a.cmax, c = x - bu * a.cmax;
-        const int nt = active(bu);
-        const int maxn = nt > 0 ? n_items[bu * TT + nt - 1] : 0;
-        val = c < maxn ? nt - first[x] : 0;
-      }
-      int tot;
-      const int ex = block_excl_scan(val, scan_sh, tot);
-      if (x < ntab) offset[x] = carry + ex;
-      carry += tot;
-    }
-  }
-  __syncthreads();
-  for (int bu = tid; bu < nbu; bu += kSchedThreads) {
-    const int nt = active(bu);
-    const int maxn = nt > 0 ? n_items[bu * TT + nt - 1] : 0;
-    // items of the unit: the offset of its last chunk (relative to the
-    // unit's first entry) plus that chunk's tile count
-    int items = 0;
-    if (maxn > 0) {
-      const int lastc = bu * a.cmax + maxn - 1;
-      items = offset[lastc] - offset[bu * a.cmax] + (nt - first[lastc]);
-    }
-    unit_base[bu] = items;  // item count for now
-    // tiles with chunks: the unit's active tiles from first[0] on
-    merge_base[bu] = maxn > 0 ? nt - first[bu * a.cmax] : 0;  // count for now
-  }
-  __syncthreads();
-  if (tid < 8) a.queue[tid] = 0;
   if (tid == 0) {
-    int s = 0;
-    for (int bu = 0; bu < nbu; ++bu) {
-      const int n = unit_base[bu];
-      unit_base[bu] = s;
-      s += n;
-    }
-    a.sched[0] = s;
-    a.sched[1] = cb;
-    int m = 0;
-    for (int bu = 0; bu < nbu; ++bu) {
-      const int n = merge_base[bu];
-      merge_base[bu] = m;
-      m += n;
-    }
-    merge_base[nbu] = m;
+    long long total = 0;
+    for (int w = 0; w < kSchedThreads / 64; ++w) total += red[w];
+    const long long tgt = a.target_items;
+    const long long c = total + tgt - 1 < INT_MAX ? (long long)(unsigned(total + tgt - 1) / unsigned(tgt))
+                                                 : (total + tgt - 1) / tgt;
+    cb_sh = int(max<long long>(kMinChunkBlocks, c));
   }
   __syncthreads();
-  // pass 5: item list (offsets relative to the unit), and the merge list
-  for (int T_ = tid; T_ < nT; T_ += kSchedThreads) {
-    const int bu = T_ / TT, t = T_ - bu * TT;
-    const int n = n_items[T_];
-    const int ub = unit_base[bu], base = offset[bu * a.cmax];
+  const int cb = cb_sh;
+  // pass 2: chunks of every active tile (meta), the first tile holding chunk
+  // c (chunks step up at tile t for c in [chunks(t-1), chunks(t))), and the
+  // chunks of each unit's last tile
+  for (int x0 = 0; x0 < NA; x0 += kSchedPer * kSchedThreads) {
+    int pos[kSchedPer], prv[kSchedPer], bus[kSchedPer];
+#pragma unroll
+    for (int j = 0; j < kSchedPer; ++j) {
+      const int x = x0 + j * kSchedThreads + tid;
+      pos[j] = prv[j] = -1;
+      bus[j] = 0;
+      if (x < NA) {
+        const int bu = unit_of(x), t = x - abase[bu];
+        bus[j] = bu;
+        pos[j] = last_pos(bu, t);
+        if (t > 0) prv[j] = last_pos(bu, t - 1);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kSchedPer; ++j) {
+      const int x = x0 + j * kSchedThreads + tid;
+      if (x >= NA) continue;
+      const int bu = bus[j], t = x - abase[bu];
+      const int n = (blocks_of(pos[j]) + cb - 1) / cb;
+      const int np = prv[j] >= 0 ? (blocks_of(prv[j]) + cb - 1) / cb : 0;
+      for (int c = np; c < n; ++c) first[bu * cmax + c] = t;
+      if (t == abase[bu + 1] - abase[bu] - 1) maxc[bu] = n;
+      int32_t* m = sv.meta + 4 * int64_t(x);
+      m[0] = bu;
+      m[1] = t;
+      m[2] = n;
+      m[3] = min(a.tpt_far, ucnt[bu] - t * a.tpt_far);
+    }
+  }
+  __syncthreads();
+  // pass 3: first item of each (unit, chunk): an exclusive scan over the flat
+  // table of the chunk sizes (tiles from first[bu][c] to the unit's last)
+  int items = 0;
+  for (int x0 = 0; x0 < ntab; x0 += kSchedThreads) {
+    const int x = x0 + tid;
+    int val = 0;
+    if (x < ntab) {
+      const int bu = x / cmax, c = x - bu * cmax;
+      if (c < maxc[bu]) val = abase[bu + 1] - abase[bu] - first[x];
+    }
+    int tot;
+    const int ex = block_excl_scan(val, scan_sh, tot);
+    if (x < ntab) off[x] = items + ex;
+    items += tot;
+  }
+  __syncthreads();
+  // pass 4: the item list
+  for (int x = tid; x < NA; x += kSchedThreads) {
+    const int32_t* m = sv.meta + 4 * int64_t(x);
+    const int bu = m[0], t = m[1], n = m[2];
     for (int c = 0; c < n; ++c) {
-      const int x = bu * a.cmax + c;
-      const int it = ub + (offset[x] - base) + (t - first[x]);
-      sv.item_tile[it] = T_;
+      const int it = off[bu * cmax + c] + t - first[bu * cmax + c];
+      sv.item_tile[it] = bu * TT + t;
       sv.item_chunk[it] = c;
     }
-    // the merge list: tiles with chunks, unit by unit
-    if (n > 0) sv.merge_tile[merge_base[bu] + t - first[bu * a.cmax]] = T_;
   }
-  // the tables for the attention and merge kernels (item_of), with offsets
-  // relative to the unit
-  if (in_lds) {
+  // the tables the merge reads, and the counts
+  if (t_lds)
     for (int x = tid; x < ntab; x += kSchedThreads) {
-      const int bu = x / a.cmax;
       sv.first[x] = first_sh[x];
-      sv.offset[x] = offset_sh[x] - offset_sh[bu * a.cmax];
+      sv.off[x] = off_sh[x];
     }
-    for (int T_ = tid; T_ < nT; T_ += kSchedThreads) sv.n_items[T_] = n_sh[T_];
-    for (int bu = tid; bu <= nbu; bu += kSchedThreads) {
-      if (bu < nbu) sv.unit_base[bu] = ubase_sh[bu];
-      sv.merge_base[bu] = mbase_sh[bu];
-    }
-  } else {
-    __syncthreads();
-    int keep[4];
-    // relative offsets in place: read every unit base first (at most
-    // 4 * kSchedThreads entries per thread pass), then subtract
-    for (int x0 = 0; x0 < ntab; x0 += 4 * kSchedThreads) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int x = x0 + j * kSchedThreads + tid;
-        keep[j] = x < ntab ? sv.offset[(x / a.cmax) * a.cmax] : 0;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int x = x0 + j * kSchedThreads + tid;
-        if (x < ntab && x % a.cmax != 0) sv.offset[x] -= keep[j];
-      }
-      __syncthreads();
-    }
-    // unit starts last (every other entry of the unit has read them)
-    for (int bu = tid; bu < nbu; bu += kSchedThreads) sv.offset[bu * a.cmax] = 0;
+  if (tid == 0) {
+    a.sched[0] = items;
+    a.sched[1] = cb;
+    a.sched[2] = NA;
   }
 }
 
@@ -890,8 +872,12 @@ SWI_DEV float sq_distance(const float (&x)[n], const float (&y)[n]) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the far tiles.  Work units are (tile with chunks, quarter of its
-// rows), taken from the schedule's list by a fixed grid; 8 threads share a
+// Merge of the far tiles.  Work units are (active tile, quarter of its
+// rows), taken by a fixed grid (tiles without chunks are skipped); the
+// schedule's record of the tile and its (unit, chunk) tables give the items
+// of its chunks, so a unit needs three rounds of dependent loads (record;
+// row positions and item numbers; partials and window output).  8 threads
+// share a
 // row, each with D/8 consecutive channels, so that many independent loads
 // are in flight (one thread per row walking its chunks one after another
 // left the kernel bound by load latency).  O_FULL of a row is the
@@ -902,25 +888,22 @@ SWI_DEV float sq_distance(const float (&x)[n], const float (&y)[n]) {
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 256;
 constexpr int kMergeTPR = 8;  // threads per row
+constexpr int kMergeBatch = 4;  // chunks whose loads are in flight together
 template <typename T, int D, bool kBoth>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PrefillArgs a) {
   constexpr int kRowsWG = kMergeThreads / kMergeTPR;  // rows per work unit
   constexpr int kParts = kRows / kRowsWG;
   constexpr int CPT = D / kMergeTPR;  // channels per thread
   SchedView sv(a);
-  const int nm = sv.merge_base[a.B * a.units];
+  const int na = a.sched[2];
   const int rr = threadIdx.x / kMergeTPR, c0 = (threadIdx.x % kMergeTPR) * CPT;
-  for (int w = blockIdx.x; w < nm * kParts; w += gridDim.x) {
-    const int T_ = sv.merge_tile[w / kParts];
+  for (int w = blockIdx.x; w < na * kParts; w += gridDim.x) {
+    const int32_t* m = sv.meta + 4 * int64_t(w / kParts);
+    const int bu = m[0], t = m[1], ni = m[2], ntok = m[3];
+    if (ni == 0) continue;
     const int r = (w % kParts) * kRowsWG + rr;
-    const int ni = sv.n_items[T_];
-    const int per_b = a.units * a.far_tiles;
-    const int b = T_ / per_b, rem = T_ - b * per_b;
-    const int u = rem / a.far_tiles, t = rem - u * a.far_tiles;
-    const int bu = b * a.units + u;
+    const int b = bu / a.units, u = bu - b * a.units;
     const int g_gate = (u * a.hpu) / a.HG;
-    const int c = far_count(a, b, g_gate);
-    const int ntok = min(a.tpt_far, c - t * a.tpt_far);
     const int slot = r / a.hpu, hh = r - slot * a.hpu;
     // (the 8 threads of a row take every branch together)
     if (slot >= ntok) continue;
@@ -928,34 +911,53 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PrefillArgs a) {
     if (tok - a.Wf < a.A) continue;  // no far keys: the window pass already holds O_FULL
     const int h = u * a.hpu + hh;
     const float ls = a.lse_s[(int64_t(b) * a.Hq + h) * a.N + tok];
-    float M = ls;
-    for (int k = 0; k < ni; ++k)
-      M = fmaxf(M, a.part_lse[int64_t(sv.item_of(bu, t, k, a.cmax)) * kRows + r]);
     T* orow = static_cast<T*>(a.O) + ((int64_t(b) * a.N + tok) * a.Hq + h) * D + c0;
-    float wsum = fast_exp2(ls - M);
     float os[CPT], o[CPT];
 #pragma unroll
     for (int i4 = 0; i4 < CPT / 4; ++i4) {
       const f32x4 v = load4(orow + i4 * 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        os[i4 * 4 + e] = v[e];
-        o[i4 * 4 + e] = wsum * v[e];
-      }
+      for (int e = 0; e < 4; ++e) os[i4 * 4 + e] = o[i4 * 4 + e] = v[e];
     }
-#pragma unroll 2
-    for (int k = 0; k < ni; ++k) {
-      const int it = sv.item_of(bu, t, k, a.cmax);
-      const float lk = a.part_lse[int64_t(it) * kRows + r];
-      const float wk = lk == kNegInf ? 0.f : fast_exp2(lk - M);
-      wsum += wk;
-      const T* prow = static_cast<const T*>(a.part_o) + (int64_t(it) * kRows + r) * D + c0;
+    // chunks in batches of kMergeBatch with all their loads in flight: the
+    // running maximum M starts at the window's normaliser and is raised once
+    // per batch (weights 2^(lse - M) on the normalised partial outputs)
+    float M = ls, wsum = 1.f;
+    for (int k0 = 0; k0 < ni; k0 += kMergeBatch) {
+      int it[kMergeBatch];
 #pragma unroll
-      for (int i4 = 0; i4 < CPT / 4; ++i4) {
-        const f32x4 v = load4(prow + i4 * 4);
+      for (int j = 0; j < kMergeBatch; ++j) it[j] = k0 + j < ni ? sv.item_of(bu, t, k0 + j, a.cmax) : -1;
+      // partials kept in their stored type until they are summed
+      using R4 = std::conditional_t<std::is_same_v<T, float>, f32x4, bf16x4>;
+      float lk[kMergeBatch];
+      R4 pv[kMergeBatch][CPT / 4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[i4 * 4 + e] = fmaf(wk, v[e], o[i4 * 4 + e]);
+      for (int j = 0; j < kMergeBatch; ++j) {
+        lk[j] = kNegInf;
+        if (it[j] < 0) continue;
+        lk[j] = a.part_lse[int64_t(it[j]) * kRows + r];
+        const T* prow = static_cast<const T*>(a.part_o) + (int64_t(it[j]) * kRows + r) * D + c0;
+#pragma unroll
+        for (int i4 = 0; i4 < CPT / 4; ++i4) pv[j][i4] = *reinterpret_cast<const R4*>(prow + i4 * 4);
       }
+      float mb = M;
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) mb = fmaxf(mb, lk[j]);
+      const float sc = fast_exp2(M - mb);
+      wsum *= sc;
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) o[e] *= sc;
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        if (it[j] < 0) continue;
+        const float wk = lk[j] == kNegInf ? 0.f : fast_exp2(lk[j] - mb);
+        wsum += wk;
+#pragma unroll
+        for (int i4 = 0; i4 < CPT / 4; ++i4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[i4 * 4 + e] = fmaf(wk, float(pv[j][i4][e]), o[i4 * 4 + e]);
+      }
+      M = mb;
     }
     const float inv = 1.f / wsum;
 #pragma unroll
@@ -1037,8 +1039,7 @@ bool plan_prefill(const PrefillShape& sh, PrefillPlan* p) {
   off = align_up(off + rowsN * 4);
   p->off_sched = off;
   const size_t nbu = size_t(sh.B) * p->units;
-  const size_t sched_ints =
-      2 + size_t(nT) + nbu + 2 * nbu * p->cmax + 2 * size_t(max_items) + nbu + 1 + size_t(nT);
+  const size_t sched_ints = 4 + 2 * size_t(max_items) + 4 * size_t(nT) + 2 * nbu * p->cmax + 3 * nbu + 1;
   off = align_up(off + sched_ints * 4);
   p->off_queue = off;
   off = align_up(off + 8 * 4);

@@ -102,11 +102,12 @@ def test_every_row_multitile_both_branch():
 
 
 def test_many_units_schedule_tables_in_global_memory():
-    """B=32 sequences x 32 KV heads (MHA) at N=2048: 1024 (sequence, unit)
-    pairs x 5 chunk slots exceed the far schedule's LDS tables, so the
-    schedule builds them in global memory.  Sampled rows of every sequence
-    against the oracle."""
-    B, N, H, d, W, p = 32, 2048, 32, 64, 64, 0.1
+    """B=33 sequences x 32 KV heads (MHA) at N=2048: 1056 (sequence, unit)
+    pairs exceed the far schedule's per-unit LDS tables (1024 entries) and,
+    with 5 chunk slots each, its (unit, chunk) tables, so the schedule builds
+    all of them in global memory.  Sampled rows of every sequence against the
+    oracle."""
+    B, N, H, d, W, p = 33, 2048, 32, 64, 64, 0.1
     say(f"schedule in global memory: B={B} N={N} MHA {H} heads d={d} W={W} p={p}")
     w = synth.long_prefill(seed=46, B=B, N=N, Hq=H, Hkv=H, d=d, W=W, p=p)
     bf = torch.bfloat16
