@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU reference sample (0 = skip)")
     ap.add_argument("--p", type=float, default=0.13, help="full-branch fraction")
-    ap.add_argument("--serve-steps", type=int, default=5,
+    ap.add_argument("--serve-steps", type=int, default=20,
                     help="timed serving decode steps (route + append + decode; after the timed steps; 0 = skip)")
     ap.add_argument("--both-steps", type=int, default=3,
                     help="timed runs of the both-branch prefill (after the timed steps; 0 = skip)")
@@ -499,7 +499,8 @@ def serve_run(swa, q, Kc, Vc, cache_len, r, bias, W, steps):
     steps): each routes 64 new tokens (hidden states drawn from a seeded
     N(0,1), router as in the prefill), appends their keys and values at
     position L-1 of the full cache (the lengths are set to L-1 before each
-    step) and decodes over L keys.  Timed with events around the whole call."""
+    step) and decodes over L keys.  The steps run back to back, each timed
+    with events around the whole call; the median is reported."""
     import torch
     B, Hq, d = q.shape
     Hkv = Kc.shape[2]
@@ -517,16 +518,20 @@ def serve_run(swa, q, Kc, Vc, cache_len, r, bias, W, steps):
     ws = torch.empty(swa.decode_workspace_size(B, Kc.shape[1], Hq, Hkv, G, d, W), dtype=torch.uint8,
                      device=dev)
     swa.decode_step(Hn, r, bias, q, k, v, Kc, Vc, L, W, gate=gate, out=o, workspace=ws)
-    times = []
+    torch.cuda.synchronize()
+    # steps back to back, as in a serving loop (the lengths are reset by a
+    # small copy before each step, outside its events); one synchronisation
+    # at the end
+    evs = []
     for _ in range(steps):
         L.copy_(before)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         swa.decode_step(Hn, r, bias, q, k, v, Kc, Vc, L, W, gate=gate, out=o, workspace=ws)
         e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    ms = float(np.mean(times))
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
     g = gate.cpu().numpy()
     lens = L.cpu().numpy()
     dbytes, keys = decode_bytes(g, lens, W, Hq, Hkv, d)
