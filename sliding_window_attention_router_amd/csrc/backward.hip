@@ -483,30 +483,27 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma_kernel(BwdArgs a) 
     const auto put_row = [&](int* rb) {
       if (tid < kRT) rb[tid] = fok ? (fwin ? fw : fl) : -1;
     };
-    // each row's LSE, D and visible keys (wave 0, one row per lane); the
-    // loads are issued before a tile's copies so that waiting for them
-    // leaves the copies in flight
+    // each row's LSE, D and visible keys (one row per lane; wave w loads
+    // and stores field w); the loads are issued before a tile's copies so
+    // that waiting for them leaves the copies in flight
+    static_assert(kRT == kWave && kBwdThreads / kWave == 4, "one info field per wave");
     float i_l = 0.f, i_d = 0.f;
     int i_row = 0, i_ok = 0;
     uint8_t i_g = 0;
     const auto load_info = [&](const int* rb) {
-      if (tid < kRT) {
-        const int r = rb[tid];
-        i_ok = r >= 0;
-        i_row = r >= 0 ? r : k0;
-        i_l = lrow[i_row];
-        i_d = drow[i_row];
-        i_g = grow[int64_t(i_row) * a.G];
-      }
+      const int r = rb[lane];
+      i_ok = r >= 0;
+      i_row = r >= 0 ? r : k0;
+      if (wave == 0) i_l = lrow[i_row];
+      else if (wave == 1) i_d = drow[i_row];
+      else if (wave == 2) i_g = grow[int64_t(i_row) * a.G];
     };
     const auto store_info = [&](char* buf) {
-      if (tid < kRT) {
-        float* info = reinterpret_cast<float*>(buf + L::kInfo);
-        info[tid] = i_ok ? i_l : __builtin_huge_valf();
-        info[kRT + tid] = i_ok ? i_d : 0.f;
-        reinterpret_cast<int*>(info)[2 * kRT + tid] = i_ok ? (i_g != 0 ? 0 : i_row - a.W + 1) : 0;
-        reinterpret_cast<int*>(info)[3 * kRT + tid] = i_ok ? i_row : -1;
-      }
+      float* info = reinterpret_cast<float*>(buf + L::kInfo);
+      if (wave == 0) info[lane] = i_ok ? i_l : __builtin_huge_valf();
+      else if (wave == 1) info[kRT + lane] = i_ok ? i_d : 0.f;
+      else if (wave == 2) reinterpret_cast<int*>(info)[2 * kRT + lane] = i_ok ? (i_g != 0 ? 0 : i_row - a.W + 1) : 0;
+      else reinterpret_cast<int*>(info)[3 * kRT + lane] = i_ok ? i_row : -1;
     };
     // the copies of one tile: copy m covers LDS bytes [1024 m, 1024 m + 1024)
     // of each matrix; lane i writes 16 bytes at 16 i, which hold chunk
@@ -564,25 +561,37 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma_kernel(BwdArgs a) 
         }
       }
       // P and dS of rows 16 rt + 4 grp + i; slot (rt % 2) * 4 + i of the
-      // 32-row step rt / 2 of the second products
+      // 32-row step rt / 2 of the second products.  A tile of gathered rows
+      // without padding sees every key of the workgroup (its rows lie past
+      // the window rows: i >= k0 + 63 + W), so it skips the visibility test.
       const float* info = reinterpret_cast<const float*>(qt + L::kInfo);
       typedef int i32x4 __attribute__((ext_vector_type(4)));
       bf16x8 pb[RT / 2], sb[RT / 2];
+      const auto p_ds = [&](auto all_visible) {
+        constexpr bool kAll = decltype(all_visible)::value;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int m0 = 16 * rt + 4 * grp;
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(info + m0);
-        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(info + kRT + m0);
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(info + 2 * kRT + m0);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(info + 3 * kRT + m0);
+        for (int rt = 0; rt < RT; ++rt) {
+          const int m0 = 16 * rt + 4 * grp;
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(info + m0);
+          const f32x4 dv4 = *reinterpret_cast<const f32x4*>(info + kRT + m0);
+          i32x4 lo = i32x4{}, hi = i32x4{};
+          if constexpr (!kAll) {
+            lo = *reinterpret_cast<const i32x4*>(info + 2 * kRT + m0);
+            hi = *reinterpret_cast<const i32x4*>(info + 3 * kRT + m0);
+          }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool vis = j >= lo[i] && j <= hi[i];
-          const float p = vis ? fast_exp2(s[rt][i] * a.sl2 - lv[i]) : 0.f;
-          pb[rt >> 1][(rt & 1) * 4 + i] = bf16_t(p);
-          sb[rt >> 1][(rt & 1) * 4 + i] = bf16_t(p * (dp[rt][i] - dv4[i]));
+          for (int i = 0; i < 4; ++i) {
+            const bool vis = kAll || (j >= lo[i] && j <= hi[i]);
+            const float p = vis ? fast_exp2(s[rt][i] * a.sl2 - lv[i]) : 0.f;
+            pb[rt >> 1][(rt & 1) * 4 + i] = bf16_t(p);
+            sb[rt >> 1][(rt & 1) * 4 + i] = bf16_t(p * (dp[rt][i] - dv4[i]));
+          }
         }
-      }
+      };
+      if (t >= nwt && f0 + (t - nwt + 1) * kRT <= n)
+        p_ds(std::true_type{});
+      else
+        p_ds(std::false_type{});
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const int c = 2 * ct + (tr_kq >> 1), cb = (tr_kq & 1) * 8;
