@@ -341,11 +341,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
         if (g == 0) a.part_lse[int64_t(slot) * a.HK + q] = lse2;
       }
     }
-    if (cur.blk0 == 0 && lane == 0) {
-      // the share that starts the pair describes it for the merge: the slot
-      // of its own piece and the last share the pair reaches (-1: whole)
-      a.info[1 + 2 * cur.bk] = whole ? -1 : 2 * w + (cur.first == s ? 0 : 1);
-      a.info[2 + 2 * cur.bk] = whole ? 0 : share_of(cur.first + cur.nb - 1, total, G);
+    if (cur.blk0 == 0 && lane == 0) {  // the share that starts the pair describes it
+      a.info[1 + 2 * cur.bk] = whole ? -1 : cur.first;
+      a.info[2 + 2 * cur.bk] = cur.nb;
     }
     if (!more) break;
     cur = nx;
@@ -358,26 +356,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
 // elements 2t, 2t+1 (+512 ...) of the pair's [HK][D] block over its pieces
 // in share order (a fixed order, so the result does not depend on timing),
 // with the log-sum-exp rule: weights 2^(lse_k - max) on the normalised
-// piece outputs.  The pieces' slots follow from the first one and the last
-// share (written by the split-K kernel): later shares start inside the pair,
-// so their piece is their first slot.
+// piece outputs.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int G) {
+  __shared__ int slots[kDecGrid];
   const int bk = blockIdx.x;
-  const int slot0 = a.info[1 + 2 * bk];
-  if (slot0 < 0) return;
-  const int w0 = slot0 >> 1, w1 = a.info[2 + 2 * bk], total = a.info[0];
+  const int first = a.info[1 + 2 * bk];
+  if (first < 0) return;
+  const int nb = a.info[2 + 2 * bk], total = a.info[0];
+  const int w0 = share_of(first, total, G), w1 = share_of(first + nb - 1, total, G);
   const int np = w1 - w0 + 1;
-  // a share without blocks (only when there are fewer blocks than
-  // workgroups) holds no piece
-  const bool dense = total >= G;
-  const auto slot_of = [&](int k) {
-    if (k >= np) return -1;
-    if (k == 0) return slot0;
+  // piece in share w0: its first or its second slot; later shares start
+  // inside the pair, so their piece is their first slot (empty shares,
+  // possible when there are fewer blocks than workgroups, hold none)
+  for (int k = threadIdx.x; k < np; k += 256) {
     const int w = w0 + k;
-    if (!dense && share_start(w, total, G) == share_start(w + 1, total, G)) return -1;
-    return 2 * w;
-  };
+    int sl = 2 * w;
+    if (k == 0) sl += share_start(w0, total, G) == first ? 0 : 1;
+    else if (share_start(w, total, G) == share_start(w + 1, total, G)) sl = -1;
+    slots[k] = sl;
+  }
+  __syncthreads();
   const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
   T* obase = static_cast<T*>(a.o) + (int64_t(b) * a.Hq + kvh * a.HK) * D;
   // pieces are read in batches of kBatch with all loads in flight; the
@@ -391,7 +390,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int G) 
       float2 v[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const int sl = slot_of(k0 + j);
+        const int sl = k0 + j < np ? slots[k0 + j] : -1;
         lk[j] = kNegInf;
         v[j] = make_float2(0.f, 0.f);
         if (sl >= 0) {
