@@ -226,7 +226,7 @@ struct KVLoader<float, D, NT, kStream> {
 // ---------------------------------------------------------------------------
 constexpr float kRescale = 8.f;
 
-template <int MD>
+template <int MD, bool kSum = true>
 SWI_DEV void online_softmax(f32x16 (&s)[2], f32x16 (&acc)[MD], float& m, float& l, int kb,
                             bool masked, int lo, int hi, float sl2, int g) {
   // Masking only rewrites the scores, in a wave-uniform branch, so masked
@@ -265,10 +265,10 @@ SWI_DEV void online_softmax(f32x16 (&s)[2], f32x16 (&acc)[MD], float& m, float& 
     for (int i = 0; i < 16; ++i) {
       const float p = fast_exp2(fmaf(s[mt][i], sl2, -mu));
       s[mt][i] = p;
-      ls += p;
+      if constexpr (kSum) ls += p;
     }
   }
-  l += ls;
+  if constexpr (kSum) l += ls;
 }
 
 // ---------------------------------------------------------------------------
@@ -594,12 +594,27 @@ struct CoreBF16Dma {
     }
     __builtin_amdgcn_s_setprio(0);
     after_scores();
-    online_softmax<MD>(s, acc, m, l, kb, masked, lo, hi, sl2, g);
+    online_softmax<MD, false>(s, acc, m, l, kb, masked, lo, hi, sl2, g);
     bf16x8 pb[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[st][e] = bf16_t(s[st >> 1][(st & 1) * 8 + e]);
+    // row sum of the probabilities as rounded for the P.V product (the
+    // normaliser then matches the numerator), two at a time
+    {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t one = {bf16_t(1.f), bf16_t(1.f)};
+      float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; e += 4) {
+          l0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pb[st][e], pb[st][e + 1]}, one, l0, false);
+          l1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pb[st][e + 2], pb[st][e + 3]}, one, l1, false);
+        }
+      l += l0 + l1;
+    }
     // k-step st, lane group g holds keys 16st + 4g + {0..3} (slots 0..3) and
     // 16st + 8 + 4g + {0..3} (slots 4..7) of P^T; the transposing reads
     // fetch V^T to match (source lane 4r + k of each 16-lane group points at
