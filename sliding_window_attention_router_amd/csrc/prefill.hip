@@ -47,6 +47,12 @@ constexpr int kRows = 128;  // query rows of every tile
 constexpr int kTargetItems = 1024;      // far work items aimed for per launch (hard gate)
 constexpr int kTargetItemsAll = 4096;   // the same when every row takes the full branch
 constexpr int kMinChunkBlocks = 8;  // far chunk is at least 8 x 64 keys
+// A hard-gate far chunk is at most kMaxChunkBlocks 64-key blocks (8 MB of
+// K and V at d = 128) unless that would need more than kTargetItemsAll
+// items: the resident items of an XCD read the same chunk, and longer
+// chunks drift apart in that L2 (at gate density 1, 1024 items of about
+// 960 blocks each took 5.8 ms against 4.5 ms for the both-branch pass).
+constexpr int kMaxChunkBlocks = 256;
 constexpr int kSchedThreads = 1024;
 
 struct PrefillArgs {
@@ -392,7 +398,8 @@ SWI_DEV void band_tile(const PrefillArgs& a, char* buf0, char* buf1, int lin) {
 // (heads that share both the KV head and the gate group).  Its far keys are
 // [0, t_last - W] where t_last is its largest token; the tile is cut into
 // chunks of `cb` 64-key blocks, cb chosen so that the launch has about
-// target_items chunks in total.
+// target_items chunks in total, with chunks of at most kMaxChunkBlocks
+// blocks while that needs no more than kTargetItemsAll items.
 // ---------------------------------------------------------------------------
 SWI_DEV int block_excl_scan(int v, int* sh, int& total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -512,10 +519,12 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
   if (tid == 0) {
     long long total = 0;
     for (int w = 0; w < kSchedThreads / 64; ++w) total += red[w];
-    const long long tgt = a.target_items;
-    const long long c = total + tgt - 1 < INT_MAX ? (long long)(unsigned(total + tgt - 1) / unsigned(tgt))
-                                                 : (total + tgt - 1) / tgt;
-    cb_sh = int(max<long long>(kMinChunkBlocks, c));
+    const auto cdiv = [](long long x, long long y) {
+      return x + y - 1 < INT_MAX ? (long long)(unsigned(x + y - 1) / unsigned(y)) : (x + y - 1) / y;
+    };
+    const long long c = cdiv(total, a.target_items);
+    const long long cap = max<long long>(kMaxChunkBlocks, cdiv(total, kTargetItemsAll));
+    cb_sh = int(max<long long>(kMinChunkBlocks, min(c, cap)));
   }
   __syncthreads();
   const int cb = cb_sh;
@@ -943,7 +952,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PrefillArgs a) {
       float mb = M;
 #pragma unroll
       for (int j = 0; j < kMergeBatch; ++j) mb = fmaxf(mb, lk[j]);
-      const float sc = fast_exp2(M - mb);
+      const float sc = mb == kNegInf ? 1.f : fast_exp2(M - mb);
       wsum *= sc;
 #pragma unroll
       for (int e = 0; e < CPT; ++e) o[e] *= sc;
@@ -1028,7 +1037,9 @@ bool plan_prefill(const PrefillShape& sh, PrefillPlan* p) {
   p->far_tiles = (sh.N + p->tpt_far - 1) / p->tpt_far;
   const long long nT = (long long)sh.B * p->units * p->far_tiles;
   p->target_items = sh.both_branch ? kTargetItemsAll : kTargetItems;
-  const long long max_items = p->target_items + nT;
+  // chunks of at least max(8, total / kTargetItemsAll) blocks: at most
+  // kTargetItemsAll items plus one partial chunk per tile
+  const long long max_items = kTargetItemsAll + nT;
   if (max_items > INT_MAX / kRows) return false;
   p->max_items = int(max_items);
   // chunks per tile <= ceil(ceil(N / 64) / kMinChunkBlocks)
