@@ -670,7 +670,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma_kernel(BwdArgs a) {
   const int rl = lane & 31, hf = lane >> 5;
   const int nbh = a.B * a.Hq;
   const int ntile = (a.N + kQRows - 1) / kQRows;
-  const int bh = blockIdx.x % nbh;
+  // workgroups are dealt to the 8 XCDs in turn: give the workgroups of one
+  // XCD neighbouring heads (the query heads of a KV head), which read the
+  // same keys
+  const int jh = blockIdx.x % nbh;
+  const int bh = nbh % 8 == 0 ? (jh % 8) * (nbh / 8) + jh / 8 : jh;
   const int b = bh / a.Hq, h = bh % a.Hq, kvh = h / a.HK, g = h / a.HG;
   const int32_t* list = a.idx + (int64_t(b) * a.G + g) * a.N;
   int tile = blockIdx.x / nbh;

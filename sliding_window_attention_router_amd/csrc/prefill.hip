@@ -666,15 +666,16 @@ SWI_DEV void far_item(const PrefillArgs& a, char* buf0, char* buf1, int item) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent window workers (DMA path).  The window tiles are split into 8
-// queues, queue x holding the x-th eighth of the tiles (consecutive tiles of
-// one KV head, which share most of their keys in that XCD's L2); a worker
+// Persistent window workers (DMA path).  The window tiles, ordered by
+// (sequence, tile, KV head), are split into 8 queues, queue x holding the
+// x-th eighth of them (one token range of every KV head: neighbouring tiles
+// of a head share most of their keys in that XCD's L2); a worker
 // takes tiles from the queue of its XCD and moves on to the others when it
 // runs dry.  Every position of every queue is handed out once (atomic
 // counters, zeroed by the schedule kernel that precedes the launch).
 // Across tiles the block stream continues without a pipeline restart: the
-// next tile id is claimed a tile ahead and published two blocks before the
-// current tile ends, the copy of its first K/V block is issued during the
+// next tile id is claimed four blocks before the current tile ends and
+// published two blocks before it ends, the copy of its first K/V block is issued during the
 // last block of the current tile, and its queries are loaded right after
 // that block's score MFMAs.
 // ---------------------------------------------------------------------------
@@ -710,9 +711,12 @@ template <bool kAnch>
 struct BandTile {
   int b, kvh, q0, kb0, nb, na;
   SWI_DEV void set(const PrefillArgs& a, int lin) {
-    const int tile = lin % a.band_tiles, bk = lin / a.band_tiles;
-    b = bk / a.Hkv;
-    kvh = bk - b * a.Hkv;
+    // KV heads fastest: an XCD's resident workers cover one token range of
+    // every KV head of the sequence
+    kvh = lin % a.Hkv;
+    const int bt = lin / a.Hkv;
+    b = bt / a.band_tiles;
+    const int tile = bt - b * a.band_tiles;
     q0 = tile * a.tpt_band;
     const int qlast = min(a.N - 1, q0 + a.tpt_band - 1);
     window_blocks(a, b, kvh, q0, qlast, kb0, nb);
