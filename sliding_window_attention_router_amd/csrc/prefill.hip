@@ -690,18 +690,36 @@ struct TileQueue {
 // split: claim() issues the increment on queue x and returns the raw
 // position without waiting for it; resolve(), a block or more later (the
 // block barriers have drained the increment by then), turns it into a tile,
-// or, if queue x ran dry, claims from the other queues in turn (waiting).
+// or, if queue x ran dry, reads all 8 counters at once (one round trip) and
+// claims, in turn, only from queues that still had tiles: a counter only
+// grows, so a queue seen dry stays dry and skipping it loses no tile.  (A
+// claim on each other queue in turn cost up to seven contended round trips
+// at the end of every worker's last tile.)  That path is kept out of line,
+// so that it does not weigh on the register allocation of the block loop.
 SWI_DEV int claim(int* queue, int x) {
   return __hip_atomic_fetch_add(queue + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
-SWI_DEV int resolve(int* queue, const TileQueue& tq, int& x, int p) {
-  for (int k = 0; k < 8; ++k) {
-    if (p < tq.len(x)) return x * tq.per + p;
-    if (k == 7) break;
-    x = (x + 1) & 7;
-    p = claim(queue, x);
+__device__ __attribute__((noinline)) int steal(int* queue, int n, int per, int x) {
+  TileQueue tq;
+  tq.n = n;
+  tq.per = per;
+  int seen[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    seen[k] = __hip_atomic_load(queue + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  for (int k = 1; k < 8; ++k) {
+    const int y = (x + k) & 7;
+    if (seen[y] >= tq.len(y)) continue;
+    const int q = claim(queue, y);
+    if (q < tq.len(y)) return y * tq.per + q;
   }
   return -1;
+}
+SWI_DEV int resolve(int* queue, const TileQueue& tq, int& x, int p) {
+  if (p < tq.len(x)) return x * tq.per + p;
+  const int lin = steal(queue, tq.n, tq.per, x);
+  if (lin >= 0) x = lin / tq.per;
+  return lin;
 }
 
 // Window tile lin: tpt_band consecutive tokens x the HK heads of one KV head.
