@@ -457,8 +457,8 @@ int swiattn_router_backward(const void* dO, const void* O_full, const void* O_sw
  *            accumulation).  Scores, softmax and D = <dO, O> are float32;
  *            the probabilities P and dS = P (dP - D) are rounded to bf16
  *            where they become operands of the dV, dQ and dK products.
- *            One launch for dQ of the gate=0 rows, one for the gathered
- *            gate=1 rows (both also write LSE and D to the workspace), one
+ *            One launch for dQ (the gathered gate=1 rows first, then the
+ *            gate=0 rows; it also writes LSE and D to the workspace), one
  *            for dK and dV per 128 keys of a KV head.
  *   float32: float32 throughout on the vector ALUs, 16 lanes per (row,
  *            query head) for dQ and per (key, KV head) for dK and dV.

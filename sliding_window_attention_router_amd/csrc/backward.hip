@@ -10,12 +10,12 @@
 //   dV_j = sum_i P_ij dO_i   (K, V gradients summed over the query heads of
 //   a KV head).
 //
-// bfloat16, on the matrix cores (three launches):
+// bfloat16, on the matrix cores (two launches):
 //   bwd_q_mfma_kernel   a workgroup per 128 query rows of a head: one online
 //                       pass over 64-key blocks gives dQ, LSE and D (the
-//                       latter two go to the workspace); launched for the
-//                       gate=0 rows in token order and for the gate=1 rows
-//                       gathered from the compacted list
+//                       latter two go to the workspace); the gate=1 rows
+//                       gathered from the compacted list, then the gate=0
+//                       rows in token order, in one grid
 //   bwd_kv_mfma_kernel  a workgroup per 128 keys of a KV head walks 64-row
 //                       tiles of the rows that see them (window rows of every
 //                       gate, then gathered gate=1 rows) for each query head
@@ -649,15 +649,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma_kernel(BwdArgs a) 
 // and at the end dQ = scale dq / l, LSE = m + log2(l), D = <dO, O> (formed
 // from the same registers before the pass).  K is read both ways (plain
 // rows for the scores, ds_read_b64_tr_b16 for K^T), with the swizzle of
-// KvTile.  kFar = false: rows in token order, only gate=0 rows written
-// (their keys are the window); kFar = true: the gate=1 rows of the head's
-// gate group, gathered from the compacted list (keys [0, i]), heaviest
-// tiles first.
+// KvTile.  One launch holds both kinds of tile: the first ntile * B * Hq
+// workgroups take the gate=1 rows of their head's gate group, gathered from
+// the compacted list (keys [0, i]), heaviest tiles first; the rest take rows
+// in token order and write only the gate=0 ones (their keys are the window).
+// The long gathered tiles are dispatched first and the short window tiles
+// fill the slots that they leave idle.
 // ---------------------------------------------------------------------------
 constexpr int kQRows = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kQKeys = 64;   // keys per LDS block
 
-template <int D, bool kFar>
+template <int D>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma_kernel(BwdArgs a) {
   using L = KvTile<D>;
   constexpr int KS = D / 16;
@@ -673,13 +675,15 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma_kernel(BwdArgs a) {
   // workgroups are dealt to the 8 XCDs in turn: give the workgroups of one
   // XCD neighbouring heads (the query heads of a KV head), which read the
   // same keys
-  const int jh = blockIdx.x % nbh;
+  const bool kFar = int(blockIdx.x) < ntile * nbh;
+  const int wg = kFar ? int(blockIdx.x) : int(blockIdx.x) - ntile * nbh;
+  const int jh = wg % nbh;
   const int bh = nbh % 8 == 0 ? (jh % 8) * (nbh / 8) + jh / 8 : jh;
   const int b = bh / a.Hq, h = bh % a.Hq, kvh = h / a.HK, g = h / a.HG;
   const int32_t* list = a.idx + (int64_t(b) * a.G + g) * a.N;
-  int tile = blockIdx.x / nbh;
+  int tile = wg / nbh;
   int n = 0;
-  if constexpr (kFar) {
+  if (kFar) {
     n = a.cnt[b * a.G + g];
     tile = ntile - 1 - tile;  // the last gathered tiles hold the longest rows: first
     if (tile * kQRows >= n) return;  // workgroup-uniform, before any barrier
@@ -688,7 +692,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma_kernel(BwdArgs a) {
   const int slot = tile * kQRows + wave * 32 + rl;
   int row, lo, hi;
   bool act;
-  if constexpr (kFar) {
+  if (kFar) {
     act = slot < n;
     row = list[act ? slot : n - 1];
     lo = 0;
@@ -701,7 +705,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma_kernel(BwdArgs a) {
   }
   // key blocks of the workgroup: the union of its rows' ranges
   int wlo, whi;
-  if constexpr (kFar) {
+  if (kFar) {
     wlo = 0;
     whi = list[min(n, tile * kQRows + kQRows) - 1];
   } else {
@@ -844,9 +848,7 @@ static hipError_t run_backward(BwdArgs& a, hipStream_t s) {
   hipError_t e;
   if constexpr (std::is_same<T, bf16_t>::value) {
     const int64_t nq = (int64_t(a.N) + kQRows - 1) / kQRows * a.B * a.Hq;
-    hipLaunchKernelGGL((bwd_q_mfma_kernel<D, false>), dim3(unsigned(nq)), dim3(kBwdThreads), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_q_mfma_kernel<D, true>), dim3(unsigned(nq)), dim3(kBwdThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_q_mfma_kernel<D>), dim3(unsigned(2 * nq)), dim3(kBwdThreads), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nkb = (int64_t(a.N) + kKvKeys - 1) / kKvKeys;
     hipLaunchKernelGGL((bwd_kv_mfma_kernel<D>), dim3(unsigned(nkb * a.B * a.Hkv)), dim3(kBwdThreads), 0, s,
