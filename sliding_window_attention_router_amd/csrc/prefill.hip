@@ -584,6 +584,7 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
     const int bu = m[0], t = m[1], n = m[2];
     for (int c = 0; c < n; ++c) {
       const int it = off[bu * cmax + c] + t - first[bu * cmax + c];
+      if (it >= a.max_items) continue;  // cannot happen: the plan's bound
       sv.item_tile[it] = bu * TT + t;
       sv.item_chunk[it] = c;
     }
@@ -595,7 +596,7 @@ __global__ __launch_bounds__(kSchedThreads) void far_schedule_kernel(PrefillArgs
       sv.off[x] = off_sh[x];
     }
   if (tid == 0) {
-    a.sched[0] = items;
+    a.sched[0] = min(items, a.max_items);
     a.sched[1] = cb;
     a.sched[2] = NA;
   }
@@ -1059,9 +1060,19 @@ bool plan_prefill(const PrefillShape& sh, PrefillPlan* p) {
   p->far_tiles = (sh.N + p->tpt_far - 1) / p->tpt_far;
   const long long nT = (long long)sh.B * p->units * p->far_tiles;
   p->target_items = sh.both_branch ? kTargetItemsAll : kTargetItems;
-  // chunks of at least max(8, total / kTargetItemsAll) blocks: at most
-  // kTargetItemsAll items plus one partial chunk per tile
-  const long long max_items = kTargetItemsAll + nT;
+  // Item bound.  The schedule cuts chunks of cb = max(8, min(c, cap))
+  // blocks, c = ceil(total / target), cap = max(kMaxChunkBlocks,
+  // ceil(total / kTargetItemsAll)), so total / cb <= kTargetItemsAll, and
+  // total / cb <= target while c <= kMaxChunkBlocks; a tile adds at most one
+  // partial chunk.  A tile has at most N / 64 + 1 far blocks, so when
+  // nT (N / 64 + 1) <= kMaxChunkBlocks target no gate can need more than
+  // target + nT items.  The far grid is sized by this bound, and its idle
+  // workgroups delay the window workers behind them (about 15 us for 4320
+  // of them at N = 4096).
+  const long long bmax = sh.N / kBN + 1;
+  const long long lim =
+      nT * bmax <= (long long)kMaxChunkBlocks * p->target_items ? p->target_items : kTargetItemsAll;
+  const long long max_items = lim + nT;
   if (max_items > INT_MAX / kRows) return false;
   p->max_items = int(max_items);
   // chunks per tile <= ceil(ceil(N / 64) / kMinChunkBlocks)

@@ -122,3 +122,24 @@ def test_many_units_schedule_tables_in_global_memory():
         err = max(err, max_abs(Oh[b:b + 1, rows], ref))
     say(f"  {rows.size} rows x {B} sequences x {H} heads: max-abs {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+def test_dense_gate_near_the_item_bound():
+    """Gate all 1 through the hard-gate path at N=8192 (GQA 16/4, W=1024):
+    the far schedule cuts about 1900 items, close to the bound the plan sizes
+    its far grid and partial buffers by for this shape (1024 + one per far
+    tile = 2048).  Sampled rows of every head against the oracle."""
+    d, W = 128, 1024
+    say(f"dense gate near the item bound: N={N} Hq={HQ} Hkv={HKV} d={d} W={W}")
+    w = synth.long_prefill(seed=48, N=N, Hq=HQ, Hkv=HKV, d=d, W=W, p=0.13)
+    gate = np.ones_like(w.gate)
+    bf = torch.bfloat16
+    O, _ = swa().prefill(dev(w.Q, bf), dev(w.K, bf), dev(w.V, bf), dev(gate), W)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(W - 8, W + 72), np.arange(N - 80, N),
+                                     np.random.default_rng(49).integers(0, N, 120)]))
+    ref = oracle.prefill(w.Q, w.K, w.V, gate, W, rows=rows)["O"]
+    err = max_abs(host(O)[:, rows], ref)
+    say(f"  {rows.size} rows x {HQ} heads: max-abs {err:.3e}")
+    assert err <= TOL["bf16"]
+
