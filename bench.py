@@ -329,10 +329,24 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+LEAD_CYCLES = 1_000_000  # about 0.4-0.5 ms of GPU clock
+
+
+def gpu_lead():
+    """Keep the GPU busy for a moment ahead of a start event (a bounded spin
+    kernel), so that the host's enqueueing of the timed calls, which follows,
+    is not inside the timed region: the events then bracket GPU work only,
+    as in the back-to-back timed steps."""
+    import torch
+    torch.cuda._sleep(LEAD_CYCLES)
+
+
 def time_ms(fn, iters, flush=None):
     """Median and minimum of the time of fn() between two events recorded on
     the launch stream (torch's current stream, which the binding launches
-    on); with `flush`, that buffer is rewritten before every run."""
+    on); with `flush`, that buffer is rewritten before every run (the write
+    also keeps the GPU busy while the run is enqueued), else a spin kernel
+    precedes the start event."""
     import torch
     fn()
     torch.cuda.synchronize()
@@ -340,6 +354,8 @@ def time_ms(fn, iters, flush=None):
     for _ in range(iters):
         if flush is not None:
             flush.fill_(1)
+        else:
+            gpu_lead()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         fn()
@@ -616,6 +632,7 @@ def backward_run(swa, Q, K, V, O, gate, idx, cnt, W, pairs, steps):
     torch.cuda.synchronize()
     times = []
     for _ in range(steps):
+        gpu_lead()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         swa.prefill_backward(Q, K, V, O, dO, gate, W, idx=idx, cnt=cnt, out=out, workspace=ws)
@@ -657,6 +674,7 @@ def router_grad_run(swa, Q, K, V, W, H, r, bias, steps):
     torch.cuda.synchronize()
     times = []
     for _ in range(steps):
+        gpu_lead()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         swa.router_backward(dO, O_full, O_swa, z, H, r, out=out, workspace=ws)
