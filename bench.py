@@ -539,6 +539,7 @@ def serve_run(swa, q, Kc, Vc, cache_len, r, bias, W, steps):
     # small copy before each step, outside its events); one synchronisation
     # at the end
     evs = []
+    gpu_lead()
     for _ in range(steps):
         L.copy_(before)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -590,6 +591,7 @@ def anchors_run(swa, Q, K, V, gate, idx, cnt, W, A, q_d, Kc, Vc, len_d, gate_d, 
             e.record()
         sets.append(ev)
     torch.cuda.synchronize()
+    gpu_lead()
     for ev in sets:
         run(ev)
     torch.cuda.synchronize()
@@ -721,6 +723,7 @@ def both_branch_run(swa, Q, K, V, gate, W, steps, H, r, bias):
             e.record()
         sets.append(ev)
     torch.cuda.synchronize()
+    gpu_lead()
     for ev in sets:
         swa.prefill(Q, K, V, gate, W, both_branch=True, out=O, diff=diff, workspace=ws, events=ev[:5])
         swa.regularizer(z, nll, diff, out=loss)
