@@ -644,10 +644,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma_kernel(BwdArgs a) 
 //   step exceeds it; dq and the sum rescaled then), p = 2^(S sl2 - m),
 //   dS^T = p (dP^T - D)
 //   dQ^T += K^T dS^T                        (channels x queries, k = keys)
-// so only one step's scores are held (251-252 VGPRs at d = 128, no AGPRs:
-// two waves per SIMD), and a step with none of the wave's pairs is skipped.
-// and at the end dQ = scale dq / l, LSE = m + log2(l), D = <dO, O> (formed
-// from the same registers before the pass).  K is read both ways (plain
+// so only one step's scores are held (246 VGPRs at d = 128, no AGPRs: two
+// waves per SIMD), and a step with none of the wave's pairs is skipped.  At
+// the end dQ = scale dq / l, LSE = m + log2(l), D = <dO, O> (formed from
+// the same registers before the pass).  K is read both ways (plain
 // rows for the scores, ds_read_b64_tr_b16 for K^T), with the swizzle of
 // KvTile.  One launch holds both kinds of tile: the first ntile * B * Hq
 // workgroups take the gate=1 rows of their head's gate group, gathered from
@@ -675,15 +675,15 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma_kernel(BwdArgs a) {
   // workgroups are dealt to the 8 XCDs in turn: give the workgroups of one
   // XCD neighbouring heads (the query heads of a KV head), which read the
   // same keys
-  const bool kFar = int(blockIdx.x) < ntile * nbh;
-  const int wg = kFar ? int(blockIdx.x) : int(blockIdx.x) - ntile * nbh;
+  const bool far = int(blockIdx.x) < ntile * nbh;
+  const int wg = far ? int(blockIdx.x) : int(blockIdx.x) - ntile * nbh;
   const int jh = wg % nbh;
   const int bh = nbh % 8 == 0 ? (jh % 8) * (nbh / 8) + jh / 8 : jh;
   const int b = bh / a.Hq, h = bh % a.Hq, kvh = h / a.HK, g = h / a.HG;
   const int32_t* list = a.idx + (int64_t(b) * a.G + g) * a.N;
   int tile = wg / nbh;
   int n = 0;
-  if (kFar) {
+  if (far) {
     n = a.cnt[b * a.G + g];
     tile = ntile - 1 - tile;  // the last gathered tiles hold the longest rows: first
     if (tile * kQRows >= n) return;  // workgroup-uniform, before any barrier
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma_kernel(BwdArgs a) {
   const int slot = tile * kQRows + wave * 32 + rl;
   int row, lo, hi;
   bool act;
-  if (kFar) {
+  if (far) {
     act = slot < n;
     row = list[act ? slot : n - 1];
     lo = 0;
@@ -705,7 +705,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma_kernel(BwdArgs a) {
   }
   // key blocks of the workgroup: the union of its rows' ranges
   int wlo, whi;
-  if (kFar) {
+  if (far) {
     wlo = 0;
     whi = list[min(n, tile * kQRows + kQRows) - 1];
   } else {
