@@ -764,7 +764,13 @@ SWI_DEV constexpr int acc_channel(int md, int i, int g) {
 // Store this lane's half of an output row: the two lanes of a row swap
 // 4-channel groups first (v_permlane32_swap), so that lane g holds channels
 // 16g .. 16g + 15 of each 32-channel tile and writes them as two 16-byte
-// stores.
+// stores.  Group i4 of a lane holds channels 8 i4 + 4 g .. + 3.  One swap
+// of (group k, group k + 2) exchanges the upper half-wave of the first
+// operand with the lower half-wave of the second, which leaves in both
+// results exactly the pieces the lane stores: lane group 0 keeps its group k
+// (first result) and receives group k of lane group 1 (second result); lane
+// group 1 receives group k + 2 of lane group 0 (first) and keeps its own
+// (second): channels 16 g + 8 k .. + 7 in order, for either group.
 template <int MD>
 SWI_DEV void store_row(bf16_t* orow, const f32x16 (&acc)[MD], float inv, int g) {
   typedef uint32_t u32x4_ __attribute__((ext_vector_type(4)));
@@ -780,26 +786,12 @@ SWI_DEV void store_row(bf16_t* orow, const f32x16 (&acc)[MD], float inv, int g) 
       pk[i4][0] = w[0];
       pk[i4][1] = w[1];
     }
-    // lane group 0 sends groups 2, 3; lane group 1 sends groups 0, 1
-    uint32_t rv[2][2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t out = g ? pk[k][h] : pk[k + 2][h];
-        const auto r = __builtin_amdgcn_permlane32_swap(out, out, false, false);
-        rv[k][h] = g ? r[0] : r[1];
-      }
-    u32x4_ s0, s1;
-    if (g == 0) {
-      s0 = u32x4_{pk[0][0], pk[0][1], rv[0][0], rv[0][1]};
-      s1 = u32x4_{pk[1][0], pk[1][1], rv[1][0], rv[1][1]};
-    } else {
-      s0 = u32x4_{rv[0][0], rv[0][1], pk[2][0], pk[2][1]};
-      s1 = u32x4_{rv[1][0], rv[1][1], pk[3][0], pk[3][1]};
+    for (int k = 0; k < 2; ++k) {
+      const auto r0 = __builtin_amdgcn_permlane32_swap(pk[k][0], pk[k + 2][0], false, false);
+      const auto r1 = __builtin_amdgcn_permlane32_swap(pk[k][1], pk[k + 2][1], false, false);
+      *reinterpret_cast<u32x4_*>(orow + md * 32 + 16 * g + 8 * k) = u32x4_{r0[0], r1[0], r0[1], r1[1]};
     }
-    *reinterpret_cast<u32x4_*>(orow + md * 32 + 16 * g) = s0;
-    *reinterpret_cast<u32x4_*>(orow + md * 32 + 16 * g + 8) = s1;
   }
 }
 template <int MD>
