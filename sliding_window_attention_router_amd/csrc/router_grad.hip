@@ -50,6 +50,22 @@ SWI_DEV void load8(const float* p, float (&x)[8]) {
     x[4 + j] = b[j];
   }
 }
+// The same for data read once: the non-temporal hint keeps the stream out
+// of the caches.
+SWI_DEV void load8_nt(const bf16_t* p, float (&x)[8]) {
+  const bf16x8 v = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = float(v[j]);
+}
+SWI_DEV void load8_nt(const float* p, float (&x)[8]) {
+  const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = a[j];
+    x[4 + j] = b[j];
+  }
+}
 SWI_DEV void store8(bf16_t* p, const float (&x)[8]) {
   bf16x8 v;
 #pragma unroll
@@ -69,7 +85,11 @@ SWI_DEV float sigmoid_grad(float x) {
   return u / (v * v);
 }
 
-template <typename T>
+// PPL > 0: a group has exactly PPL * 64 pieces of 8 elements, so a lane
+// issues all 3 PPL of its loads before the first product (one memory round
+// trip per token and group); PPL = 0: any size, piece by piece.  Either way
+// a lane sums its pieces in the same order.
+template <typename T, int PPL>
 __global__ __launch_bounds__(kRgThreads) void router_grad_token_kernel(const T* dO, const T* Of,
                                                                        const T* Os, const float* z,
                                                                        const T* r, float* dz, T* dH,
@@ -84,14 +104,29 @@ __global__ __launch_bounds__(kRgThreads) void router_grad_token_kernel(const T* 
     const int64_t base = t * row;
     for (int g = 0; g < G; ++g) {
       float acc = 0.f;
-      for (int p = lane; p < pieces; p += kWave) {
-        const int64_t e = base + int64_t(g) * per_group + int64_t(p) * 8;
-        float a[8], f[8], w[8];
-        load8(dO + e, a);
-        load8(Of + e, f);
-        load8(Os + e, w);
+      if constexpr (PPL > 0) {
+        float a[PPL][8], f[PPL][8], w[PPL][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc = fmaf(a[j], f[j] - w[j], acc);
+        for (int k = 0; k < PPL; ++k) {
+          const int64_t e = base + int64_t(g) * per_group + int64_t(lane + kWave * k) * 8;
+          load8_nt(dO + e, a[k]);
+          load8_nt(Of + e, f[k]);
+          load8_nt(Os + e, w[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < PPL; ++k)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc = fmaf(a[k][j], f[k][j] - w[k][j], acc);
+      } else {
+        for (int p = lane; p < pieces; p += kWave) {
+          const int64_t e = base + int64_t(g) * per_group + int64_t(p) * 8;
+          float a[8], f[8], w[8];
+          load8_nt(dO + e, a);
+          load8_nt(Of + e, f);
+          load8_nt(Os + e, w);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc = fmaf(a[j], f[j] - w[j], acc);
+        }
       }
       const float sgrp = wave_sum(acc);
       const float v = sgrp * sigmoid_grad(z[t * G + g]);
@@ -102,13 +137,22 @@ __global__ __launch_bounds__(kRgThreads) void router_grad_token_kernel(const T* 
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    // dH row: 8 consecutive hidden units per lane and step (hidden % 8 == 0)
+    // dH row: 8 consecutive hidden units per lane and step (hidden % 8 == 0);
+    // with one group the 8 weights are one 16-byte piece of r
     for (int p = lane; p < hidden / 8; p += kWave) {
       float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int g = 0; g < G; ++g) {
-        const float v = s_dz[wave][g];
+      if (G == 1) {
+        float rr[8];
+        load8(r + int64_t(p) * 8, rr);
+        const float v = s_dz[wave][0];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = fmaf(v, Elem<T>::load(r + int64_t(p * 8 + j) * G + g), o[j]);
+        for (int j = 0; j < 8; ++j) o[j] = fmaf(v, rr[j], o[j]);
+      } else {
+        for (int g = 0; g < G; ++g) {
+          const float v = s_dz[wave][g];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[j] = fmaf(v, Elem<T>::load(r + int64_t(p * 8 + j) * G + g), o[j]);
+        }
       }
       store8(dH + t * hidden + int64_t(p) * 8, o);
     }
@@ -137,7 +181,7 @@ __global__ __launch_bounds__(kRgThreads) void router_grad_weight_kernel(const T*
       accb += w;
       if (cols) {
         float h[8];
-        load8(H + t * hidden + k0, h);
+        load8_nt(H + t * hidden + k0, h);
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = fmaf(w, h[j], acc[j]);
       }
@@ -195,8 +239,16 @@ static hipError_t run_router_grad(const T* dO, const T* Of, const T* Os, const f
   const int64_t waves = ntok;
   const int64_t want = (waves + (kRgThreads / kWave) - 1) / (kRgThreads / kWave);
   const int grid = int(want < 8192 ? want : 8192);
-  hipLaunchKernelGGL((router_grad_token_kernel<T>), dim3(grid), dim3(kRgThreads), 0, s, dO, Of, Os, z, r,
-                     dz, dH, ntok, row, hidden, G);
+  const int pieces = row / G / 8;
+  if (pieces == 4 * kWave)
+    hipLaunchKernelGGL((router_grad_token_kernel<T, 4>), dim3(grid), dim3(kRgThreads), 0, s, dO, Of, Os, z,
+                       r, dz, dH, ntok, row, hidden, G);
+  else if (pieces == 2 * kWave)
+    hipLaunchKernelGGL((router_grad_token_kernel<T, 2>), dim3(grid), dim3(kRgThreads), 0, s, dO, Of, Os, z,
+                       r, dz, dH, ntok, row, hidden, G);
+  else
+    hipLaunchKernelGGL((router_grad_token_kernel<T, 0>), dim3(grid), dim3(kRgThreads), 0, s, dO, Of, Os, z,
+                       r, dz, dH, ntok, row, hidden, G);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t splits = (ntok + kSplitTokens - 1) / kSplitTokens;

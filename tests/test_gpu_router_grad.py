@@ -77,6 +77,8 @@ CASES = [
     (1, 1, 4, 128, 64, 4, "bf16"),       # one token, one head per group
     (3, 130, 12, 64, 96, 3, "f32"),      # float32, three groups of four heads
     (1, 517, 2, 64, 2056, 1, "f32"),     # hidden past one column block
+    (1, 300, 16, 64, 128, 1, "bf16"),    # 2 x 64 pieces of 8 elements per group: loads issued together
+    (2, 77, 16, 128, 64, 1, "f32"),      # 4 x 64 pieces per group, float32
 ]
 
 
