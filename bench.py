@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--extra-steps", type=int, default=5,
                     help="timed runs of each extra configuration (layer, gate bounds, structured routing, "
                          "decode densities; after the timed steps; 0 = skip)")
+    ap.add_argument("--stage-steps", type=int, default=20,
+                    help="steps run after the timed ones with the library's stage events, for the "
+                         "per-kernel times")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB before the steps "
                          "(a known-size reference for hardware byte counters)")
@@ -195,16 +198,24 @@ def main():
         return evs
 
     def step(ev=None):
-        # ev: 9 events: [route start] + prefill stages 0..3 + decode stages 0..2 + [end]
+        # ev: 3 events: [route start, prefill end = decode start, decode end]
         if ev is not None:
             ev[0].record()
         swa.route(H, r, bias, out=(gate, idx, cnt))
-        swa.prefill(Q, K, V, gate, W, idx=idx, cnt=cnt, out=O, workspace=ws_p,
-                    events=ev[1:5] if ev is not None else None)
-        swa.decode(q_d, Kc, Vc, len_d, gate_d, W, out=o_d, workspace=ws_d,
-                   events=ev[5:8] if ev is not None else None)
+        swa.prefill(Q, K, V, gate, W, idx=idx, cnt=cnt, out=O, workspace=ws_p)
         if ev is not None:
-            ev[8].record()
+            ev[1].record()
+        swa.decode(q_d, Kc, Vc, len_d, gate_d, W, out=o_d, workspace=ws_d)
+        if ev is not None:
+            ev[2].record()
+
+    def staged_step(ev):
+        # ev: 9 events: [route start] + prefill stages 0..3 + decode stages 0..2 + [end]
+        ev[0].record()
+        swa.route(H, r, bias, out=(gate, idx, cnt))
+        swa.prefill(Q, K, V, gate, W, idx=idx, cnt=cnt, out=O, workspace=ws_p, events=ev[1:5])
+        swa.decode(q_d, Kc, Vc, len_d, gate_d, W, out=o_d, workspace=ws_d, events=ev[5:8])
+        ev[8].record()
 
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -217,7 +228,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evsets = [new_events(9) for _ in range(args.steps)]
+    evsets = [new_events(3) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
@@ -225,9 +236,21 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     print(f"[bench] {args.steps} timed steps in {wall:.3f}s", file=sys.stderr, flush=True)
+    prefill_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evsets]))
+    decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evsets]))
+    step_ms = wall * 1e3 / args.steps
+
+    # Per-kernel times from further steps with the library's stage events
+    # (each event between two launches lengthens the step by a few us, so
+    # the timed steps above carry none).
+    stsets = [new_events(9) for _ in range(max(1, args.stage_steps))]
+    torch.cuda.synchronize()
+    for ev in stsets:
+        staged_step(ev)
+    torch.cuda.synchronize()
 
     def avg(i, j):
-        return float(np.mean([e[i].elapsed_time(e[j]) for e in evsets]))
+        return float(np.mean([e[i].elapsed_time(e[j]) for e in stsets]))
 
     t = {
         "route_compact": avg(0, 1),
@@ -237,9 +260,6 @@ def main():
         "decode_splitk": avg(5, 6),
         "decode_merge": avg(6, 7),
     }
-    prefill_ms = avg(0, 4)
-    decode_ms = avg(5, 7)
-    step_ms = wall * 1e3 / args.steps
 
     g_host = gate.cpu().numpy()
     useful, band_pairs, far_pairs = prefill_pairs(g_host, W, Hq, G)
@@ -582,14 +602,30 @@ def anchors_run(swa, Q, K, V, gate, idx, cnt, W, A, q_d, Kc, Vc, len_d, gate_d, 
         swa.decode(q_d, Kc, Vc, len_d, gate_d, W, out=o, workspace=ws_d, anchors=A,
                    events=ev[4:7] if ev is not None else None)
 
+    def new_sets(n):
+        sets = []
+        for _ in range(steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+            for e in ev:
+                e.record()
+            sets.append(ev)
+        return sets
+
     run()
     torch.cuda.synchronize()
-    sets = []
-    for _ in range(steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
-        for e in ev:
-            e.record()
-        sets.append(ev)
+    # whole calls first, with events only around them; then the stage times
+    # from the library's events (which lengthen a call by a few us)
+    ends = new_sets(3)
+    torch.cuda.synchronize()
+    gpu_lead()
+    for ev in ends:
+        ev[0].record()
+        swa.prefill(Q, K, V, gate, W, idx=idx, cnt=cnt, out=O, workspace=ws_p, anchors=A)
+        ev[1].record()
+        swa.decode(q_d, Kc, Vc, len_d, gate_d, W, out=o, workspace=ws_d, anchors=A)
+        ev[2].record()
+    torch.cuda.synchronize()
+    sets = new_sets(7)
     torch.cuda.synchronize()
     gpu_lead()
     for ev in sets:
@@ -599,7 +635,9 @@ def anchors_run(swa, Q, K, V, gate, idx, cnt, W, A, q_d, Kc, Vc, len_d, gate_d, 
     def avg(i, j):
         return float(np.mean([ev[i].elapsed_time(ev[j]) for ev in sets]))
 
-    pre_ms, attn_ms, dec_ms, split_ms = avg(0, 3), avg(1, 2), avg(4, 6), avg(4, 5)
+    pre_ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in ends]))
+    dec_ms = float(np.mean([ev[1].elapsed_time(ev[2]) for ev in ends]))
+    attn_ms, split_ms = avg(1, 2), avg(4, 5)
     useful = prefill_pairs(gate.cpu().numpy(), W, Hq, G, A)[0]
     flop = 4.0 * d * useful
     dbytes, keys = decode_bytes(dec["gate"], dec["cache_len"], W, Hq, Hkv, d, A=A)
