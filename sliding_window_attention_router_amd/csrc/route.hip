@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ H,
 // 16-byte loads (kTok rows x the vectors it owns) before reducing, and the
 // weight vectors a lane owns are loaded once.  Same per-lane order and xor
 // tree as route_kernel.
-constexpr int kTok = 4;
+constexpr int kTok = 1;  // tokens per wave (1 measured fastest: more waves in flight than 2, 3, 4 or 8)
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void route_g1_kernel(const T* __restrict__ H,
                                                        const T* __restrict__ r,
