@@ -560,6 +560,18 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma_kernel(BwdArgs a) 
           dp[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, vreg[ks], dp[rt], 0, 0, 0);
         }
       }
+      // instruction order for the scheduler: eight operand reads ahead, then
+      // each product followed by the next read (LDS latency covered by the
+      // products instead of waited for before each one)
+      constexpr int kMfS = 2 * RT * KS;  // products and operand reads of this phase
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
+#pragma unroll
+      for (int i = 0; i < kMfS - 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       // P and dS of rows 16 rt + 4 grp + i; slot (rt % 2) * 4 + i of the
       // 32-row step rt / 2 of the second products.  A tile of gathered rows
       // without padding sees every key of the workgroup (its rows lie past
@@ -606,6 +618,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma_kernel(BwdArgs a) 
           dk[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, sb[st], dk[ct], 0, 0, 0);
         }
       }
+      // the same for the second products: eight transposing reads ahead,
+      // then two reads after each product
+      constexpr int kMfP = 2 * CT * (RT / 2);  // products; twice as many reads
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < kMfP - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (more) store_info(lds[(t + 1) & 1]);
       if (t + 2 < nt) put_row(rowbuf[t & 1]);
     }
