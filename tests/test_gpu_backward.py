@@ -176,3 +176,51 @@ def test_prefill_backward_32k_layer():
         bound = REL["bf16"] * float(np.abs(r).max())
         say(f"  {keys.size} sampled {name} keys x {Hkv} KV heads: max-abs {err:.3e} (bound {bound:.3e})")
         assert err <= bound
+
+
+@pytest.mark.parametrize("Hq,Hkv,G,d,W,p", [
+    (16, 4, 1, 128, 1024, 0.13),   # the long-prefill heads at a quarter of its length
+    (16, 16, 2, 64, 256, 0.3),     # MHA, two gate groups, d=64
+])
+def test_prefill_backward_8k_sampled(Hq, Hkv, G, d, W, p):
+    """N=8192: the dQ grid holds 64 row tiles per head of each kind (gathered
+    gate=1 rows, heaviest first, then the window rows), dK/dV 128 key blocks
+    per KV head, so every grid runs in several waves of workgroups.  Two runs
+    bitwise equal; sampled dQ rows (start, window edge, end, routed and
+    unrouted) and sampled dK, dV keys of every KV head against the
+    reference."""
+    N, B = 8192, 1
+    say(f"backward N={N} Hq={Hq} Hkv={Hkv} G={G} d={d} W={W} p={p}")
+    rng = np.random.default_rng(93)
+    w = synth.long_prefill(seed=94, N=N, Hq=Hq, Hkv=Hkv, d=d, W=W, p=p)
+    gate = (rng.random((B, N, G)) < p).astype(np.uint8) if G > 1 else w.gate
+    dO = synth.round_bf16(rng.standard_normal(w.Q.shape, dtype=np.float32))
+    bf = torch.bfloat16
+    Qg, Kg, Vg, dOg, gg = dev(w.Q, bf), dev(w.K, bf), dev(w.V, bf), dev(dO, bf), dev(gate)
+    O, _ = swa().prefill(Qg, Kg, Vg, gg, W)
+    g1 = swa().prefill_backward(Qg, Kg, Vg, O, dOg, gg, W)
+    g2 = swa().prefill_backward(Qg, Kg, Vg, O, dOg, gg, W)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b), "two runs differ"
+    dQ, dK, dV = (host(x) for x in g1)
+    assert np.all(np.isfinite(dQ)) and np.all(np.isfinite(dK)) and np.all(np.isfinite(dV))
+    routed = np.flatnonzero(gate[0, :, 0])
+    unrouted = np.flatnonzero(gate[0, :, 0] == 0)
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(W - 3, W + 3), np.arange(N - 4, N),
+                                     rng.choice(routed, 24, replace=False),
+                                     rng.choice(unrouted, 24, replace=False)]))
+    ref = oracle.prefill_backward_rows(w.Q, w.K, w.V, gate, W, dO, rows)
+    err = max_abs(dQ[:, rows], ref)
+    bound = REL["bf16"] * float(np.abs(ref).max())
+    say(f"  {rows.size} sampled dQ rows x {Hq} heads: max-abs {err:.3e} (bound {bound:.3e})")
+    assert err <= bound
+    keys = np.array([0, 1, 64, W - 1, W, N // 3, N // 2, N - W - 1, N - W, N - 65, N - 1])
+    refk = oracle.prefill_backward_keys(w.Q, w.K, w.V, gate, W, dO, keys)
+    for name, got in (("dK", dK), ("dV", dV)):
+        r = refk[name]
+        err = max_abs(got[:, keys], r)
+        bound = REL["bf16"] * float(np.abs(r).max())
+        say(f"  {keys.size} sampled {name} keys x {Hkv} KV heads: max-abs {err:.3e} (bound {bound:.3e})")
+        assert err <= bound
+
