@@ -667,7 +667,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma_kernel(BwdArgs a) 
 //   step exceeds it; dq and the sum rescaled then), p = 2^(S sl2 - m),
 //   dS^T = p (dP^T - D)
 //   dQ^T += K^T dS^T                        (channels x queries, k = keys)
-// so only one step's scores are held (246 VGPRs at d = 128, no AGPRs: two
+// so only one step's scores are held (237 VGPRs at d = 128, no AGPRs: two
 // waves per SIMD), and a step with none of the wave's pairs is skipped.  At
 // the end dQ = scale dq / l, LSE = m + log2(l), D = <dO, O> (formed from
 // the same registers before the pass).  K is read both ways (plain
@@ -737,6 +737,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma_kernel(BwdArgs a) {
   }
   const int kb0 = wlo / kQKeys, kb1 = whi / kQKeys;
   const int vlo = wave_min_i(act ? lo : INT_MAX), vhi = wave_max_i(act ? hi : -1);  // this wave's keys
+  // keys every active row of the wave sees: [flo, fhi]
+  const int flo = wave_max_i(act ? lo : INT_MIN), fhi = wave_min_i(act ? hi : INT_MAX);
   const int64_t qrs = int64_t(a.Hq) * D;
   const int64_t qoff = (int64_t(b) * a.N + row) * qrs + int64_t(h) * D + 8 * hf;
   bf16x8 qreg[KS], oreg[KS];
@@ -797,12 +799,20 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma_kernel(BwdArgs a) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, oreg[ks], dp, 0, 0, 0);
       }
-      // element i: key key0 + 8 (i/4) + 4 hf + i%4
+      // element i: key key0 + 8 (i/4) + 4 hf + i%4.  Masking only rewrites
+      // the scores, in a wave-uniform branch skipped by steps whose keys
+      // every active row sees.
+      if (key0 < flo || key0 + 31 > fhi) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+          if (key < lo || key > hi) s[i] = kNegInf;
+        }
+      }
       float bmax = kNegInf;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = key0 + 8 * (i >> 2) + 4 * hf + (i & 3);
-        const float x = (key >= lo && key <= hi) ? s[i] * a.sl2 : kNegInf;
+        const float x = s[i] * a.sl2;
         s[i] = x;
         bmax = fmaxf(bmax, x);
       }
@@ -819,10 +829,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma_kernel(BwdArgs a) {
       }
       // dS^T of k-steps st = 2 mt + j (slot e: key 16 st + 8 (e/4) + 4 hf + e%4)
       bf16x8 sb[2];
+      const float mu = m == kNegInf ? 0.f : m;  // -inf while no key was seen: p = 0 then
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float x = s[i];
-        const float p = x == kNegInf ? 0.f : fast_exp2(x - m);
+        const float p = fast_exp2(x - mu);
         l += p;
         sb[i >> 3][i & 7] = bf16_t(p * (dp[i] - Dv));
       }
