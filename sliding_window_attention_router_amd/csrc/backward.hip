@@ -573,9 +573,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma_kernel(BwdArgs a) 
 #pragma unroll
       for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       // P and dS of rows 16 rt + 4 grp + i; slot (rt % 2) * 4 + i of the
-      // 32-row step rt / 2 of the second products.  A tile of gathered rows
-      // without padding sees every key of the workgroup (its rows lie past
-      // the window rows: i >= k0 + 63 + W), so it skips the visibility test.
+      // 32-row step rt / 2 of the second products.  Two kinds of tile see
+      // every key of the workgroup and skip the visibility test: gathered
+      // rows without padding (they lie past the window rows: i >= k0 + 63 + W)
+      // and window tiles t >= 1 whose last row still has key k0 in its
+      // window (k0 + 64 t + 63 - W + 1 <= k0) and lies before N.
       const float* info = reinterpret_cast<const float*>(qt + L::kInfo);
       typedef int i32x4 __attribute__((ext_vector_type(4)));
       bf16x8 pb[RT / 2], sb[RT / 2];
@@ -600,7 +602,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma_kernel(BwdArgs a) 
           }
         }
       };
-      if (t >= nwt && f0 + (t - nwt + 1) * kRT <= n)
+      if ((t >= nwt && f0 + (t - nwt + 1) * kRT <= n) ||
+          (t >= 1 && (t + 1) * kRT <= a.W && k0 + (t + 1) * kRT <= a.N))
         p_ds(std::true_type{});
       else
         p_ds(std::false_type{});

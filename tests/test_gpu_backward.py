@@ -53,6 +53,10 @@ CASES = [
     # window and gathered tiles per key block for dK, dV; ragged N
     (1, 1531, 8, 2, 2, 128, 200, 0.3, "bf16"),
     (2, 777, 4, 4, 1, 64, 97, 0.5, "bf16"),
+    # W a multiple of the 64-row tile: row tiles whose rows all see a key
+    # block's 64 keys border tiles that do not, on both sides
+    (1, 705, 4, 2, 1, 128, 128, 0.2, "bf16"),
+    (1, 650, 4, 4, 2, 64, 192, 0.0, "bf16"),
 ]
 
 
