@@ -373,7 +373,7 @@ SWI_DEV s16x4 lds_tr16(const char* p) {
 // Q^T) come from two ds_read_b64_tr_b16 each with the same row order
 // (within 16 lanes, source lane 4r + k points at row r, channels
 // c0 + 4k .. c0 + 4k + 3, and lane i receives channel c0 + i of rows
-// 0..3).  With 221 VGPRs a wave (d = 128; no AGPRs, no scratch) two
+// 0..3).  With 243 VGPRs a wave (d = 128; no AGPRs, no scratch) two
 // workgroups share a CU: two waves per SIMD, so one wave's exponentials and
 // conversions can overlap the other's products.
 // Layout of the row tiles (Kv16Tile), from LDS bank-conflict counts measured
