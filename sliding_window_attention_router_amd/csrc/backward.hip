@@ -16,10 +16,10 @@
 //                       latter two go to the workspace); the gate=1 rows
 //                       gathered from the compacted list, then the gate=0
 //                       rows in token order, in one grid
-//   bwd_kv_mfma_kernel  a workgroup per 128 keys of a KV head walks 64-row
-//                       tiles of the rows that see them (window rows of every
-//                       gate, then gathered gate=1 rows) for each query head
-//                       and accumulates dK, dV
+//   bwd_kv_mfma_kernel  a workgroup per 64 keys of a KV head (16 a wave)
+//                       walks 64-row tiles of the rows that see them (window
+//                       rows of every gate, then gathered gate=1 rows) for
+//                       each query head and accumulates dK, dV
 // float32, on the vector ALU (three launches):
 //   bwd_row_kernel  one 16-lane group per (token, query head): one online
 //                   pass over S_i gives dQ_i, LSE_i and D_i; launched for
