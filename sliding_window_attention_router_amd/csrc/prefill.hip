@@ -28,12 +28,20 @@
 // visited twice with different keys), and the far part of a gate=1 row
 // shrinks to [A, i-W].
 //
+// Per-layer window offsets (weimeta SWA glossary, section
+// "两个核心工程参数（W 和步长 S）详解"): with an offset o the window
+// of query i is that of query i - o, [max(0, i-o-W+1), i-o] (empty for
+// i < o); a gate=1 row still takes all of [0, i], the keys (i-o, i] in its
+// window pass (window_row).
+//
 // Both-branch mode: the same launches with every row taking the full
 // branch (no compaction: the far tiles are consecutive positions).  The
 // merge then also writes the per-(head, token) squared distance between
 // O_FULL and O_SWA, and replaces the window output only where the gate is
 // 1; diff_kernel sums the distance over heads (the regulariser paragraph
-// of the same section uses this distance).
+// of the same section uses this distance).  On request the same pass also
+// writes both branch outputs of every row, O_FULL and O_SWA (the router
+// gradient's inputs; store_branches and the merge).
 #include <atomic>
 #include <climits>
 #include <type_traits>
