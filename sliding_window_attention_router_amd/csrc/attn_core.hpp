@@ -24,9 +24,7 @@
 namespace swi {
 
 constexpr int kBN = 64;  // keys per LDS block
-#ifndef SWI_MFMA_PRIO
-#define SWI_MFMA_PRIO 1  // wave issue priority inside MFMA sections
-#endif
+constexpr int kMfmaPrio = 1;  // wave issue priority inside MFMA sections
 constexpr int kQR = 32;  // query rows per wave
 
 template <typename T, int D>
@@ -301,7 +299,7 @@ struct CoreBF16 {
     f32x16 s[2];
     // Issue priority: a wave raises it for its MFMA sections, so the SIMD's
     // other wave fills the VALU while the matrix pipe stays busy.
-    __builtin_amdgcn_s_setprio(SWI_MFMA_PRIO);
+    __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       s[mt] = f32x16{};
@@ -322,7 +320,7 @@ struct CoreBF16 {
     // k-step st covers keys 16st..16st+15; lane group g supplies quarters
     // 4st+g and 4st+g+2, stored adjacently (Lds::vq_offset)
     const char* vt = lds + L::kKBytes;
-    __builtin_amdgcn_s_setprio(SWI_MFMA_PRIO);
+    __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
       const char* vp = vt + (md * 32 + q) * L::kVStride + g * 16;
@@ -578,7 +576,7 @@ struct CoreBF16Dma {
     read_k<0>(ka, a0);
     lds_wait(a0);
     if (KS == 8) read_k<1>(ka, a1);
-    __builtin_amdgcn_s_setprio(SWI_MFMA_PRIO);
+    __builtin_amdgcn_s_setprio(kMfmaPrio);
     if (KS == 8) {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
@@ -626,7 +624,7 @@ struct CoreBF16Dma {
       va[md] = base + (L::v_pos(4 * g + r, md * 4 + 2 * hh + (k >> 1)) - L::kKBytes) + (k & 1) * 8;
     s16x4 v0[8], v1[8];
     read_v<0>(va[0], v0);
-    __builtin_amdgcn_s_setprio(SWI_MFMA_PRIO);
+    __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
       s16x4(&cur)[8] = (md & 1) ? v1 : v0;

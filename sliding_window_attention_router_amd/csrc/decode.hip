@@ -20,6 +20,12 @@
 //                      written there; a pair cut by share boundaries leaves a
 //                      normalised partial output + log-sum-exp per piece
 // decode_merge_kernel  log-sum-exp merge of the pieces of each cut pair
+// step_prep_kernel     serving step: routes each sequence's new token,
+//                      appends its key and value rows and advances the
+//                      length, ahead of the two launches above
+// The allocation-free entry point runs the same launches on a fixed
+// per-device scratch array instead of a caller workspace.  With a window
+// offset o a window head takes the window of position L-1-o.
 //
 // Global anchors (weimeta SWA glossary, section "SWA 落地的四个常见坑",
 // pitfall 1, fix 2): with A > 0 a window head also reads the first
@@ -36,9 +42,8 @@ namespace swi {
 
 constexpr int kDecThreads = 64;  // one wave per workgroup
 constexpr int kDecGrid = 1024;   // four single-wave workgroups per CU (bf16: 32 KB LDS each)
-#ifndef SWI_DEC_STREAM
-#define SWI_DEC_STREAM true
-#endif
+// K/V rows carry the non-temporal hint: the cache is read once per step.
+constexpr bool kDecStream = true;
 
 struct DecodeArgs {
   const void* q;
@@ -205,14 +210,14 @@ struct DecCfg;
 template <int D>
 struct DecCfg<bf16_t, D> {
   using Core = CoreBF16Dma<D>;
-  using Loader = KVRegDma<D, kDecThreads, SWI_DEC_STREAM>;
+  using Loader = KVRegDma<D, kDecThreads, kDecStream>;
   static constexpr int kLds = LdsDma<D>::kBytes;
   static constexpr bool kSplit = true;
 };
 template <int D>
 struct DecCfg<float, D> {
   using Core = CoreF32<D>;
-  using Loader = DecF32Stage<D, SWI_DEC_STREAM>;
+  using Loader = DecF32Stage<D, kDecStream>;
   static constexpr int kLds = Lds<float, D>::kBytes;
   static constexpr bool kSplit = false;
 };
