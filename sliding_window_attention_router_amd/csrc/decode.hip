@@ -386,7 +386,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int G) 
   T* obase = static_cast<T*>(a.o) + (int64_t(b) * a.Hq + kvh * a.HK) * D;
   // pieces are read in batches of kBatch with all loads in flight; the
   // running maximum is raised once per batch
-  constexpr int kBatch = 16;
+  constexpr int kBatch = 32;  // a full-cache pair at 32K keys has about 24 pieces
   for (int e0 = 2 * threadIdx.x; e0 < a.HK * D; e0 += 512) {
     const int r = e0 / D;
     float M = kNegInf, Ls = 0.f, o0 = 0.f, o1 = 0.f;
