@@ -459,7 +459,7 @@ int swiattn_router_backward(const void* dO, const void* O_full, const void* O_sw
  *            where they become operands of the dV, dQ and dK products.
  *            One launch for dQ (the gathered gate=1 rows first, then the
  *            gate=0 rows; it also writes LSE and D to the workspace), one
- *            for dK and dV per 128 keys of a KV head.
+ *            for dK and dV (a workgroup per 64 keys of a KV head).
  *   float32: float32 throughout on the vector ALUs, 16 lanes per (row,
  *            query head) for dQ and per (key, KV head) for dK and dV.
  * Outputs must not overlap inputs.
