@@ -326,6 +326,10 @@ DECODE_CASES = [
     (40, 200, 4, 2, 1, 128, 32, [int(x) for x in np.random.default_rng(11).integers(1, 61, 40)], "bf16"),
     # 400 (sequence, KV head) pairs, ragged: pairs cut across several shares
     (100, 2048, 8, 4, 2, 64, 300, [int(x) for x in np.random.default_rng(12).integers(1, 2049, 100)], "bf16"),
+    # fewer blocks than workgroups and a full 4096-key sequence: its pairs are
+    # cut into 64 one-block pieces each, more than one merge batch
+    (2, 4096, 4, 2, 1, 128, 256, [4096, 3000], "bf16"),
+    (1, 2600, 2, 1, 1, 64, 100, [2600], "f32"),
 ]
 
 
